@@ -1,0 +1,311 @@
+// Host side of libsvq: argument validation, the one-time repack of a
+// canonical SVQ matrix into coded units (svq_internal.h), and dispatch of the
+// decode-and-multiply kernels.  Method: "SAGE: Pushing 2-Bit Vector-Quantized
+// LLMs toward Real-World Usability", Fig. 2 caption (what a code holds) and
+// Fig. 6 caption (subvectors multiply reordered activations).
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <vector>
+
+#include "../../include/svq.h"
+#include "svq_internal.h"
+
+namespace svq {
+int gemm_m_pad(int m);
+hipError_t launch_moe(const svq_handle *experts, int32_t num_experts, const void *x, int64_t ldx,
+                      int32_t x_per_slot, const int32_t *expert_ids, int64_t m, int32_t topk,
+                      void *y, int64_t ldy, int ydt, void *ws, size_t ws_bytes, hipStream_t s,
+                      size_t *need);
+}
+
+using namespace svq;
+
+namespace {
+
+constexpr uint32_t FIELD_MASK = (1u << 18) - 1;
+
+// IEEE binary16 -> float (exact).
+float half_to_float(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h >> 15) << 31;
+  const uint32_t exp = (h >> 10) & 0x1F, frac = h & 0x3FF;
+  uint32_t u;
+  if (exp == 0) {
+    if (frac == 0) {
+      u = sign;
+    } else {  // subnormal: frac * 2^-24, normalise
+      int e = -1;
+      uint32_t f = frac;
+      do {
+        f <<= 1;
+        ++e;
+      } while ((f & 0x400) == 0);
+      u = sign | ((uint32_t)(127 - 15 - e) << 23) | ((f & 0x3FF) << 13);
+    }
+  } else if (exp == 0x1F) {
+    u = sign | 0x7F800000u | (frac << 13);
+  } else {
+    u = sign | ((exp + 112) << 23) | (frac << 13);
+  }
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// float -> bfloat16 bits, round to nearest even.
+uint16_t float_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFF) ? 0x40 : 0));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct Layout {
+  int32_t n_tiles, units;
+  size_t off_dtab, off_rtab, off_btab, off_perm, off_codes, padded_code_bytes, bytes;
+};
+
+Layout make_layout(int32_t n, int32_t k) {
+  Layout L;
+  L.n_tiles = (n + UNIT_ROWS - 1) / UNIT_ROWS;
+  L.units = (k + UNIT_SLOTS - 1) / UNIT_SLOTS;
+  size_t off = 0;
+  L.off_dtab = off;
+  off += align256(DTAB_BYTES);
+  L.off_rtab = off;
+  off += align256(RTAB_BYTES);
+  L.off_btab = off;
+  off += align256(BTAB_BYTES);
+  L.off_perm = off;
+  off += align256((size_t)k * 2);
+  L.off_codes = off;
+  L.padded_code_bytes = (size_t)L.n_tiles * L.units * UNIT_BYTES;
+  off += align256(L.padded_code_bytes);
+  L.bytes = off;
+  return L;
+}
+
+svq_status validate_desc(const svq_matrix_desc *d) {
+  if (!d) return SVQ_ERR_INVALID_ARG;
+  if (d->n <= 0 || d->k <= 0 || d->k % 8 != 0) return SVQ_ERR_INVALID_ARG;
+  if (d->bd + d->br != 10) return SVQ_ERR_INVALID_ARG;
+  if (d->bd < 6 || d->bd > 8) return SVQ_ERR_UNSUPPORTED;
+  if (d->k > SVQ_MAX_K || d->n > SVQ_MAX_N) return SVQ_ERR_UNSUPPORTED;
+  if (!d->codes || !d->dir_codebook || !d->radius_table || !d->perm) return SVQ_ERR_INVALID_ARG;
+  std::vector<uint8_t> seen((size_t)d->k, 0);
+  for (int32_t p = 0; p < d->k; ++p) {
+    const int32_t c = d->perm[p];
+    if (c < 0 || c >= d->k || seen[(size_t)c]) return SVQ_ERR_INVALID_ARG;
+    seen[(size_t)c] = 1;
+  }
+  return SVQ_OK;
+}
+
+svq_status validate_handle(const svq_handle *w) {
+  if (!w || !w->dev) return SVQ_ERR_INVALID_ARG;
+  if (w->n <= 0 || w->k <= 0 || w->k % 8 != 0 || w->bd < 6 || w->bd > 8 || w->bd + w->br != 10)
+    return SVQ_ERR_INVALID_ARG;
+  const Layout L = make_layout(w->n, w->k);
+  if (w->n_tiles != L.n_tiles || w->units != L.units || w->off_codes != L.off_codes ||
+      w->off_dtab != L.off_dtab || w->off_rtab != L.off_rtab || w->off_btab != L.off_btab ||
+      w->off_perm != L.off_perm || w->bytes != L.bytes)
+    return SVQ_ERR_INVALID_ARG;
+  return SVQ_OK;
+}
+
+// Build the whole packed image on the host.
+void build_image(const svq_matrix_desc *d, const Layout &L, std::vector<uint8_t> &img) {
+  img.assign(L.bytes, 0);
+  const uint32_t dmask = (1u << d->bd) - 1;
+  const int nr = 1 << d->br;
+  // direction rows by low index byte
+  uint16_t *dtab = (uint16_t *)(img.data() + L.off_dtab);
+  for (int b = 0; b < 256; ++b)
+    for (int l = 0; l < 8; ++l) dtab[b * 8 + l] = d->dir_codebook[(b & dmask) * 8 + l];
+  uint16_t *rtab = (uint16_t *)(img.data() + L.off_rtab);
+  for (int r = 0; r < nr; ++r) rtab[r] = d->radius_table[r];
+  // bf16 products by full 10-bit index: R*D is exact in float (22 bits)
+  uint16_t *btab = (uint16_t *)(img.data() + L.off_btab);
+  for (int idx = 0; idx < 1024; ++idx) {
+    const int dd = idx & (int)dmask, r = idx >> d->bd;
+    const float R = half_to_float(d->radius_table[r]);
+    for (int l = 0; l < 8; ++l)
+      btab[idx * 8 + l] = float_to_bf16(R * half_to_float(d->dir_codebook[dd * 8 + l]));
+  }
+  uint16_t *perm = (uint16_t *)(img.data() + L.off_perm);
+  for (int p = 0; p < d->k; ++p) perm[p] = (uint16_t)d->perm[p];
+
+  // coded units
+  const int64_t C = d->k / 8;
+  const uint8_t *st = d->codes;
+  const size_t nbytes = ((size_t)d->n * (size_t)C * 18 + 7) / 8;
+  uint8_t *codes = img.data() + L.off_codes;
+  for (int64_t i = 0; i < d->n; ++i) {
+    const int64_t rt = i / UNIT_ROWS, rho = i % UNIT_ROWS;
+    for (int64_t c = 0; c < C; ++c) {
+      const uint64_t bit = (uint64_t)(i * C + c) * 18;
+      const size_t byte = bit >> 3;
+      uint32_t wv = st[byte];
+      if (byte + 1 < nbytes) wv |= (uint32_t)st[byte + 1] << 8;
+      if (byte + 2 < nbytes) wv |= (uint32_t)st[byte + 2] << 16;
+      const uint32_t code = (wv >> (bit & 7)) & FIELD_MASK;
+      const int64_t u = c / UNIT_CODES, cc = c % UNIT_CODES;
+      const int q = (int)(cc & 3), kb = (int)(cc >> 2);
+      const int lane = (int)rho + 16 * q;
+      uint8_t *ub = codes + ((size_t)rt * L.units + (size_t)u) * UNIT_BYTES;
+      uint32_t *S = (uint32_t *)(ub + PLANE_SIGN + 16 * lane);
+      for (int j = 0; j < 4; ++j) {
+        S[j] |= ((code >> (2 * j)) & 1u) << (15 - kb);
+        S[j] |= ((code >> (2 * j + 1)) & 1u) << (31 - kb);
+      }
+      const uint32_t idx = code >> 8;
+      ub[PLANE_LOW + 16 * lane + kb] = (uint8_t)(idx & 0xFF);
+      uint32_t *H = (uint32_t *)(ub + PLANE_HIGH + 4 * lane);
+      *H |= (idx >> 8) << (2 * kb);
+    }
+  }
+}
+
+MatView view_of(const svq_handle *w) {
+  MatView v;
+  v.base = (const uint8_t *)w->dev;
+  v.off_dtab = (uint32_t)w->off_dtab;
+  v.off_rtab = (uint32_t)w->off_rtab;
+  v.off_btab = (uint32_t)w->off_btab;
+  v.off_perm = (uint32_t)w->off_perm;
+  v.off_codes = w->off_codes;
+  v.n = w->n;
+  v.k = w->k;
+  v.bd = w->bd;
+  v.n_tiles = w->n_tiles;
+  v.units = w->units;
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *svq_status_string(svq_status s) {
+  switch (s) {
+    case SVQ_OK: return "ok";
+    case SVQ_ERR_INVALID_ARG: return "invalid argument";
+    case SVQ_ERR_UNSUPPORTED: return "unsupported";
+    case SVQ_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case SVQ_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+svq_status svq_pack(const svq_matrix_desc *src, void *dst_dev, size_t *dst_bytes, svq_handle *out,
+                    void *stream) {
+  if (!dst_bytes) return SVQ_ERR_INVALID_ARG;
+  const svq_status st = validate_desc(src);
+  if (st != SVQ_OK) return st;
+  const Layout L = make_layout(src->n, src->k);
+  if (!dst_dev) {
+    *dst_bytes = L.bytes;
+    return SVQ_OK;
+  }
+  if (*dst_bytes < L.bytes) {
+    *dst_bytes = L.bytes;
+    return SVQ_ERR_BUFFER_TOO_SMALL;
+  }
+  if (!out) return SVQ_ERR_INVALID_ARG;
+  std::vector<uint8_t> img;
+  build_image(src, L, img);
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(dst_dev, img.data(), L.bytes, hipMemcpyHostToDevice, s) != hipSuccess)
+    return SVQ_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return SVQ_ERR_HIP;
+  std::memset(out, 0, sizeof(*out));
+  out->dev = dst_dev;
+  out->n = src->n;
+  out->k = src->k;
+  out->bd = src->bd;
+  out->br = src->br;
+  out->n_tiles = L.n_tiles;
+  out->units = L.units;
+  out->off_dtab = L.off_dtab;
+  out->off_rtab = L.off_rtab;
+  out->off_btab = L.off_btab;
+  out->off_perm = L.off_perm;
+  out->off_codes = L.off_codes;
+  out->code_bytes = ((uint64_t)src->n * (uint64_t)(src->k / 8) * 18 + 7) / 8;
+  out->padded_code_bytes = L.padded_code_bytes;
+  out->bytes = L.bytes;
+  *dst_bytes = L.bytes;
+  return SVQ_OK;
+}
+
+svq_status svq_linear(const svq_handle *w, const void *x, int64_t m, int64_t ldx, void *y,
+                      int64_t ldy, svq_dtype ydt, void *workspace, size_t *workspace_bytes,
+                      void *stream) {
+  if (!workspace_bytes) return SVQ_ERR_INVALID_ARG;
+  const svq_status st = validate_handle(w);
+  if (st != SVQ_OK) return st;
+  if (m < 1 || m > (1 << 24) || ldx < w->k || ldy < w->n) return SVQ_ERR_INVALID_ARG;
+  if (ydt != SVQ_BF16 && ydt != SVQ_F32) return SVQ_ERR_INVALID_ARG;
+  const size_t Kp = (size_t)w->units * UNIT_SLOTS;
+  size_t need;
+  const bool exact = m <= EXACT_MAX_M;
+  int m_pad = 0;
+  if (exact) {
+    need = align256((size_t)m * Kp * 2) + 256;
+  } else {
+    m_pad = gemm_m_pad((int)m);
+    need = align256((size_t)m_pad * Kp * 2);
+  }
+  if (!workspace) {
+    *workspace_bytes = need;
+    return SVQ_OK;
+  }
+  if (*workspace_bytes < need) return SVQ_ERR_BUFFER_TOO_SMALL;
+  if (!x || !y) return SVQ_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const MatView v = view_of(w);
+  hipError_t e;
+  if (exact) {
+    uint16_t *xw = (uint16_t *)workspace;
+    int32_t *esc = (int32_t *)((uint8_t *)workspace + align256((size_t)m * Kp * 2));
+    e = launch_prep_exact(v, (const uint16_t *)x, ldx, (int)m, xw, esc, s);
+    if (e == hipSuccess) e = launch_gemv_exact(v, xw, esc, (int)m, y, ldy, (int)ydt, s);
+  } else {
+    uint16_t *xb = (uint16_t *)workspace;
+    e = launch_prep_bf16(v, (const uint16_t *)x, ldx, (int)m, m_pad, xb, s);
+    if (e == hipSuccess) e = launch_gemm_bf16(v, xb, (int)m, m_pad, y, ldy, (int)ydt, s);
+  }
+  return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+}
+
+svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts, const void *x,
+                          int64_t ldx, int32_t x_per_slot, const int32_t *expert_ids, int64_t m,
+                          int32_t topk, void *y, int64_t ldy, svq_dtype ydt, void *workspace,
+                          size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes || !experts) return SVQ_ERR_INVALID_ARG;
+  if (num_experts < 1 || num_experts > MAX_EXPERTS) return SVQ_ERR_UNSUPPORTED;
+  if (topk < 1 || topk > num_experts || m < 1 || m > (1 << 20)) return SVQ_ERR_INVALID_ARG;
+  if (x_per_slot != 0 && x_per_slot != 1) return SVQ_ERR_INVALID_ARG;
+  if (ydt != SVQ_BF16 && ydt != SVQ_F32) return SVQ_ERR_INVALID_ARG;
+  for (int32_t e = 0; e < num_experts; ++e) {
+    const svq_status st = validate_handle(&experts[e]);
+    if (st != SVQ_OK) return st;
+    if (experts[e].n != experts[0].n || experts[e].k != experts[0].k) return SVQ_ERR_INVALID_ARG;
+  }
+  if (ldx < experts[0].k || ldy < experts[0].n) return SVQ_ERR_INVALID_ARG;
+  size_t need = 0;
+  hipError_t e = launch_moe(experts, num_experts, x, ldx, x_per_slot, expert_ids, m, topk, y, ldy,
+                            (int)ydt, nullptr, 0, (hipStream_t)stream, &need);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return SVQ_OK;
+  }
+  if (*workspace_bytes < need) return SVQ_ERR_BUFFER_TOO_SMALL;
+  if (!x || !y || !expert_ids) return SVQ_ERR_INVALID_ARG;
+  e = launch_moe(experts, num_experts, x, ldx, x_per_slot, expert_ids, m, topk, y, ldy, (int)ydt,
+                 workspace, *workspace_bytes, (hipStream_t)stream, &need);
+  return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Internal layout and launch interfaces of libsvq (not part of the public ABI).
+//
+// Packed matrix buffer (all offsets 256-byte aligned, see svq_handle):
+//
+//   dtab   256 x 8 fp16   row b = D[b & ((1<<bd)-1)]: the direction row picked
+//                         by the low byte of a code's 10-bit index
+//   rtab   16 fp16        R[r], zero padded to 16 entries
+//   btab   1024 x 8 bf16  row idx = RNE_bf16(R[idx >> bd] * D[idx & mask][l])
+//   perm   k uint16       slot p takes input channel perm[p]
+//   codes  n_tiles x units coded units of UNIT_BYTES each
+//
+// A coded unit covers 16 output rows x 64 consecutive codes (512 permuted
+// input slots).  It is laid out for one wavefront of 64 lanes: lane L owns
+// row (L & 15) of the tile and, for i = 0..15, the code in column
+// 64*u + 4*i + (L >> 4).  That is exactly the B operand of a
+// v_mfma_*_16x16x32 instruction for K-block i (lane L holds 8 consecutive k
+// of column L & 15), so a lane decodes straight into MFMA registers.
+// The 18 bits of the lane's 16 codes are split into three planes so that
+// every lane reads them with three coalesced loads:
+//
+//   bytes    0..1023  sign plane: lane L's 16 bytes are dwords S0..S3;
+//                     bit (15-i) of S_j = sign bit 2j of code i,
+//                     bit (31-i) of S_j = sign bit 2j+1 of code i,
+//                     so (S_j << i) carries the two signs of pair j of code
+//                     i at the fp16/bf16 sign positions 15 and 31
+//   bytes 1024..2047  index-low plane: byte i of lane L's 16 bytes = low 8
+//                     bits of code i's 10-bit index (direction | radius<<bd)
+//   bytes 2048..2303  index-high plane: bits 2i..2i+1 of lane L's dword =
+//                     index bits 8..9 of code i
+//
+// 64 codes x 18 bits = 2304 bytes: the layout keeps 18 bits per 8 weights.
+// Padding codes (rows >= n, slots >= k) are zero.
+#pragma once
+#include <stdint.h>
+#include <stddef.h>
+#include <hip/hip_runtime.h>
+
+namespace svq {
+
+constexpr int UNIT_ROWS = 16;
+constexpr int UNIT_CODES = 64;
+constexpr int UNIT_SLOTS = UNIT_CODES * 8;  // 512 permuted input slots
+constexpr int UNIT_BYTES = 2304;
+constexpr int PLANE_SIGN = 0;
+constexpr int PLANE_LOW = 1024;
+constexpr int PLANE_HIGH = 2048;
+constexpr int DTAB_BYTES = 256 * 16;
+constexpr int RTAB_BYTES = 256;   // 16 fp16, padded
+constexpr int BTAB_BYTES = 1024 * 16;
+constexpr int EXACT_MAX_M = 4;    // m <= 4: exact fp32 decode path
+constexpr int MAX_EXPERTS = 256;
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Matrix view passed to kernels by value.
+struct MatView {
+  const uint8_t *base;  // packed buffer
+  uint32_t off_dtab, off_rtab, off_btab, off_perm;
+  uint64_t off_codes;
+  int32_t n, k, bd;
+  int32_t n_tiles, units;
+};
+
+// ---- dense path ---------------------------------------------------------
+// Exact path (m <= 4): prep writes xw = fp16(x[a][perm[p]] * 2^e_a) for
+// p < units*512 (zero beyond k) and e_a; the GEMV kernel multiplies.
+hipError_t launch_prep_exact(const MatView &w, const uint16_t *x, int64_t ldx, int m,
+                             uint16_t *xw, int32_t *escale, hipStream_t s);
+hipError_t launch_gemv_exact(const MatView &w, const uint16_t *xw, const int32_t *escale, int m,
+                             void *y, int64_t ldy, int ydt, hipStream_t s);
+
+// bf16 path (m > 4): prep writes xb = x[row][perm[p]] (bf16), zero padded to
+// m_pad rows and units*512 slots; the GEMM kernel multiplies.
+hipError_t launch_prep_bf16(const MatView &w, const uint16_t *x, int64_t ldx, int m, int m_pad,
+                            uint16_t *xb, hipStream_t s);
+hipError_t launch_gemm_bf16(const MatView &w, const uint16_t *xb, int m, int m_pad,
+                            void *y, int64_t ldy, int ydt, hipStream_t s);
+
+// ---- MoE ----------------------------------------------------------------
+struct ExpertTable {
+  const uint8_t *base[MAX_EXPERTS];
+  uint8_t bd[MAX_EXPERTS];
+};
+
+struct MoeShape {
+  uint32_t off_dtab, off_rtab, off_btab, off_perm;
+  uint64_t off_codes;
+  int32_t n, k, n_tiles, units;
+  int32_t num_experts;
+};
+
+}  // namespace svq

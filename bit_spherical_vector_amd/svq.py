@@ -1,0 +1,255 @@
+"""Thin Python binding of libsvq (ctypes).
+
+Argument marshalling only: every step of the decode-and-multiply runs in the
+HIP library.  PyTorch supplies device memory and streams.  The C functions
+keep their names (``svq_pack``, ``svq_linear``, ``svq_moe_linear``); the
+``pack``/``linear``/``moe_linear`` helpers below only allocate the
+caller-owned buffers with torch and pass pointers.
+
+If ``libsvq.so`` is missing the import of this module raises: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+# torch is imported before libsvq.so is loaded so that both bind to one HIP
+# runtime: torch ships its own libamdhip64 with the same SONAME, and a
+# second copy loaded later would not share device allocations or streams.
+import torch  # noqa: F401
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsvq.so")
+
+SVQ_OK = 0
+SVQ_ERR_INVALID_ARG = -1
+SVQ_ERR_UNSUPPORTED = -2
+SVQ_ERR_BUFFER_TOO_SMALL = -3
+SVQ_ERR_HIP = -4
+SVQ_BF16 = 0
+SVQ_F32 = 1
+
+EXPORTED = ("svq_pack", "svq_linear", "svq_moe_linear", "svq_status_string")
+
+
+class SvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+class MatrixDesc(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("bd", ctypes.c_int32), ("br", ctypes.c_int32),
+        ("codes", ctypes.c_void_p), ("dir_codebook", ctypes.c_void_p),
+        ("radius_table", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+    ]
+
+
+class Handle(ctypes.Structure):
+    _fields_ = [
+        ("dev", ctypes.c_void_p),
+        ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("bd", ctypes.c_int32), ("br", ctypes.c_int32),
+        ("n_tiles", ctypes.c_int32), ("units", ctypes.c_int32),
+        ("off_dtab", ctypes.c_uint64), ("off_rtab", ctypes.c_uint64),
+        ("off_btab", ctypes.c_uint64), ("off_perm", ctypes.c_uint64),
+        ("off_codes", ctypes.c_uint64), ("code_bytes", ctypes.c_uint64),
+        ("padded_code_bytes", ctypes.c_uint64), ("bytes", ctypes.c_uint64),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "or python -m bit_spherical_vector_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.svq_status_string.restype = ctypes.c_char_p
+    lib.svq_status_string.argtypes = [ctypes.c_int]
+    lib.svq_pack.restype = ctypes.c_int
+    lib.svq_pack.argtypes = [ctypes.POINTER(MatrixDesc), ctypes.c_void_p,
+                             ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(Handle),
+                             ctypes.c_void_p]
+    lib.svq_linear.restype = ctypes.c_int
+    lib.svq_linear.argtypes = [ctypes.POINTER(Handle), ctypes.c_void_p, ctypes.c_int64,
+                               ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                               ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
+    lib.svq_moe_linear.restype = ctypes.c_int
+    lib.svq_moe_linear.argtypes = [ctypes.POINTER(Handle), ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
+    return lib
+
+
+LIB = _load()
+
+
+def status_string(status: int) -> str:
+    return LIB.svq_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != SVQ_OK:
+        raise SvqError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# C calls with their own names (pointers and sizes in, status out)
+# ---------------------------------------------------------------------------
+
+def svq_pack(desc: MatrixDesc, dst_dev: Optional[int], dst_bytes: int,
+             handle: Optional[Handle], stream: int) -> tuple:
+    nbytes = ctypes.c_size_t(dst_bytes)
+    st = LIB.svq_pack(ctypes.byref(desc), dst_dev, ctypes.byref(nbytes),
+                      ctypes.byref(handle) if handle is not None else None, stream)
+    return st, nbytes.value
+
+
+def svq_linear(handle: Handle, x_ptr: int, m: int, ldx: int, y_ptr: int, ldy: int, ydt: int,
+               ws_ptr: Optional[int], ws_bytes: int, stream: int) -> tuple:
+    nbytes = ctypes.c_size_t(ws_bytes)
+    st = LIB.svq_linear(ctypes.byref(handle), x_ptr, m, ldx, y_ptr, ldy, ydt, ws_ptr,
+                        ctypes.byref(nbytes), stream)
+    return st, nbytes.value
+
+
+def svq_moe_linear(handles, num_experts: int, x_ptr: int, ldx: int, x_per_slot: int,
+                   ids_ptr: int, m: int, topk: int, y_ptr: int, ldy: int, ydt: int,
+                   ws_ptr: Optional[int], ws_bytes: int, stream: int) -> tuple:
+    nbytes = ctypes.c_size_t(ws_bytes)
+    st = LIB.svq_moe_linear(handles, num_experts, x_ptr, ldx, x_per_slot, ids_ptr, m, topk,
+                            y_ptr, ldy, ydt, ws_ptr, ctypes.byref(nbytes), stream)
+    return st, nbytes.value
+
+
+# ---------------------------------------------------------------------------
+# torch-side helpers (allocation of caller-owned buffers only)
+# ---------------------------------------------------------------------------
+
+def _stream_handle(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def make_desc(n: int, k: int, bd: int, br: int, codes: np.ndarray, codebook: np.ndarray,
+              radius: np.ndarray, perm: np.ndarray) -> tuple:
+    """Build a MatrixDesc over host numpy arrays (kept alive in the result)."""
+    keep = (np.ascontiguousarray(codes, dtype=np.uint8),
+            np.ascontiguousarray(codebook, dtype=np.uint16),
+            np.ascontiguousarray(radius, dtype=np.uint16),
+            np.ascontiguousarray(perm, dtype=np.int32))
+    desc = MatrixDesc(n, k, bd, br, keep[0].ctypes.data, keep[1].ctypes.data,
+                      keep[2].ctypes.data, keep[3].ctypes.data)
+    return desc, keep
+
+
+class PackedMatrix:
+    """A packed SVQ matrix: torch device buffer + svq_handle."""
+
+    def __init__(self, buf, handle: Handle):
+        self.buf = buf
+        self.handle = handle
+
+    @property
+    def n(self) -> int:
+        return self.handle.n
+
+    @property
+    def k(self) -> int:
+        return self.handle.k
+
+    @property
+    def code_bytes(self) -> int:
+        return int(self.handle.code_bytes)
+
+    @property
+    def padded_code_bytes(self) -> int:
+        return int(self.handle.padded_code_bytes)
+
+
+def pack(mat, device="cuda", stream=None) -> PackedMatrix:
+    """Pack a canonical matrix (any object with n, k, bd, br, codes, codebook,
+    radius, perm attributes, e.g. ``synth.MatrixInputs``)."""
+    import torch
+    desc, keep = make_desc(mat.n, mat.k, mat.bd, mat.br, mat.codes, mat.codebook, mat.radius,
+                           mat.perm)
+    st, nbytes = svq_pack(desc, None, 0, None, 0)
+    _check(st, "svq_pack (size query)")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    h = Handle()
+    st, _ = svq_pack(desc, buf.data_ptr(), nbytes, h, _stream_handle(stream))
+    _check(st, "svq_pack")
+    del keep
+    return PackedMatrix(buf, h)
+
+
+def linear_workspace_bytes(pm: PackedMatrix, m: int) -> int:
+    st, nbytes = svq_linear(pm.handle, None, m, pm.k, None, pm.n, SVQ_BF16, None, 0, 0)
+    _check(st, "svq_linear (workspace query)")
+    return nbytes
+
+
+def linear(pm: PackedMatrix, x, out=None, out_dtype=None, workspace=None, stream=None):
+    """y = x @ What^T.  x: bf16 [m, >=k] CUDA tensor (row stride = x.stride(0))."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    m = x.shape[0]
+    if out is None:
+        dt = out_dtype or torch.bfloat16
+        out = torch.empty((m, pm.n), dtype=dt, device=x.device)
+    ydt = SVQ_F32 if out.dtype == torch.float32 else SVQ_BF16
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(1) != 1:
+        raise ValueError("out must be bf16 or fp32 with unit column stride")
+    need = linear_workspace_bytes(pm, m)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st, _ = svq_linear(pm.handle, x.data_ptr(), m, x.stride(0), out.data_ptr(), out.stride(0),
+                       ydt, workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
+    _check(st, "svq_linear")
+    return out
+
+
+def handle_array(pms: Sequence[PackedMatrix]):
+    arr = (Handle * len(pms))()
+    for i, pm in enumerate(pms):
+        arr[i] = pm.handle
+    return arr
+
+
+def moe_workspace_bytes(handles, num_experts: int, m: int, topk: int, x_per_slot: int) -> int:
+    st, nbytes = svq_moe_linear(handles, num_experts, None, handles[0].k, x_per_slot, None, m,
+                                topk, None, handles[0].n, SVQ_BF16, None, 0, 0)
+    _check(st, "svq_moe_linear (workspace query)")
+    return nbytes
+
+
+def moe_linear(pms: Sequence[PackedMatrix], x, expert_ids, topk: int, x_per_slot: bool,
+               out=None, out_dtype=None, workspace=None, handles=None, stream=None):
+    """One MoE projection: y[q] = x[row(q)] @ What_{ids[q]}^T for every slot q."""
+    import torch
+    if handles is None:
+        handles = handle_array(pms)
+    n_exp = len(handles)
+    s_total = expert_ids.numel()
+    m = s_total // topk
+    n = handles[0].n
+    if out is None:
+        out = torch.empty((s_total, n), dtype=out_dtype or torch.bfloat16, device=x.device)
+    ydt = SVQ_F32 if out.dtype == torch.float32 else SVQ_BF16
+    need = moe_workspace_bytes(handles, n_exp, m, topk, int(x_per_slot))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st, _ = svq_moe_linear(handles, n_exp, x.data_ptr(), x.stride(0), int(x_per_slot),
+                           expert_ids.data_ptr(), m, topk, out.data_ptr(), out.stride(0), ydt,
+                           workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
+    _check(st, "svq_moe_linear")
+    return out

@@ -1,0 +1,164 @@
+/*
+ * libsvq - spherical vector quantization (SVQ) decode-and-multiply for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described in "SAGE: Pushing 2-Bit Vector-Quantized
+ * LLMs toward Real-World Usability" (cited below as "SAGE").  Each subvector
+ * of 8 weights is coded as 8 sign bits, a direction index into a per-matrix
+ * codebook and an index into a per-matrix table of quantized radii, with a
+ * per-matrix split of 10 index bits between the two (SAGE, Fig. 2 caption;
+ * 18 bits per 8 weights = 2.25 bits per weight, SAGE Table 1, SPHQuant row).
+ * Weights are rebuilt on demand inside the product, never stored decoded
+ * (SAGE, Fig. 1 and Fig. 5 captions), and the 8 inputs of a subvector are
+ * reordered activations (SAGE, Fig. 6 caption).
+ *
+ * Canonical input format (the pages leave it open; this is the library's
+ * contract, identical to the CPU oracle shipped with the tests):
+ *
+ *   - code g = i*(k/8) + c covers row i, permuted slots 8c..8c+7, and occupies
+ *     bits [18g, 18g+18) of the code stream; stream bit t is bit (t % 8) of
+ *     byte t / 8 (LSB first, rows back to back, no padding);
+ *   - inside a code, LSB first: bits 0-7 signs (bit l for lane l, 1 means
+ *     negative), then bd direction bits, then br = 10 - bd radius bits;
+ *   - decoded weight: What[i, perm[8c+l]] = R[r] * (-1)^{s_l} * D[d][l],
+ *     where D is the (1<<bd) x 8 fp16 direction codebook and R the (1<<br)
+ *     fp16 radius table; slot p of the permuted order takes input channel
+ *     perm[p] (a gather permutation);
+ *   - y[m, i] = sum_j What[i, j] * x[m, j]  with x bf16, y bf16 or fp32.
+ *
+ * Numerics.  For m <= 4 (the batch-1/small-batch GEMV path) each decoded
+ * weight is the exact fp32 product R*D (fp16 x fp16 fits in 22 bits), the
+ * activations enter the dot products as fp16 after an exact per-row power of
+ * two scaling, and accumulation is fp32.  For m > 4 (skinny and prefill GEMM
+ * on the matrix cores) a weight enters as RNE_bf16(R*D) with its sign, x as
+ * bf16, accumulation fp32.  bf16 outputs are rounded to nearest even.
+ *
+ * Ownership.  The caller owns every byte: the packed matrix buffer and the
+ * workspace are device memory the caller allocates (size queries below);
+ * handles are plain structs held by the caller.  The library allocates no
+ * device memory and keeps no global state, so there is nothing to free.
+ *
+ * Errors.  Every call returns an svq_status and never aborts.  Arguments are
+ * validated before any device work.  HIP errors map to SVQ_ERR_HIP.  All
+ * device work is asynchronous on the given stream (NULL = default stream),
+ * except that svq_pack waits for its own copies before returning.
+ *
+ * Streams: `stream` arguments are hipStream_t values passed as void*.
+ */
+#ifndef SVQ_H
+#define SVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVQ_OK = 0,
+  SVQ_ERR_INVALID_ARG = -1,      /* null pointer, bad size, not a permutation ... */
+  SVQ_ERR_UNSUPPORTED = -2,      /* bd outside {6,7,8}, shape beyond the limits */
+  SVQ_ERR_BUFFER_TOO_SMALL = -3, /* dst / workspace smaller than required       */
+  SVQ_ERR_HIP = -4               /* a HIP runtime call or launch failed          */
+} svq_status;
+
+typedef enum { SVQ_BF16 = 0, SVQ_F32 = 1 } svq_dtype;
+
+/* Limits checked by svq_pack. */
+#define SVQ_MAX_K 65536 /* the permutation is stored as uint16 */
+#define SVQ_MAX_N (1 << 24)
+
+/* One SVQ-coded matrix in canonical form.  HOST pointers, read only.
+ * n: output rows; k: input channels, k % 8 == 0; bd + br == 10, bd in {6,7,8}
+ * (direction codebook <= 4 KB; SAGE Fig. 2 caption: the split is chosen per
+ * matrix).  codes: n*(k/8) 18-bit fields as described above, ceil(n*k*9/32)
+ * bytes.  dir_codebook: (1<<bd) rows of 8 fp16 bit patterns, row-major.
+ * radius_table: (1<<br) fp16 bit patterns.  perm: k distinct values in
+ * [0, k). */
+typedef struct {
+  int32_t n, k;
+  int32_t bd, br;
+  const uint8_t *codes;
+  const uint16_t *dir_codebook;
+  const uint16_t *radius_table;
+  const int32_t *perm;
+} svq_matrix_desc;
+
+/* A packed matrix: a caller-owned POD that names a caller-owned device
+ * buffer.  Filled by svq_pack; read by svq_linear / svq_moe_linear.  The
+ * offsets are byte offsets from `dev`. */
+typedef struct {
+  void *dev;
+  int32_t n, k, bd, br;
+  int32_t n_tiles;   /* ceil(n / 16) row tiles                         */
+  int32_t units;     /* code units per row tile: ceil(k / 512)          */
+  uint64_t off_dtab; /* 256 x 8 fp16: direction rows by low index byte  */
+  uint64_t off_rtab; /* 16 fp16: radius by radius index (zero padded)   */
+  uint64_t off_btab; /* 1024 x 8 bf16: RNE_bf16(R[r] * D[d][l]) by index */
+  uint64_t off_perm; /* k uint16 slots -> channels                      */
+  uint64_t off_codes;/* n_tiles * units * 2304 bytes of coded units     */
+  uint64_t code_bytes;    /* canonical code bytes: ceil(n*k*9/32)       */
+  uint64_t padded_code_bytes; /* bytes of coded units including padding  */
+  uint64_t bytes;    /* total packed buffer size                         */
+} svq_handle;
+
+/* svq_pack: one-time repack of a canonical matrix into the kernel layout
+ * (SAGE Fig. 2 caption for what a code holds; the layout itself keeps the
+ * 18 bits per 8 weights and only regroups them for 128-bit loads).
+ *   src:        canonical matrix (host memory).
+ *   dst_dev:    device buffer of at least *dst_bytes bytes, or NULL to only
+ *               query the size.
+ *   dst_bytes:  in: capacity of dst_dev (ignored when dst_dev is NULL);
+ *               out: bytes required.
+ *   out:        filled on success when dst_dev is not NULL (may be NULL for a
+ *               size query).
+ * Validates src fully (including that perm is a permutation) before any
+ * device work.  Copies on `stream` and synchronizes it before returning, so
+ * the host arrays may be freed afterwards. */
+svq_status svq_pack(const svq_matrix_desc *src, void *dst_dev, size_t *dst_bytes,
+                    svq_handle *out, void *stream);
+
+/* svq_linear: y = x * What^T for one packed matrix (SAGE Fig. 1 / Fig. 5
+ * captions: weights reconstructed on demand; Fig. 6 caption: reordered
+ * activations gathered per subvector).
+ *   w:          packed matrix.
+ *   x:          device bf16 [m][ldx], ldx >= k.
+ *   m:          rows of x, >= 1.
+ *   y:          device [m][ldy] of type ydt, ldy >= n.
+ *   workspace:  device scratch of at least *workspace_bytes bytes, or NULL to
+ *               query the size (then nothing is launched).
+ * The workspace holds the permuted activations of this call; calls that
+ * share a workspace must be ordered on one stream.  x, y and the workspace
+ * must not overlap. */
+svq_status svq_linear(const svq_handle *w, const void *x, int64_t m, int64_t ldx,
+                      void *y, int64_t ldy, svq_dtype ydt,
+                      void *workspace, size_t *workspace_bytes, void *stream);
+
+/* svq_moe_linear: one projection of a routed mixture of experts, one output
+ * row per routed (token, expert) slot; the grouped form of svq_linear.
+ *   experts:      host array of num_experts packed matrices, all with the
+ *                 same n and k (bd may differ per expert).
+ *   x:            device bf16; row t (token) when x_per_slot == 0, row
+ *                 q = t*topk + j (slot) when x_per_slot == 1; stride ldx.
+ *   expert_ids:   device int32 [m*topk]; slot q = t*topk + j uses expert
+ *                 expert_ids[q], each in [0, num_experts).  Ids outside that
+ *                 range make the results undefined.
+ *   y:            device [m*topk][ldy] of type ydt, slot-major.
+ *   workspace:    as for svq_linear (routing tables and permuted inputs).
+ * Routing weights, the activation between projections and the combine over
+ * a token's experts are the caller's. */
+svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts,
+                          const void *x, int64_t ldx, int32_t x_per_slot,
+                          const int32_t *expert_ids, int64_t m, int32_t topk,
+                          void *y, int64_t ldy, svq_dtype ydt,
+                          void *workspace, size_t *workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *svq_status_string(svq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVQ_H */

@@ -1,0 +1,179 @@
+"""libsvq C ABI on a host without a GPU: the library loads, exports every
+function include/svq.h declares, answers size queries and rejects bad
+arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from tests.conftest import ROOT
+
+svq = pytest.importorskip("bit_spherical_vector_amd.svq")
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "svq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert set(declared) == {"svq_pack", "svq_linear", "svq_moe_linear", "svq_status_string"}
+    for name in declared:
+        assert hasattr(svq.LIB, name), name
+    assert set(declared) == set(svq.EXPORTED)
+
+
+def test_status_strings():
+    assert svq.status_string(0) == "ok"
+    assert svq.status_string(-3) == "buffer too small"
+    assert svq.status_string(-99) == "unknown status"
+
+
+def _desc(mat, **over):
+    fields = dict(n=mat.n, k=mat.k, bd=mat.bd, br=mat.br, codes=mat.codes,
+                  codebook=mat.codebook, radius=mat.radius, perm=mat.perm)
+    fields.update(over)
+    return svq.make_desc(**fields)
+
+
+def _expected_bytes(n, k):
+    a = lambda v: (v + 255) // 256 * 256
+    tiles, units = (n + 15) // 16, (k + 511) // 512
+    return a(4096) + a(256) + a(16384) + a(2 * k) + a(tiles * units * 2304)
+
+
+@pytest.mark.parametrize("n,k,bd", [(512, 1024, 8), (37, 104, 6), (1, 8, 7), (2048, 768, 7)])
+def test_pack_size_query(n, k, bd):
+    mat = synth.random_matrix(n, k, bd, seed=(20, n, k))
+    desc, keep = _desc(mat)
+    st, nbytes = svq.svq_pack(desc, None, 0, None, 0)
+    assert st == svq.SVQ_OK
+    assert nbytes == _expected_bytes(n, k)
+
+
+def test_pack_rejects_bad_arguments():
+    mat = synth.random_matrix(32, 64, 7, seed=(21, 0, 0))
+    cases = [
+        (dict(k=60), svq.SVQ_ERR_INVALID_ARG),          # k % 8 != 0
+        (dict(n=0), svq.SVQ_ERR_INVALID_ARG),
+        (dict(k=0), svq.SVQ_ERR_INVALID_ARG),
+        (dict(br=4), svq.SVQ_ERR_INVALID_ARG),          # bd + br != 10
+        (dict(bd=5, br=5), svq.SVQ_ERR_UNSUPPORTED),     # codebook split outside {6,7,8}
+        (dict(bd=9, br=1), svq.SVQ_ERR_UNSUPPORTED),
+        (dict(k=65544), svq.SVQ_ERR_UNSUPPORTED),        # beyond the uint16 permutation
+    ]
+    for over, expect in cases:
+        if "k" in over and over["k"] not in (0, 60):
+            continue  # perm length would not match; covered separately
+        desc, keep = _desc(mat, **over)
+        st, _ = svq.svq_pack(desc, None, 0, None, 0)
+        assert st == expect, over
+    # non-permutations
+    bad = mat.perm.copy()
+    bad[3] = bad[4]
+    desc, keep = _desc(mat, perm=bad)
+    assert svq.svq_pack(desc, None, 0, None, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    bad = mat.perm.copy()
+    bad[0] = 64
+    desc, keep = _desc(mat, perm=bad)
+    assert svq.svq_pack(desc, None, 0, None, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    bad = mat.perm.copy()
+    bad[0] = -1
+    desc, keep = _desc(mat, perm=bad)
+    assert svq.svq_pack(desc, None, 0, None, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    # null pointers
+    desc, keep = _desc(mat)
+    desc.codes = None
+    assert svq.svq_pack(desc, None, 0, None, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    # null desc / null size
+    assert svq.LIB.svq_pack(None, None, ctypes.byref(ctypes.c_size_t(0)), None, None) == \
+        svq.SVQ_ERR_INVALID_ARG
+    desc, keep = _desc(mat)
+    assert svq.LIB.svq_pack(ctypes.byref(desc), None, None, None, None) == svq.SVQ_ERR_INVALID_ARG
+
+
+def test_pack_k_limit():
+    k = 65536 + 8
+    mat = synth.random_matrix(1, 8, 7, seed=(22, 0, 0))
+    desc, keep = svq.make_desc(1, k, 7, 3, np.zeros(k * 9 // 32 + 1, np.uint8), mat.codebook,
+                               mat.radius, np.arange(k, dtype=np.int32))
+    assert svq.svq_pack(desc, None, 0, None, 0)[0] == svq.SVQ_ERR_UNSUPPORTED
+
+
+def test_pack_undersized_destination_before_device_work():
+    mat = synth.random_matrix(16, 64, 8, seed=(23, 0, 0))
+    desc, keep = _desc(mat)
+    st, need = svq.svq_pack(desc, None, 0, None, 0)
+    h = svq.Handle()
+    # a fake non-null device pointer: the size check fails before any copy
+    st, reported = svq.svq_pack(desc, 0x1000, need - 1, h, 0)
+    assert st == svq.SVQ_ERR_BUFFER_TOO_SMALL
+    assert reported == need
+
+
+def _fake_handle(n, k, bd):
+    a = lambda v: (v + 255) // 256 * 256
+    h = svq.Handle()
+    h.dev = 0x1000
+    h.n, h.k, h.bd, h.br = n, k, bd, 10 - bd
+    h.n_tiles, h.units = (n + 15) // 16, (k + 511) // 512
+    h.off_dtab = 0
+    h.off_rtab = a(4096)
+    h.off_btab = h.off_rtab + a(256)
+    h.off_perm = h.off_btab + a(16384)
+    h.off_codes = h.off_perm + a(2 * k)
+    h.padded_code_bytes = h.n_tiles * h.units * 2304
+    h.bytes = h.off_codes + a(h.padded_code_bytes)
+    h.code_bytes = (n * k * 9 + 31) // 32
+    return h
+
+
+def test_linear_workspace_query_and_validation():
+    h = _fake_handle(512, 1024, 8)
+    for m, expect in [(1, 2048 + 256), (4, 4 * 2048 + 256), (5, 64 * 2048), (64, 64 * 2048),
+                      (65, 128 * 2048)]:
+        st, need = svq.svq_linear(h, None, m, 1024, None, 512, svq.SVQ_BF16, None, 0, 0)
+        assert st == svq.SVQ_OK and need == expect, (m, need)
+    # bad arguments
+    assert svq.svq_linear(h, None, 0, 1024, None, 512, 0, None, 0, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    assert svq.svq_linear(h, None, 1, 1000, None, 512, 0, None, 0, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    assert svq.svq_linear(h, None, 1, 1024, None, 500, 0, None, 0, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    assert svq.svq_linear(h, None, 1, 1024, None, 512, 7, None, 0, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    # undersized workspace: rejected before launching
+    st, _ = svq.svq_linear(h, 0x2000, 1, 1024, 0x3000, 512, 0, 0x4000, 100, 0)
+    assert st == svq.SVQ_ERR_BUFFER_TOO_SMALL
+    # null x / y with a workspace
+    st, _ = svq.svq_linear(h, None, 1, 1024, 0x3000, 512, 0, 0x4000, 1 << 20, 0)
+    assert st == svq.SVQ_ERR_INVALID_ARG
+    # a handle that does not describe a packed buffer
+    bad = _fake_handle(512, 1024, 8)
+    bad.off_codes += 256
+    assert svq.svq_linear(bad, None, 1, 1024, None, 512, 0, None, 0, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    bad = _fake_handle(512, 1024, 8)
+    bad.dev = None
+    assert svq.svq_linear(bad, None, 1, 1024, None, 512, 0, None, 0, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+
+
+def test_moe_workspace_query_and_validation():
+    hs = (svq.Handle * 4)()
+    for e in range(4):
+        hs[e] = _fake_handle(768, 2048, 6 + e % 3)
+    st, need_small = svq.svq_moe_linear(hs, 4, None, 2048, 0, None, 1, 2, None, 768, 0, None, 0, 0)
+    assert st == svq.SVQ_OK and need_small > 0
+    st, need_big = svq.svq_moe_linear(hs, 4, None, 2048, 0, None, 512, 2, None, 768, 0, None, 0, 0)
+    assert st == svq.SVQ_OK and need_big > need_small
+    # topk > experts, bad x_per_slot, mismatched shapes
+    assert svq.svq_moe_linear(hs, 4, None, 2048, 0, None, 1, 5, None, 768, 0, None, 0, 0)[0] == \
+        svq.SVQ_ERR_INVALID_ARG
+    assert svq.svq_moe_linear(hs, 4, None, 2048, 2, None, 1, 2, None, 768, 0, None, 0, 0)[0] == \
+        svq.SVQ_ERR_INVALID_ARG
+    hs[2] = _fake_handle(768, 1024, 7)
+    assert svq.svq_moe_linear(hs, 4, None, 2048, 0, None, 1, 2, None, 768, 0, None, 0, 0)[0] == \
+        svq.SVQ_ERR_INVALID_ARG
+    assert svq.svq_moe_linear(hs, 0, None, 2048, 0, None, 1, 1, None, 768, 0, None, 0, 0)[0] == \
+        svq.SVQ_ERR_UNSUPPORTED

@@ -1,0 +1,186 @@
+"""GPU parity of svq_linear against the CPU oracle (dense matrices).
+
+Bar: decoded weights bit-exact (observed through one-hot activations), every
+output within |y - y_ref| <= 8e-3 * sum_j |W_ij||x_j| + 1e-6.  The m <= 4
+path decodes exactly in fp32 and is also held to a bound 8x tighter; the
+m > 4 path's weights are RNE_bf16 of the exact products and are compared
+bit-exactly with the oracle's rounding of them.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import svq_oracle as so
+from tests.gpu_common import (assert_within_tolerance, equal_pm0, one_hot_bits, out_to_f64,
+                              require_gpu, to_device_bf16, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def svq():
+    return require_gpu()
+
+
+def _run(svq, pm, x_bits, out_dtype, ldx_pad=0, ldy_pad=0):
+    m, k = x_bits.shape
+    xp = np.zeros((m, k + ldx_pad), dtype=np.uint16)
+    xp[:, :k] = x_bits
+    x = to_device_bf16(xp)[:, :k]
+    if ldy_pad:
+        out = torch.full((m, pm.n + ldy_pad), float("nan"), dtype=out_dtype, device="cuda")
+        y = svq.linear(pm, x, out=out[:, :pm.n])
+        torch.cuda.synchronize()
+        assert torch.isnan(out[:, pm.n:]).all(), "write outside the output rows"
+    else:
+        y = svq.linear(pm, x, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out_to_f64(y)
+
+
+def _check_outputs(svq, mat, x_bits, label):
+    pm = svq.pack(mat)
+    y64, W = so.linear_from_inputs(mat, x_bits)
+    m = x_bits.shape[0]
+    for dt in (torch.float32, torch.bfloat16):
+        y = _run(svq, pm, x_bits, dt)
+        assert_within_tolerance(y, y64, x_bits, W, label=f"{label} {dt}")
+        if dt == torch.float32 and m <= 4:
+            assert_within_tolerance(y, y64, x_bits, W, rel=1e-3, label=f"{label} exact-path")
+    return pm, W
+
+
+def _one_hot_check(svq, pm, W, cols, batch):
+    """Decoded weights through one-hot activations, fp32 output."""
+    k = W.shape[1]
+    for s in range(0, len(cols), batch):
+        cs = cols[s:s + batch]
+        y = _run(svq, pm, one_hot_bits(k, cs), torch.float32)
+        for r, j in enumerate(cs):
+            ref = W[:, j] if len(cs) <= 4 else so.round_to_bf16(W[:, j])
+            ok = equal_pm0(y[r], ref)
+            assert ok.all(), f"column {j}: {int((~ok).sum())} decoded weights differ"
+
+
+def test_single_matrix_m1(svq):
+    mat, x = synth.single_matrix()
+    pm, W = _check_outputs(svq, mat, x, "512x1024 m=1")
+    # every decoded weight, 4 columns per call through the exact path
+    _one_hot_check(svq, pm, W, list(range(mat.k)), 4)
+    # and a few through m = 1 itself
+    _one_hot_check(svq, pm, W, [0, 1, 511, 1023], 1)
+
+
+@pytest.mark.parametrize("j", range(7))
+def test_dense_layer_m1(svq, j):
+    mats, xs = synth.dense_layer()
+    mat, x = mats[j], xs[j]
+    pm, W = _check_outputs(svq, mat, x, f"layer {mat.name} m=1")
+    rng = np.random.default_rng(100 + j)
+    cols = sorted(rng.choice(mat.k, 256, replace=False).tolist())
+    _one_hot_check(svq, pm, W, cols, 4)
+
+
+@pytest.mark.parametrize("m", [4, 16])
+@pytest.mark.parametrize("j", range(7))
+def test_dense_layer_small_batch(svq, j, m):
+    mats, _ = synth.dense_layer()
+    mat = mats[j]
+    x = synth.dense_layer_activations(m)[j]
+    pm, W = _check_outputs(svq, mat, x, f"layer {mat.name} m={m}")
+    if m == 16 and j in (0, 6):
+        rng = np.random.default_rng(200 + j)
+        cols = sorted(rng.choice(mat.k, 64, replace=False).tolist())
+        _one_hot_check(svq, pm, W, cols, 16)
+
+
+@pytest.mark.parametrize("j", range(3))
+def test_prefill_m2048(svq, j):
+    mats, xs = synth.prefill_set()
+    mat, x = mats[j], xs[j]
+    pm = svq.pack(mat)
+    W = so.decode_matrix(mat.codes, mat.n, mat.k, mat.bd, mat.codebook, mat.radius, mat.perm)
+    rows = np.sort(np.random.default_rng(300 + j).choice(x.shape[0], 48, replace=False))
+    rows = np.concatenate([[0], rows, [x.shape[0] - 1]])
+    y64 = so.linear(x[rows], W)
+    for dt in (torch.bfloat16, torch.float32):
+        y = _run(svq, pm, x, dt)
+        assert y.shape == (2048, mat.n)
+        assert np.isfinite(y).all()
+        assert_within_tolerance(y[rows], y64, x[rows], W, label=f"prefill {mat.name} {dt}")
+
+
+EDGE = [
+    # n, k, bd, m
+    (1, 8, 8, 1),
+    (1, 8, 6, 5),
+    (37, 104, 6, 3),
+    (16, 512, 7, 4),
+    (33, 1032, 8, 17),
+    (100, 104, 7, 16),
+    (2048, 768, 7, 1),
+    (2048, 768, 7, 2),
+    (17, 520, 6, 64),
+    (15, 2048, 8, 65),
+    (64, 4096, 6, 1),
+]
+
+
+@pytest.mark.parametrize("n,k,bd,m", EDGE)
+def test_edge_shapes(svq, n, k, bd, m):
+    mat = synth.random_matrix(n, k, bd, seed=(30, n, k))
+    x = synth.random_activations(m, k, seed=(30, m, k))
+    pm, W = _check_outputs(svq, mat, x, f"edge n={n} k={k} bd={bd} m={m}")
+    cols = sorted(set([0, k - 1] + list(range(0, k, max(1, k // 8)))))
+    _one_hot_check(svq, pm, W, cols, 4 if m <= 4 else 16)
+
+
+@pytest.mark.parametrize("m", [1, 3, 20])
+def test_strided_input_output(svq, m):
+    mat = synth.random_matrix(48, 640, 7, seed=(31, m, 0))
+    x = synth.random_activations(m, 640, seed=(31, m, 1))
+    pm = svq.pack(mat)
+    y64, W = so.linear_from_inputs(mat, x)
+    y = _run(svq, pm, x, torch.float32, ldx_pad=24, ldy_pad=8)
+    assert_within_tolerance(y, y64, x, W, label="strided")
+
+
+def test_deterministic(svq):
+    mat = synth.random_matrix(256, 2560, 8, seed=(32, 0, 0))
+    for m in (1, 4, 33):
+        x = synth.random_activations(m, 2560, seed=(32, m, 0))
+        pm = svq.pack(mat)
+        a = _run(svq, pm, x, torch.float32)
+        b = _run(svq, pm, x, torch.float32)
+        assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def test_zero_and_extreme_activations(svq):
+    mat = synth.random_matrix(64, 1024, 8, seed=(33, 0, 0))
+    pm = svq.pack(mat)
+    W = so.decode_matrix(mat.codes, mat.n, mat.k, mat.bd, mat.codebook, mat.radius, mat.perm)
+    zero = np.zeros((2, 1024), dtype=np.uint16)
+    assert np.all(_run(svq, pm, zero, torch.float32) == 0)
+    assert np.all(_run(svq, pm, np.zeros((9, 1024), dtype=np.uint16), torch.float32) == 0)
+    # very large and very small magnitudes in one row (fp16 range is far exceeded)
+    rng = np.random.default_rng(5)
+    for scale in (1e30, 1e-30):
+        xf = (rng.standard_normal((3, 1024)) * scale).astype(np.float32)
+        xf[0, :5] *= 1e3
+        x = synth.bf16_bits_from_f32(xf)
+        y64 = so.linear(x, W)
+        for m_rows in (x[:1], x):
+            y = _run(svq, pm, m_rows, torch.float32)
+            assert_within_tolerance(y, y64[:m_rows.shape[0]], m_rows, W, label=f"scale {scale}")
+
+
+def test_subnormal_codebook_entries_decode_exactly(svq):
+    mat = synth.random_matrix(32, 512, 8, seed=(34, 0, 0))
+    cb = mat.codebook.copy()
+    cb[:, 3] = np.arange(cb.shape[0], dtype=np.uint16) % 0x3FF + 1  # fp16 subnormals
+    cb[5, :] = 0x0001  # smallest subnormal
+    mat.codebook = cb
+    pm = svq.pack(mat)
+    W = so.decode_matrix(mat.codes, mat.n, mat.k, mat.bd, mat.codebook, mat.radius, mat.perm)
+    _one_hot_check(svq, pm, W, list(range(0, 512, 3)), 4)
+    _one_hot_check(svq, pm, W, list(range(0, 512, 37)), 16)
