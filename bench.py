@@ -1,0 +1,234 @@
+"""Benchmark of the SVQ decode-and-multiply path on one MI355X.
+
+Default workload: the seven linears of a 4B-class decoder layer (q 4096x2560,
+k/v 1024x2560, o 2560x4096, gate/up 9728x2560, down 2560x9728) at batch 1,
+per-matrix direction bits drawn from {6,7,8}; synthetic seeded inputs.  A
+step is one svq_linear call per matrix (activation gather + decode-and-
+multiply), i.e. the whole hot path over one batch.  Every step reads a
+different copy of the packed layer (cold-cache rotation over more than twice
+the 256 MB Infinity Cache), so the code bytes come from HBM.
+
+Prints ONE JSON line.  ``value`` is packed-code bytes per second over the
+timed steps (GB/s); ``roofline`` reports the decode-and-multiply calls timed
+one by one with HIP events on the launch stream against the 8 TB/s HBM
+peak; ``cpu_baseline`` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+COLD_BYTES = 600 << 20  # > 2 x 256 MB MALL
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="layer4b_m1",
+                    choices=["layer4b_m1", "layer4b_m4", "layer4b_m16", "single_512x1024_m1",
+                             "prefill_m2048", "moe128_m1", "moe128_m512"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def cpu_baseline_dense(mats, xs, budget_s=20.0):
+    """Time the CPU oracle (unpack, exact decode, un-permute, fp64 product)
+    matrix by matrix until the time budget is used; GB/s of code bytes."""
+    from oracle import svq_oracle as so
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    t0 = time.perf_counter()
+    done_bytes, done = 0, []
+    for mat, x in zip(mats, xs):
+        y64, _ = so.linear_from_inputs(mat, x)
+        done_bytes += mat.codes.size
+        done.append(mat.name)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{len(done)} of {len(mats)} matrices ({','.join(done)}), one pass each, "
+                      f"{dt:.1f} s; decode single-threaded numpy, product BLAS"}
+
+
+def cpu_baseline_prefill(mats, xs, rows=32):
+    from oracle import svq_oracle as so
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    t0 = time.perf_counter()
+    flops = 0
+    for mat, x in zip(mats, xs):
+        W = so.decode_matrix(mat.codes, mat.n, mat.k, mat.bd, mat.codebook, mat.radius, mat.perm)
+        so.linear(x[:rows], W)
+        flops += 2.0 * rows * mat.n * mat.k
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{len(mats)} matrices, {rows} of 2048 activation rows each (full decode), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path does not "
+              "shard across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from bit_spherical_vector_amd import svq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.workload]
+    m = wl["m"]
+    stream = torch.cuda.current_stream()
+
+    if wl["kind"] != "dense":
+        raise SystemExit("MoE benchmarking is not wired into bench.py yet")
+
+    if args.workload.startswith("layer4b"):
+        mats, xs1 = synth.dense_layer()
+        xs = xs1 if m == 1 else synth.dense_layer_activations(m)
+    elif args.workload.startswith("single"):
+        mat, x = synth.single_matrix(m=m)
+        mats, xs = [mat], [x]
+    else:
+        mats, xs = synth.prefill_set(m=m)
+
+    packed = [svq.pack(mat) for mat in mats]
+    code_bytes = sum(mat.codes.size for mat in mats)
+    set_bytes = sum(pm.handle.bytes for pm in packed)
+    copies = max(1, -(-COLD_BYTES // set_bytes))
+    # independent device copies of every packed matrix (same content)
+    rot = []
+    for c in range(copies):
+        group = []
+        for pm in packed:
+            buf = pm.buf.clone() if c else pm.buf
+            h = svq.Handle.from_buffer_copy(pm.handle)
+            h.dev = buf.data_ptr()
+            group.append(svq.PackedMatrix(buf, h))
+        rot.append(group)
+    x_dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in xs]
+    y_dev = [torch.empty((m, mat.n), dtype=torch.bfloat16, device=dev) for mat in mats]
+    ws = [torch.empty(max(1, svq.linear_workspace_bytes(pm, m)), dtype=torch.uint8, device=dev)
+          for pm in packed]
+    sh = svq._stream_handle(stream)
+    calls = []
+    for c in range(copies):
+        row = []
+        for j, pm in enumerate(rot[c]):
+            row.append((pm.handle, x_dev[j].data_ptr(), m, x_dev[j].stride(0), y_dev[j].data_ptr(),
+                        y_dev[j].stride(0), svq.SVQ_BF16, ws[j].data_ptr(), ws[j].numel(), sh))
+        calls.append(row)
+
+    def step(i):
+        for a in calls[i % copies]:
+            st, _ = svq.svq_linear(*a)
+            if st != svq.SVQ_OK:
+                raise svq.SvqError(st, "svq_linear")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+
+    # per-call timing with events on the launch stream (same cold rotation)
+    nev = min(args.steps, 100)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in mats] for _ in range(nev)]
+    torch.cuda.synchronize()
+    for i in range(nev):
+        for j, a in enumerate(calls[i % copies]):
+            evs[i][j][0].record(stream)
+            svq.svq_linear(*a)
+            evs[i][j][1].record(stream)
+    torch.cuda.synchronize()
+    per_call_ms = np.array([[a.elapsed_time(b) for (a, b) in row] for row in evs])
+
+    flops = sum(2.0 * m * mat.n * mat.k for mat in mats)
+    if m >= 64:
+        metric, unit = "prefill dequant-GEMM TFLOP/s", "TFLOP/s"
+        value = flops * args.steps / (ms_total * 1e-3) / 1e12
+        ach = flops * nev / (per_call_ms.sum() * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 3), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        metric, unit = "packed-weight GB/s (batch-%d GEMV)" % m, "GB/s"
+        value = code_bytes * args.steps / (ms_total * 1e-3) / 1e9
+        ach = code_bytes * nev / (per_call_ms.sum() * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    per_matrix = {mat.name: round(float(np.median(per_call_ms[:, j])) * 1e3, 2)
+                  for j, mat in enumerate(mats)}
+
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        if m >= 64:
+            cpu = cpu_baseline_prefill(mats, xs)
+        else:
+            cpu = cpu_baseline_dense(mats, xs)
+
+    out = {
+        "metric": metric,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xf16->f32 (exact decode)" if m <= 4 else "bf16xbf16->f32",
+        "data": "synthetic (seeded codes, codebooks, radii, permutations, activations)",
+        "config": {"workload": args.workload, "matrices": len(mats), "m": m,
+                   "code_bytes": int(code_bytes), "cold_copies": int(copies),
+                   "calls_per_step": len(mats), "median_call_us": per_matrix},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
