@@ -3,8 +3,9 @@
 Default workload: the seven linears of a 4B-class decoder layer (q 4096x2560,
 k/v 1024x2560, o 2560x4096, gate/up 9728x2560, down 2560x9728) at batch 1,
 per-matrix direction bits drawn from {6,7,8}; synthetic seeded inputs.  A
-step is one svq_linear call per matrix (activation gather + decode-and-
-multiply), i.e. the whole hot path over one batch.  Every step reads a
+step is one svq_linear_batched call over all matrices of the workload
+(activation gather + decode-and-multiply; one kernel launch for m <= 4),
+i.e. the whole hot path over one batch.  Every step reads a
 different copy of the packed layer (cold-cache rotation over more than twice
 the 256 MB Infinity Cache), so the code bytes come from HBM.
 
@@ -135,22 +136,13 @@ def main():
         rot.append(group)
     x_dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in xs]
     y_dev = [torch.empty((m, mat.n), dtype=torch.bfloat16, device=dev) for mat in mats]
-    ws = [torch.empty(max(1, svq.linear_workspace_bytes(pm, m)), dtype=torch.uint8, device=dev)
-          for pm in packed]
-    sh = svq._stream_handle(stream)
-    calls = []
-    for c in range(copies):
-        row = []
-        for j, pm in enumerate(rot[c]):
-            row.append((pm.handle, x_dev[j].data_ptr(), m, x_dev[j].stride(0), y_dev[j].data_ptr(),
-                        y_dev[j].stride(0), svq.SVQ_BF16, ws[j].data_ptr(), ws[j].numel(), sh))
-        calls.append(row)
+    calls = [svq.BatchedCall(rot[c], x_dev, y_dev, stream=stream) for c in range(1)]
+    ws = calls[0].workspace
+    calls += [svq.BatchedCall(rot[c], x_dev, y_dev, workspace=ws, stream=stream)
+              for c in range(1, copies)]
 
     def step(i):
-        for a in calls[i % copies]:
-            st, _ = svq.svq_linear(*a)
-            if st != svq.SVQ_OK:
-                raise svq.SvqError(st, "svq_linear")
+        calls[i % copies]()
 
     for i in range(args.warmup):
         step(i)
@@ -164,18 +156,19 @@ def main():
     ms_total = e0.elapsed_time(e1)
     ms_per_step = ms_total / args.steps
 
-    # per-call timing with events on the launch stream (same cold rotation)
+    # each call timed alone with HIP events on the launch stream (same cold
+    # rotation); the host waits between calls so that no launch gap or queued
+    # work is inside a measurement
     nev = min(args.steps, 100)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in mats] for _ in range(nev)]
-    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nev)]
     for i in range(nev):
-        for j, a in enumerate(calls[i % copies]):
-            evs[i][j][0].record(stream)
-            svq.svq_linear(*a)
-            evs[i][j][1].record(stream)
+        torch.cuda.synchronize()
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
-    per_call_ms = np.array([[a.elapsed_time(b) for (a, b) in row] for row in evs])
+    per_call_ms = np.array([a.elapsed_time(b) for (a, b) in evs])
 
     flops = sum(2.0 * m * mat.n * mat.k for mat in mats)
     if m >= 64:
@@ -190,8 +183,7 @@ def main():
         ach = code_bytes * nev / (per_call_ms.sum() * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
-    per_matrix = {mat.name: round(float(np.median(per_call_ms[:, j])) * 1e3, 2)
-                  for j, mat in enumerate(mats)}
+    launches = 1 if m <= 4 else 2 * len(mats)
 
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -223,7 +215,8 @@ def main():
         "data": "synthetic (seeded codes, codebooks, radii, permutations, activations)",
         "config": {"workload": args.workload, "matrices": len(mats), "m": m,
                    "code_bytes": int(code_bytes), "cold_copies": int(copies),
-                   "calls_per_step": len(mats), "median_call_us": per_matrix},
+                   "launches_per_step": launches,
+                   "median_call_us": round(float(np.median(per_call_ms)) * 1e3, 2)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

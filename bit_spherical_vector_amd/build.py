@@ -17,6 +17,8 @@ HIPCC_FLAGS = [
     "-shared",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs (no accvgpr copies in the decode loops)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -78,7 +78,7 @@ Layout make_layout(int32_t n, int32_t k) {
   L.off_btab = off;
   off += align256(BTAB_BYTES);
   L.off_perm = off;
-  off += align256((size_t)k * 2);
+  off += align256((size_t)L.units * UNIT_SLOTS * 2);  // zero padded to the unit width
   L.off_codes = off;
   L.padded_code_bytes = (size_t)L.n_tiles * L.units * UNIT_BYTES;
   off += align256(L.padded_code_bytes);
@@ -239,44 +239,129 @@ svq_status svq_pack(const svq_matrix_desc *src, void *dst_dev, size_t *dst_bytes
   return SVQ_OK;
 }
 
-svq_status svq_linear(const svq_handle *w, const void *x, int64_t m, int64_t ldx, void *y,
-                      int64_t ldy, svq_dtype ydt, void *workspace, size_t *workspace_bytes,
-                      void *stream) {
-  if (!workspace_bytes) return SVQ_ERR_INVALID_ARG;
-  const svq_status st = validate_handle(w);
-  if (st != SVQ_OK) return st;
-  if (m < 1 || m > (1 << 24) || ldx < w->k || ldy < w->n) return SVQ_ERR_INVALID_ARG;
+// Exact path (m <= 4): plan the blocks of one fused launch over `count`
+// matrices.  R (row tiles per block) gives each block about 20 work items
+// (row tile x 512-slot unit, ~46 KB of codes), so blocks of different K
+// carry similar work; R shrinks while the launch has fewer than 512 blocks.
+static int plan_gemv(GemvBatch &b) {
+  // longest blocks first: jobs with the largest k (longest prologue and the
+  // most units per row tile) get the lowest block ids, so they are
+  // dispatched first
+  for (int i = 1; i < b.count; ++i)
+    for (int j = i; j > 0 && b.job[j].w.k > b.job[j - 1].w.k; --j) {
+      const GemvJob t = b.job[j];
+      b.job[j] = b.job[j - 1];
+      b.job[j - 1] = t;
+    }
+  int R[GV_MAX_JOBS];
+  for (int j = 0; j < b.count; ++j) {
+    const int U = b.job[j].w.units;
+    int r = 20 / U;
+    R[j] = r < 1 ? 1 : (r > 4 ? 4 : r);
+  }
+  auto total = [&]() {
+    int t = 0;
+    for (int j = 0; j < b.count; ++j) t += (b.job[j].w.n_tiles + R[j] - 1) / R[j];
+    return t;
+  };
+  while (total() < 512) {
+    int best = -1;
+    for (int j = 0; j < b.count; ++j)
+      if (R[j] > 1 && (best < 0 || R[j] > R[best])) best = j;
+    if (best < 0) break;
+    --R[best];
+  }
+  int begin = 0;
+  for (int j = 0; j < b.count; ++j) {
+    b.job[j].R = R[j];
+    b.job[j].block_begin = begin;
+    begin += (b.job[j].w.n_tiles + R[j] - 1) / R[j];
+  }
+  return begin;
+}
+
+static svq_status linear_impl(const svq_handle *w, int32_t count, const void *const *xs,
+                              const int64_t *ldx, int64_t m, void *const *ys, const int64_t *ldy,
+                              svq_dtype ydt, void *workspace, size_t *workspace_bytes,
+                              void *stream) {
+  if (!workspace_bytes || !w) return SVQ_ERR_INVALID_ARG;
+  if (count < 1 || count > GV_MAX_JOBS) return SVQ_ERR_INVALID_ARG;
+  if (m < 1 || m > (1 << 24)) return SVQ_ERR_INVALID_ARG;
   if (ydt != SVQ_BF16 && ydt != SVQ_F32) return SVQ_ERR_INVALID_ARG;
-  const size_t Kp = (size_t)w->units * UNIT_SLOTS;
-  size_t need;
-  const bool exact = m <= EXACT_MAX_M;
+  for (int32_t j = 0; j < count; ++j) {
+    const svq_status st = validate_handle(&w[j]);
+    if (st != SVQ_OK) return st;
+  }
+  // the exact path keeps the permuted activations of a block in LDS
+  int k_max = 0, u_max = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    k_max = w[j].k > k_max ? w[j].k : k_max;
+    u_max = w[j].units > u_max ? w[j].units : u_max;
+  }
+  const bool exact = m <= EXACT_MAX_M && gemv_smem_bytes((int)m, k_max, u_max) <= GV_LDS_LIMIT;
+  size_t need = 256;
   int m_pad = 0;
-  if (exact) {
-    need = align256((size_t)m * Kp * 2) + 256;
-  } else {
+  if (!exact) {
     m_pad = gemm_m_pad((int)m);
-    need = align256((size_t)m_pad * Kp * 2);
+    need = 0;
+    for (int32_t j = 0; j < count; ++j)
+      need += align256((size_t)m_pad * w[j].units * UNIT_SLOTS * 2);
   }
   if (!workspace) {
+    if (ldx && ldy)
+      for (int32_t j = 0; j < count; ++j)
+        if (ldx[j] < w[j].k || ldy[j] < w[j].n) return SVQ_ERR_INVALID_ARG;
     *workspace_bytes = need;
     return SVQ_OK;
   }
+  if (!xs || !ys || !ldx || !ldy) return SVQ_ERR_INVALID_ARG;
+  for (int32_t j = 0; j < count; ++j) {
+    if (!xs[j] || !ys[j]) return SVQ_ERR_INVALID_ARG;
+    if (ldx[j] < w[j].k || ldy[j] < w[j].n) return SVQ_ERR_INVALID_ARG;
+  }
   if (*workspace_bytes < need) return SVQ_ERR_BUFFER_TOO_SMALL;
-  if (!x || !y) return SVQ_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  const MatView v = view_of(w);
-  hipError_t e;
+  hipError_t e = hipSuccess;
   if (exact) {
-    uint16_t *xw = (uint16_t *)workspace;
-    int32_t *esc = (int32_t *)((uint8_t *)workspace + align256((size_t)m * Kp * 2));
-    e = launch_prep_exact(v, (const uint16_t *)x, ldx, (int)m, xw, esc, s);
-    if (e == hipSuccess) e = launch_gemv_exact(v, xw, esc, (int)m, y, ldy, (int)ydt, s);
+    GemvBatch b;
+    std::memset(&b, 0, sizeof(b));
+    b.count = count;
+    b.m = (int)m;
+    b.ydt = (int)ydt;
+    for (int32_t j = 0; j < count; ++j) {
+      b.job[j].w = view_of(&w[j]);
+      b.job[j].x = (const uint16_t *)xs[j];
+      b.job[j].ldx = ldx[j];
+      b.job[j].y = ys[j];
+      b.job[j].ldy = ldy[j];
+    }
+    const int blocks = plan_gemv(b);
+    e = launch_gemv_batched(b, blocks, gemv_smem_bytes((int)m, k_max, u_max), s);
   } else {
-    uint16_t *xb = (uint16_t *)workspace;
-    e = launch_prep_bf16(v, (const uint16_t *)x, ldx, (int)m, m_pad, xb, s);
-    if (e == hipSuccess) e = launch_gemm_bf16(v, xb, (int)m, m_pad, y, ldy, (int)ydt, s);
+    uint8_t *ws = (uint8_t *)workspace;
+    for (int32_t j = 0; j < count && e == hipSuccess; ++j) {
+      const MatView v = view_of(&w[j]);
+      uint16_t *xb = (uint16_t *)ws;
+      ws += align256((size_t)m_pad * w[j].units * UNIT_SLOTS * 2);
+      e = launch_prep_bf16(v, (const uint16_t *)xs[j], ldx[j], (int)m, m_pad, xb, s);
+      if (e == hipSuccess) e = launch_gemm_bf16(v, xb, (int)m, m_pad, ys[j], ldy[j], (int)ydt, s);
+    }
   }
   return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+}
+
+svq_status svq_linear(const svq_handle *w, const void *x, int64_t m, int64_t ldx, void *y,
+                      int64_t ldy, svq_dtype ydt, void *workspace, size_t *workspace_bytes,
+                      void *stream) {
+  void *yy = y;
+  return linear_impl(w, 1, &x, &ldx, m, &yy, &ldy, ydt, workspace, workspace_bytes, stream);
+}
+
+svq_status svq_linear_batched(const svq_handle *w, int32_t count, const void *const *x,
+                              const int64_t *ldx, int64_t m, void *const *y, const int64_t *ldy,
+                              svq_dtype ydt, void *workspace, size_t *workspace_bytes,
+                              void *stream) {
+  return linear_impl(w, count, x, ldx, m, y, ldy, ydt, workspace, workspace_bytes, stream);
 }
 
 svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts, const void *x,

@@ -6,7 +6,8 @@
 //                         by the low byte of a code's 10-bit index
 //   rtab   16 fp16        R[r], zero padded to 16 entries
 //   btab   1024 x 8 bf16  row idx = RNE_bf16(R[idx >> bd] * D[idx & mask][l])
-//   perm   k uint16       slot p takes input channel perm[p]
+//   perm   units*512 uint16  slot p takes input channel perm[p]; slots
+//                         p >= k hold 0 (padding, multiplied by zero)
 //   codes  n_tiles x units coded units of UNIT_BYTES each
 //
 // A coded unit covers 16 output rows x 64 consecutive codes (512 permuted
@@ -62,12 +63,26 @@ struct MatView {
 };
 
 // ---- dense path ---------------------------------------------------------
-// Exact path (m <= 4): prep writes xw = fp16(x[a][perm[p]] * 2^e_a) for
-// p < units*512 (zero beyond k) and e_a; the GEMV kernel multiplies.
-hipError_t launch_prep_exact(const MatView &w, const uint16_t *x, int64_t ldx, int m,
-                             uint16_t *xw, int32_t *escale, hipStream_t s);
-hipError_t launch_gemv_exact(const MatView &w, const uint16_t *xw, const int32_t *escale, int m,
-                             void *y, int64_t ldy, int ydt, hipStream_t s);
+// Exact path (m <= 4): one fused kernel per call (gather, scale, decode and
+// multiply) over up to GV_MAX_JOBS matrices; a block owns R row tiles of one
+// matrix ("job").
+constexpr int GV_MAX_JOBS = 8;
+struct GemvJob {
+  MatView w;
+  const uint16_t *x;
+  int64_t ldx;
+  void *y;
+  int64_t ldy;
+  int32_t R;            // row tiles per block
+  int32_t block_begin;  // first block of this job
+};
+struct GemvBatch {
+  GemvJob job[GV_MAX_JOBS];
+  int32_t count, m, ydt;
+};
+constexpr size_t GV_LDS_LIMIT = 160 * 1024;  // LDS per workgroup on gfx950
+size_t gemv_smem_bytes(int m, int k_max, int units_max);
+hipError_t launch_gemv_batched(GemvBatch &b, int blocks, size_t smem, hipStream_t s);
 
 // bf16 path (m > 4): prep writes xb = x[row][perm[p]] (bf16), zero padded to
 // m_pad rows and units*512 slots; the GEMM kernel multiplies.

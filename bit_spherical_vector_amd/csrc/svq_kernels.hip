@@ -68,130 +68,355 @@ __device__ __forceinline__ uint32_t code_index(u4 L, uint32_t H, int i) {
 }
 
 // ---------------------------------------------------------------------------
-// Exact path
+// Exact path (m <= 4), fused: gather + scale + decode-and-multiply in one
+// kernel.
 // ---------------------------------------------------------------------------
-
-// Block-level: permute one activation row (gather, Fig. 6 "reordered
-// activations"), scale it by 2^e with e chosen so that max|x| * 2^e lies in
-// [2^14, 2^15) (exact for every bf16 value above 2^-17 * max), convert to
-// fp16.  Slots >= k are zero.  blockDim.x == 256.
-__device__ void prep_exact_row(const uint16_t *__restrict__ perm, int K, int Kp,
-                               const uint16_t *__restrict__ xr, uint16_t *__restrict__ xo,
-                               int32_t *__restrict__ esc, float *red4) {
-  float mx = 0.f;
-  for (int j = threadIdx.x; j < K; j += 256) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(xr[j])));
-  for (int off = 32; off; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
-  const int e = mx > 0.f ? 14 - ilogbf(mx) : 0;
-  for (int p = threadIdx.x; p < Kp; p += 256) {
-    float v = p < K ? bf16_bits_to_f32(xr[perm[p]]) : 0.f;
-    _Float16 h = (_Float16)ldexpf(v, e);
-    xo[p] = __builtin_bit_cast(uint16_t, h);
-  }
-  if (threadIdx.x == 0) *esc = e;
-}
-
-__global__ __launch_bounds__(256) void prep_exact_kernel(MatView w, const uint16_t *__restrict__ x,
-                                                          int64_t ldx, uint16_t *__restrict__ xw,
-                                                          int32_t *__restrict__ escale) {
-  __shared__ float red4[4];
-  const int a = blockIdx.x;
-  const int Kp = w.units * UNIT_SLOTS;
-  prep_exact_row((const uint16_t *)(w.base + w.off_perm), w.k, Kp, x + (int64_t)a * ldx,
-                 xw + (size_t)a * Kp, escale + a, red4);
-}
-
-// GEMV of one 16-row tile for m <= 4 activation rows.  The block's W waves
-// take the tile's coded units round-robin and meet in LDS at the end.
 //
-// MFMA mapping for K-block i of unit u (4 codes, 32 permuted slots):
+// A block owns R consecutive 16-row tiles of one matrix and all of its K.
+// Prologue: the block stages each activation row in LDS, and its 4 waves
+// gather the permuted slots (Fig. 6 caption: a subvector multiplies eight
+// reordered activations) unit by unit.  Each 512-slot unit u gets its own
+// exact power-of-two scale 2^e_u with max|x_u| * 2^e_u in [2^14, 2^15), so
+// the fp16 copy is exact for every bf16 value above 2^-17 * max|x_u|; the
+// scale is undone once per (row tile, unit) in fp32.
+//
+// Main loop: work item t = rt*U + u (row tile rt, unit u) goes to wave
+// t mod 4.  The item's 2304 code bytes are contiguous and prefetched one
+// item ahead.  MFMA mapping for K-block i of the unit (4 codes):
 //   B[k][n]: lane L holds the signed direction row of its code (row n =
 //            L & 15, code group q = L >> 4), k = 8q..8q+7.
-//   A[m][k]: m = 4q' + a selects code group q' and activation row a; lane L
-//            holds A[L & 15][k-group L >> 4], non-zero only when
-//            (L & 15) >> 2 == L >> 4 ("diagonal" lanes), where it is the
-//            8 scaled activations of code (4i + q) for row a = L & 3.
-//   C[m][n]: lane L receives rows 4q + a (a = 0..3) of column L & 15, i.e.
-//            exactly the dot products of the code it decoded, one per
-//            activation row.
-// xw rows are Kp = units*512 fp16 apart; output row a goes to y + a*ldy.
+//   A[m][k]: m = 4q' + a; lane L holds A[L & 15][k-group L >> 4], which is
+//            non-zero only on the "diagonal" lanes (L & 15) >> 2 == L >> 4,
+//            where it is the 8 scaled activations of code 4i + q for
+//            activation row a = L & 3 (read from LDS under the exec mask,
+//            so the other lanes keep their zeros).
+//   C[m][n]: lane L receives rows 4q + a of column L & 15: the dot products
+//            of exactly the code it decoded, one per activation row.
+// The radius multiply R[r] * dot is an fp32 FMA per code; R*D is never
+// rounded.  Partial sums meet in LDS at the end of the block.
+
+constexpr int GV_WAVES = 4;
+constexpr int GV_MAX_R = 4;
+// LDS: direction table (GV_REP copies interleaved: row b, copy j at
+// b*16*GV_REP + 16*j; lane L reads copy L % GV_REP), radius table, unit
+// scales, cross-wave partial sums, then the permuted activations and the
+// staging row.
+constexpr int GV_REP = 1;
+constexpr int GV_DTAB_BYTES = 256 * 16 * GV_REP;
+constexpr int GV_OFF_RTAB = GV_DTAB_BYTES;
+constexpr int GV_OFF_MAX = GV_OFF_RTAB + 256;
+constexpr int GV_OFF_RED = GV_OFF_MAX + 128 * 4 * 4;  // [U <= 128][M <= 4] scales
+constexpr int GV_SMEM_FIXED = GV_OFF_RED + 4096;
+constexpr int GV_PRE_UNITS = 5;   // permutation vectors prefetched per wave
+constexpr int GV_STAGE_BATCH = 5; // x loads in flight per thread while staging
+
+// Maximum over the 64 lanes of a non-negative float (returned in every
+// lane): DPP row shifts within the 16-lane rows, row broadcasts across rows,
+// then lane 63.
+__device__ __forceinline__ float wave_max(float v) {
+  int b = __builtin_bit_cast(int, v);  // non-negative floats order as ints
+  b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x111, 0xF, 0xF, false));  // row_shr:1
+  b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x112, 0xF, 0xF, false));  // row_shr:2
+  b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x114, 0xF, 0xF, false));  // row_shr:4
+  b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x118, 0xF, 0xF, false));  // row_shr:8
+  b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63));
+}
+
 template <int M>
-__device__ void gemv_exact_tile(const MatView &w, int rt, const uint16_t *__restrict__ xw,
-                                const int32_t *__restrict__ escale, void *__restrict__ y,
-                                int64_t ldy, int ydt, u4 *s_dtab, _Float16 *s_rtab,
-                                float (*s_red)[EXACT_MAX_M][16]) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, W = blockDim.x >> 6;
-  const u4 *dtab_g = (const u4 *)(w.base + w.off_dtab);
-  for (int j = tid; j < 256; j += blockDim.x) s_dtab[j] = dtab_g[j];
+__device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ x, int64_t ldx,
+                                 void *__restrict__ y, int64_t ldy, int ydt, int rt0, int R,
+                                 uint8_t *smem) {
+  u4 *s_dtab = (u4 *)smem;
+  _Float16 *s_rtab = (_Float16 *)(smem + GV_OFF_RTAB);
+  float *s_scale = (float *)(smem + GV_OFF_MAX);          // [U][M] 2^-e per unit
+  float *s_red = (float *)(smem + GV_OFF_RED);            // [W][GV_MAX_R][M][16]
+  uint16_t *s_xp = (uint16_t *)(smem + GV_SMEM_FIXED);    // [M][Kp] fp16
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int U = w.units, Kp = U * UNIT_SLOTS, K = w.k;
+  uint16_t *s_stage = s_xp + (size_t)M * Kp;              // [K] bf16
+  const int items = R * U;
+  const uint8_t *codes0 = w.base + w.off_codes + (size_t)rt0 * U * UNIT_BYTES;
+  // wave wv owns the contiguous run of work items [t_begin, t_end) in
+  // unit-major order t = u*R + rt
+  const int per = (items + GV_WAVES - 1) / GV_WAVES;
+  const int t_begin = wv * per;
+  const int t_end = min(items, t_begin + per);
+
+  // Global loads of the prologue are issued first, in the order they are
+  // needed (vmcnt counts in order): the direction table row of this thread,
+  // the permutation vectors of the wave's units, the first activation row,
+  // and only then the first work item's codes, whose HBM latency overlaps
+  // the rest of the prologue.
+  const int u_lo = t_begin / R, u_hi = t_end > t_begin ? (t_end - 1) / R : u_lo - 1;
+  const u4 drow = ((const u4 *)(w.base + w.off_dtab))[tid];
+  const uint16_t *perm = (const uint16_t *)(w.base + w.off_perm);
+  u4 pvec[GV_PRE_UNITS];
+#pragma unroll
+  for (int j = 0; j < GV_PRE_UNITS; ++j) {
+    const int uu = u_lo + j;
+    pvec[j] = uu <= u_hi ? *(const u4 *)(perm + uu * UNIT_SLOTS + 8 * lane) : (u4){0u, 0u, 0u, 0u};
+  }
+  const int n8 = K / 8;
+  const bool x_vec = ((((uintptr_t)x) | ((uintptr_t)ldx * 2)) & 15) == 0;
+  u4 xv[GV_STAGE_BATCH];
+  if (x_vec) {
+#pragma unroll
+    for (int b = 0; b < GV_STAGE_BATCH; ++b) {
+      const int j = tid + 256 * b;
+      xv[b] = j < n8 ? ((const u4 *)x)[j] : (u4){0u, 0u, 0u, 0u};
+    }
+  }
+  u4 S = (u4){0u, 0u, 0u, 0u}, L = S;
+  uint32_t H = 0;
+  int u = u_lo, rt = t_begin - u_lo * R;
+  if (t_begin < t_end) {
+    const uint8_t *ub = codes0 + (size_t)(rt * U + u) * UNIT_BYTES;
+    S = *(const u4 *)(ub + PLANE_SIGN + 16 * lane);
+    L = *(const u4 *)(ub + PLANE_LOW + 16 * lane);
+    H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * lane);
+  }
+#pragma unroll
+  for (int j = 0; j < GV_REP; ++j) s_dtab[tid * GV_REP + j] = drow;
   if (tid < 16) s_rtab[tid] = ((const _Float16 *)(w.base + w.off_rtab))[tid];
-  __syncthreads();
+
+  // The units this wave multiplies: its items t in [t_begin, t_end) are
+  // unit-major, so they cover units u_lo..u_hi.
+
+  // One activation row at a time: stage it in LDS (one barrier), then every
+  // wave gathers the permuted slots of its own units (Fig. 6 "reordered
+  // activations") and converts them to fp16 with a per-unit scale 2^e,
+  // chosen so that max|x_unit| * 2^e lies in [2^14, 2^15): exact for every
+  // bf16 value above 2^-17 of the unit's maximum.  Waves that share a unit
+  // write identical values.
+  for (int a = 0; a < M; ++a) {
+    const uint16_t *xr = x + (int64_t)a * ldx;
+    if (a > 0) __syncthreads();  // previous row's gathers are done
+    if (x_vec) {
+      for (int j0 = tid; j0 < n8; j0 += 256 * GV_STAGE_BATCH) {
+        if (a > 0 || j0 != tid) {
+#pragma unroll
+          for (int b = 0; b < GV_STAGE_BATCH; ++b) {
+            const int j = j0 + 256 * b;
+            xv[b] = j < n8 ? ((const u4 *)xr)[j] : (u4){0u, 0u, 0u, 0u};
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < GV_STAGE_BATCH; ++b) {
+          const int j = j0 + 256 * b;
+          if (j < n8) ((u4 *)s_stage)[j] = xv[b];
+        }
+      }
+    } else {
+      for (int j = tid; j < K; j += 256) s_stage[j] = xr[j];
+    }
+    __syncthreads();
+    for (int uu = u_lo; uu <= u_hi; ++uu) {
+      const int p0 = uu * UNIT_SLOTS + 8 * lane;
+      u4 pv;
+      const int j = uu - u_lo;
+      if (j < GV_PRE_UNITS) {
+        pv = pvec[0];
+#pragma unroll
+        for (int jj = 1; jj < GV_PRE_UNITS; ++jj)
+          if (jj == j) pv = pvec[jj];
+      } else {
+        pv = *(const u4 *)(perm + p0);
+      }
+      float v[8];
+      float mx = 0.f;
+#pragma unroll
+      for (int l = 0; l < 4; ++l) {
+        const uint32_t c0 = pv[l] & 0xFFFFu, c1 = pv[l] >> 16;
+        // perm is zero padded to the unit width, so c0, c1 < K always
+        const float g0 = bf16_bits_to_f32(s_stage[c0]), g1 = bf16_bits_to_f32(s_stage[c1]);
+        v[2 * l] = (p0 + 2 * l < K) ? g0 : 0.f;
+        v[2 * l + 1] = (p0 + 2 * l + 1 < K) ? g1 : 0.f;
+        mx = fmaxf(mx, fmaxf(fabsf(v[2 * l]), fabsf(v[2 * l + 1])));
+      }
+      mx = wave_max(mx);
+      const int e = mx > 0.f ? 14 - ilogbf(mx) : 0;
+      u4 h;
+#pragma unroll
+      for (int l = 0; l < 4; ++l) {
+        const _Float16 lo = (_Float16)ldexpf(v[2 * l], e), hi = (_Float16)ldexpf(v[2 * l + 1], e);
+        h[l] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      ((u4 *)(s_xp + (size_t)a * Kp))[64 * uu + lane] = h;
+      if (lane == 0) s_scale[uu * M + a] = ldexpf(1.f, -e);
+    }
+  }
+  // the gathered activations of a unit are read back only by the wave that
+  // wrote them (or an identical copy): a wave-level fence suffices
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   const int q = lane >> 4;
-  const int a_lane = lane & 3;
-  const bool diag = (((lane & 15) >> 2) == q) && (a_lane < M);
-  const int Kp = w.units * UNIT_SLOTS;
-  const u4 *xa = (const u4 *)(xw + (size_t)(diag ? a_lane : 0) * Kp) + q;
   const int bd = w.bd;
-  const uint8_t *tile = w.base + w.off_codes + (size_t)rt * w.units * UNIT_BYTES;
+  float acc[GV_MAX_R][M];
+#pragma unroll
+  for (int r = 0; r < GV_MAX_R; ++r)
+#pragma unroll
+    for (int a = 0; a < M; ++a) acc[r][a] = 0.f;
+  u4 A[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) A[i] = (u4){0u, 0u, 0u, 0u};
 
-  float acc[M];
-#pragma unroll
-  for (int a = 0; a < M; ++a) acc[a] = 0.f;
-  u4 A[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) A[i] = (u4){0u, 0u, 0u, 0u};
+  // Diagonal lanes of the block-diagonal A operand: (L & 15) >> 2 == L >> 4.
+  //  M == 1: four K-blocks i = 4g + j (j = 0..3) are chained into one C;
+  //          lane 20q + j carries code 4i + q of K-block j, so C row 4q + j
+  //          of lane L (q = L >> 4) is the dot of the code that lane decoded
+  //          for K-block 4g + j.
+  //  M > 1:  one C per K-block; lane 20q + a carries row a of code 4i + q,
+  //          and C row 4q + a is that code's dot for activation row a.
+  const bool diag = (((lane & 15) >> 2) == q) && (M == 1 || (lane & 3) < M);
+  const int a_lane = M == 1 ? 0 : (lane & 3);
+  const int j_lane = lane & 3;  // M == 1: which K-block of the group
+  const u4 *xa = (const u4 *)(s_xp + (size_t)(diag ? a_lane : 0) * Kp) + q;
+  const u4 *dtab_l = s_dtab + (lane & (GV_REP - 1));  // this lane's replica
 
-  for (int u = wv; u < w.units; u += W) {
-    const uint8_t *ub = tile + (size_t)u * UNIT_BYTES;
-    const u4 S = *(const u4 *)(ub + PLANE_SIGN + 16 * lane);
-    const u4 L = *(const u4 *)(ub + PLANE_LOW + 16 * lane);
-    const uint32_t H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * lane);
-    if (diag) {
+  for (int t = t_begin; t < t_end; ++t) {
+    // prefetch the next item's codes
+    int un = u, rn = rt + 1;
+    if (rn == R) {
+      rn = 0;
+      ++un;
+    }
+    u4 S2 = S, L2 = L;
+    uint32_t H2 = H;
+    if (t + 1 < t_end) {
+      const uint8_t *ub = codes0 + (size_t)(rn * U + un) * UNIT_BYTES;
+      S2 = *(const u4 *)(ub + PLANE_SIGN + 16 * lane);
+      L2 = *(const u4 *)(ub + PLANE_LOW + 16 * lane);
+      H2 = *(const uint32_t *)(ub + PLANE_HIGH + 4 * lane);
+    }
+    float tmp[M];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) A[i] = xa[64 * u + 4 * i];
+    for (int a = 0; a < M; ++a) tmp[a] = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (M == 1) {
+        // lane 20q + j feeds only K-block 4g + j of the group; every other
+        // lane keeps zeros in A[j]
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (diag && j_lane == j) A[j] = xa[64 * u + 4 * (4 * g + j)];
+      } else if (diag) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A[j] = xa[64 * u + 16 * g + 4 * j];
+      }
+      if (M == 1) {
+        f4 C = (f4){0.f, 0.f, 0.f, 0.f};
+        float Rv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * g + j;
+          const uint32_t idx = code_index(L, H, i);
+          const u4 D = apply_signs(dtab_l[(idx & 0xFFu) * GV_REP], S, i);
+          C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, A[j]),
+                                                     __builtin_bit_cast(h8, D), C, 0, 0, 0);
+          Rv[j] = (float)s_rtab[idx >> bd];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tmp[0] = __builtin_fmaf(Rv[j], C[j], tmp[0]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * g + j;
+          const uint32_t idx = code_index(L, H, i);
+          const u4 D = apply_signs(dtab_l[(idx & 0xFFu) * GV_REP], S, i);
+          const f4 C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, A[j]),
+                                                              __builtin_bit_cast(h8, D),
+                                                              (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          const float Rv = (float)s_rtab[idx >> bd];
+#pragma unroll
+          for (int a = 0; a < M; ++a) tmp[a] = __builtin_fmaf(Rv, C[a], tmp[a]);
+        }
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t idx = code_index(L, H, i);
-      const u4 D = apply_signs(s_dtab[idx & 0xFFu], S, i);
-      const f4 C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, A[i]),
-                                                          __builtin_bit_cast(h8, D),
-                                                          (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      const float R = (float)s_rtab[idx >> bd];
+    for (int a = 0; a < M; ++a) {
+      const float sc = s_scale[u * M + a];
 #pragma unroll
-      for (int a = 0; a < M; ++a) acc[a] = __builtin_fmaf(R, C[a], acc[a]);
+      for (int r = 0; r < GV_MAX_R; ++r)
+        if (r == rt) acc[r][a] = __builtin_fmaf(tmp[a], sc, acc[r][a]);
     }
+    S = S2;
+    L = L2;
+    H = H2;
+    u = un;
+    rt = rn;
   }
+
 #pragma unroll
-  for (int a = 0; a < M; ++a) {
-    acc[a] += __shfl_xor(acc[a], 16);
-    acc[a] += __shfl_xor(acc[a], 32);
-  }
-  if (lane < 16) {
+  for (int r = 0; r < GV_MAX_R; ++r) {
 #pragma unroll
-    for (int a = 0; a < M; ++a) s_red[wv][a][lane] = acc[a];
+    for (int a = 0; a < M; ++a) {
+      float v = acc[r][a];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 16) s_red[((wv * GV_MAX_R + r) * M + a) * 16 + lane] = v;
+    }
   }
   __syncthreads();
-  if (tid < 16 * M) {
-    const int a = tid >> 4, r = tid & 15;
-    float s = 0.f;
-    for (int j = 0; j < W; ++j) s += s_red[j][a][r];
-    s = ldexpf(s, -escale[a]);
-    const int n = rt * 16 + r;
-    if (n < w.n) store_out(y, (size_t)a * ldy + n, s, ydt);
+  for (int o = tid; o < R * M * 16; o += 256) {
+    const int r = o / (M * 16), a = (o / 16) % M, row = o & 15;
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < GV_WAVES; ++j) sum += s_red[((j * GV_MAX_R + r) * M + a) * 16 + row];
+    const int n = (rt0 + r) * 16 + row;
+    if (n < w.n) store_out(y, (size_t)a * ldy + n, sum, ydt);
   }
 }
 
 template <int M>
-__global__ __launch_bounds__(512) void gemv_exact_kernel(MatView w, const uint16_t *__restrict__ xw,
-                                                         const int32_t *__restrict__ escale,
-                                                         void *__restrict__ y, int64_t ldy, int ydt) {
-  __shared__ u4 s_dtab[256];
-  __shared__ _Float16 s_rtab[16];
-  __shared__ float s_red[8][EXACT_MAX_M][16];
-  gemv_exact_tile<M>(w, blockIdx.x, xw, escale, y, ldy, ydt, s_dtab, s_rtab, s_red);
+__global__ __launch_bounds__(256) void gemv_batched_kernel(GemvBatch b) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int j = 0;
+  while (j + 1 < b.count && (int)blockIdx.x >= b.job[j + 1].block_begin) ++j;
+  const GemvJob &jb = b.job[j];
+  const int rt0 = ((int)blockIdx.x - jb.block_begin) * jb.R;
+  const int R = min(jb.R, jb.w.n_tiles - rt0);
+  gemv_fused_block<M>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, R, smem);
+}
+
+size_t gemv_smem_bytes(int m, int k_max, int units_max) {
+  return (size_t)GV_SMEM_FIXED + (size_t)m * units_max * UNIT_SLOTS * 2 + (size_t)k_max * 2;
+}
+
+template <typename Kern>
+static hipError_t allow_smem(Kern k, size_t bytes) {
+  if (bytes > 64 * 1024)
+    return hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+  return hipSuccess;
+}
+
+hipError_t launch_gemv_batched(GemvBatch &b, int blocks, size_t smem, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  switch (b.m) {
+    case 1:
+      e = allow_smem(gemv_batched_kernel<1>, smem);
+      if (e == hipSuccess) hipLaunchKernelGGL(gemv_batched_kernel<1>, dim3(blocks), dim3(256), smem, s, b);
+      break;
+    case 2:
+      e = allow_smem(gemv_batched_kernel<2>, smem);
+      if (e == hipSuccess) hipLaunchKernelGGL(gemv_batched_kernel<2>, dim3(blocks), dim3(256), smem, s, b);
+      break;
+    case 3:
+      e = allow_smem(gemv_batched_kernel<3>, smem);
+      if (e == hipSuccess) hipLaunchKernelGGL(gemv_batched_kernel<3>, dim3(blocks), dim3(256), smem, s, b);
+      break;
+    default:
+      e = allow_smem(gemv_batched_kernel<4>, smem);
+      if (e == hipSuccess) hipLaunchKernelGGL(gemv_batched_kernel<4>, dim3(blocks), dim3(256), smem, s, b);
+      break;
+  }
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -312,39 +537,22 @@ __device__ __forceinline__ MatView expert_view(const MoeShape &sh, const ExpertT
   return v;
 }
 
-// Exact per-slot preparation: slot q's activation row permuted by its
-// expert's permutation.
-__global__ __launch_bounds__(256) void moe_prep_exact_kernel(MoeShape sh, ExpertTable tab,
-                                                              const uint16_t *__restrict__ x,
-                                                              int64_t ldx, int x_per_slot, int topk,
-                                                              const int32_t *__restrict__ ids,
-                                                              uint16_t *__restrict__ xw,
-                                                              int32_t *__restrict__ escale) {
-  __shared__ float red4[4];
-  const int q = blockIdx.x;
-  const int e = ids[q];
-  const int src = x_per_slot ? q : q / topk;
-  const int Kp = sh.units * UNIT_SLOTS;
-  prep_exact_row((const uint16_t *)(tab.base[e] + sh.off_perm), sh.k, Kp, x + (int64_t)src * ldx,
-                 xw + (size_t)q * Kp, escale + q, red4);
-}
-
-// Exact per-slot GEMV: block (row tile, slot).
-__global__ __launch_bounds__(512) void moe_gemv_exact_kernel(MoeShape sh, ExpertTable tab,
-                                                             const int32_t *__restrict__ ids,
-                                                             const uint16_t *__restrict__ xw,
-                                                             const int32_t *__restrict__ escale,
-                                                             void *__restrict__ y, int64_t ldy,
-                                                             int ydt) {
-  __shared__ u4 s_dtab[256];
-  __shared__ _Float16 s_rtab[16];
-  __shared__ float s_red[8][EXACT_MAX_M][16];
+// Per-slot fused GEMV (one activation row per slot): block (row group, slot),
+// matrix = the slot's expert.
+__global__ __launch_bounds__(256) void moe_gemv_kernel(MoeShape sh, ExpertTable tab,
+                                                       const int32_t *__restrict__ ids,
+                                                       const uint16_t *__restrict__ x, int64_t ldx,
+                                                       int x_per_slot, int topk,
+                                                       void *__restrict__ y, int64_t ldy, int ydt,
+                                                       int R) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int q = blockIdx.y;
   const MatView w = expert_view(sh, tab, ids[q]);
-  const int Kp = sh.units * UNIT_SLOTS;
+  const int src = x_per_slot ? q : q / topk;
+  const int rt0 = blockIdx.x * R;
+  const int Reff = min(R, w.n_tiles - rt0);
   char *yq = (char *)y + (size_t)q * ldy * (ydt == 0 ? 2 : 4);
-  gemv_exact_tile<1>(w, blockIdx.x, xw + (size_t)q * Kp, escale + q, yq, ldy, ydt, s_dtab, s_rtab,
-                     s_red);
+  gemv_fused_block<1>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, Reff, smem);
 }
 
 // Routing for the grouped GEMM: counting sort of slots by expert and a list
@@ -448,25 +656,6 @@ __global__ __launch_bounds__(256) void moe_gemm_bf16_kernel(MoeShape sh, ExpertT
 // Launchers
 // ---------------------------------------------------------------------------
 
-hipError_t launch_prep_exact(const MatView &w, const uint16_t *x, int64_t ldx, int m, uint16_t *xw,
-                             int32_t *escale, hipStream_t s) {
-  hipLaunchKernelGGL(prep_exact_kernel, dim3(m), dim3(256), 0, s, w, x, ldx, xw, escale);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemv_exact(const MatView &w, const uint16_t *xw, const int32_t *escale, int m,
-                             void *y, int64_t ldy, int ydt, hipStream_t s) {
-  const int waves = w.units < 8 ? w.units : 8;
-  dim3 grid(w.n_tiles), block(64 * waves);
-  switch (m) {
-    case 1: hipLaunchKernelGGL(gemv_exact_kernel<1>, grid, block, 0, s, w, xw, escale, y, ldy, ydt); break;
-    case 2: hipLaunchKernelGGL(gemv_exact_kernel<2>, grid, block, 0, s, w, xw, escale, y, ldy, ydt); break;
-    case 3: hipLaunchKernelGGL(gemv_exact_kernel<3>, grid, block, 0, s, w, xw, escale, y, ldy, ydt); break;
-    default: hipLaunchKernelGGL(gemv_exact_kernel<4>, grid, block, 0, s, w, xw, escale, y, ldy, ydt); break;
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_prep_bf16(const MatView &w, const uint16_t *x, int64_t ldx, int m, int m_pad,
                             uint16_t *xb, hipStream_t s) {
   const int stage = w.k <= 32768 ? 1 : 0;
@@ -518,17 +707,14 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   }
   const uint16_t *xp = (const uint16_t *)x;
   if (S <= MOE_EXACT_MAX_SLOTS) {
-    const size_t o_esc = align256((size_t)S * Kp * 2);
-    *need = o_esc + align256((size_t)S * 4);
+    *need = 256;
     if (!ws) return hipSuccess;
-    if (ws_bytes < *need) return hipErrorInvalidValue;
-    uint16_t *xw = (uint16_t *)ws;
-    int32_t *esc = (int32_t *)((uint8_t *)ws + o_esc);
-    hipLaunchKernelGGL(moe_prep_exact_kernel, dim3(S), dim3(256), 0, s, sh, tab, xp, ldx,
-                       x_per_slot, topk, ids, xw, esc);
-    const int waves = sh.units < 8 ? sh.units : 8;
-    hipLaunchKernelGGL(moe_gemv_exact_kernel, dim3(sh.n_tiles, S), dim3(64 * waves), 0, s, sh, tab,
-                       ids, (const uint16_t *)xw, (const int32_t *)esc, y, ldy, ydt);
+    const int R = 1;
+    const size_t smem = gemv_smem_bytes(1, sh.k, sh.units);
+    hipError_t e = allow_smem(moe_gemv_kernel, smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(moe_gemv_kernel, dim3((sh.n_tiles + R - 1) / R, S), dim3(256), smem, s, sh,
+                       tab, ids, xp, ldx, x_per_slot, topk, y, ldy, ydt, R);
     return hipGetLastError();
   }
   const int rows_per_item = 16 * GEMM_BMT;

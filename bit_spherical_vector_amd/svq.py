@@ -33,7 +33,8 @@ SVQ_ERR_HIP = -4
 SVQ_BF16 = 0
 SVQ_F32 = 1
 
-EXPORTED = ("svq_pack", "svq_linear", "svq_moe_linear", "svq_status_string")
+EXPORTED = ("svq_pack", "svq_linear", "svq_linear_batched", "svq_moe_linear",
+            "svq_status_string")
 
 
 class SvqError(RuntimeError):
@@ -79,6 +80,14 @@ def _load() -> ctypes.CDLL:
     lib.svq_linear.argtypes = [ctypes.POINTER(Handle), ctypes.c_void_p, ctypes.c_int64,
                                ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
+    lib.svq_linear_batched.restype = ctypes.c_int
+    lib.svq_linear_batched.argtypes = [ctypes.POINTER(Handle), ctypes.c_int32,
+                                       ctypes.POINTER(ctypes.c_void_p),
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+                                       ctypes.POINTER(ctypes.c_void_p),
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
+                                       ctypes.c_void_p]
     lib.svq_moe_linear.restype = ctypes.c_int
     lib.svq_moe_linear.argtypes = [ctypes.POINTER(Handle), ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
@@ -117,6 +126,16 @@ def svq_linear(handle: Handle, x_ptr: int, m: int, ldx: int, y_ptr: int, ldy: in
     nbytes = ctypes.c_size_t(ws_bytes)
     st = LIB.svq_linear(ctypes.byref(handle), x_ptr, m, ldx, y_ptr, ldy, ydt, ws_ptr,
                         ctypes.byref(nbytes), stream)
+    return st, nbytes.value
+
+
+def svq_linear_batched(handles, count: int, x_ptrs, ldx, m: int, y_ptrs, ldy, ydt: int,
+                       ws_ptr: Optional[int], ws_bytes: int, stream: int) -> tuple:
+    """handles: ctypes array of Handle; x_ptrs/y_ptrs: ctypes c_void_p arrays;
+    ldx/ldy: ctypes c_int64 arrays (or None for a workspace query)."""
+    nbytes = ctypes.c_size_t(ws_bytes)
+    st = LIB.svq_linear_batched(handles, count, x_ptrs, ldx, m, y_ptrs, ldy, ydt, ws_ptr,
+                                ctypes.byref(nbytes), stream)
     return st, nbytes.value
 
 
@@ -216,6 +235,47 @@ def linear(pm: PackedMatrix, x, out=None, out_dtype=None, workspace=None, stream
                        ydt, workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
     _check(st, "svq_linear")
     return out
+
+
+class BatchedCall:
+    """Pre-marshalled arguments of one svq_linear_batched call (device
+    tensors are owned by the caller and must outlive the object)."""
+
+    def __init__(self, pms: Sequence[PackedMatrix], xs, ys, workspace=None, stream=None):
+        import torch
+        n = len(pms)
+        self.keep = (list(pms), list(xs), list(ys))
+        self.handles = handle_array(pms)
+        self.count = n
+        self.m = xs[0].shape[0]
+        self.x_ptrs = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+        self.y_ptrs = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+        self.ldx = (ctypes.c_int64 * n)(*[x.stride(0) for x in xs])
+        self.ldy = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
+        self.ydt = SVQ_F32 if ys[0].dtype == torch.float32 else SVQ_BF16
+        st, need = svq_linear_batched(self.handles, n, None, None, self.m, None, None, self.ydt,
+                                      None, 0, 0)
+        _check(st, "svq_linear_batched (workspace query)")
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xs[0].device)
+        self.workspace = workspace
+        self.stream = _stream_handle(stream)
+
+    def __call__(self) -> None:
+        st, _ = svq_linear_batched(self.handles, self.count, self.x_ptrs, self.ldx, self.m,
+                                   self.y_ptrs, self.ldy, self.ydt, self.workspace.data_ptr(),
+                                   self.workspace.numel(), self.stream)
+        _check(st, "svq_linear_batched")
+
+
+def linear_batched(pms: Sequence[PackedMatrix], xs, outs=None, out_dtype=None, stream=None):
+    """svq_linear over several matrices sharing m in one call."""
+    import torch
+    if outs is None:
+        outs = [torch.empty((x.shape[0], pm.n), dtype=out_dtype or torch.bfloat16,
+                            device=x.device) for pm, x in zip(pms, xs)]
+    BatchedCall(pms, xs, outs, stream=stream)()
+    return outs
 
 
 def handle_array(pms: Sequence[PackedMatrix]):

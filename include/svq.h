@@ -135,6 +135,18 @@ svq_status svq_linear(const svq_handle *w, const void *x, int64_t m, int64_t ldx
                       void *y, int64_t ldy, svq_dtype ydt,
                       void *workspace, size_t *workspace_bytes, void *stream);
 
+/* svq_linear_batched: svq_linear for `count` (1..8) independent matrices
+ * that share m, e.g. the linears of one decoder layer, in one call (a single
+ * kernel launch when m <= 4).  Arrays are host arrays of length count:
+ * w[j] (packed matrices, shapes may differ), x[j] / ldx[j] (device bf16
+ * inputs), y[j] / ldy[j] (device outputs of type ydt).  The workspace query
+ * (workspace == NULL) only needs w, count, m and ydt; ldx / ldy are checked
+ * when given.  Same numerics, ownership and error rules as svq_linear. */
+svq_status svq_linear_batched(const svq_handle *w, int32_t count, const void *const *x,
+                              const int64_t *ldx, int64_t m, void *const *y, const int64_t *ldy,
+                              svq_dtype ydt, void *workspace, size_t *workspace_bytes,
+                              void *stream);
+
 /* svq_moe_linear: one projection of a routed mixture of experts, one output
  * row per routed (token, expert) slot; the grouped form of svq_linear.
  *   experts:      host array of num_experts packed matrices, all with the

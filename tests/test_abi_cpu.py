@@ -22,7 +22,8 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol():
     declared = _declared_functions()
-    assert set(declared) == {"svq_pack", "svq_linear", "svq_moe_linear", "svq_status_string"}
+    assert set(declared) == {"svq_pack", "svq_linear", "svq_linear_batched", "svq_moe_linear",
+                             "svq_status_string"}
     for name in declared:
         assert hasattr(svq.LIB, name), name
     assert set(declared) == set(svq.EXPORTED)
@@ -44,7 +45,7 @@ def _desc(mat, **over):
 def _expected_bytes(n, k):
     a = lambda v: (v + 255) // 256 * 256
     tiles, units = (n + 15) // 16, (k + 511) // 512
-    return a(4096) + a(256) + a(16384) + a(2 * k) + a(tiles * units * 2304)
+    return a(4096) + a(256) + a(16384) + a(2 * units * 512) + a(tiles * units * 2304)
 
 
 @pytest.mark.parametrize("n,k,bd", [(512, 1024, 8), (37, 104, 6), (1, 8, 7), (2048, 768, 7)])
@@ -126,7 +127,7 @@ def _fake_handle(n, k, bd):
     h.off_rtab = a(4096)
     h.off_btab = h.off_rtab + a(256)
     h.off_perm = h.off_btab + a(16384)
-    h.off_codes = h.off_perm + a(2 * k)
+    h.off_codes = h.off_perm + a(2 * h.units * 512)
     h.padded_code_bytes = h.n_tiles * h.units * 2304
     h.bytes = h.off_codes + a(h.padded_code_bytes)
     h.code_bytes = (n * k * 9 + 31) // 32
@@ -135,8 +136,7 @@ def _fake_handle(n, k, bd):
 
 def test_linear_workspace_query_and_validation():
     h = _fake_handle(512, 1024, 8)
-    for m, expect in [(1, 2048 + 256), (4, 4 * 2048 + 256), (5, 64 * 2048), (64, 64 * 2048),
-                      (65, 128 * 2048)]:
+    for m, expect in [(1, 256), (4, 256), (5, 64 * 2048), (64, 64 * 2048), (65, 128 * 2048)]:
         st, need = svq.svq_linear(h, None, m, 1024, None, 512, svq.SVQ_BF16, None, 0, 0)
         assert st == svq.SVQ_OK and need == expect, (m, need)
     # bad arguments
@@ -177,3 +177,26 @@ def test_moe_workspace_query_and_validation():
         svq.SVQ_ERR_INVALID_ARG
     assert svq.svq_moe_linear(hs, 0, None, 2048, 0, None, 1, 1, None, 768, 0, None, 0, 0)[0] == \
         svq.SVQ_ERR_UNSUPPORTED
+
+
+def test_linear_batched_query_and_validation():
+    hs = (svq.Handle * 3)(_fake_handle(512, 1024, 8), _fake_handle(64, 2560, 6),
+                          _fake_handle(300, 768, 7))
+    st, need = svq.svq_linear_batched(hs, 3, None, None, 1, None, None, 0, None, 0, 0)
+    assert st == svq.SVQ_OK and need == 256
+    st, need = svq.svq_linear_batched(hs, 3, None, None, 16, None, None, 0, None, 0, 0)
+    a = lambda v: (v + 255) // 256 * 256
+    assert st == svq.SVQ_OK and need == a(64 * 1024 * 2) + a(64 * 2560 * 2) + a(64 * 1024 * 2)
+    assert svq.svq_linear_batched(hs, 0, None, None, 1, None, None, 0, None, 0, 0)[0] == \
+        svq.SVQ_ERR_INVALID_ARG
+    assert svq.svq_linear_batched(hs, 9, None, None, 1, None, None, 0, None, 0, 0)[0] == \
+        svq.SVQ_ERR_INVALID_ARG
+    ldx = (ctypes.c_int64 * 3)(1024, 2000, 768)  # 2000 < k of the second matrix
+    ldy = (ctypes.c_int64 * 3)(512, 64, 300)
+    assert svq.svq_linear_batched(hs, 3, None, ldx, 1, None, ldy, 0, None, 0, 0)[0] == \
+        svq.SVQ_ERR_INVALID_ARG
+    ldx[1] = 2560
+    assert svq.svq_linear_batched(hs, 3, None, ldx, 1, None, ldy, 0, None, 0, 0)[0] == svq.SVQ_OK
+    # missing pointer arrays with a workspace
+    assert svq.svq_linear_batched(hs, 3, None, ldx, 1, None, ldy, 0, 0x1000, 4096, 0)[0] == \
+        svq.SVQ_ERR_INVALID_ARG

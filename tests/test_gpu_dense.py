@@ -184,3 +184,21 @@ def test_subnormal_codebook_entries_decode_exactly(svq):
     W = so.decode_matrix(mat.codes, mat.n, mat.k, mat.bd, mat.codebook, mat.radius, mat.perm)
     _one_hot_check(svq, pm, W, list(range(0, 512, 3)), 4)
     _one_hot_check(svq, pm, W, list(range(0, 512, 37)), 16)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+def test_batched_layer_call(svq, m):
+    """All seven layer matrices through one svq_linear_batched call."""
+    mats, xs1 = synth.dense_layer()
+    xs = xs1 if m == 1 else [synth.random_activations(m, w.k, seed=(35, m, j))
+                             for j, w in enumerate(mats)]
+    pms = [svq.pack(w) for w in mats]
+    xd = [to_device_bf16(x) for x in xs]
+    outs = svq.linear_batched(pms, xd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for w, x, o in zip(mats, xs, outs):
+        y64, W = so.linear_from_inputs(w, x)
+        y = out_to_f64(o)
+        assert_within_tolerance(y, y64, x, W, label=f"batched {w.name} m={m}")
+        if m <= 4:
+            assert_within_tolerance(y, y64, x, W, rel=1e-3, label=f"batched exact {w.name}")
