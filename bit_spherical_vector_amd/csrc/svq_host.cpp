@@ -118,13 +118,12 @@ svq_status validate_handle(const svq_handle *w) {
 void build_image(const svq_matrix_desc *d, const Layout &L, std::vector<uint8_t> &img) {
   img.assign(L.bytes, 0);
   const uint32_t dmask = (1u << d->bd) - 1;
-  const int nr = 1 << d->br;
   // direction rows by low index byte
   uint16_t *dtab = (uint16_t *)(img.data() + L.off_dtab);
   for (int b = 0; b < 256; ++b)
     for (int l = 0; l < 8; ++l) dtab[b * 8 + l] = d->dir_codebook[(b & dmask) * 8 + l];
   uint16_t *rtab = (uint16_t *)(img.data() + L.off_rtab);
-  for (int r = 0; r < nr; ++r) rtab[r] = d->radius_table[r];
+  for (int idx = 0; idx < 1024; ++idx) rtab[idx] = d->radius_table[idx >> d->bd];
   // bf16 products by full 10-bit index: R*D is exact in float (22 bits)
   uint16_t *btab = (uint16_t *)(img.data() + L.off_btab);
   for (int idx = 0; idx < 1024; ++idx) {
@@ -151,8 +150,9 @@ void build_image(const svq_matrix_desc *d, const Layout &L, std::vector<uint8_t>
       if (byte + 2 < nbytes) wv |= (uint32_t)st[byte + 2] << 16;
       const uint32_t code = (wv >> (bit & 7)) & FIELD_MASK;
       const int64_t u = c / UNIT_CODES, cc = c % UNIT_CODES;
-      const int q = (int)(cc & 3), kb = (int)(cc >> 2);
-      const int lane = (int)rho + 16 * q;
+      // lane 4b + j, code kb = 4*ri + ci: row 4*ri + j, column 16*ci + b
+      const int lane = 4 * (int)(cc & 15) + (int)(rho & 3);
+      const int kb = 4 * (int)(rho >> 2) + (int)(cc >> 4);
       uint8_t *ub = codes + ((size_t)rt * L.units + (size_t)u) * UNIT_BYTES;
       uint32_t *S = (uint32_t *)(ub + PLANE_SIGN + 16 * lane);
       for (int j = 0; j < 4; ++j) {
@@ -240,13 +240,11 @@ svq_status svq_pack(const svq_matrix_desc *src, void *dst_dev, size_t *dst_bytes
 }
 
 // Exact path (m <= 4): plan the blocks of one fused launch over `count`
-// matrices.  R (row tiles per block) gives each block about 20 work items
-// (row tile x 512-slot unit, ~46 KB of codes), so blocks of different K
-// carry similar work; R shrinks while the launch has fewer than 512 blocks.
+// matrices.  R (row tiles per block, 1, 2 or 4) is the largest that keeps
+// every wave's work items (one 512-slot unit of one row tile each) within
+// GV_ITEMS_PER_WAVE; R halves while the launch has fewer than 512 blocks.  Jobs with the largest k come first (their
+// blocks run longest).
 static int plan_gemv(GemvBatch &b) {
-  // longest blocks first: jobs with the largest k (longest prologue and the
-  // most units per row tile) get the lowest block ids, so they are
-  // dispatched first
   for (int i = 1; i < b.count; ++i)
     for (int j = i; j > 0 && b.job[j].w.k > b.job[j - 1].w.k; --j) {
       const GemvJob t = b.job[j];
@@ -256,8 +254,7 @@ static int plan_gemv(GemvBatch &b) {
   int R[GV_MAX_JOBS];
   for (int j = 0; j < b.count; ++j) {
     const int U = b.job[j].w.units;
-    int r = 20 / U;
-    R[j] = r < 1 ? 1 : (r > 4 ? 4 : r);
+    R[j] = U <= GV_ITEMS_PER_WAVE ? 4 : (U <= 2 * GV_ITEMS_PER_WAVE ? 2 : 1);
   }
   auto total = [&]() {
     int t = 0;
@@ -269,7 +266,7 @@ static int plan_gemv(GemvBatch &b) {
     for (int j = 0; j < b.count; ++j)
       if (R[j] > 1 && (best < 0 || R[j] > R[best])) best = j;
     if (best < 0) break;
-    --R[best];
+    R[best] /= 2;
   }
   int begin = 0;
   for (int j = 0; j < b.count; ++j) {
@@ -335,8 +332,11 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
       b.job[j].y = ys[j];
       b.job[j].ldy = ldy[j];
     }
+    bool xvec = true;
+    for (int32_t j = 0; j < count; ++j)
+      if ((((uintptr_t)xs[j]) | ((uintptr_t)ldx[j] * 2)) & 15) xvec = false;
     const int blocks = plan_gemv(b);
-    e = launch_gemv_batched(b, blocks, gemv_smem_bytes((int)m, k_max, u_max), s);
+    e = launch_gemv_batched(b, blocks, gemv_smem_bytes((int)m, k_max, u_max), xvec, s);
   } else {
     uint8_t *ws = (uint8_t *)workspace;
     for (int32_t j = 0; j < count && e == hipSuccess; ++j) {

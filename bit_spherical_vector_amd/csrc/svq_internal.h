@@ -4,20 +4,22 @@
 //
 //   dtab   256 x 8 fp16   row b = D[b & ((1<<bd)-1)]: the direction row picked
 //                         by the low byte of a code's 10-bit index
-//   rtab   16 fp16        R[r], zero padded to 16 entries
+//   rtab   1024 fp16      entry idx = R[idx >> bd]: the radius picked by the
+//                         10-bit index (direction | radius << bd)
 //   btab   1024 x 8 bf16  row idx = RNE_bf16(R[idx >> bd] * D[idx & mask][l])
 //   perm   units*512 uint16  slot p takes input channel perm[p]; slots
 //                         p >= k hold 0 (padding, multiplied by zero)
 //   codes  n_tiles x units coded units of UNIT_BYTES each
 //
 // A coded unit covers 16 output rows x 64 consecutive codes (512 permuted
-// input slots).  It is laid out for one wavefront of 64 lanes: lane L owns
-// row (L & 15) of the tile and, for i = 0..15, the code in column
-// 64*u + 4*i + (L >> 4).  That is exactly the B operand of a
-// v_mfma_*_16x16x32 instruction for K-block i (lane L holds 8 consecutive k
-// of column L & 15), so a lane decodes straight into MFMA registers.
-// The 18 bits of the lane's 16 codes are split into three planes so that
-// every lane reads them with three coalesced loads:
+// input slots) and is laid out for one wavefront of 64 lanes.  Lane
+// L = 4b + j (b = L >> 2, j = L & 3) owns 16 codes; its code i = 4*ri + ci
+// (ri, ci in 0..3) sits in row 4*ri + j of the tile and code column
+// 16*ci + b of the unit.  The four lanes 4b..4b+3 thus hold four rows of one
+// code column, the shape of one block of v_mfma_f32_4x4x4_16b_f16 (the
+// activations of that column are shared by the block), and a lane holds only
+// four distinct code columns.  The 18 bits of the lane's 16 codes are split
+// into three planes so that every lane reads them with three coalesced loads:
 //
 //   bytes    0..1023  sign plane: lane L's 16 bytes are dwords S0..S3;
 //                     bit (15-i) of S_j = sign bit 2j of code i,
@@ -46,7 +48,7 @@ constexpr int PLANE_SIGN = 0;
 constexpr int PLANE_LOW = 1024;
 constexpr int PLANE_HIGH = 2048;
 constexpr int DTAB_BYTES = 256 * 16;
-constexpr int RTAB_BYTES = 256;   // 16 fp16, padded
+constexpr int RTAB_BYTES = 1024 * 2;  // radius by 10-bit index, fp16
 constexpr int BTAB_BYTES = 1024 * 16;
 constexpr int EXACT_MAX_M = 4;    // m <= 4: exact fp32 decode path
 constexpr int MAX_EXPERTS = 256;
@@ -64,8 +66,8 @@ struct MatView {
 
 // ---- dense path ---------------------------------------------------------
 // Exact path (m <= 4): one fused kernel per call (gather, scale, decode and
-// multiply) over up to GV_MAX_JOBS matrices; a block owns R row tiles of one
-// matrix ("job").
+// multiply) over up to GV_MAX_JOBS matrices; a block owns R in {1, 2, 4} row
+// tiles of one matrix ("job").
 constexpr int GV_MAX_JOBS = 8;
 struct GemvJob {
   MatView w;
@@ -82,7 +84,9 @@ struct GemvBatch {
 };
 constexpr size_t GV_LDS_LIMIT = 160 * 1024;  // LDS per workgroup on gfx950
 size_t gemv_smem_bytes(int m, int k_max, int units_max);
-hipError_t launch_gemv_batched(GemvBatch &b, int blocks, size_t smem, hipStream_t s);
+// xvec: every activation row of every job starts 16-byte aligned.
+hipError_t launch_gemv_batched(GemvBatch &b, int blocks, size_t smem, bool xvec, hipStream_t s);
+constexpr int GV_ITEMS_PER_WAVE = 5;  // work items per wave the planner aims for
 
 // bf16 path (m > 4): prep writes xb = x[row][perm[p]] (bf16), zero padded to
 // m_pad rows and units*512 slots; the GEMM kernel multiplies.

@@ -32,6 +32,8 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __builtin_bit_cast(float, b << 16);
@@ -50,65 +52,69 @@ __device__ __forceinline__ void store_out(void *y, size_t i, float v, int ydt) {
   else ((float *)y)[i] = v;
 }
 
-// Apply the 8 sign bits of code i (carried in S, see svq_internal.h) to the
-// 8 fp16/bf16 values in D: the sign bit of every 16-bit half is bit 15/31.
-__device__ __forceinline__ u4 apply_signs(u4 D, u4 S, int i) {
-  const uint32_t M = 0x80008000u;
-  D[0] ^= (S[0] << i) & M;
-  D[1] ^= (S[1] << i) & M;
-  D[2] ^= (S[2] << i) & M;
-  D[3] ^= (S[3] << i) & M;
-  return D;
-}
-
-// 10-bit index of code i from the two index planes.
-__device__ __forceinline__ uint32_t code_index(u4 L, uint32_t H, int i) {
-  uint32_t lo = (L[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-  return lo | (((H >> (2 * i)) & 3u) << 8);
-}
-
 // ---------------------------------------------------------------------------
 // Exact path (m <= 4), fused: gather + scale + decode-and-multiply in one
 // kernel.
 // ---------------------------------------------------------------------------
 //
-// A block owns R consecutive 16-row tiles of one matrix and all of its K.
-// Prologue: the block stages each activation row in LDS, and its 4 waves
-// gather the permuted slots (Fig. 6 caption: a subvector multiplies eight
-// reordered activations) unit by unit.  Each 512-slot unit u gets its own
-// exact power-of-two scale 2^e_u with max|x_u| * 2^e_u in [2^14, 2^15), so
-// the fp16 copy is exact for every bf16 value above 2^-17 * max|x_u|; the
-// scale is undone once per (row tile, unit) in fp32.
+// A block owns R in {1, 2, 4} consecutive 16-row tiles of one matrix and all
+// of its K; each tile gets 4/R of the block's 4 waves, which split its 512-slot
+// units between them.
+// Prologue: the block stages each activation row in LDS and gathers the
+// permuted slots (Fig. 6 caption: a subvector multiplies eight reordered
+// activations) unit by unit.  Each unit u gets its own exact power-of-two
+// scale 2^e_u with max|x_u| * 2^e_u in [2^14, 2^15), so the fp16 copy is
+// exact for every bf16 value above 2^-17 * max|x_u|; the scale is undone once
+// per (row tile, unit) in fp32.
 //
-// Main loop: work item t = rt*U + u (row tile rt, unit u) goes to wave
-// t mod 4.  The item's 2304 code bytes are contiguous and prefetched one
-// item ahead.  MFMA mapping for K-block i of the unit (4 codes):
-//   B[k][n]: lane L holds the signed direction row of its code (row n =
-//            L & 15, code group q = L >> 4), k = 8q..8q+7.
-//   A[m][k]: m = 4q' + a; lane L holds A[L & 15][k-group L >> 4], which is
-//            non-zero only on the "diagonal" lanes (L & 15) >> 2 == L >> 4,
-//            where it is the 8 scaled activations of code 4i + q for
-//            activation row a = L & 3 (read from LDS under the exec mask,
-//            so the other lanes keep their zeros).
-//   C[m][n]: lane L receives rows 4q + a of column L & 15: the dot products
-//            of exactly the code it decoded, one per activation row.
-// The radius multiply R[r] * dot is an fp32 FMA per code; R*D is never
-// rounded.  Partial sums meet in LDS at the end of the block.
+// Main loop: one work item is one coded unit (16 rows x 64 codes, 2304
+// contiguous bytes, 36 per lane).  The codes of up to GV_PIPE items are in
+// flight per wave, issued before the prologue so that their HBM latency
+// overlaps it.  MFMA mapping (v_mfma_f32_4x4x4_16b_f16: 16 blocks of 4 lanes,
+// lane 4b + j):
+//   B: lane 4b + j holds 4 signed direction values of its code (one half of
+//      the code's 8), column j of block b;
+//   A: lane 4b + j holds the matching 4 scaled activations of activation row
+//      j (rows >= m repeat row 0), row j of block b; all four lanes of a
+//      block share the code column, so A is read once per column group and
+//      reused for the 4 codes of that column;
+//   C: lane 4b + j receives, for activation row a, the dot product of its
+//      own code's half with row a; two chained halves give the code's 8-term
+//      dot product.
+// The radius multiply R[r] * dot is an fp32 FMA per code, so R*D is never
+// rounded.  Partial sums meet across lanes (shuffles) and waves (LDS).
 
 constexpr int GV_WAVES = 4;
-constexpr int GV_MAX_R = 4;
-// LDS: direction table (GV_REP copies interleaved: row b, copy j at
-// b*16*GV_REP + 16*j; lane L reads copy L % GV_REP), radius table, unit
-// scales, cross-wave partial sums, then the permuted activations and the
-// staging row.
-constexpr int GV_REP = 1;
-constexpr int GV_DTAB_BYTES = 256 * 16 * GV_REP;
-constexpr int GV_OFF_RTAB = GV_DTAB_BYTES;
-constexpr int GV_OFF_MAX = GV_OFF_RTAB + 256;
-constexpr int GV_OFF_RED = GV_OFF_MAX + 128 * 4 * 4;  // [U <= 128][M <= 4] scales
-constexpr int GV_SMEM_FIXED = GV_OFF_RED + 4096;
-constexpr int GV_PRE_UNITS = 5;   // permutation vectors prefetched per wave
-constexpr int GV_STAGE_BATCH = 5; // x loads in flight per thread while staging
+#ifndef SVQ_GV_PIPE
+#define SVQ_GV_PIPE 2
+#endif
+// Work items whose codes are in flight per wave.  A CU can only keep a
+// limited number of requests in flight; a wave that asks for more stalls at
+// issue and cannot do other work meanwhile, so the ring is kept short and
+// refilled after each item's compute.
+constexpr int GV_PIPE = SVQ_GV_PIPE;
+constexpr int GV_PRE_UNITS = 5;   // permutation vectors prefetched per wave (gather)
+constexpr int GV_STAGE_BATCH = 5; // 16-byte activation loads per thread per staging pass
+// LDS: direction table, radius table by 10-bit index, unit scales, cross-wave
+// partial sums, then the permuted activations and the staging row.
+constexpr int GV_OFF_RTAB = DTAB_BYTES;
+constexpr int GV_OFF_SCALE = GV_OFF_RTAB + RTAB_BYTES;
+constexpr int GV_OFF_RED = GV_OFF_SCALE + 128 * 4 * 4;  // [U <= 128][M <= 4] scales
+constexpr int GV_SMEM_FIXED = GV_OFF_RED + GV_WAVES * 4 * 4 * 4 * 4;
+
+// The 36 code bytes one lane holds for one work item (16 codes).
+struct ItemCodes {
+  u4 S, L;
+  uint32_t H;
+};
+
+__device__ __forceinline__ ItemCodes load_item(const uint8_t *ub, int lane) {
+  ItemCodes c;
+  c.S = *(const u4 *)(ub + PLANE_SIGN + 16 * lane);
+  c.L = *(const u4 *)(ub + PLANE_LOW + 16 * lane);
+  c.H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * lane);
+  return c;
+}
 
 // Maximum over the 64 lanes of a non-negative float (returned in every
 // lane): DPP row shifts within the 16-lane rows, row broadcasts across rows,
@@ -124,98 +130,237 @@ __device__ __forceinline__ float wave_max(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63));
 }
 
+// (byte k of v) << SH in one VALU op (SDWA source select).
+template <int K, int SH>
+__device__ __forceinline__ uint32_t byte_shl(uint32_t v) {
+  uint32_t r;
+  if (K == 0)
+    asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r) : "v"(v), "i"(SH));
+  else if (K == 1)
+    asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(v), "i"(SH));
+  else if (K == 2)
+    asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "v"(v), "i"(SH));
+  else
+    asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "v"(v), "i"(SH));
+  return r;
+}
+
+// 64-bit left shift by a constant in one VALU op (the compiler otherwise
+// splits it into a shift and a funnel shift).
+template <int SH>
+__device__ __forceinline__ uint64_t shl64(uint64_t v) {
+  if (SH == 0) return v;
+  uint64_t r;
+  asm("v_lshlrev_b64 %0, %2, %1" : "=v"(r) : "v"(v), "i"(SH));
+  return r;
+}
+
+// Reads from the start of dynamic LDS by absolute address.  The exact-path
+// kernels declare no static LDS, so dynamic LDS begins at address 0 (checked
+// by the launcher) and the table offsets go straight into the instruction's
+// address and offset fields.
+typedef __attribute__((address_space(3))) const u4 lds_u4_t;
+typedef __attribute__((address_space(3))) const _Float16 lds_f16_t;
+__device__ __forceinline__ u4 lds_u4(uint32_t addr) { return *(lds_u4_t *)(size_t)addr; }
+__device__ __forceinline__ _Float16 lds_f16(uint32_t addr) { return *(lds_f16_t *)(size_t)addr; }
+
+// Table reads of the four codes of column group ci: direction rows (signs
+// not yet applied) and radii.
+template <int CI>
+__device__ __forceinline__ void gemv_group_reads(const ItemCodes &c, u4 (&D)[4], _Float16 (&R)[4]) {
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri) {
+    const int i = 4 * ri + CI;
+    const uint32_t lo16 = byte_shl<CI, 4>(c.L[ri]);  // low index byte * 16
+    const uint32_t lo2 = byte_shl<CI, 1>(c.L[ri]);   // low index byte * 2
+    const int sh = 9 - 2 * i;
+    const uint32_t hs = sh >= 0 ? c.H << sh : c.H >> -sh;
+    const uint32_t idx2 = (hs & 0x600u) | lo2;       // 10-bit index * 2
+    D[ri] = lds_u4(lo16);
+    R[ri] = lds_f16(GV_OFF_RTAB + idx2);
+  }
+}
+
+// Sign carriers of code i (see the sign plane): bits 15 and 31 of c[j] are
+// the signs of pair j.
+template <int I>
+__device__ __forceinline__ void sign_carriers(uint64_t S01, uint64_t S23, uint32_t (&cr)[4]) {
+  const uint64_t c01 = shl64<I>(S01), c23 = shl64<I>(S23);
+  cr[0] = (uint32_t)c01;
+  cr[1] = (uint32_t)(c01 >> 32);
+  cr[2] = (uint32_t)c23;
+  cr[3] = (uint32_t)(c23 >> 32);
+}
+
+// Decode-and-multiply of the four codes of column group ci (see the mapping
+// above): tmp[ri][a] += R * dot(code, activation row a).  The four codes go
+// through each phase together (signs, first-half MFMAs, second-half MFMAs,
+// radius FMAs), so that independent MFMAs cover each other's latency.
+template <int M, int CI>
+__device__ __forceinline__ void gemv_group_mul(uint64_t S01, uint64_t S23, const u4 &A,
+                                              const u4 (&Din)[4], const _Float16 (&R)[4],
+                                              float (&tmp)[4][M]) {
+  const uint32_t SM = 0x80008000u;
+  const h4 A0 = __builtin_bit_cast(h4, (u2){A[0], A[1]});
+  const h4 A1 = __builtin_bit_cast(h4, (u2){A[2], A[3]});
+  u4 D[4];
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri) {
+    uint32_t cr[4];
+    switch (ri) {
+      case 0: sign_carriers<CI>(S01, S23, cr); break;
+      case 1: sign_carriers<4 + CI>(S01, S23, cr); break;
+      case 2: sign_carriers<8 + CI>(S01, S23, cr); break;
+      default: sign_carriers<12 + CI>(S01, S23, cr); break;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) D[ri][j] = Din[ri][j] ^ (cr[j] & SM);
+  }
+  f4 C[4];
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri)
+    C[ri] = __builtin_amdgcn_mfma_f32_4x4x4f16(A0, __builtin_bit_cast(h4, (u2){D[ri][0], D[ri][1]}),
+                                               (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri)
+    C[ri] = __builtin_amdgcn_mfma_f32_4x4x4f16(A1, __builtin_bit_cast(h4, (u2){D[ri][2], D[ri][3]}),
+                                               C[ri], 0, 0, 0);
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri) {
+    const float Rf = (float)R[ri];
+#pragma unroll
+    for (int a = 0; a < M; ++a) tmp[ri][a] = __builtin_fmaf(Rf, C[ri][a], tmp[ri][a]);
+  }
+  // materialise the partial sums here: left alone, instruction selection
+  // sinks every radius FMA of the item to its end and keeps all 16 MFMA
+  // results live
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+    for (int a = 0; a < M; ++a) asm volatile("" : "+v"(tmp[ri][a]));
+}
+
+// One work item: the lane's 16 codes, column group by column group, with
+// the table reads of the next group issued before the current one is used.
 template <int M>
+__device__ __forceinline__ void gemv_item(const ItemCodes &c, const uint8_t *xu,
+                                          float (&tmp)[4][M]) {
+  const uint64_t S01 = (uint64_t)c.S[0] | ((uint64_t)c.S[1] << 32);
+  const uint64_t S23 = (uint64_t)c.S[2] | ((uint64_t)c.S[3] << 32);
+  u4 D0[4], D1[4];
+  _Float16 R0[4], R1[4];
+  // phases are kept in this order (scheduling barriers): the reads of group
+  // g + 1 are in flight while group g is decoded and multiplied
+  u4 A0 = *(const u4 *)(xu);
+  gemv_group_reads<0>(c, D0, R0);
+  u4 A1 = *(const u4 *)(xu + 256);
+  gemv_group_reads<1>(c, D1, R1);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_group_mul<M, 0>(S01, S23, A0, D0, R0, tmp);
+  __builtin_amdgcn_sched_barrier(0);
+  A0 = *(const u4 *)(xu + 512);
+  gemv_group_reads<2>(c, D0, R0);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_group_mul<M, 1>(S01, S23, A1, D1, R1, tmp);
+  __builtin_amdgcn_sched_barrier(0);
+  A1 = *(const u4 *)(xu + 768);
+  gemv_group_reads<3>(c, D1, R1);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_group_mul<M, 2>(S01, S23, A0, D0, R0, tmp);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_group_mul<M, 3>(S01, S23, A1, D1, R1, tmp);
+}
+
+// XVEC: every activation row starts 16-byte aligned (vector staging loads).
+template <int M, bool XVEC>
 __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ x, int64_t ldx,
                                  void *__restrict__ y, int64_t ldy, int ydt, int rt0, int R,
-                                 uint8_t *smem) {
+                                 int Reff, uint8_t *smem) {
   u4 *s_dtab = (u4 *)smem;
   _Float16 *s_rtab = (_Float16 *)(smem + GV_OFF_RTAB);
-  float *s_scale = (float *)(smem + GV_OFF_MAX);          // [U][M] 2^-e per unit
-  float *s_red = (float *)(smem + GV_OFF_RED);            // [W][GV_MAX_R][M][16]
+  float *s_scale = (float *)(smem + GV_OFF_SCALE);        // [U][M] 2^-e per unit
+  float *s_red = (float *)(smem + GV_OFF_RED);            // [W][4][M][4]
   uint16_t *s_xp = (uint16_t *)(smem + GV_SMEM_FIXED);    // [M][Kp] fp16
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int U = w.units, Kp = U * UNIT_SLOTS, K = w.k;
   uint16_t *s_stage = s_xp + (size_t)M * Kp;              // [K] bf16
-  const int items = R * U;
-  const uint8_t *codes0 = w.base + w.off_codes + (size_t)rt0 * U * UNIT_BYTES;
-  // wave wv owns the contiguous run of work items [t_begin, t_end) in
-  // unit-major order t = u*R + rt
-  const int per = (items + GV_WAVES - 1) / GV_WAVES;
-  const int t_begin = wv * per;
-  const int t_end = min(items, t_begin + per);
+  const int n8 = K / 8;
 
-  // Global loads of the prologue are issued first, in the order they are
-  // needed (vmcnt counts in order): the direction table row of this thread,
-  // the permutation vectors of the wave's units, the first activation row,
-  // and only then the first work item's codes, whose HBM latency overlaps
-  // the rest of the prologue.
-  const int u_lo = t_begin / R, u_hi = t_end > t_begin ? (t_end - 1) / R : u_lo - 1;
+  // this wave's work: tile rt0 + wt, units [u_begin, u_end)
+  const int wpt_log = R == 4 ? 0 : (R == 2 ? 1 : 2);  // log2 of waves per tile
+  const int wpt = 1 << wpt_log;
+  const int wt = wv >> wpt_log, part = wv & (wpt - 1);
+  const int uper = (U + wpt - 1) >> wpt_log;
+  const int u_begin = part * uper;
+  const int u_end = wt < Reff ? min(U, u_begin + uper) : u_begin;
+  const uint8_t *tile = w.base + w.off_codes + (size_t)(rt0 + wt) * U * UNIT_BYTES;
+  // this wave's share of the gather: units [g_lo, g_hi]
+  const int gper = (U + GV_WAVES - 1) >> 2;
+  const int g_lo = wv * gper, g_hi = min(U, g_lo + gper) - 1;
+
+  // Global loads of the prologue, all unconditional (clamped addresses) so
+  // that the wait counts stay exact, in the order they are needed: tables,
+  // permutation vectors of the wave's gather units and the first staging
+  // pass of every activation row; the codes follow once row 0 is staged.
   const u4 drow = ((const u4 *)(w.base + w.off_dtab))[tid];
+  const u2 rrow = ((const u2 *)(w.base + w.off_rtab))[tid];
   const uint16_t *perm = (const uint16_t *)(w.base + w.off_perm);
   u4 pvec[GV_PRE_UNITS];
 #pragma unroll
-  for (int j = 0; j < GV_PRE_UNITS; ++j) {
-    const int uu = u_lo + j;
-    pvec[j] = uu <= u_hi ? *(const u4 *)(perm + uu * UNIT_SLOTS + 8 * lane) : (u4){0u, 0u, 0u, 0u};
-  }
-  const int n8 = K / 8;
-  const bool x_vec = ((((uintptr_t)x) | ((uintptr_t)ldx * 2)) & 15) == 0;
-  u4 xv[GV_STAGE_BATCH];
-  if (x_vec) {
+  for (int j = 0; j < GV_PRE_UNITS; ++j)
+    pvec[j] = *(const u4 *)(perm + min(g_lo + j, U - 1) * UNIT_SLOTS + 8 * lane);
+  u4 xv[M][GV_STAGE_BATCH];
+  if (XVEC) {
 #pragma unroll
-    for (int b = 0; b < GV_STAGE_BATCH; ++b) {
-      const int j = tid + 256 * b;
-      xv[b] = j < n8 ? ((const u4 *)x)[j] : (u4){0u, 0u, 0u, 0u};
-    }
-  }
-  u4 S = (u4){0u, 0u, 0u, 0u}, L = S;
-  uint32_t H = 0;
-  int u = u_lo, rt = t_begin - u_lo * R;
-  if (t_begin < t_end) {
-    const uint8_t *ub = codes0 + (size_t)(rt * U + u) * UNIT_BYTES;
-    S = *(const u4 *)(ub + PLANE_SIGN + 16 * lane);
-    L = *(const u4 *)(ub + PLANE_LOW + 16 * lane);
-    H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * lane);
-  }
+    for (int a = 0; a < M; ++a)
 #pragma unroll
-  for (int j = 0; j < GV_REP; ++j) s_dtab[tid * GV_REP + j] = drow;
-  if (tid < 16) s_rtab[tid] = ((const _Float16 *)(w.base + w.off_rtab))[tid];
+      for (int b = 0; b < GV_STAGE_BATCH; ++b)
+        xv[a][b] = ((const u4 *)(x + (int64_t)a * ldx))[min(tid + 256 * b, n8 - 1)];
+  }
+  ItemCodes ring[GV_PIPE];
+  int ul = u_begin;  // next unit to load
+  s_dtab[tid] = drow;
+  ((u2 *)s_rtab)[tid] = rrow;
 
-  // The units this wave multiplies: its items t in [t_begin, t_end) are
-  // unit-major, so they cover units u_lo..u_hi.
-
-  // One activation row at a time: stage it in LDS (one barrier), then every
-  // wave gathers the permuted slots of its own units (Fig. 6 "reordered
-  // activations") and converts them to fp16 with a per-unit scale 2^e,
-  // chosen so that max|x_unit| * 2^e lies in [2^14, 2^15): exact for every
-  // bf16 value above 2^-17 of the unit's maximum.  Waves that share a unit
-  // write identical values.
+  // One activation row at a time: stage it in LDS, then every wave gathers
+  // the permuted slots of its gather units and converts them to fp16 with a
+  // per-unit scale 2^e, max|x_unit| * 2^e in [2^14, 2^15).  (Unrolled: xv
+  // is indexed by the row.)
+#pragma unroll
   for (int a = 0; a < M; ++a) {
     const uint16_t *xr = x + (int64_t)a * ldx;
     if (a > 0) __syncthreads();  // previous row's gathers are done
-    if (x_vec) {
-      for (int j0 = tid; j0 < n8; j0 += 256 * GV_STAGE_BATCH) {
-        if (a > 0 || j0 != tid) {
+    if (XVEC) {
 #pragma unroll
-          for (int b = 0; b < GV_STAGE_BATCH; ++b) {
-            const int j = j0 + 256 * b;
-            xv[b] = j < n8 ? ((const u4 *)xr)[j] : (u4){0u, 0u, 0u, 0u};
-          }
-        }
-#pragma unroll
-        for (int b = 0; b < GV_STAGE_BATCH; ++b) {
-          const int j = j0 + 256 * b;
-          if (j < n8) ((u4 *)s_stage)[j] = xv[b];
-        }
+      for (int b = 0; b < GV_STAGE_BATCH; ++b) {
+        const int j = tid + 256 * b;
+        if (j < n8) ((u4 *)s_stage)[j] = xv[a][b];
       }
+      for (int j = tid + 256 * GV_STAGE_BATCH; j < n8; j += 256) ((u4 *)s_stage)[j] = ((const u4 *)xr)[j];
     } else {
       for (int j = tid; j < K; j += 256) s_stage[j] = xr[j];
     }
+    if (a == 0) {
+      // The codes of the first GV_PIPE items are requested only now: while
+      // the HBM queues are still empty the activations arrive quickly, and
+      // the code latency then overlaps the gather.
+#pragma unroll
+      for (int s = 0; s < GV_PIPE; ++s) {
+        const uint8_t *ub = ul < u_end ? tile + (size_t)ul * UNIT_BYTES : w.base;
+        ring[s] = load_item(ub, lane);
+        ++ul;
+      }
+    }
     __syncthreads();
-    for (int uu = u_lo; uu <= u_hi; ++uu) {
+    for (int uu = g_lo; uu <= g_hi; ++uu) {
       const int p0 = uu * UNIT_SLOTS + 8 * lane;
       u4 pv;
-      const int j = uu - u_lo;
+      const int j = uu - g_lo;
       if (j < GV_PRE_UNITS) {
         pv = pvec[0];
 #pragma unroll
@@ -248,139 +393,97 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
       if (lane == 0) s_scale[uu * M + a] = ldexpf(1.f, -e);
     }
   }
-  // the gathered activations of a unit are read back only by the wave that
-  // wrote them (or an identical copy): a wave-level fence suffices
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __syncthreads();  // gathered activations, scales and tables are visible
 
-  const int q = lane >> 4;
-  const int bd = w.bd;
-  float acc[GV_MAX_R][M];
+  // lane 4b + j reads activation row j (row 0 when j >= M) of code column
+  // 16*ci + b of the current unit
+  const int jl = lane & 3, bl = lane >> 2;
+  const uint8_t *xa = (const uint8_t *)(s_xp + (size_t)(jl < M ? jl : 0) * Kp) + 16 * bl;
+  float acc[4][M];
 #pragma unroll
-  for (int r = 0; r < GV_MAX_R; ++r)
+  for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
-    for (int a = 0; a < M; ++a) acc[r][a] = 0.f;
-  u4 A[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) A[i] = (u4){0u, 0u, 0u, 0u};
+    for (int a = 0; a < M; ++a) acc[ri][a] = 0.f;
 
-  // Diagonal lanes of the block-diagonal A operand: (L & 15) >> 2 == L >> 4.
-  //  M == 1: four K-blocks i = 4g + j (j = 0..3) are chained into one C;
-  //          lane 20q + j carries code 4i + q of K-block j, so C row 4q + j
-  //          of lane L (q = L >> 4) is the dot of the code that lane decoded
-  //          for K-block 4g + j.
-  //  M > 1:  one C per K-block; lane 20q + a carries row a of code 4i + q,
-  //          and C row 4q + a is that code's dot for activation row a.
-  const bool diag = (((lane & 15) >> 2) == q) && (M == 1 || (lane & 3) < M);
-  const int a_lane = M == 1 ? 0 : (lane & 3);
-  const int j_lane = lane & 3;  // M == 1: which K-block of the group
-  const u4 *xa = (const u4 *)(s_xp + (size_t)(diag ? a_lane : 0) * Kp) + q;
-  const u4 *dtab_l = s_dtab + (lane & (GV_REP - 1));  // this lane's replica
-
-  for (int t = t_begin; t < t_end; ++t) {
-    // prefetch the next item's codes
-    int un = u, rn = rt + 1;
-    if (rn == R) {
-      rn = 0;
-      ++un;
-    }
-    u4 S2 = S, L2 = L;
-    uint32_t H2 = H;
-    if (t + 1 < t_end) {
-      const uint8_t *ub = codes0 + (size_t)(rn * U + un) * UNIT_BYTES;
-      S2 = *(const u4 *)(ub + PLANE_SIGN + 16 * lane);
-      L2 = *(const u4 *)(ub + PLANE_LOW + 16 * lane);
-      H2 = *(const uint32_t *)(ub + PLANE_HIGH + 4 * lane);
-    }
-    float tmp[M];
+  auto step = [&](const ItemCodes &c, int u) __attribute__((always_inline)) {
+    // items are scheduled one at a time: interleaving several items only
+    // raises register pressure past the occupancy target
+    __builtin_amdgcn_sched_barrier(0);
+    float tmp[4][M];
 #pragma unroll
-    for (int a = 0; a < M; ++a) tmp[a] = 0.f;
+    for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (M == 1) {
-        // lane 20q + j feeds only K-block 4g + j of the group; every other
-        // lane keeps zeros in A[j]
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (diag && j_lane == j) A[j] = xa[64 * u + 4 * (4 * g + j)];
-      } else if (diag) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) A[j] = xa[64 * u + 16 * g + 4 * j];
-      }
-      if (M == 1) {
-        f4 C = (f4){0.f, 0.f, 0.f, 0.f};
-        float Rv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * g + j;
-          const uint32_t idx = code_index(L, H, i);
-          const u4 D = apply_signs(dtab_l[(idx & 0xFFu) * GV_REP], S, i);
-          C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, A[j]),
-                                                     __builtin_bit_cast(h8, D), C, 0, 0, 0);
-          Rv[j] = (float)s_rtab[idx >> bd];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tmp[0] = __builtin_fmaf(Rv[j], C[j], tmp[0]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * g + j;
-          const uint32_t idx = code_index(L, H, i);
-          const u4 D = apply_signs(dtab_l[(idx & 0xFFu) * GV_REP], S, i);
-          const f4 C = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, A[j]),
-                                                              __builtin_bit_cast(h8, D),
-                                                              (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          const float Rv = (float)s_rtab[idx >> bd];
-#pragma unroll
-          for (int a = 0; a < M; ++a) tmp[a] = __builtin_fmaf(Rv, C[a], tmp[a]);
-        }
-      }
-    }
+      for (int a = 0; a < M; ++a) tmp[ri][a] = 0.f;
+    gemv_item<M>(c, xa + (size_t)u * (UNIT_CODES * 16), tmp);
 #pragma unroll
     for (int a = 0; a < M; ++a) {
       const float sc = s_scale[u * M + a];
 #pragma unroll
-      for (int r = 0; r < GV_MAX_R; ++r)
-        if (r == rt) acc[r][a] = __builtin_fmaf(tmp[a], sc, acc[r][a]);
+      for (int ri = 0; ri < 4; ++ri) acc[ri][a] = __builtin_fmaf(tmp[ri][a], sc, acc[ri][a]);
     }
-    S = S2;
-    L = L2;
-    H = H2;
-    u = un;
-    rt = rn;
+  };
+
+  // Items of the wave: units u_begin .. u_end-1 (slot (u - u_begin) % GV_PIPE).
+  // While a later chunk exists, every processed slot is refilled at once
+  // (unconditional loads, dummy address past the end); the last chunk has
+  // no refills.
+  int u = u_begin;
+  while (u + GV_PIPE < u_end) {
+#pragma unroll
+    for (int s = 0; s < GV_PIPE; ++s) {
+      step(ring[s], u);
+      ++u;
+      const uint8_t *ub = ul < u_end ? tile + (size_t)ul * UNIT_BYTES : w.base;
+      ring[s] = load_item(ub, lane);
+      ++ul;
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < GV_PIPE; ++s) {
+    if (u < u_end) step(ring[s], u);
+    ++u;
   }
 
+  // sum over the 16 code columns of each lane group (lanes with equal j),
+  // then over the waves of the tile
 #pragma unroll
-  for (int r = 0; r < GV_MAX_R; ++r) {
+  for (int ri = 0; ri < 4; ++ri) {
 #pragma unroll
     for (int a = 0; a < M; ++a) {
-      float v = acc[r][a];
+      float v = acc[ri][a];
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
       v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
-      if (lane < 16) s_red[((wv * GV_MAX_R + r) * M + a) * 16 + lane] = v;
+      if (lane < 4) s_red[((wv * 4 + ri) * M + a) * 4 + lane] = v;
     }
   }
   __syncthreads();
-  for (int o = tid; o < R * M * 16; o += 256) {
-    const int r = o / (M * 16), a = (o / 16) % M, row = o & 15;
+  for (int o = tid; o < Reff * 16 * M; o += 256) {
+    const int t = o / (16 * M), a = (o / 16) % M, row = o & 15;
+    const int ri = row >> 2, j = row & 3;
     float sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < GV_WAVES; ++j) sum += s_red[((j * GV_MAX_R + r) * M + a) * 16 + row];
-    const int n = (rt0 + r) * 16 + row;
+    for (int p = 0; p < wpt; ++p) sum += s_red[(((t * wpt + p) * 4 + ri) * M + a) * 4 + j];
+    const int n = (rt0 + t) * 16 + row;
     if (n < w.n) store_out(y, (size_t)a * ldy + n, sum, ydt);
   }
 }
 
-template <int M>
-__global__ __launch_bounds__(256) void gemv_batched_kernel(GemvBatch b) {
+// Occupancy: three 256-thread blocks per CU at m = 1 (the tables, activations
+// and staging row of a 2560..9728-wide matrix fit 3x in LDS); at m >= 2 the
+// permuted activation rows already limit LDS to one or two blocks per CU, so
+// the register budget is relaxed accordingly.
+#define SVQ_GEMV_OCCUPANCY(M) \
+  __attribute__((amdgpu_waves_per_eu((M) == 1 ? 3 : ((M) == 2 ? 2 : 1))))
+template <int M, bool XVEC>
+__global__ __launch_bounds__(256) SVQ_GEMV_OCCUPANCY(M) void gemv_batched_kernel(GemvBatch b) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int j = 0;
   while (j + 1 < b.count && (int)blockIdx.x >= b.job[j + 1].block_begin) ++j;
   const GemvJob &jb = b.job[j];
   const int rt0 = ((int)blockIdx.x - jb.block_begin) * jb.R;
-  const int R = min(jb.R, jb.w.n_tiles - rt0);
-  gemv_fused_block<M>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, R, smem);
+  const int Reff = min(jb.R, jb.w.n_tiles - rt0);
+  gemv_fused_block<M, XVEC>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
 }
 
 size_t gemv_smem_bytes(int m, int k_max, int units_max) {
@@ -395,28 +498,33 @@ static hipError_t allow_smem(Kern k, size_t bytes) {
   return hipSuccess;
 }
 
-hipError_t launch_gemv_batched(GemvBatch &b, int blocks, size_t smem, hipStream_t s) {
-  hipError_t e = hipSuccess;
-  switch (b.m) {
-    case 1:
-      e = allow_smem(gemv_batched_kernel<1>, smem);
-      if (e == hipSuccess) hipLaunchKernelGGL(gemv_batched_kernel<1>, dim3(blocks), dim3(256), smem, s, b);
-      break;
-    case 2:
-      e = allow_smem(gemv_batched_kernel<2>, smem);
-      if (e == hipSuccess) hipLaunchKernelGGL(gemv_batched_kernel<2>, dim3(blocks), dim3(256), smem, s, b);
-      break;
-    case 3:
-      e = allow_smem(gemv_batched_kernel<3>, smem);
-      if (e == hipSuccess) hipLaunchKernelGGL(gemv_batched_kernel<3>, dim3(blocks), dim3(256), smem, s, b);
-      break;
-    default:
-      e = allow_smem(gemv_batched_kernel<4>, smem);
-      if (e == hipSuccess) hipLaunchKernelGGL(gemv_batched_kernel<4>, dim3(blocks), dim3(256), smem, s, b);
-      break;
-  }
+// The exact-path kernels address their LDS tables from 0 (see lds_u4), which
+// holds when they declare no static LDS.
+template <typename Kern>
+static hipError_t check_no_static_lds(Kern k) {
+  hipFuncAttributes attr;
+  hipError_t e = hipFuncGetAttributes(&attr, (const void *)k);
   if (e != hipSuccess) return e;
+  return attr.sharedSizeBytes == 0 ? hipSuccess : hipErrorInvalidKernelFile;
+}
+
+template <int M, bool XVEC>
+static hipError_t launch_gemv_m(GemvBatch &b, int blocks, size_t smem, hipStream_t s) {
+  static const hipError_t lds_ok = check_no_static_lds(gemv_batched_kernel<M, XVEC>);
+  if (lds_ok != hipSuccess) return lds_ok;
+  hipError_t e = allow_smem(gemv_batched_kernel<M, XVEC>, smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemv_batched_kernel<M, XVEC>), dim3(blocks), dim3(256), smem, s, b);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_batched(GemvBatch &b, int blocks, size_t smem, bool xvec, hipStream_t s) {
+  switch (b.m) {
+    case 1: return xvec ? launch_gemv_m<1, true>(b, blocks, smem, s) : launch_gemv_m<1, false>(b, blocks, smem, s);
+    case 2: return xvec ? launch_gemv_m<2, true>(b, blocks, smem, s) : launch_gemv_m<2, false>(b, blocks, smem, s);
+    case 3: return xvec ? launch_gemv_m<3, true>(b, blocks, smem, s) : launch_gemv_m<3, false>(b, blocks, smem, s);
+    default: return xvec ? launch_gemv_m<4, true>(b, blocks, smem, s) : launch_gemv_m<4, false>(b, blocks, smem, s);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -456,6 +564,12 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(MatView w, const uint16_
 // 16-row activation tiles starting at activation row m0 of xb (rows Kp
 // apart).  Each decoded code (B operand) is reused across the BMT activation
 // tiles.  Output row mm (m0 <= mm < m_end) goes to y row out_row(mm).
+//
+// v_mfma_f32_16x16x32_bf16 for K-block kb (code columns 4kb..4kb+3 of the
+// unit) takes from lane L the code in row L & 15, column 4kb + (L >> 4).  In
+// the unit layout that code is code 4c + (kb >> 2), c = (L >> 2) & 3, of lane
+// record 16(kb & 3) + 4(L >> 4) + (L & 3); so each lane reads four records
+// and decodes four codes from each.
 template <int BMT, typename RowMap>
 __device__ void gemm_bf16_tile(const MatView &w, int rt, const uint16_t *__restrict__ xb, int m0,
                                int m_end, void *__restrict__ y, int64_t ldy, int ydt,
@@ -465,6 +579,9 @@ __device__ void gemm_bf16_tile(const MatView &w, int rt, const uint16_t *__restr
   const uint8_t *tile = w.base + w.off_codes + (size_t)rt * w.units * UNIT_BYTES;
   const u4 *xrow = (const u4 *)(xb + (size_t)(m0 + (lane & 15)) * Kp) + (lane >> 4);
   const size_t xstride = (size_t)16 * Kp / 8;  // 16 rows, in u4 units
+  const int c = (lane >> 2) & 3;
+  const int rec0 = 4 * (lane >> 4) + (lane & 3);
+  const uint32_t SM = 0x80008000u;
 
   f4 C[BMT];
 #pragma unroll
@@ -472,18 +589,28 @@ __device__ void gemm_bf16_tile(const MatView &w, int rt, const uint16_t *__restr
 
   for (int u = 0; u < w.units; ++u) {
     const uint8_t *ub = tile + (size_t)u * UNIT_BYTES;
-    const u4 S = *(const u4 *)(ub + PLANE_SIGN + 16 * lane);
-    const u4 L = *(const u4 *)(ub + PLANE_LOW + 16 * lane);
-    const uint32_t H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * lane);
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t idx = code_index(L, H, i);
-      const u4 B = apply_signs(s_btab[idx], S, i);
 #pragma unroll
-      for (int t = 0; t < BMT; ++t) {
-        const u4 A = xrow[t * xstride + 64 * u + 4 * i];
-        C[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, A),
-                                                       __builtin_bit_cast(b8, B), C[t], 0, 0, 0);
+    for (int t = 0; t < 4; ++t) {
+      const int rec = rec0 + 16 * t;
+      u4 S = *(const u4 *)(ub + PLANE_SIGN + 16 * rec);
+      const u4 L = *(const u4 *)(ub + PLANE_LOW + 16 * rec);
+      const uint32_t H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * rec) >> (8 * c);
+      const uint32_t Lc = c == 0 ? L[0] : c == 1 ? L[1] : c == 2 ? L[2] : L[3];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[j] <<= 4 * c;
+#pragma unroll
+      for (int sidx = 0; sidx < 4; ++sidx) {
+        const int kb = 4 * sidx + t;
+        const uint32_t idx = ((Lc >> (8 * sidx)) & 0xFFu) | (((H >> (2 * sidx)) & 3u) << 8);
+        u4 B = s_btab[idx];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) B[j] ^= (S[j] << sidx) & SM;
+#pragma unroll
+        for (int tt = 0; tt < BMT; ++tt) {
+          const u4 A = xrow[tt * xstride + 64 * u + 4 * kb];
+          C[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, A),
+                                                          __builtin_bit_cast(b8, B), C[tt], 0, 0, 0);
+        }
       }
     }
   }
@@ -537,22 +664,21 @@ __device__ __forceinline__ MatView expert_view(const MoeShape &sh, const ExpertT
   return v;
 }
 
-// Per-slot fused GEMV (one activation row per slot): block (row group, slot),
+// Per-slot fused GEMV (one activation row per slot): block (row tile, slot),
 // matrix = the slot's expert.
-__global__ __launch_bounds__(256) void moe_gemv_kernel(MoeShape sh, ExpertTable tab,
+template <bool XVEC>
+__global__ __launch_bounds__(256) SVQ_GEMV_OCCUPANCY(1) void moe_gemv_kernel(MoeShape sh, ExpertTable tab,
                                                        const int32_t *__restrict__ ids,
                                                        const uint16_t *__restrict__ x, int64_t ldx,
                                                        int x_per_slot, int topk,
-                                                       void *__restrict__ y, int64_t ldy, int ydt,
-                                                       int R) {
+                                                       void *__restrict__ y, int64_t ldy, int ydt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int q = blockIdx.y;
   const MatView w = expert_view(sh, tab, ids[q]);
   const int src = x_per_slot ? q : q / topk;
-  const int rt0 = blockIdx.x * R;
-  const int Reff = min(R, w.n_tiles - rt0);
+  const int rt0 = blockIdx.x;
   char *yq = (char *)y + (size_t)q * ldy * (ydt == 0 ? 2 : 4);
-  gemv_fused_block<1>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, Reff, smem);
+  gemv_fused_block<1, XVEC>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, 1, 1, smem);
 }
 
 // Routing for the grouped GEMM: counting sort of slots by expert and a list
@@ -709,12 +835,19 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   if (S <= MOE_EXACT_MAX_SLOTS) {
     *need = 256;
     if (!ws) return hipSuccess;
-    const int R = 1;
     const size_t smem = gemv_smem_bytes(1, sh.k, sh.units);
-    hipError_t e = allow_smem(moe_gemv_kernel, smem);
+    const bool xvec = ((((uintptr_t)x) | ((uintptr_t)ldx * 2)) & 15) == 0;
+    static const hipError_t lds_ok_t = check_no_static_lds(moe_gemv_kernel<true>);
+    static const hipError_t lds_ok_f = check_no_static_lds(moe_gemv_kernel<false>);
+    if ((xvec ? lds_ok_t : lds_ok_f) != hipSuccess) return xvec ? lds_ok_t : lds_ok_f;
+    hipError_t e = xvec ? allow_smem(moe_gemv_kernel<true>, smem) : allow_smem(moe_gemv_kernel<false>, smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_gemv_kernel, dim3((sh.n_tiles + R - 1) / R, S), dim3(256), smem, s, sh,
-                       tab, ids, xp, ldx, x_per_slot, topk, y, ldy, ydt, R);
+    if (xvec)
+      hipLaunchKernelGGL(moe_gemv_kernel<true>, dim3(sh.n_tiles, S), dim3(256), smem, s, sh, tab, ids,
+                         xp, ldx, x_per_slot, topk, y, ldy, ydt);
+    else
+      hipLaunchKernelGGL(moe_gemv_kernel<false>, dim3(sh.n_tiles, S), dim3(256), smem, s, sh, tab, ids,
+                         xp, ldx, x_per_slot, topk, y, ldy, ydt);
     return hipGetLastError();
   }
   const int rows_per_item = 16 * GEMM_BMT;

@@ -45,7 +45,7 @@ def _desc(mat, **over):
 def _expected_bytes(n, k):
     a = lambda v: (v + 255) // 256 * 256
     tiles, units = (n + 15) // 16, (k + 511) // 512
-    return a(4096) + a(256) + a(16384) + a(2 * units * 512) + a(tiles * units * 2304)
+    return a(4096) + a(2048) + a(16384) + a(2 * units * 512) + a(tiles * units * 2304)
 
 
 @pytest.mark.parametrize("n,k,bd", [(512, 1024, 8), (37, 104, 6), (1, 8, 7), (2048, 768, 7)])
@@ -125,7 +125,7 @@ def _fake_handle(n, k, bd):
     h.n_tiles, h.units = (n + 15) // 16, (k + 511) // 512
     h.off_dtab = 0
     h.off_rtab = a(4096)
-    h.off_btab = h.off_rtab + a(256)
+    h.off_btab = h.off_rtab + a(2048)
     h.off_perm = h.off_btab + a(16384)
     h.off_codes = h.off_perm + a(2 * h.units * 512)
     h.padded_code_bytes = h.n_tiles * h.units * 2304
