@@ -145,6 +145,24 @@ def test_strided_input_output(svq, m):
     assert_within_tolerance(y, y64, x, W, label="strided")
 
 
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+def test_unaligned_activations(svq, m):
+    """Rows that do not start 16-byte aligned (odd row stride, base pointer
+    two bytes into the buffer) take the scalar staging path."""
+    k = 640
+    mat = synth.random_matrix(48, k, 7, seed=(36, m, 0))
+    x = synth.random_activations(m, k, seed=(36, m, 1))
+    pm = svq.pack(mat)
+    y64, W = so.linear_from_inputs(mat, x)
+    buf = np.zeros((m, k + 3), dtype=np.uint16)
+    buf[:, 1:k + 1] = x
+    xd = to_device_bf16(buf)[:, 1:k + 1]
+    assert (xd.data_ptr() % 16) != 0 and (xd.stride(0) * 2) % 16 != 0
+    y = svq.linear(pm, xd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_within_tolerance(out_to_f64(y), y64, x, W, label=f"unaligned m={m}")
+
+
 def test_deterministic(svq):
     mat = synth.random_matrix(256, 2560, 8, seed=(32, 0, 0))
     for m in (1, 4, 33):
