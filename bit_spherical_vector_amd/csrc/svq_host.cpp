@@ -298,8 +298,9 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
   const bool exact = m <= EXACT_MAX_M && gemv_smem_bytes((int)m, k_max, u_max) <= GV_LDS_LIMIT;
   size_t need = 256;
   int m_pad = 0;
+  const bool prefill = !exact && m >= PREFILL_MIN_M;
   if (!exact) {
-    m_pad = gemm_m_pad((int)m);
+    m_pad = prefill ? prefill_m_pad((int)m) : gemm_m_pad((int)m);
     need = 0;
     for (int32_t j = 0; j < count; ++j)
       need += align256((size_t)m_pad * w[j].units * UNIT_SLOTS * 2);
@@ -344,7 +345,9 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
       uint16_t *xb = (uint16_t *)ws;
       ws += align256((size_t)m_pad * w[j].units * UNIT_SLOTS * 2);
       e = launch_prep_bf16(v, (const uint16_t *)xs[j], ldx[j], (int)m, m_pad, xb, s);
-      if (e == hipSuccess) e = launch_gemm_bf16(v, xb, (int)m, m_pad, ys[j], ldy[j], (int)ydt, s);
+      if (e == hipSuccess)
+        e = prefill ? launch_prefill_gemm(v, xb, (int)m, m_pad, ys[j], ldy[j], (int)ydt, s)
+                    : launch_gemm_bf16(v, xb, (int)m, m_pad, ys[j], ldy[j], (int)ydt, s);
     }
   }
   return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;

@@ -94,6 +94,12 @@ hipError_t launch_prep_bf16(const MatView &w, const uint16_t *x, int64_t ldx, in
                             uint16_t *xb, hipStream_t s);
 hipError_t launch_gemm_bf16(const MatView &w, const uint16_t *xb, int m, int m_pad,
                             void *y, int64_t ldy, int ydt, hipStream_t s);
+// Prefill (m >= PREFILL_MIN_M): LDS-tiled dequant-GEMM over xb padded to
+// prefill_m_pad(m) rows.
+constexpr int PREFILL_MIN_M = 256;
+int prefill_m_pad(int m);
+hipError_t launch_prefill_gemm(const MatView &w, const uint16_t *xb, int m, int m_pad, void *y,
+                               int64_t ldy, int ydt, hipStream_t s);
 
 // ---- MoE ----------------------------------------------------------------
 struct ExpertTable {

@@ -135,6 +135,26 @@ def test_edge_shapes(svq, n, k, bd, m):
     _one_hot_check(svq, pm, W, cols, 4 if m <= 4 else 16)
 
 
+PREFILL_EDGE = [
+    # n, k, bd, m: ragged row tiles, a partial last unit, m not a multiple of 256
+    (200, 1032, 8, 300),
+    (129, 520, 6, 256),
+    (16, 8, 7, 257),
+    (300, 2560, 7, 511),
+]
+
+
+@pytest.mark.parametrize("n,k,bd,m", PREFILL_EDGE)
+def test_prefill_path_edges(svq, n, k, bd, m):
+    """m >= 256 takes the LDS-tiled prefill kernel; its decoded weights are
+    observed through 256 one-hot rows (one block of activation rows)."""
+    mat = synth.random_matrix(n, k, bd, seed=(37, n, k))
+    x = synth.random_activations(m, k, seed=(37, m, k))
+    pm, W = _check_outputs(svq, mat, x, f"prefill edge n={n} k={k} bd={bd} m={m}")
+    cols = [(j * k) // 256 for j in range(256)]
+    _one_hot_check(svq, pm, W, cols, 256)
+
+
 @pytest.mark.parametrize("m", [1, 3, 20])
 def test_strided_input_output(svq, m):
     mat = synth.random_matrix(48, 640, 7, seed=(31, m, 0))
