@@ -1,0 +1,60 @@
+// Device-side helpers shared by the kernel translation units of libsvq.
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "svq_internal.h"
+
+namespace svq {
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16x __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+
+// float -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// y[i] = v as bf16 (ydt 0, RNE) or fp32 (ydt 1).
+__device__ __forceinline__ void store_out(void *y, size_t i, float v, int ydt) {
+  if (ydt == 0) ((uint16_t *)y)[i] = f32_to_bf16_bits(v);
+  else ((float *)y)[i] = v;
+}
+
+// The 36 code bytes one lane record holds (16 codes, see the unit layout).
+struct ItemCodes {
+  u4 S, L;
+  uint32_t H;
+};
+
+// Lane record `rec` of the coded unit at ub.
+__device__ __forceinline__ ItemCodes load_item(const uint8_t *ub, int rec) {
+  ItemCodes c;
+  c.S = *(const u4 *)(ub + PLANE_SIGN + 16 * rec);
+  c.L = *(const u4 *)(ub + PLANE_LOW + 16 * rec);
+  c.H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * rec);
+  return c;
+}
+
+// Opt a kernel into more than 64 KB of dynamic LDS.
+template <typename Kern>
+static hipError_t allow_smem(Kern k, size_t bytes) {
+  if (bytes > 64 * 1024)
+    return hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+  return hipSuccess;
+}
+
+}  // namespace svq

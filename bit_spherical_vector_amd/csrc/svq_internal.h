@@ -94,12 +94,27 @@ hipError_t launch_prep_bf16(const MatView &w, const uint16_t *x, int64_t ldx, in
                             uint16_t *xb, hipStream_t s);
 hipError_t launch_gemm_bf16(const MatView &w, const uint16_t *xb, int m, int m_pad,
                             void *y, int64_t ldy, int ydt, hipStream_t s);
-// Prefill (m >= PREFILL_MIN_M): LDS-tiled dequant-GEMM over xb padded to
-// prefill_m_pad(m) rows.
+// Prefill (m >= PREFILL_MIN_M): one LDS-tiled dequant-GEMM launch over the
+// permuted activations xb (padded to prefill_m_pad(m) rows) of every matrix
+// of a call; a block owns one output tile of one matrix ("job").
 constexpr int PREFILL_MIN_M = 256;
+struct PrefillJob {
+  MatView w;
+  const uint16_t *xb;
+  int32_t m;
+  void *y;
+  int64_t ldy;
+  int32_t tiles_n;      // output tiles along n
+  int32_t tiles_m;      // output tiles along m
+  int32_t block_begin;  // first block of this job
+};
+struct PrefillBatch {
+  PrefillJob job[GV_MAX_JOBS];
+  int32_t count, ydt;
+};
 int prefill_m_pad(int m);
-hipError_t launch_prefill_gemm(const MatView &w, const uint16_t *xb, int m, int m_pad, void *y,
-                               int64_t ldy, int ydt, hipStream_t s);
+int prefill_tiles_n(int n_tiles);
+hipError_t launch_prefill_batched(PrefillBatch &b, int blocks, hipStream_t s);
 
 // ---- MoE ----------------------------------------------------------------
 struct ExpertTable {

@@ -23,34 +23,10 @@
 //   signs from a 1024-row table (one row per direction/radius index), which
 //   is the B operand of v_mfma_f32_16x16x32_bf16; activations are the
 //   A operand.
-#include "svq_internal.h"
+#include "svq_device.h"
 #include "../../include/svq.h"
 
 namespace svq {
-
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef __bf16 b8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
-  return __builtin_bit_cast(float, b << 16);
-}
-
-// float -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ void store_out(void *y, size_t i, float v, int ydt) {
-  if (ydt == 0) ((uint16_t *)y)[i] = f32_to_bf16_bits(v);
-  else ((float *)y)[i] = v;
-}
 
 // ---------------------------------------------------------------------------
 // Exact path (m <= 4), fused: gather + scale + decode-and-multiply in one
@@ -101,20 +77,6 @@ constexpr int GV_OFF_RTAB = DTAB_BYTES;
 constexpr int GV_OFF_SCALE = GV_OFF_RTAB + RTAB_BYTES;
 constexpr int GV_OFF_RED = GV_OFF_SCALE + 128 * 4 * 4;  // [U <= 128][M <= 4] scales
 constexpr int GV_SMEM_FIXED = GV_OFF_RED + GV_WAVES * 4 * 4 * 4 * 4;
-
-// The 36 code bytes one lane holds for one work item (16 codes).
-struct ItemCodes {
-  u4 S, L;
-  uint32_t H;
-};
-
-__device__ __forceinline__ ItemCodes load_item(const uint8_t *ub, int lane) {
-  ItemCodes c;
-  c.S = *(const u4 *)(ub + PLANE_SIGN + 16 * lane);
-  c.L = *(const u4 *)(ub + PLANE_LOW + 16 * lane);
-  c.H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * lane);
-  return c;
-}
 
 // Maximum over the 64 lanes of a non-negative float (returned in every
 // lane): DPP row shifts within the 16-lane rows, row broadcasts across rows,
@@ -490,14 +452,6 @@ size_t gemv_smem_bytes(int m, int k_max, int units_max) {
   return (size_t)GV_SMEM_FIXED + (size_t)m * units_max * UNIT_SLOTS * 2 + (size_t)k_max * 2;
 }
 
-template <typename Kern>
-static hipError_t allow_smem(Kern k, size_t bytes) {
-  if (bytes > 64 * 1024)
-    return hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)bytes);
-  return hipSuccess;
-}
-
 // The exact-path kernels address their LDS tables from 0 (see lds_u4), which
 // holds when they declare no static LDS.
 template <typename Kern>
@@ -642,189 +596,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(MatView w, const uint16_
   if (rt >= w.n_tiles) return;
   gemm_bf16_tile<BMT>(w, rt, xb, blockIdx.y * 16 * BMT, m, y, ldy, ydt, s_btab, IdentityRows{});
 }
-
-// ---------------------------------------------------------------------------
-// Prefill GEMM (m >= PF_BM): LDS-tiled dequant-GEMM
-// ---------------------------------------------------------------------------
-//
-// Block tile PF_BM (activation rows) x PF_BN (weight rows, 8 unit row tiles),
-// K-step PF_BK = 64 permuted slots (8 codes per weight row), 4 waves in a
-// 2 x 2 grid of 128 x 64 wave tiles, v_mfma_f32_32x32x16_bf16 from LDS.
-// Each K-step the block stages the bf16 activation tile (from the permuted
-// copy xb) and decodes the weight tile, RNE_bf16(R*D) with its signs, into
-// LDS; two stages alternate so that the next step's loads and decode overlap
-// the current step's MFMAs with one barrier per step.
-//
-// Decode mapping (unit layout in svq_internal.h): K-step t of a unit covers
-// code columns 8t..8t+7, i.e. ci = t >> 1 and b in 8(t & 1) + [0, 8).  Thread
-// tau decodes, for row tile tau >> 5, lane record 4b + j (b = 8(t & 1) +
-// ((tau & 31) >> 2), j = tau & 3): its four codes 4*ri + ci, rows 4*ri + j,
-// column b - 8(t & 1) of the step.  The two records a thread needs per unit
-// are loaded once per unit.
-//
-// MFMA operands (32x32x16): lane L holds row (L & 31) of a 32-row fragment
-// and k = 8(L >> 5)..+7 of the 16-k substep; C element e of lane L is row
-// (e & 3) + 8(e >> 2) + 4(L >> 5), column L & 31.
-
-constexpr int PF_BM = 256, PF_BN = 128, PF_BK = 64;
-constexpr int PF_LDA = PF_BK + 8;                 // bf16 per LDS row (16 B pad)
-constexpr int PF_ROW_BYTES = PF_LDA * 2;          // 144
-constexpr int PF_A_BYTES = PF_BM * PF_ROW_BYTES;  // 36864
-constexpr int PF_B_BYTES = PF_BN * PF_ROW_BYTES;  // 18432
-constexpr int PF_STAGE = PF_A_BYTES + PF_B_BYTES;
-constexpr int PF_OFF_BTAB = 2 * PF_STAGE;
-constexpr int PF_SMEM = PF_OFF_BTAB + BTAB_BYTES;  // 126976
-
-typedef float f16x __attribute__((ext_vector_type(16)));
-
-// Decode the four codes of column group CI from one lane record into the
-// weight tile of a stage.
-template <int CI>
-__device__ __forceinline__ void pf_decode(const ItemCodes &c, const u4 *s_btab, uint8_t *bdst) {
-  const uint32_t SM = 0x80008000u;
-#pragma unroll
-  for (int ri = 0; ri < 4; ++ri) {
-    const int i = 4 * ri + CI;
-    const uint32_t idx = ((c.L[ri] >> (8 * CI)) & 0xFFu) | (((c.H >> (2 * i)) & 3u) << 8);
-    u4 v = s_btab[idx];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] ^= (c.S[q] << i) & SM;
-    *(u4 *)(bdst + 4 * ri * PF_ROW_BYTES) = v;
-  }
-}
-
-__global__ __launch_bounds__(256) void prefill_gemm_kernel(MatView w, const uint16_t *__restrict__ xb,
-                                                           int m, void *__restrict__ y, int64_t ldy,
-                                                           int ydt) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 1, wn = wv & 1;
-  const int U = w.units, Kp = U * UNIT_SLOTS;
-  const int rt0 = blockIdx.x * (PF_BN / UNIT_ROWS);
-  const int m0 = blockIdx.y * PF_BM;
-
-  u4 *s_btab = (u4 *)(smem + PF_OFF_BTAB);
-  for (int j = tid; j < 1024; j += 256) s_btab[j] = ((const u4 *)(w.base + w.off_btab))[j];
-
-  // activation tile: thread -> rows 32q + (tid >> 3), 16-byte chunk tid & 7
-  const uint16_t *a_src = xb + (size_t)(m0 + (tid >> 3)) * Kp + 8 * (tid & 7);
-  const size_t a_q = (size_t)32 * Kp;
-  const int a_dst = (tid >> 3) * PF_ROW_BYTES + (tid & 7) * 16;
-  // weight tile: row tile tid >> 5 (clamped to the matrix), records 4b + j
-  const int rtl = tid >> 5, bl = (tid & 31) >> 2, jr = tid & 3;
-  const int rt = min(rt0 + rtl, w.n_tiles - 1);
-  const uint8_t *codes = w.base + w.off_codes + (size_t)rt * U * UNIT_BYTES;
-  const int recA = 4 * bl + jr, recB = recA + 32;
-  const int b_dst = PF_A_BYTES + (rtl * UNIT_ROWS + jr) * PF_ROW_BYTES + bl * 16;
-
-  auto load_rec = [&](int u, int rec) __attribute__((always_inline)) {
-    const uint8_t *ub = codes + (size_t)u * UNIT_BYTES;
-    ItemCodes c;
-    c.S = *(const u4 *)(ub + PLANE_SIGN + 16 * rec);
-    c.L = *(const u4 *)(ub + PLANE_LOW + 16 * rec);
-    c.H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * rec);
-    return c;
-  };
-
-  f16x C[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) C[i][j] = (f16x){};
-
-  // prologue: records of unit 0, step 0 into stage 0
-  ItemCodes rA = load_rec(0, recA), rB = load_rec(0, recB);
-  u4 areg[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) areg[q] = *(const u4 *)(a_src + q * a_q);
-  __syncthreads();  // btab
-  pf_decode<0>(rA, s_btab, smem + b_dst);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) *(u4 *)(smem + a_dst + q * 32 * PF_ROW_BYTES) = areg[q];
-  __syncthreads();
-
-  const int a_frag = (128 * wm + (lane & 31)) * PF_ROW_BYTES + 16 * (lane >> 5);
-  const int b_frag = PF_A_BYTES + (64 * wn + (lane & 31)) * PF_ROW_BYTES + 16 * (lane >> 5);
-
-  for (int u = 0; u < U; ++u) {
-    // records of the next unit, used from the last step of this one
-    ItemCodes nA = rA, nB = rB;
-    if (u + 1 < U) {
-      nA = load_rec(u + 1, recA);
-      nB = load_rec(u + 1, recB);
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int s = u * 8 + t;
-      const bool more = (t < 7) || (u + 1 < U);
-      const uint8_t *cur = smem + (t & 1) * PF_STAGE;
-      uint8_t *nxt = smem + ((t + 1) & 1) * PF_STAGE;
-      if (more) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) areg[q] = *(const u4 *)(a_src + q * a_q + (size_t)(s + 1) * PF_BK);
-      }
-#pragma unroll
-      for (int ks = 0; ks < PF_BK / 16; ++ks) {
-        u4 af[4], bf[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = *(const u4 *)(cur + a_frag + i * 32 * PF_ROW_BYTES + 32 * ks);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bf[j] = *(const u4 *)(cur + b_frag + j * 32 * PF_ROW_BYTES + 32 * ks);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            C[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8, af[i]),
-                                                              __builtin_bit_cast(b8, bf[j]), C[i][j], 0,
-                                                              0, 0);
-      }
-      if (more) {
-        // decode step s + 1: same unit for t < 7, else step 0 of the next unit
-        switch (t) {
-          case 0: pf_decode<0>(rB, s_btab, nxt + b_dst); break;
-          case 1: pf_decode<1>(rA, s_btab, nxt + b_dst); break;
-          case 2: pf_decode<1>(rB, s_btab, nxt + b_dst); break;
-          case 3: pf_decode<2>(rA, s_btab, nxt + b_dst); break;
-          case 4: pf_decode<2>(rB, s_btab, nxt + b_dst); break;
-          case 5: pf_decode<3>(rA, s_btab, nxt + b_dst); break;
-          case 6: pf_decode<3>(rB, s_btab, nxt + b_dst); break;
-          default: pf_decode<0>(nA, s_btab, nxt + b_dst); break;
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) *(u4 *)(nxt + a_dst + q * 32 * PF_ROW_BYTES) = areg[q];
-      }
-      __syncthreads();
-    }
-    rA = nA;
-    rB = nB;
-  }
-
-  // epilogue
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = rt0 * UNIT_ROWS + 64 * wn + 32 * j + (lane & 31);
-      if (n >= w.n) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int mm = m0 + 128 * wm + 32 * i + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5);
-        if (mm < m) store_out(y, (size_t)mm * ldy + n, C[i][j][e], ydt);
-      }
-    }
-}
-
-hipError_t launch_prefill_gemm(const MatView &w, const uint16_t *xb, int m, int m_pad, void *y,
-                               int64_t ldy, int ydt, hipStream_t s) {
-  hipError_t e = allow_smem(prefill_gemm_kernel, PF_SMEM);
-  if (e != hipSuccess) return e;
-  dim3 grid((w.n_tiles + PF_BN / UNIT_ROWS - 1) / (PF_BN / UNIT_ROWS), m_pad / PF_BM);
-  hipLaunchKernelGGL(prefill_gemm_kernel, grid, dim3(256), PF_SMEM, s, w, xb, m, y, ldy, ydt);
-  return hipGetLastError();
-}
-
-int prefill_m_pad(int m) { return ((m + PF_BM - 1) / PF_BM) * PF_BM; }
 
 // ---------------------------------------------------------------------------
 // Mixture of experts (grouped form; routing is not on the pages and follows

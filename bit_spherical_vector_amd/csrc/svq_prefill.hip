@@ -1,0 +1,326 @@
+// Prefill dequant-GEMM of libsvq (m >= PREFILL_MIN_M) for gfx950.
+//
+// Method: "SAGE: Pushing 2-Bit Vector-Quantized LLMs toward Real-World
+// Usability".  Weights are rebuilt on demand (Fig. 1 and Fig. 5 captions)
+// from sign bits, a direction index and a quantized radius (Fig. 2 caption)
+// and multiply reordered activations (Fig. 6 caption); at prefill sizes the
+// product is a dense contraction, so the decoded tile feeds the matrix cores.
+//
+// One launch covers every matrix of a call ("jobs", longest k first).  A
+// block computes a P_BM x P_BN output tile (activation rows x weight rows)
+// over K in steps of P_BK = 64 permuted slots (8 codes per weight row).  Each
+// step stages the bf16 activation tile (from the permuted copy xb, loaded
+// straight into LDS) and the decoded weight tile RNE_bf16(R*D), signs
+// applied; two stages alternate so that the next step's loads and decode
+// overlap the current step's MFMAs, with one barrier per step.  Four waves
+// in a 2 x 2 grid each own a 128 x 128 tile: 16 accumulators of v_mfma_f32_32x32x16_bf16 (held in
+// accumulation registers; this translation unit is built without the
+// VGPR-form MFMA option of the exact-path kernels).  Fragments of the next
+// 16-wide k substep are read while the current one's MFMAs run.
+//
+// 32x32x16 operands: lane L holds row L & 31 of a 32-row fragment and
+// k = 8(L >> 5)..+7; accumulator element e of lane L is row
+// (e & 3) + 8(e >> 2) + 4(L >> 5), column L & 31.
+//
+// Decode mapping (unit layout in svq_internal.h): K-step t of a unit covers
+// code columns 8t..8t+7, i.e. ci = t >> 1 and b in 8(t & 1) + [0, 8).
+// Thread tau handles, for row tiles (tau >> 5) and (tau >> 5) + 8, lane
+// record 4b + j (b = 8(t & 1) + ((tau & 31) >> 2), j = tau & 3): its four
+// codes 4*ri + ci sit in rows 4*ri + j, column b - 8(t & 1) of the step.  A
+// thread needs four records per unit (two row tiles x two halves); those of
+// the next unit are loaded during the last two steps of the current one.
+#include "svq_device.h"
+#include "../../include/svq.h"
+
+namespace svq {
+
+constexpr int P_BM = 256, P_BN = 256, P_BK = 64;
+constexpr int P_ROW = P_BK * 2;                  // 128 bytes per LDS row
+constexpr int P_A = P_BM * P_ROW;                // activation tile, 32 KB
+constexpr int P_B = P_BN * P_ROW;                // weight tile, 32 KB
+constexpr int P_STAGE = P_A + P_B;
+constexpr int P_OFF_BTAB = 2 * P_STAGE;
+constexpr int P_SMEM = P_OFF_BTAB + BTAB_BYTES;  // 144 KB
+static_assert(P_SMEM <= 160 * 1024, "prefill LDS exceeds a workgroup's 160 KB");
+
+// LDS tiles hold rows of 8 chunks of 16 bytes; chunk c of row r is stored at
+// position c ^ swz(r).  With swz(r) = (r >> 1) & 7 the 16 consecutive rows a
+// fragment read touches at one chunk fall in 16 distinct bank groups.
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 1) & 7u; }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// Decode the four codes of column group CI of one lane record: table rows
+// first (all reads before any write: the writes could alias them), then the
+// signed rows into the weight tile.  Row of code ri: row0 + 4*ri; chunk bl.
+template <int CI>
+__device__ __forceinline__ void p_decode(const ItemCodes &c, const uint8_t *s_btab, uint8_t *tile,
+                                         int row0, int bl, u4 (&v)[4]) {
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri) {
+    const int i = 4 * ri + CI;
+    const uint32_t idx = ((c.L[ri] >> (8 * CI)) & 0xFFu) | (((c.H >> (2 * i)) & 3u) << 8);
+    v[ri] = *(const u4 *)(s_btab + 16 * idx);
+  }
+}
+// Sign carrier S << I, computed where it is used: as plain C the 128
+// carriers of a unit are all computed at its start and spilled.
+template <int I>
+__device__ __forceinline__ uint32_t carrier(uint32_t S) {
+  if (I == 0) return S;
+  uint32_t r;
+  asm volatile("v_lshlrev_b32 %0, %1, %2" : "=v"(r) : "i"(I), "v"(S));
+  return r;
+}
+
+template <int CI>
+__device__ __forceinline__ void p_store(const ItemCodes &c, uint8_t *tile, int row0, int bl,
+                                        u4 (&v)[4]) {
+  const uint32_t SM = 0x80008000u;
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri) {
+    const int i = 4 * ri + CI;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t cr;
+      switch (ri) {
+        case 0: cr = carrier<CI>(c.S[q]); break;
+        case 1: cr = carrier<4 + CI>(c.S[q]); break;
+        case 2: cr = carrier<8 + CI>(c.S[q]); break;
+        default: cr = carrier<12 + CI>(c.S[q]); break;
+      }
+      v[ri][q] ^= cr & SM;
+    }
+    const int r = row0 + 4 * ri;
+    *(u4 *)(tile + r * P_ROW + ((bl ^ swz(r)) << 4)) = v[ri];
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_batched_kernel(PrefillBatch b) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int jn = 0;
+  while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].block_begin) ++jn;
+  const PrefillJob &J = b.job[jn];
+  const MatView &w = J.w;
+  // Blocks are dealt to the 8 XCDs round-robin (block i on XCD i % 8) and
+  // each XCD has its own L2: with m-tile = local % tiles_m, the blocks that
+  // share one 256-row activation tile run on the same XCD (when tiles_m
+  // divides 8 or is a multiple of it and jobs start on multiples of 8), so
+  // that tile is fetched into one L2 and reused there.
+  const int local = (int)blockIdx.x - J.block_begin;
+  if (local >= J.tiles_n * J.tiles_m) return;  // padding block (uniform, before any barrier)
+  const int mt = local % J.tiles_m, nt = local / J.tiles_m;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
+  const int U = w.units, Kp = U * UNIT_SLOTS;
+  const int rt0 = nt * (P_BN / UNIT_ROWS);
+  const int m0 = mt * P_BM;
+
+  uint8_t *s_btab = smem + P_OFF_BTAB;
+  for (int j = tid; j < 1024; j += 256) ((u4 *)s_btab)[j] = ((const u4 *)(w.base + w.off_btab))[j];
+
+  // activation tile, straight from global memory into LDS: wave wv fills
+  // rows 64wv .. 64wv+63, eight rows (1 KB) per instruction q; lane L lands
+  // at row 64wv + 8q + (L >> 3), position L & 7, so it loads global chunk
+  // (L & 7) ^ swz(row).  swz of that row is ((L >> 4) + 4q) & 7: the chunk
+  // for odd q is the even-q chunk ^ 4.
+  const int a_row = 64 * wv + (lane >> 3);
+  const int a_chunk = (lane & 7) ^ (int)swz(a_row);
+  const uint16_t *a_row_ptr = J.xb + (size_t)(m0 + a_row) * Kp;
+  const uint16_t *a_src_e = a_row_ptr + 8 * a_chunk, *a_src_o = a_row_ptr + 8 * (a_chunk ^ 4);
+  const size_t a_q = (size_t)8 * Kp;  // eight rows, in elements
+  auto load_a = [&](int step, uint8_t *stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_global_load_lds(
+          (gbl_void_t *)((q & 1 ? a_src_o : a_src_e) + q * a_q + (size_t)step * P_BK),
+          (lds_void_t *)(stage + (64 * wv + 8 * q) * P_ROW), 16, 0, 0);
+  };
+  // weight tile: row tiles rtl and rtl + 8 (clamped to the matrix; rows past
+  // n are decoded from the last tile and never stored)
+  const int rtl = tid >> 5, bl = (tid & 31) >> 2, jr = tid & 3;
+  const int rtA = min(rt0 + rtl, w.n_tiles - 1), rtB = min(rt0 + rtl + 8, w.n_tiles - 1);
+  const uint8_t *codesA = w.base + w.off_codes + (size_t)rtA * U * UNIT_BYTES;
+  const uint8_t *codesB = w.base + w.off_codes + (size_t)rtB * U * UNIT_BYTES;
+  const int rec0 = 4 * bl + jr, rec1 = rec0 + 32;
+  const int rowA = P_BM + rtl * UNIT_ROWS + jr;  // rows of the weight tile follow the A rows
+  const int rowB = rowA + 8 * UNIT_ROWS;
+
+  f16x C[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) C[i][j] = (f16x){};
+
+  // records of the current unit: [row tile A/B][half 0/1]
+  ItemCodes r00 = load_item(codesA, rec0), r01 = load_item(codesA, rec1);
+  ItemCodes r10 = load_item(codesB, rec0), r11 = load_item(codesB, rec1);
+  load_a(0, smem);
+  __syncthreads();  // btab
+  {
+    u4 va[4], vb[4];
+    p_decode<0>(r00, s_btab, smem, rowA, bl, va);
+    p_decode<0>(r10, s_btab, smem, rowB, bl, vb);
+    p_store<0>(r00, smem, rowA, bl, va);
+    p_store<0>(r10, smem, rowB, bl, vb);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's activation rows are in LDS
+  __syncthreads();
+
+  // fragment rows: 32i + (lane & 31) of the wave's A rows / B rows; the chunk
+  // of k substep ks is 2ks + (lane >> 5), stored at that ^ swz(row), and
+  // swz(row) = ((lane & 31) >> 1) & 7 for every fragment
+  const int sl = ((lane & 31) >> 1) & 7, hl = lane >> 5;
+  const int a_frag = (128 * wm + (lane & 31)) * P_ROW;
+  const int b_frag = (P_BM + 128 * wn + (lane & 31)) * P_ROW;
+
+  for (int u = 0; u < U; ++u) {
+    // records of the next unit (the last unit reloads itself): half 0 is
+    // first needed by step 7's decode and loaded at step 6, after the
+    // current half 0 was last used; half 1 is loaded at step 7
+    const size_t nu = (size_t)min(u + 1, U - 1) * UNIT_BYTES;
+    ItemCodes n00, n01, n10, n11;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t == 6) {
+        n00 = load_item(codesA + nu, rec0);
+        n10 = load_item(codesB + nu, rec0);
+      }
+      if (t == 7) {
+        n01 = load_item(codesA + nu, rec1);
+        n11 = load_item(codesB + nu, rec1);
+      }
+      // One K-step is one branch-free region: the next step's activation
+      // loads (clamped on the last step: a harmless reload), table reads,
+      // signed stores and fragment reads are interleaved with this step's 64
+      // MFMAs (sched_group_barrier), so they run in the MFMA shadow.
+      const int sn = min(u * 8 + t + 1, 8 * U - 1);
+      const uint8_t *cur = smem + (t & 1) * P_STAGE;
+      uint8_t *nxt = smem + ((t + 1) & 1) * P_STAGE;
+      // the next step's activation rows go first: the compiler's wait
+      // counting cannot order LDS reads behind these DMA loads, so the next
+      // LDS wait is a full one, and here that is the wait for the first
+      // fragments anyway
+      load_a(sn, nxt);
+      u4 va[4], vb[4];
+      u4 af[2][4], bf[2][4];
+      {
+        const int pos = ((hl ^ sl) << 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[0][i] = *(const u4 *)(cur + a_frag + i * 32 * P_ROW + pos);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[0][j] = *(const u4 *)(cur + b_frag + j * 32 * P_ROW + pos);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < P_BK / 16; ++ks) {
+        const int c = ks & 1;
+        // This substep's fragments (read one substep ago) must have landed;
+        // waiting here, before the next reads are issued, keeps that wait
+        // from covering them (with the activation DMA in flight the compiler
+        // only places full LDS waits).
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        if (ks + 1 < P_BK / 16) {
+          const int pos = (((2 * (ks + 1) + hl) ^ sl) << 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) af[c ^ 1][i] = *(const u4 *)(cur + a_frag + i * 32 * P_ROW + pos);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bf[c ^ 1][j] = *(const u4 *)(cur + b_frag + j * 32 * P_ROW + pos);
+        }
+        if (ks == 0) {
+          switch (t) {  // table rows of the next step's decode
+            case 0: p_decode<0>(r01, s_btab, nxt, rowA, bl, va); p_decode<0>(r11, s_btab, nxt, rowB, bl, vb); break;
+            case 1: p_decode<1>(r00, s_btab, nxt, rowA, bl, va); p_decode<1>(r10, s_btab, nxt, rowB, bl, vb); break;
+            case 2: p_decode<1>(r01, s_btab, nxt, rowA, bl, va); p_decode<1>(r11, s_btab, nxt, rowB, bl, vb); break;
+            case 3: p_decode<2>(r00, s_btab, nxt, rowA, bl, va); p_decode<2>(r10, s_btab, nxt, rowB, bl, vb); break;
+            case 4: p_decode<2>(r01, s_btab, nxt, rowA, bl, va); p_decode<2>(r11, s_btab, nxt, rowB, bl, vb); break;
+            case 5: p_decode<3>(r00, s_btab, nxt, rowA, bl, va); p_decode<3>(r10, s_btab, nxt, rowB, bl, vb); break;
+            case 6: p_decode<3>(r01, s_btab, nxt, rowA, bl, va); p_decode<3>(r11, s_btab, nxt, rowB, bl, vb); break;
+            default: p_decode<0>(n00, s_btab, nxt, rowA, bl, va); p_decode<0>(n10, s_btab, nxt, rowB, bl, vb); break;
+          }
+        }
+        if (ks == 1) {
+          switch (t) {
+            case 0: p_store<0>(r01, nxt, rowA, bl, va); break;
+            case 1: p_store<1>(r00, nxt, rowA, bl, va); break;
+            case 2: p_store<1>(r01, nxt, rowA, bl, va); break;
+            case 3: p_store<2>(r00, nxt, rowA, bl, va); break;
+            case 4: p_store<2>(r01, nxt, rowA, bl, va); break;
+            case 5: p_store<3>(r00, nxt, rowA, bl, va); break;
+            case 6: p_store<3>(r01, nxt, rowA, bl, va); break;
+            default: p_store<0>(n00, nxt, rowA, bl, va); break;
+          }
+        }
+        if (ks == 2) {
+          switch (t) {
+            case 0: p_store<0>(r11, nxt, rowB, bl, vb); break;
+            case 1: p_store<1>(r10, nxt, rowB, bl, vb); break;
+            case 2: p_store<1>(r11, nxt, rowB, bl, vb); break;
+            case 3: p_store<2>(r10, nxt, rowB, bl, vb); break;
+            case 4: p_store<2>(r11, nxt, rowB, bl, vb); break;
+            case 5: p_store<3>(r10, nxt, rowB, bl, vb); break;
+            case 6: p_store<3>(r11, nxt, rowB, bl, vb); break;
+            default: p_store<0>(n10, nxt, rowB, bl, vb); break;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            C[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8, af[c][i]),
+                                                              __builtin_bit_cast(b8, bf[c][j]),
+                                                              C[i][j], 0, 0, 0);
+        // Interleave: the next substep's fragment reads (and, in substep 0,
+        // the table reads) right after the wait, then MFMAs alternating with
+        // the step's vector work and stores.
+        if (ks + 1 < P_BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads
+        if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // table reads
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+          if (ks == 1 || ks == 2) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU (signs)
+            if (g & 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next step's activation rows landed
+      __syncthreads();
+    }
+    r00 = n00;
+    r01 = n01;
+    r10 = n10;
+    r11 = n11;
+  }
+
+  // epilogue
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = rt0 * UNIT_ROWS + 128 * wn + 32 * j + (lane & 31);
+      if (n >= w.n) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int mm = m0 + 128 * wm + 32 * i + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5);
+        if (mm < J.m) store_out(J.y, (size_t)mm * J.ldy + n, C[i][j][e], b.ydt);
+      }
+    }
+}
+
+int prefill_m_pad(int m) { return ((m + P_BM - 1) / P_BM) * P_BM; }
+
+int prefill_tiles_n(int n_tiles) { return (n_tiles + P_BN / UNIT_ROWS - 1) / (P_BN / UNIT_ROWS); }
+
+hipError_t launch_prefill_batched(PrefillBatch &b, int blocks, hipStream_t s) {
+  hipError_t e = allow_smem(prefill_batched_kernel, P_SMEM);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prefill_batched_kernel, dim3(blocks), dim3(256), P_SMEM, s, b);
+  return hipGetLastError();
+}
+
+}  // namespace svq
