@@ -23,6 +23,8 @@
 //   signs from a 1024-row table (one row per direction/radius index), which
 //   is the B operand of v_mfma_f32_16x16x32_bf16; activations are the
 //   A operand.
+#include <type_traits>
+
 #include "svq_device.h"
 #include "../../include/svq.h"
 
@@ -289,10 +291,24 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   s_dtab[tid] = drow;
   ((u2 *)s_rtab)[tid] = rrow;
 
+  // fp16 copy of gathered unit uu of activation row a with its exact
+  // power-of-two scale: 2^e with max|x_unit| * 2^e in [2^14, 2^15), i.e.
+  // e = 14 - ilogb(max) = 15 - (frexp exponent of max).
+  auto gather_store = [&](int a, int uu, const float (&v)[8], float mxw) __attribute__((always_inline)) {
+    const int e = mxw > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mxw) : 0;
+    u4 h;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const _Float16 lo = (_Float16)ldexpf(v[2 * l], e), hi = (_Float16)ldexpf(v[2 * l + 1], e);
+      h[l] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    ((u4 *)(s_xp + (size_t)a * Kp))[64 * uu + lane] = h;
+    if (lane == 0) s_scale[uu * M + a] = ldexpf(1.f, -e);
+  };
+
   // One activation row at a time: stage it in LDS, then every wave gathers
-  // the permuted slots of its gather units and converts them to fp16 with a
-  // per-unit scale 2^e, max|x_unit| * 2^e in [2^14, 2^15).  (Unrolled: xv
-  // is indexed by the row.)
+  // the permuted slots of its gather units and converts them to fp16 with
+  // their per-unit scale.  (Unrolled: xv is indexed by the row.)
 #pragma unroll
   for (int a = 0; a < M; ++a) {
     const uint16_t *xr = x + (int64_t)a * ldx;
@@ -319,40 +335,52 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
       }
     }
     __syncthreads();
-    for (int uu = g_lo; uu <= g_hi; ++uu) {
-      const int p0 = uu * UNIT_SLOTS + 8 * lane;
-      u4 pv;
-      const int j = uu - g_lo;
-      if (j < GV_PRE_UNITS) {
-        pv = pvec[0];
+    // The wave's first GV_PRE_UNITS gather units side by side (unrolled, so
+    // that their LDS reads and wave reductions overlap), two at a time and
+    // the remaining three together when the wave has them; slots past the
+    // wave's units read a clamped unit and store nothing.
+    const int npre = min(g_hi - g_lo + 1, GV_PRE_UNITS);  // may be <= 0
+    auto gather_group = [&](auto J0, auto NJ) __attribute__((always_inline)) {
+      constexpr int j0 = decltype(J0)::value, nj = decltype(NJ)::value;
+      float v[nj][8], mx[nj];
 #pragma unroll
-        for (int jj = 1; jj < GV_PRE_UNITS; ++jj)
-          if (jj == j) pv = pvec[jj];
-      } else {
-        pv = *(const u4 *)(perm + p0);
+      for (int jj = 0; jj < nj; ++jj) {
+        const int p0 = (g_lo + j0 + jj) * UNIT_SLOTS + 8 * lane;
+        mx[jj] = 0.f;
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+          const uint32_t c0 = pvec[j0 + jj][l] & 0xFFFFu, c1 = pvec[j0 + jj][l] >> 16;
+          // perm is zero padded to the unit width, so c0, c1 < K always
+          const float g0 = bf16_bits_to_f32(s_stage[c0]), g1 = bf16_bits_to_f32(s_stage[c1]);
+          v[jj][2 * l] = (p0 + 2 * l < K) ? g0 : 0.f;
+          v[jj][2 * l + 1] = (p0 + 2 * l + 1 < K) ? g1 : 0.f;
+          mx[jj] = fmaxf(mx[jj], fmaxf(fabsf(v[jj][2 * l]), fabsf(v[jj][2 * l + 1])));
+        }
       }
-      float v[8];
-      float mx = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < nj; ++jj) mx[jj] = wave_max(mx[jj]);
+#pragma unroll
+      for (int jj = 0; jj < nj; ++jj)
+        if (j0 + jj < npre) gather_store(a, g_lo + j0 + jj, v[jj], mx[jj]);
+    };
+    static_assert(GV_PRE_UNITS == 5, "gather groups cover 2 + 3 units");
+    if (npre > 0) gather_group(std::integral_constant<int, 0>(), std::integral_constant<int, 2>());
+    if (npre > 2) gather_group(std::integral_constant<int, 2>(), std::integral_constant<int, 3>());
+    // units beyond the prefetched ones (k > 4 * GV_PRE_UNITS * 512 only)
+    for (int uu = g_lo + GV_PRE_UNITS; uu <= g_hi; ++uu) {
+      const int p0 = uu * UNIT_SLOTS + 8 * lane;
+      const u4 pv = *(const u4 *)(perm + p0);
+      float w8[8];
+      float m1 = 0.f;
 #pragma unroll
       for (int l = 0; l < 4; ++l) {
         const uint32_t c0 = pv[l] & 0xFFFFu, c1 = pv[l] >> 16;
-        // perm is zero padded to the unit width, so c0, c1 < K always
         const float g0 = bf16_bits_to_f32(s_stage[c0]), g1 = bf16_bits_to_f32(s_stage[c1]);
-        v[2 * l] = (p0 + 2 * l < K) ? g0 : 0.f;
-        v[2 * l + 1] = (p0 + 2 * l + 1 < K) ? g1 : 0.f;
-        mx = fmaxf(mx, fmaxf(fabsf(v[2 * l]), fabsf(v[2 * l + 1])));
+        w8[2 * l] = (p0 + 2 * l < K) ? g0 : 0.f;
+        w8[2 * l + 1] = (p0 + 2 * l + 1 < K) ? g1 : 0.f;
+        m1 = fmaxf(m1, fmaxf(fabsf(w8[2 * l]), fabsf(w8[2 * l + 1])));
       }
-      mx = wave_max(mx);
-      const int e = mx > 0.f ? 14 - ilogbf(mx) : 0;
-      u4 h;
-#pragma unroll
-      for (int l = 0; l < 4; ++l) {
-        const _Float16 lo = (_Float16)ldexpf(v[2 * l], e), hi = (_Float16)ldexpf(v[2 * l + 1], e);
-        h[l] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-      }
-      ((u4 *)(s_xp + (size_t)a * Kp))[64 * uu + lane] = h;
-      if (lane == 0) s_scale[uu * M + a] = ldexpf(1.f, -e);
+      gather_store(a, uu, w8, wave_max(m1));
     }
   }
   __syncthreads();  // gathered activations, scales and tables are visible
