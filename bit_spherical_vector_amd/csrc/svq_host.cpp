@@ -339,39 +339,50 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
     const int blocks = plan_gemv(b);
     e = launch_gemv_batched(b, blocks, gemv_smem_bytes((int)m, k_max, u_max), xvec, s);
   } else if (prefill) {
-    // permuted activations of every matrix, then one GEMM launch over all of
-    // them with the longest-k jobs first
+    // permuted activations of every matrix in fragment order (one prep
+    // launch), then one GEMM launch over all of them, longest k first
     PrefillBatch b;
     std::memset(&b, 0, sizeof(b));
     b.count = count;
     b.ydt = (int)ydt;
     uint8_t *ws = (uint8_t *)workspace;
-    for (int32_t j = 0; j < count && e == hipSuccess; ++j) {
+    bool xvec = true;
+    for (int32_t j = 0; j < count; ++j) {
       const MatView v = view_of(&w[j]);
-      uint16_t *xb = (uint16_t *)ws;
-      ws += align256((size_t)m_pad * w[j].units * UNIT_SLOTS * 2);
-      e = launch_prep_bf16(v, (const uint16_t *)xs[j], ldx[j], (int)m, m_pad, xb, s);
       b.job[j].w = v;
-      b.job[j].xb = xb;
+      b.job[j].x = (const uint16_t *)xs[j];
+      b.job[j].ldx = ldx[j];
+      b.job[j].xb = (uint16_t *)ws;
+      ws += align256((size_t)m_pad * w[j].units * UNIT_SLOTS * 2);
       b.job[j].m = (int32_t)m;
       b.job[j].y = ys[j];
       b.job[j].ldy = ldy[j];
       b.job[j].tiles_n = prefill_tiles_n(v.n_tiles);
+      if ((((uintptr_t)xs[j]) | ((uintptr_t)ldx[j] * 2)) & 15) xvec = false;
     }
+    const size_t esz = ydt == SVQ_BF16 ? 2 : 4;
+    b.yvec = 1;
+    for (int32_t j = 0; j < count; ++j)
+      if ((((uintptr_t)ys[j]) | ((uintptr_t)ldy[j] * esz)) & 15) b.yvec = 0;
     for (int i = 1; i < b.count; ++i)
       for (int j = i; j > 0 && b.job[j].w.k > b.job[j - 1].w.k; --j) {
         const PrefillJob t = b.job[j];
         b.job[j] = b.job[j - 1];
         b.job[j - 1] = t;
       }
-    // jobs start on multiples of 8 blocks (the XCD count) so that a job's
-    // blocks with one m-tile share an XCD; the padding blocks exit at once
-    int blocks = 0;
+    const int rpb = prefill_prep_rows(k_max);
+    // jobs start on multiples of 8 GEMM blocks (the XCD count) so that a
+    // job's blocks with one m-tile share an XCD; the padding blocks exit at
+    // once
+    int blocks = 0, prep_blocks = 0;
     for (int j = 0; j < b.count; ++j) {
       b.job[j].tiles_m = m_pad / prefill_m_pad(1);
       b.job[j].block_begin = blocks;
       blocks += (b.job[j].tiles_n * b.job[j].tiles_m + 7) / 8 * 8;
+      b.job[j].prep_begin = prep_blocks;
+      prep_blocks += m_pad / rpb;
     }
+    e = launch_prefill_prep(b, prep_blocks, rpb, k_max, xvec, s);
     if (e == hipSuccess) e = launch_prefill_batched(b, blocks, s);
   } else {
     uint8_t *ws = (uint8_t *)workspace;

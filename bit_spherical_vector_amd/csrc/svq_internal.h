@@ -94,26 +94,35 @@ hipError_t launch_prep_bf16(const MatView &w, const uint16_t *x, int64_t ldx, in
                             uint16_t *xb, hipStream_t s);
 hipError_t launch_gemm_bf16(const MatView &w, const uint16_t *xb, int m, int m_pad,
                             void *y, int64_t ldy, int ydt, hipStream_t s);
-// Prefill (m >= PREFILL_MIN_M): one LDS-tiled dequant-GEMM launch over the
-// permuted activations xb (padded to prefill_m_pad(m) rows) of every matrix
-// of a call; a block owns one output tile of one matrix ("job").
+// Prefill (m >= PREFILL_MIN_M): a prep launch writes the permuted
+// activations of every matrix of the call ("jobs") in MFMA fragment order
+// (xb, padded to prefill_m_pad(m) rows), then one LDS-tiled dequant-GEMM
+// launch covers all jobs; a GEMM block owns one output tile of one job.
 constexpr int PREFILL_MIN_M = 256;
 struct PrefillJob {
   MatView w;
-  const uint16_t *xb;
+  const uint16_t *x;    // activations, bf16 [m][ldx]
+  int64_t ldx;
+  uint16_t *xb;         // permuted activations in fragment order (workspace)
   int32_t m;
   void *y;
   int64_t ldy;
   int32_t tiles_n;      // output tiles along n
   int32_t tiles_m;      // output tiles along m
-  int32_t block_begin;  // first block of this job
+  int32_t block_begin;  // first GEMM block of this job
+  int32_t prep_begin;   // first prep block of this job
 };
 struct PrefillBatch {
   PrefillJob job[GV_MAX_JOBS];
   int32_t count, ydt;
+  int32_t yvec;  // every output row of every job starts 16-byte aligned
 };
 int prefill_m_pad(int m);
 int prefill_tiles_n(int n_tiles);
+int prefill_prep_rows(int k_max);  // activation rows per prep block
+// xvec: every activation row of every job starts 16-byte aligned.
+hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, int rpb, int k_max, bool xvec,
+                               hipStream_t s);
 hipError_t launch_prefill_batched(PrefillBatch &b, int blocks, hipStream_t s);
 
 // ---- MoE ----------------------------------------------------------------

@@ -8,15 +8,18 @@
 //
 // One launch covers every matrix of a call ("jobs", longest k first).  A
 // block computes a P_BM x P_BN output tile (activation rows x weight rows)
-// over K in steps of P_BK = 64 permuted slots (8 codes per weight row).  Each
-// step stages the bf16 activation tile (from the permuted copy xb, loaded
-// straight into LDS) and the decoded weight tile RNE_bf16(R*D), signs
-// applied; two stages alternate so that the next step's loads and decode
-// overlap the current step's MFMAs, with one barrier per step.  Four waves
-// in a 2 x 2 grid each own a 128 x 128 tile: 16 accumulators of v_mfma_f32_32x32x16_bf16 (held in
-// accumulation registers; this translation unit is built without the
-// VGPR-form MFMA option of the exact-path kernels).  Fragments of the next
-// 16-wide k substep are read while the current one's MFMAs run.
+// over K in steps of P_BK = 64 permuted slots (8 codes per weight row).  The
+// decoded weight tile of each step, RNE_bf16(R*D) with the signs applied,
+// goes through LDS (two stages: the next step's decode overlaps the current
+// step's MFMAs, one barrier per step).  The activations never touch LDS: a
+// prep launch writes the permuted activations in MFMA fragment order (see
+// prefill_prep_kernel), so each wave loads its A fragments straight into
+// registers with fully coalesced 1 KB loads, one step ahead.  Four waves in
+// a 2 x 2 grid each own a 128 x 128 tile: 16 accumulators of
+// v_mfma_f32_32x32x16_bf16 (held in accumulation registers; this
+// translation unit is built without the VGPR-form MFMA option of the
+// exact-path kernels).  B fragments of the next 16-wide k substep are read
+// while the current one's MFMAs run.
 //
 // 32x32x16 operands: lane L holds row L & 31 of a 32-row fragment and
 // k = 8(L >> 5)..+7; accumulator element e of lane L is row
@@ -36,20 +39,26 @@ namespace svq {
 
 constexpr int P_BM = 256, P_BN = 256, P_BK = 64;
 constexpr int P_ROW = P_BK * 2;                  // 128 bytes per LDS row
-constexpr int P_A = P_BM * P_ROW;                // activation tile, 32 KB
 constexpr int P_B = P_BN * P_ROW;                // weight tile, 32 KB
-constexpr int P_STAGE = P_A + P_B;
+constexpr int P_STAGE = P_B;
 constexpr int P_OFF_BTAB = 2 * P_STAGE;
-constexpr int P_SMEM = P_OFF_BTAB + BTAB_BYTES;  // 144 KB
+constexpr int P_SMEM = P_OFF_BTAB + BTAB_BYTES;  // 80 KB
 static_assert(P_SMEM <= 160 * 1024, "prefill LDS exceeds a workgroup's 160 KB");
+
+// Fragment order of the permuted activations xb (per job, m_pad x Kp bf16):
+// the 1 KB block F(rb, s, ks) holds, for 32-row block rb, K-step s and k
+// substep ks, lane L's eight values (row 32rb + (L & 31), slots
+// 64s + 16ks + 8(L >> 5) + 0..7) at bytes 16L..16L+15 -- exactly one
+// 32x32x16 A fragment -- and the blocks are ordered (rb, s, ks).
+__device__ __forceinline__ size_t xb_frag_offset(int r, int p, int S) {
+  const int rb = r >> 5, s = p >> 6, ks = (p >> 4) & 3, L = (r & 31) + 32 * ((p >> 3) & 1);
+  return ((((size_t)rb * S + s) * 4 + ks) * 64 + L) * 8 + (p & 7);
+}
 
 // LDS tiles hold rows of 8 chunks of 16 bytes; chunk c of row r is stored at
 // position c ^ swz(r).  With swz(r) = (r >> 1) & 7 the 16 consecutive rows a
 // fragment read touches at one chunk fall in 16 distinct bank groups.
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 1) & 7u; }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 // Decode the four codes of column group CI of one lane record: table rows
 // first (all reads before any write: the writes could alias them), then the
@@ -122,23 +131,13 @@ void prefill_batched_kernel(PrefillBatch b) {
   uint8_t *s_btab = smem + P_OFF_BTAB;
   for (int j = tid; j < 1024; j += 256) ((u4 *)s_btab)[j] = ((const u4 *)(w.base + w.off_btab))[j];
 
-  // activation tile, straight from global memory into LDS: wave wv fills
-  // rows 64wv .. 64wv+63, eight rows (1 KB) per instruction q; lane L lands
-  // at row 64wv + 8q + (L >> 3), position L & 7, so it loads global chunk
-  // (L & 7) ^ swz(row).  swz of that row is ((L >> 4) + 4q) & 7: the chunk
-  // for odd q is the even-q chunk ^ 4.
-  const int a_row = 64 * wv + (lane >> 3);
-  const int a_chunk = (lane & 7) ^ (int)swz(a_row);
-  const uint16_t *a_row_ptr = J.xb + (size_t)(m0 + a_row) * Kp;
-  const uint16_t *a_src_e = a_row_ptr + 8 * a_chunk, *a_src_o = a_row_ptr + 8 * (a_chunk ^ 4);
-  const size_t a_q = (size_t)8 * Kp;  // eight rows, in elements
-  auto load_a = [&](int step, uint8_t *stage) __attribute__((always_inline)) {
+  // A fragments of the wave: 32-row blocks rb = m0/32 + 4wm + i; step s,
+  // substep ks at a_ptr[i] + s * 2048 + ks * 512 elements (one 1 KB block)
+  const int S = Kp / P_BK;
+  const uint16_t *a_ptr[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      __builtin_amdgcn_global_load_lds(
-          (gbl_void_t *)((q & 1 ? a_src_o : a_src_e) + q * a_q + (size_t)step * P_BK),
-          (lds_void_t *)(stage + (64 * wv + 8 * q) * P_ROW), 16, 0, 0);
-  };
+  for (int i = 0; i < 4; ++i)
+    a_ptr[i] = J.xb + ((size_t)((m0 >> 5) + 4 * wm + i) * S * 4 * 64 + lane) * 8;
   // weight tile: row tiles rtl and rtl + 8 (clamped to the matrix; rows past
   // n are decoded from the last tile and never stored)
   const int rtl = tid >> 5, bl = (tid & 31) >> 2, jr = tid & 3;
@@ -146,7 +145,7 @@ void prefill_batched_kernel(PrefillBatch b) {
   const uint8_t *codesA = w.base + w.off_codes + (size_t)rtA * U * UNIT_BYTES;
   const uint8_t *codesB = w.base + w.off_codes + (size_t)rtB * U * UNIT_BYTES;
   const int rec0 = 4 * bl + jr, rec1 = rec0 + 32;
-  const int rowA = P_BM + rtl * UNIT_ROWS + jr;  // rows of the weight tile follow the A rows
+  const int rowA = rtl * UNIT_ROWS + jr;
   const int rowB = rowA + 8 * UNIT_ROWS;
 
   f16x C[4][4];
@@ -158,7 +157,12 @@ void prefill_batched_kernel(PrefillBatch b) {
   // records of the current unit: [row tile A/B][half 0/1]
   ItemCodes r00 = load_item(codesA, rec0), r01 = load_item(codesA, rec1);
   ItemCodes r10 = load_item(codesB, rec0), r11 = load_item(codesB, rec1);
-  load_a(0, smem);
+  // A fragments of step 0: af[ks][i]
+  u4 af[4][4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[ks][i] = *(const u4 *)(a_ptr[i] + ks * 512);
   __syncthreads();  // btab
   {
     u4 va[4], vb[4];
@@ -167,15 +171,13 @@ void prefill_batched_kernel(PrefillBatch b) {
     p_store<0>(r00, smem, rowA, bl, va);
     p_store<0>(r10, smem, rowB, bl, vb);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's activation rows are in LDS
   __syncthreads();
 
-  // fragment rows: 32i + (lane & 31) of the wave's A rows / B rows; the chunk
+  // B fragment rows: 32j + (lane & 31) of the wave's weight rows; the chunk
   // of k substep ks is 2ks + (lane >> 5), stored at that ^ swz(row), and
   // swz(row) = ((lane & 31) >> 1) & 7 for every fragment
   const int sl = ((lane & 31) >> 1) & 7, hl = lane >> 5;
-  const int a_frag = (128 * wm + (lane & 31)) * P_ROW;
-  const int b_frag = (P_BM + 128 * wn + (lane & 31)) * P_ROW;
+  const int b_frag = (128 * wn + (lane & 31)) * P_ROW;
 
   for (int u = 0; u < U; ++u) {
     // records of the next unit (the last unit reloads itself): half 0 is
@@ -193,24 +195,17 @@ void prefill_batched_kernel(PrefillBatch b) {
         n01 = load_item(codesA + nu, rec1);
         n11 = load_item(codesB + nu, rec1);
       }
-      // One K-step is one branch-free region: the next step's activation
+      // One K-step is one branch-free region: the next step's A fragment
       // loads (clamped on the last step: a harmless reload), table reads,
-      // signed stores and fragment reads are interleaved with this step's 64
-      // MFMAs (sched_group_barrier), so they run in the MFMA shadow.
+      // signed stores and B fragment reads are interleaved with this step's
+      // 64 MFMAs (sched_group_barrier), so they run in the MFMA shadow.
       const int sn = min(u * 8 + t + 1, 8 * U - 1);
       const uint8_t *cur = smem + (t & 1) * P_STAGE;
       uint8_t *nxt = smem + ((t + 1) & 1) * P_STAGE;
-      // the next step's activation rows go first: the compiler's wait
-      // counting cannot order LDS reads behind these DMA loads, so the next
-      // LDS wait is a full one, and here that is the wait for the first
-      // fragments anyway
-      load_a(sn, nxt);
       u4 va[4], vb[4];
-      u4 af[2][4], bf[2][4];
+      u4 bf[2][4];
       {
         const int pos = ((hl ^ sl) << 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[0][i] = *(const u4 *)(cur + a_frag + i * 32 * P_ROW + pos);
 #pragma unroll
         for (int j = 0; j < 4; ++j) bf[0][j] = *(const u4 *)(cur + b_frag + j * 32 * P_ROW + pos);
       }
@@ -218,15 +213,8 @@ void prefill_batched_kernel(PrefillBatch b) {
 #pragma unroll
       for (int ks = 0; ks < P_BK / 16; ++ks) {
         const int c = ks & 1;
-        // This substep's fragments (read one substep ago) must have landed;
-        // waiting here, before the next reads are issued, keeps that wait
-        // from covering them (with the activation DMA in flight the compiler
-        // only places full LDS waits).
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         if (ks + 1 < P_BK / 16) {
           const int pos = (((2 * (ks + 1) + hl) ^ sl) << 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) af[c ^ 1][i] = *(const u4 *)(cur + a_frag + i * 32 * P_ROW + pos);
 #pragma unroll
           for (int j = 0; j < 4; ++j) bf[c ^ 1][j] = *(const u4 *)(cur + b_frag + j * 32 * P_ROW + pos);
         }
@@ -270,17 +258,22 @@ void prefill_batched_kernel(PrefillBatch b) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            C[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8, af[c][i]),
+            C[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8, af[ks][i]),
                                                               __builtin_bit_cast(b8, bf[c][j]),
                                                               C[i][j], 0, 0, 0);
-        // Interleave: the next substep's fragment reads (and, in substep 0,
-        // the table reads) right after the wait, then MFMAs alternating with
-        // the step's vector work and stores.
-        if (ks + 1 < P_BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads
+        // the next step's A fragments of this substep, into the registers
+        // these MFMAs just read
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[ks][i] = *(const u4 *)(a_ptr[i] + (size_t)sn * 2048 + ks * 512);
+        // Interleave: the next substep's B fragment reads (and, in substep
+        // 0, the table reads) first, then MFMAs alternating with the A
+        // loads and the step's vector work and stores.
+        if (ks + 1 < P_BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
         if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // table reads
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+          if (g == 7) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);  // VMEM reads (A)
           if (ks == 1 || ks == 2) {
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU (signs)
             if (g & 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
@@ -288,7 +281,6 @@ void prefill_batched_kernel(PrefillBatch b) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next step's activation rows landed
       __syncthreads();
     }
     r00 = n00;
@@ -297,19 +289,119 @@ void prefill_batched_kernel(PrefillBatch b) {
     r11 = n11;
   }
 
-  // epilogue
+  // Epilogue through LDS (the weight stages are free now): each wave turns
+  // its 128 x 128 accumulator tile into output-type rows in a private 16 KB
+  // region, 64 (bf16) or 32 (fp32) rows per pass, and writes them back as
+  // whole 16-byte pieces of consecutive output columns.
+  __syncthreads();
+  {
+    uint8_t *s_c = smem + wv * 16384;
+    const int esz = b.ydt == 0 ? 2 : 4;
+    const int ipp = b.ydt == 0 ? 2 : 1;           // 32-row blocks per pass
+    const int cpr = 128 * esz / 16;               // 16-byte pieces per row
+    const int per = 16 / esz;                     // columns per piece
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i0 = 0; i0 < 4; ++i0) {
+      if (i0 % ipp != 0) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = rt0 * UNIT_ROWS + 128 * wn + 32 * j + (lane & 31);
-      if (n >= w.n) continue;
+      for (int ii = 0; ii < 2; ++ii) {
+        if (ii >= ipp) continue;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int mm = m0 + 128 * wm + 32 * i + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5);
-        if (mm < J.m) store_out(J.y, (size_t)mm * J.ldy + n, C[i][j][e], b.ydt);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = 32 * ii + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5), c = 32 * j + (lane & 31);
+            const float val = C[i0 + ii][j][e];
+            if (b.ydt == 0) ((uint16_t *)s_c)[r * 128 + c] = f32_to_bf16_bits(val);
+            else ((float *)s_c)[r * 128 + c] = val;
+          }
       }
+      __syncthreads();
+      for (int q = lane; q < 32 * ipp * cpr; q += 64) {
+        const int r = q / cpr, ch = q % cpr;
+        const int mm = m0 + 128 * wm + 32 * i0 + r;
+        const int n0 = rt0 * UNIT_ROWS + 128 * wn + ch * per;
+        if (mm >= J.m) continue;
+        const u4 v = *(const u4 *)(s_c + r * 128 * esz + ch * 16);
+        char *dst = (char *)J.y + ((size_t)mm * J.ldy + n0) * esz;
+        if (b.yvec && n0 + per <= w.n) {
+          *(u4 *)dst = v;
+        } else {
+          for (int l = 0; l < per; ++l) {
+            if (n0 + l >= w.n) break;
+            if (esz == 2) ((uint16_t *)dst)[l] = (uint16_t)(v[l >> 1] >> (16 * (l & 1)));
+            else ((uint32_t *)dst)[l] = v[l];
+          }
+        }
+      }
+      __syncthreads();
     }
+  }
+}
+
+// Prep for the prefill launch: the permuted activations of every job in
+// fragment order (xb_frag_offset), rows >= m and slots >= k zero.  A block
+// takes `rpb` consecutive activation rows of one job and stages them in LDS
+// (rpb * k bf16); thread tau handles row tau % rpb and every (256 / rpb)-th
+// 8-slot chunk, so the rpb threads of one chunk write rpb * 16 contiguous
+// bytes.
+template <bool XVEC>
+__global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int rpb) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_rows[];
+  int jn = 0;
+  while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].prep_begin) ++jn;
+  const PrefillJob &J = b.job[jn];
+  const MatView &w = J.w;
+  const int K = w.k, Kp = w.units * UNIT_SLOTS, S = Kp / P_BK;
+  const int r0 = ((int)blockIdx.x - J.prep_begin) * rpb;
+  const int tid = threadIdx.x;
+  for (int rr = 0; rr < rpb; ++rr) {
+    const int r = r0 + rr;
+    const uint16_t *xr = J.x + (int64_t)r * J.ldx;
+    uint16_t *dst = s_rows + (size_t)rr * K;
+    if (r >= J.m) {
+      for (int j = tid; j < K / 8; j += 256) ((u4 *)dst)[j] = (u4){0u, 0u, 0u, 0u};
+    } else if (XVEC) {
+      for (int j = tid; j < K / 8; j += 256) ((u4 *)dst)[j] = ((const u4 *)xr)[j];
+    } else {
+      for (int j = tid; j < K; j += 256) dst[j] = xr[j];
+    }
+  }
+  __syncthreads();
+  const uint16_t *perm = (const uint16_t *)(w.base + w.off_perm);
+  const int rr = tid % rpb, r = r0 + rr;
+  const uint16_t *row = s_rows + (size_t)rr * K;
+  for (int c = tid / rpb; c < Kp / 8; c += 256 / rpb) {
+    // perm is zero padded to the unit width, so every index is < k
+    const u4 pv = *(const u4 *)(perm + 8 * c);
+    u4 v;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const uint32_t lo = 8 * c + 2 * l < K ? row[pv[l] & 0xFFFFu] : 0u;
+      const uint32_t hi = 8 * c + 2 * l + 1 < K ? row[pv[l] >> 16] : 0u;
+      v[l] = lo | (hi << 16);
+    }
+    *(u4 *)(J.xb + xb_frag_offset(r, 8 * c, S)) = v;
+  }
+}
+
+int prefill_prep_rows(int k_max) {
+  int rpb = 8;
+  while (rpb > 1 && (size_t)rpb * k_max * 2 > GV_LDS_LIMIT) rpb /= 2;
+  return rpb;
+}
+
+hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, int rpb, int k_max, bool xvec,
+                               hipStream_t s) {
+  const size_t lds = (size_t)rpb * k_max * 2;
+  if (lds > GV_LDS_LIMIT) return hipErrorInvalidValue;
+  hipError_t e = xvec ? allow_smem(prefill_prep_kernel<true>, lds) : allow_smem(prefill_prep_kernel<false>, lds);
+  if (e != hipSuccess) return e;
+  if (xvec)
+    hipLaunchKernelGGL(prefill_prep_kernel<true>, dim3(blocks), dim3(256), lds, s, b, rpb);
+  else
+    hipLaunchKernelGGL(prefill_prep_kernel<false>, dim3(blocks), dim3(256), lds, s, b, rpb);
+  return hipGetLastError();
 }
 
 int prefill_m_pad(int m) { return ((m + P_BM - 1) / P_BM) * P_BM; }
