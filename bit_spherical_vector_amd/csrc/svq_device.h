@@ -19,12 +19,10 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __builtin_bit_cast(float, b << 16);
 }
 
-// float -> bf16 bits, round to nearest even (NaN stays NaN).
+// float -> bf16 bits, round to nearest even (NaN stays NaN): gfx950
+// converts in hardware (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // y[i] = v as bf16 (ydt 0, RNE) or fp32 (ydt 1).

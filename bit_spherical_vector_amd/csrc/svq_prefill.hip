@@ -32,6 +32,8 @@
 // codes 4*ri + ci sit in rows 4*ri + j, column b - 8(t & 1) of the step.  A
 // thread needs four records per unit (two row tiles x two halves); those of
 // the next unit are loaded during the last two steps of the current one.
+#include <type_traits>
+
 #include "svq_device.h"
 #include "../../include/svq.h"
 
@@ -296,10 +298,11 @@ void prefill_batched_kernel(PrefillBatch b) {
   __syncthreads();
   {
     uint8_t *s_c = smem + wv * 16384;
-    const int esz = b.ydt == 0 ? 2 : 4;
-    const int ipp = b.ydt == 0 ? 2 : 1;           // 32-row blocks per pass
-    const int cpr = 128 * esz / 16;               // 16-byte pieces per row
-    const int per = 16 / esz;                     // columns per piece
+    const bool bf = b.ydt == 0;
+    const int esz = bf ? 2 : 4;
+    const int ipp = bf ? 2 : 1;           // 32-row blocks per pass
+    const int cpr = 128 * esz / 16;       // 16-byte pieces per row
+    const int per = 16 / esz;             // columns per piece
 #pragma unroll
     for (int i0 = 0; i0 < 4; ++i0) {
       if (i0 % ipp != 0) continue;
@@ -312,7 +315,7 @@ void prefill_batched_kernel(PrefillBatch b) {
           for (int e = 0; e < 16; ++e) {
             const int r = 32 * ii + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5), c = 32 * j + (lane & 31);
             const float val = C[i0 + ii][j][e];
-            if (b.ydt == 0) ((uint16_t *)s_c)[r * 128 + c] = f32_to_bf16_bits(val);
+            if (bf) ((uint16_t *)s_c)[r * 128 + c] = f32_to_bf16_bits(val);
             else ((float *)s_c)[r * 128 + c] = val;
           }
       }
@@ -329,7 +332,7 @@ void prefill_batched_kernel(PrefillBatch b) {
         } else {
           for (int l = 0; l < per; ++l) {
             if (n0 + l >= w.n) break;
-            if (esz == 2) ((uint16_t *)dst)[l] = (uint16_t)(v[l >> 1] >> (16 * (l & 1)));
+            if (bf) ((uint16_t *)dst)[l] = (uint16_t)(v[l >> 1] >> (16 * (l & 1)));
             else ((uint32_t *)dst)[l] = v[l];
           }
         }
@@ -355,45 +358,69 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int r
   const int K = w.k, Kp = w.units * UNIT_SLOTS, S = Kp / P_BK;
   const int r0 = ((int)blockIdx.x - J.prep_begin) * rpb;
   const int tid = threadIdx.x;
-  for (int rr = 0; rr < rpb; ++rr) {
-    const int r = r0 + rr;
-    const uint16_t *xr = J.x + (int64_t)r * J.ldx;
-    uint16_t *dst = s_rows + (size_t)rr * K;
-    if (r >= J.m) {
-      for (int j = tid; j < K / 8; j += 256) ((u4 *)dst)[j] = (u4){0u, 0u, 0u, 0u};
-    } else if (XVEC) {
-      for (int j = tid; j < K / 8; j += 256) ((u4 *)dst)[j] = ((const u4 *)xr)[j];
-    } else {
+  // Stage the rows (rows >= m read row m - 1 and are zeroed below), LDS row
+  // stride k + 8: the rpb threads of one chunk read one column of rpb rows,
+  // and the 16-byte pad puts those rows in different banks.  Eight 16-byte
+  // loads per thread are in flight at a time.
+  const int ks_ = K + 8;
+  if (XVEC) {
+    const int n8 = K / 8, tot = rpb * n8;
+    constexpr int B = 8;
+    for (int q0 = tid; q0 < tot; q0 += 256 * B) {
+      u4 v[B];
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) {
+        const int q = min(q0 + 256 * bb, tot - 1);
+        const int rr = q / n8, c = q - rr * n8;
+        v[bb] = *(const u4 *)(J.x + (int64_t)min(r0 + rr, J.m - 1) * J.ldx + 8 * c);
+      }
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) {
+        const int q = q0 + 256 * bb;
+        if (q < tot) {
+          const int rr = q / n8, c = q - rr * n8;
+          *(u4 *)(s_rows + (size_t)rr * ks_ + 8 * c) = v[bb];
+        }
+      }
+    }
+  } else {
+    for (int rr = 0; rr < rpb; ++rr) {
+      const uint16_t *xr = J.x + (int64_t)min(r0 + rr, J.m - 1) * J.ldx;
+      uint16_t *dst = s_rows + (size_t)rr * ks_;
       for (int j = tid; j < K; j += 256) dst[j] = xr[j];
     }
   }
   __syncthreads();
   const uint16_t *perm = (const uint16_t *)(w.base + w.off_perm);
   const int rr = tid % rpb, r = r0 + rr;
-  const uint16_t *row = s_rows + (size_t)rr * K;
+  const uint16_t *row = s_rows + (size_t)rr * ks_;
+  const bool live = r < J.m;
   for (int c = tid / rpb; c < Kp / 8; c += 256 / rpb) {
     // perm is zero padded to the unit width, so every index is < k
     const u4 pv = *(const u4 *)(perm + 8 * c);
     u4 v;
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
-      const uint32_t lo = 8 * c + 2 * l < K ? row[pv[l] & 0xFFFFu] : 0u;
-      const uint32_t hi = 8 * c + 2 * l + 1 < K ? row[pv[l] >> 16] : 0u;
+      const uint32_t lo = live && 8 * c + 2 * l < K ? row[pv[l] & 0xFFFFu] : 0u;
+      const uint32_t hi = live && 8 * c + 2 * l + 1 < K ? row[pv[l] >> 16] : 0u;
       v[l] = lo | (hi << 16);
     }
     *(u4 *)(J.xb + xb_frag_offset(r, 8 * c, S)) = v;
   }
 }
 
+// LDS of a prep block: rpb staged rows of k + 8 values.
+static size_t prep_lds(int rpb, int k_max) { return (size_t)rpb * (k_max + 8) * 2; }
+
 int prefill_prep_rows(int k_max) {
   int rpb = 8;
-  while (rpb > 1 && (size_t)rpb * k_max * 2 > GV_LDS_LIMIT) rpb /= 2;
+  while (rpb > 1 && prep_lds(rpb, k_max) > GV_LDS_LIMIT) rpb /= 2;
   return rpb;
 }
 
 hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, int rpb, int k_max, bool xvec,
                                hipStream_t s) {
-  const size_t lds = (size_t)rpb * k_max * 2;
+  const size_t lds = prep_lds(rpb, k_max);
   if (lds > GV_LDS_LIMIT) return hipErrorInvalidValue;
   hipError_t e = xvec ? allow_smem(prefill_prep_kernel<true>, lds) : allow_smem(prefill_prep_kernel<false>, lds);
   if (e != hipSuccess) return e;
