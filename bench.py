@@ -123,6 +123,132 @@ def cpu_baseline_prefill(mats, xs, rows=32):
                       f"{dt:.1f} s"}
 
 
+def cpu_baseline_moe(mats, xs, ids, m, budget_s=12.0):
+    """Time the CPU oracle on the routed experts of the step (decode of each
+    routed expert matrix, then the grouped fp64 product), whole steps or
+    whole projections until about budget_s; GB/s of routed code bytes (m = 1)
+    or TFLOP/s (m > 1)."""
+    import numpy as np
+    from oracle import svq_oracle as so
+    topk = ids.size // m
+    t0 = time.perf_counter()
+    done_bytes, flops, projs = 0, 0.0, 0
+    routed = np.unique(ids)
+    while True:
+        for p in range(3):
+            Ws = [None] * len(mats[p])
+            for e in routed:
+                w = mats[p][e]
+                Ws[e] = so.decode_matrix(w.codes, w.n, w.k, w.bd, w.codebook, w.radius, w.perm)
+                done_bytes += w.codes.size
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            if any(Ws[e] is None for e in routed):
+                break
+            so.moe_linear(xs[p], ids, topk, p == 2, Ws)
+            flops += 2.0 * ids.size * mats[p][0].n * mats[p][0].k
+            projs += 1
+        if time.perf_counter() - t0 > budget_s or projs == 0:
+            break
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    if m == 1:
+        value, unit = done_bytes / dt / 1e9, "GB/s"
+    else:
+        value, unit = flops / dt / 1e12, "TFLOP/s"
+    return {"value": round(value, 6), "unit": unit, "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{projs} projection(s) over the {routed.size} routed experts of one step "
+                      f"(decode + grouped product), {dt:.1f} s"}
+
+
+def bench_moe(args, wl, svq, synth, dev, stream):
+    """MoE FFN step: the gate, up and down projections of the routed experts
+    for m tokens (top-8 of 128 experts), one svq_moe_linear call each."""
+    import numpy as np
+    import torch
+    m = wl["m"]
+    topk = synth.MOE_TOPK
+    bd = synth.moe_expert_bd()
+    mats = [[synth.moe_expert(e, p, int(bd[e])) for e in range(synth.MOE_EXPERTS)] for p in range(3)]
+    packed = [[svq.pack(w) for w in mats[p]] for p in range(3)]
+    ids = synth.moe_routing(m)
+    xs = [synth.moe_activations(m, p) for p in range(3)]
+    routed = np.unique(ids)
+    # bytes of the routed experts' codes per step, and the step's flops
+    step_bytes = sum(mats[p][e].codes.size for p in range(3) for e in routed)
+    flops = sum(2.0 * ids.size * mats[p][0].n * mats[p][0].k for p in range(3))
+    set_bytes = sum(pm.handle.bytes for p in range(3) for pm in packed[p])
+    copies = max(1, -(-COLD_BYTES // set_bytes))
+    d_ids = torch.from_numpy(ids).to(dev)
+    x_dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in xs]
+    y_dev = [torch.empty((ids.size, mats[p][0].n), dtype=torch.bfloat16, device=dev) for p in range(3)]
+    calls, ws = [], None
+    for c in range(copies):
+        group = []
+        for p in range(3):
+            pms = []
+            for pm in packed[p]:
+                buf = pm.buf.clone() if c else pm.buf
+                h = svq.Handle.from_buffer_copy(pm.handle)
+                h.dev = buf.data_ptr()
+                pms.append(svq.PackedMatrix(buf, h))
+            call = svq.MoeCall(pms, x_dev[p], d_ids, topk, p == 2, y_dev[p], workspace=ws,
+                               stream=stream)
+            ws = call.workspace if ws is None or call.workspace.numel() > ws.numel() else ws
+            group.append(call)
+        calls.append(group)
+
+    def step(i):
+        for call in calls[i % copies]:
+            call()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    if m == 1:
+        metric, unit = "routed packed-weight GB/s (MoE, batch-1)", "GB/s"
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        metric, unit = "MoE grouped dequant-GEMM TFLOP/s", "TFLOP/s"
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(value, 3), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(value / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_moe(mats, xs, ids, m)
+    out = {
+        "metric": metric,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xf16->f32 (exact decode)" if ids.size <= 64 else "bf16xbf16->f32",
+        "data": "synthetic (seeded codes, codebooks, radii, permutations, routing, activations)",
+        "config": {"workload": args.workload, "experts": synth.MOE_EXPERTS, "topk": topk, "m": m,
+                   "routed_experts": int(routed.size), "routed_code_bytes": int(step_bytes),
+                   "cold_copies": int(copies), "launch_calls_per_step": 3},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -142,8 +268,8 @@ def main():
     m = wl["m"]
     stream = torch.cuda.current_stream()
 
-    if wl["kind"] != "dense":
-        raise SystemExit("MoE benchmarking is not wired into bench.py yet")
+    if wl["kind"] == "moe":
+        return bench_moe(args, wl, svq, synth, dev, stream)
 
     if args.workload.startswith("layer4b"):
         mats, xs1 = synth.dense_layer()

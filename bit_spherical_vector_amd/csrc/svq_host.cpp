@@ -12,7 +12,6 @@
 #include "svq_internal.h"
 
 namespace svq {
-int gemm_m_pad(int m);
 hipError_t launch_moe(const svq_handle *experts, int32_t num_experts, const void *x, int64_t ldx,
                       int32_t x_per_slot, const int32_t *expert_ids, int64_t m, int32_t topk,
                       void *y, int64_t ldy, int ydt, void *ws, size_t ws_bytes, hipStream_t s,
@@ -277,6 +276,54 @@ static int plan_gemv(GemvBatch &b) {
   return begin;
 }
 
+// Compute units of the current device.
+static int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// K splits of the dequant-GEMM jobs: when the output tiles alone give fewer
+// than two blocks per compute unit (small m), each job's units are cut into
+// splits of about the same number of units, so that about two blocks per
+// compute unit result.  ups[j] = units per split; returns the partial-sum
+// workspace bytes (0 without splits).
+static size_t plan_splits(const svq_handle *w, int32_t count, int m_pad, int bm, int *splits,
+                          int *ups) {
+  const int tiles_m = m_pad / bm;
+  int64_t blocks = 0, work = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const int64_t tn = prefill_tiles_n((w[j].n + UNIT_ROWS - 1) / UNIT_ROWS);
+    blocks += tn * tiles_m;
+    work += tn * tiles_m * w[j].units;
+    splits[j] = 1;
+    ups[j] = w[j].units;
+  }
+  const int64_t target = 2 * (int64_t)device_cus();
+  if (blocks >= target) return 0;
+  const int64_t per = (work + target - 1) / target;  // units per block
+  size_t bytes = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const int U = w[j].units;
+    int sp = (int)((U + per - 1) / per);
+    sp = sp < 1 ? 1 : sp;
+    ups[j] = (U + sp - 1) / sp;
+    splits[j] = (U + ups[j] - 1) / ups[j];
+    if (splits[j] > 1) {
+      const size_t n_pad = (size_t)prefill_tiles_n((w[j].n + UNIT_ROWS - 1) / UNIT_ROWS) * 256;
+      bytes += align256((size_t)splits[j] * m_pad * n_pad * 4);
+    }
+  }
+  return bytes;
+}
+
 static svq_status linear_impl(const svq_handle *w, int32_t count, const void *const *xs,
                               const int64_t *ldx, int64_t m, void *const *ys, const int64_t *ldy,
                               svq_dtype ydt, void *workspace, size_t *workspace_bytes,
@@ -298,10 +345,10 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
   const bool exact = m <= EXACT_MAX_M && gemv_smem_bytes((int)m, k_max, u_max) <= GV_LDS_LIMIT;
   size_t need = 256;
   int m_pad = 0;
-  const bool prefill = !exact && m >= PREFILL_MIN_M;
+  int splits[GV_MAX_JOBS], ups[GV_MAX_JOBS];
   if (!exact) {
-    m_pad = prefill ? prefill_m_pad((int)m) : gemm_m_pad((int)m);
-    need = 0;
+    m_pad = prefill_m_pad((int)m);
+    need = plan_splits(w, count, m_pad, prefill_bm((int)m), splits, ups);
     for (int32_t j = 0; j < count; ++j)
       need += align256((size_t)m_pad * w[j].units * UNIT_SLOTS * 2);
   }
@@ -338,7 +385,7 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
       if ((((uintptr_t)xs[j]) | ((uintptr_t)ldx[j] * 2)) & 15) xvec = false;
     const int blocks = plan_gemv(b);
     e = launch_gemv_batched(b, blocks, gemv_smem_bytes((int)m, k_max, u_max), xvec, s);
-  } else if (prefill) {
+  } else {
     // permuted activations of every matrix in fragment order (one prep
     // launch), then one GEMM launch over all of them, longest k first
     PrefillBatch b;
@@ -358,7 +405,19 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
       b.job[j].y = ys[j];
       b.job[j].ldy = ldy[j];
       b.job[j].tiles_n = prefill_tiles_n(v.n_tiles);
+      b.job[j].splits = splits[j];
+      b.job[j].units_per_split = ups[j];
+      b.job[j].m_pad = m_pad;
+      b.job[j].n_pad = b.job[j].tiles_n * 256;
       if ((((uintptr_t)xs[j]) | ((uintptr_t)ldx[j] * 2)) & 15) xvec = false;
+    }
+    bool any_split = false;
+    for (int32_t j = 0; j < count; ++j) {
+      if (splits[j] > 1) {
+        b.job[j].part = (float *)ws;
+        ws += align256((size_t)splits[j] * m_pad * b.job[j].n_pad * 4);
+        any_split = true;
+      }
     }
     const size_t esz = ydt == SVQ_BF16 ? 2 : 4;
     b.yvec = 1;
@@ -374,25 +433,19 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
     // jobs start on multiples of 8 GEMM blocks (the XCD count) so that a
     // job's blocks with one m-tile share an XCD; the padding blocks exit at
     // once
-    int blocks = 0, prep_blocks = 0;
+    int blocks = 0, prep_blocks = 0, red_blocks = 0;
     for (int j = 0; j < b.count; ++j) {
-      b.job[j].tiles_m = m_pad / prefill_m_pad(1);
+      b.job[j].tiles_m = m_pad / prefill_bm((int)m);
       b.job[j].block_begin = blocks;
-      blocks += (b.job[j].tiles_n * b.job[j].tiles_m + 7) / 8 * 8;
+      blocks += (b.job[j].tiles_n * b.job[j].tiles_m * b.job[j].splits + 7) / 8 * 8;
       b.job[j].prep_begin = prep_blocks;
       prep_blocks += m_pad / rpb;
+      b.job[j].red_begin = red_blocks;
+      if (b.job[j].splits > 1) red_blocks += (int)m * ((b.job[j].w.n + 1023) / 1024);
     }
     e = launch_prefill_prep(b, prep_blocks, rpb, k_max, xvec, s);
-    if (e == hipSuccess) e = launch_prefill_batched(b, blocks, s);
-  } else {
-    uint8_t *ws = (uint8_t *)workspace;
-    for (int32_t j = 0; j < count && e == hipSuccess; ++j) {
-      const MatView v = view_of(&w[j]);
-      uint16_t *xb = (uint16_t *)ws;
-      ws += align256((size_t)m_pad * w[j].units * UNIT_SLOTS * 2);
-      e = launch_prep_bf16(v, (const uint16_t *)xs[j], ldx[j], (int)m, m_pad, xb, s);
-      if (e == hipSuccess) e = launch_gemm_bf16(v, xb, (int)m, m_pad, ys[j], ldy[j], (int)ydt, s);
-    }
+    if (e == hipSuccess) e = launch_prefill_batched(b, prefill_bm((int)m), blocks, s);
+    if (e == hipSuccess && any_split) e = launch_prefill_reduce(b, red_blocks, s);
   }
   return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
 }

@@ -88,13 +88,8 @@ size_t gemv_smem_bytes(int m, int k_max, int units_max);
 hipError_t launch_gemv_batched(GemvBatch &b, int blocks, size_t smem, bool xvec, hipStream_t s);
 constexpr int GV_ITEMS_PER_WAVE = 5;  // work items per wave the planner aims for
 
-// bf16 path (m > 4): prep writes xb = x[row][perm[p]] (bf16), zero padded to
-// m_pad rows and units*512 slots; the GEMM kernel multiplies.
-hipError_t launch_prep_bf16(const MatView &w, const uint16_t *x, int64_t ldx, int m, int m_pad,
-                            uint16_t *xb, hipStream_t s);
-hipError_t launch_gemm_bf16(const MatView &w, const uint16_t *xb, int m, int m_pad,
-                            void *y, int64_t ldy, int ydt, hipStream_t s);
-// Prefill (m >= PREFILL_MIN_M): a prep launch writes the permuted
+// Dequant-GEMM path (m > EXACT_MAX_M; "prefill" for m >= PREFILL_MIN_M, with
+// 64-row block tiles below that): a prep launch writes the permuted
 // activations of every matrix of the call ("jobs") in MFMA fragment order
 // (xb, padded to prefill_m_pad(m) rows), then one LDS-tiled dequant-GEMM
 // launch covers all jobs; a GEMM block owns one output tile of one job.
@@ -111,19 +106,28 @@ struct PrefillJob {
   int32_t tiles_m;      // output tiles along m
   int32_t block_begin;  // first GEMM block of this job
   int32_t prep_begin;   // first prep block of this job
+  // K split (small m): GEMM block (mt, nt, sp) covers units
+  // [sp * units_per_split, ...); with splits > 1 each writes an fp32 partial
+  // tile to part[sp][m_pad][n_pad] and the reduce launch sums them into y
+  int32_t splits, units_per_split;
+  float *part;
+  int32_t m_pad, n_pad;
+  int32_t red_begin;    // first reduce block of this job
 };
 struct PrefillBatch {
   PrefillJob job[GV_MAX_JOBS];
   int32_t count, ydt;
   int32_t yvec;  // every output row of every job starts 16-byte aligned
 };
-int prefill_m_pad(int m);
+int prefill_bm(int m);      // activation rows per block tile: 256 (m >= PREFILL_MIN_M) or 64
+int prefill_m_pad(int m);   // m rounded up to prefill_bm(m)
 int prefill_tiles_n(int n_tiles);
 int prefill_prep_rows(int k_max);  // activation rows per prep block
 // xvec: every activation row of every job starts 16-byte aligned.
 hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, int rpb, int k_max, bool xvec,
                                hipStream_t s);
-hipError_t launch_prefill_batched(PrefillBatch &b, int blocks, hipStream_t s);
+hipError_t launch_prefill_batched(PrefillBatch &b, int bm, int blocks, hipStream_t s);
+hipError_t launch_prefill_reduce(PrefillBatch &b, int blocks, hipStream_t s);
 
 // ---- MoE ----------------------------------------------------------------
 struct ExpertTable {

@@ -527,20 +527,7 @@ __device__ void prep_bf16_row(const uint16_t *__restrict__ perm, int K, int Kp,
   }
 }
 
-__global__ __launch_bounds__(256) void prep_bf16_kernel(MatView w, const uint16_t *__restrict__ x,
-                                                         int64_t ldx, int m, uint16_t *__restrict__ xb,
-                                                         int stage) {
-  extern __shared__ uint16_t s_row[];
-  const int r = blockIdx.x;
-  const int Kp = w.units * UNIT_SLOTS;
-  uint16_t *xo = xb + (size_t)r * Kp;
-  if (r >= m) {
-    for (int p = threadIdx.x; p < Kp; p += 256) xo[p] = 0;
-    return;
-  }
-  prep_bf16_row((const uint16_t *)(w.base + w.off_perm), w.k, Kp, x + (int64_t)r * ldx, xo, s_row,
-                stage);
-}
+constexpr int GEMM_BMT = 4;  // 64 activation rows per MoE GEMM block
 
 // GEMM tile: wave wv of the block owns row tile rt (16 output rows) and BMT
 // 16-row activation tiles starting at activation row m0 of xb (rows Kp
@@ -606,23 +593,6 @@ __device__ void gemm_bf16_tile(const MatView &w, int rt, const uint16_t *__restr
       if (mm < m_end) store_out(y, (size_t)out_row(mm) * ldy + n, C[t][j], ydt);
     }
   }
-}
-
-struct IdentityRows {
-  __device__ int operator()(int mm) const { return mm; }
-};
-
-template <int BMT>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(MatView w, const uint16_t *__restrict__ xb,
-                                                        int m, void *__restrict__ y, int64_t ldy,
-                                                        int ydt) {
-  __shared__ u4 s_btab[1024];
-  const u4 *btab_g = (const u4 *)(w.base + w.off_btab);
-  for (int j = threadIdx.x; j < 1024; j += 256) s_btab[j] = btab_g[j];
-  __syncthreads();
-  const int rt = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (rt >= w.n_tiles) return;
-  gemm_bf16_tile<BMT>(w, rt, xb, blockIdx.y * 16 * BMT, m, y, ldy, ydt, s_btab, IdentityRows{});
 }
 
 // ---------------------------------------------------------------------------
@@ -764,24 +734,6 @@ __global__ __launch_bounds__(256) void moe_gemm_bf16_kernel(MoeShape sh, ExpertT
 // Launchers
 // ---------------------------------------------------------------------------
 
-hipError_t launch_prep_bf16(const MatView &w, const uint16_t *x, int64_t ldx, int m, int m_pad,
-                            uint16_t *xb, hipStream_t s) {
-  const int stage = w.k <= 32768 ? 1 : 0;
-  const size_t lds = stage ? (size_t)w.k * 2 : 0;
-  hipLaunchKernelGGL(prep_bf16_kernel, dim3(m_pad), dim3(256), lds, s, w, x, ldx, m, xb, stage);
-  return hipGetLastError();
-}
-
-constexpr int GEMM_BMT = 4;  // 64 activation rows per block
-
-hipError_t launch_gemm_bf16(const MatView &w, const uint16_t *xb, int m, int m_pad, void *y,
-                            int64_t ldy, int ydt, hipStream_t s) {
-  dim3 grid((w.n_tiles + 3) / 4, m_pad / (16 * GEMM_BMT)), block(256);
-  hipLaunchKernelGGL(gemm_bf16_kernel<GEMM_BMT>, grid, block, 0, s, w, xb, m, y, ldy, ydt);
-  return hipGetLastError();
-}
-
-int gemm_m_pad(int m) { return ((m + 16 * GEMM_BMT - 1) / (16 * GEMM_BMT)) * (16 * GEMM_BMT); }
 
 // ---------------------------------------------------------------------------
 // MoE launcher.  Workspace layout depends on the path:

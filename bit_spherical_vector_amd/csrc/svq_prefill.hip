@@ -39,7 +39,7 @@
 
 namespace svq {
 
-constexpr int P_BM = 256, P_BN = 256, P_BK = 64;
+constexpr int P_BN = 256, P_BK = 64;
 constexpr int P_ROW = P_BK * 2;                  // 128 bytes per LDS row
 constexpr int P_B = P_BN * P_ROW;                // weight tile, 32 KB
 constexpr int P_STAGE = P_B;
@@ -108,8 +108,15 @@ __device__ __forceinline__ void p_store(const ItemCodes &c, uint8_t *tile, int r
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// BM = 256: four waves in a 2 x 2 grid of 128 x 128 tiles, one block per CU.
+// BM = 64 (activation row counts below 256): four waves side by side, each
+// 64 x 64, with a register budget for two blocks per CU.
+template <int BM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BM == 256 ? 1 : 2, BM == 256 ? 1 : 2)))
 void prefill_batched_kernel(PrefillBatch b) {
+  constexpr int WM = BM == 256 ? 2 : 1, WN = 4 / WM;  // wave grid
+  constexpr int TM = BM / WM, TN = P_BN / WN;         // wave tile
+  constexpr int NI = TM / 32, NJ = TN / 32;           // 32 x 32 accumulator blocks
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int jn = 0;
   while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].block_begin) ++jn;
@@ -121,25 +128,27 @@ void prefill_batched_kernel(PrefillBatch b) {
   // divides 8 or is a multiple of it and jobs start on multiples of 8), so
   // that tile is fetched into one L2 and reused there.
   const int local = (int)blockIdx.x - J.block_begin;
-  if (local >= J.tiles_n * J.tiles_m) return;  // padding block (uniform, before any barrier)
-  const int mt = local % J.tiles_m, nt = local / J.tiles_m;
+  if (local >= J.tiles_n * J.tiles_m * J.splits) return;  // padding block (uniform, before any barrier)
+  const int mt = local % J.tiles_m, nt = (local / J.tiles_m) % J.tiles_n;
+  const int sp = local / (J.tiles_m * J.tiles_n);  // K split: units [u0, u1)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / WN, wn = wv % WN;
   const int U = w.units, Kp = U * UNIT_SLOTS;
+  const int u0 = sp * J.units_per_split, u1 = min(U, u0 + J.units_per_split);
   const int rt0 = nt * (P_BN / UNIT_ROWS);
-  const int m0 = mt * P_BM;
+  const int m0 = mt * BM;
 
   uint8_t *s_btab = smem + P_OFF_BTAB;
   for (int j = tid; j < 1024; j += 256) ((u4 *)s_btab)[j] = ((const u4 *)(w.base + w.off_btab))[j];
 
-  // A fragments of the wave: 32-row blocks rb = m0/32 + 4wm + i; step s,
+  // A fragments of the wave: 32-row blocks rb = m0/32 + NI*wm + i; step s,
   // substep ks at a_ptr[i] + s * 2048 + ks * 512 elements (one 1 KB block)
   const int S = Kp / P_BK;
-  const uint16_t *a_ptr[4];
+  const uint16_t *a_ptr[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    a_ptr[i] = J.xb + ((size_t)((m0 >> 5) + 4 * wm + i) * S * 4 * 64 + lane) * 8;
+  for (int i = 0; i < NI; ++i)
+    a_ptr[i] = J.xb + ((size_t)((m0 >> 5) + NI * wm + i) * S * 4 * 64 + lane) * 8;
   // weight tile: row tiles rtl and rtl + 8 (clamped to the matrix; rows past
   // n are decoded from the last tile and never stored)
   const int rtl = tid >> 5, bl = (tid & 31) >> 2, jr = tid & 3;
@@ -150,21 +159,22 @@ void prefill_batched_kernel(PrefillBatch b) {
   const int rowA = rtl * UNIT_ROWS + jr;
   const int rowB = rowA + 8 * UNIT_ROWS;
 
-  f16x C[4][4];
+  f16x C[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) C[i][j] = (f16x){};
+    for (int j = 0; j < NJ; ++j) C[i][j] = (f16x){};
 
   // records of the current unit: [row tile A/B][half 0/1]
-  ItemCodes r00 = load_item(codesA, rec0), r01 = load_item(codesA, rec1);
-  ItemCodes r10 = load_item(codesB, rec0), r11 = load_item(codesB, rec1);
-  // A fragments of step 0: af[ks][i]
-  u4 af[4][4];
+  const size_t cu0 = (size_t)u0 * UNIT_BYTES;
+  ItemCodes r00 = load_item(codesA + cu0, rec0), r01 = load_item(codesA + cu0, rec1);
+  ItemCodes r10 = load_item(codesB + cu0, rec0), r11 = load_item(codesB + cu0, rec1);
+  // A fragments of the first step: af[ks][i]
+  u4 af[4][NI];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[ks][i] = *(const u4 *)(a_ptr[i] + ks * 512);
+    for (int i = 0; i < NI; ++i) af[ks][i] = *(const u4 *)(a_ptr[i] + (size_t)u0 * 8 * 2048 + ks * 512);
   __syncthreads();  // btab
   {
     u4 va[4], vb[4];
@@ -179,13 +189,13 @@ void prefill_batched_kernel(PrefillBatch b) {
   // of k substep ks is 2ks + (lane >> 5), stored at that ^ swz(row), and
   // swz(row) = ((lane & 31) >> 1) & 7 for every fragment
   const int sl = ((lane & 31) >> 1) & 7, hl = lane >> 5;
-  const int b_frag = (128 * wn + (lane & 31)) * P_ROW;
+  const int b_frag = (TN * wn + (lane & 31)) * P_ROW;
 
-  for (int u = 0; u < U; ++u) {
+  for (int u = u0; u < u1; ++u) {
     // records of the next unit (the last unit reloads itself): half 0 is
     // first needed by step 7's decode and loaded at step 6, after the
     // current half 0 was last used; half 1 is loaded at step 7
-    const size_t nu = (size_t)min(u + 1, U - 1) * UNIT_BYTES;
+    const size_t nu = (size_t)min(u + 1, u1 - 1) * UNIT_BYTES;
     ItemCodes n00, n01, n10, n11;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -201,15 +211,15 @@ void prefill_batched_kernel(PrefillBatch b) {
       // loads (clamped on the last step: a harmless reload), table reads,
       // signed stores and B fragment reads are interleaved with this step's
       // 64 MFMAs (sched_group_barrier), so they run in the MFMA shadow.
-      const int sn = min(u * 8 + t + 1, 8 * U - 1);
+      const int sn = min(u * 8 + t + 1, 8 * u1 - 1);
       const uint8_t *cur = smem + (t & 1) * P_STAGE;
       uint8_t *nxt = smem + ((t + 1) & 1) * P_STAGE;
       u4 va[4], vb[4];
-      u4 bf[2][4];
+      u4 bf[2][NJ];
       {
         const int pos = ((hl ^ sl) << 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bf[0][j] = *(const u4 *)(cur + b_frag + j * 32 * P_ROW + pos);
+        for (int j = 0; j < NJ; ++j) bf[0][j] = *(const u4 *)(cur + b_frag + j * 32 * P_ROW + pos);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -218,7 +228,7 @@ void prefill_batched_kernel(PrefillBatch b) {
         if (ks + 1 < P_BK / 16) {
           const int pos = (((2 * (ks + 1) + hl) ^ sl) << 4);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) bf[c ^ 1][j] = *(const u4 *)(cur + b_frag + j * 32 * P_ROW + pos);
+          for (int j = 0; j < NJ; ++j) bf[c ^ 1][j] = *(const u4 *)(cur + b_frag + j * 32 * P_ROW + pos);
         }
         if (ks == 0) {
           switch (t) {  // table rows of the next step's decode
@@ -257,25 +267,25 @@ void prefill_batched_kernel(PrefillBatch b) {
           }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < NJ; ++j)
             C[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8, af[ks][i]),
                                                               __builtin_bit_cast(b8, bf[c][j]),
                                                               C[i][j], 0, 0, 0);
         // the next step's A fragments of this substep, into the registers
         // these MFMAs just read
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[ks][i] = *(const u4 *)(a_ptr[i] + (size_t)sn * 2048 + ks * 512);
+        for (int i = 0; i < NI; ++i) af[ks][i] = *(const u4 *)(a_ptr[i] + (size_t)sn * 2048 + ks * 512);
         // Interleave: the next substep's B fragment reads (and, in substep
         // 0, the table reads) first, then MFMAs alternating with the A
         // loads and the step's vector work and stores.
-        if (ks + 1 < P_BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+        if (ks + 1 < P_BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, NJ, 0);  // DS reads
         if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // table reads
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
+        for (int g = 0; g < NI * NJ / 2; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-          if (g == 7) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);  // VMEM reads (A)
+          if (g == NI * NJ / 2 - 1) __builtin_amdgcn_sched_group_barrier(0x020, NI, 0);  // VMEM reads (A)
           if (ks == 1 || ks == 2) {
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU (signs)
             if (g & 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
@@ -292,46 +302,53 @@ void prefill_batched_kernel(PrefillBatch b) {
   }
 
   // Epilogue through LDS (the weight stages are free now): each wave turns
-  // its 128 x 128 accumulator tile into output-type rows in a private 16 KB
-  // region, 64 (bf16) or 32 (fp32) rows per pass, and writes them back as
+  // its TM x TN accumulator tile into output-type rows in a private 16 KB
+  // region, as many 32-row blocks per pass as fit, and writes them back as
   // whole 16-byte pieces of consecutive output columns.
   __syncthreads();
   {
     uint8_t *s_c = smem + wv * 16384;
-    const bool bf = b.ydt == 0;
+    // destination: y, or this split's fp32 partial tile (summed by the
+    // reduce launch) when K is split
+    const bool split = J.splits > 1;
+    void *const ybase = split ? (void *)(J.part + (size_t)sp * J.m_pad * J.n_pad) : J.y;
+    const int64_t yld = split ? J.n_pad : J.ldy;
+    const int nlim = split ? J.n_pad : w.n;
+    const bool yv = split || b.yvec;
+    const bool bf = !split && b.ydt == 0;
     const int esz = bf ? 2 : 4;
-    const int ipp = bf ? 2 : 1;           // 32-row blocks per pass
-    const int cpr = 128 * esz / 16;       // 16-byte pieces per row
-    const int per = 16 / esz;             // columns per piece
+    const int ipp = min(NI, 16384 / (32 * TN * esz));  // 32-row blocks per pass
+    const int cpr = TN * esz / 16;                      // 16-byte pieces per row
+    const int per = 16 / esz;                           // columns per piece
 #pragma unroll
-    for (int i0 = 0; i0 < 4; ++i0) {
+    for (int i0 = 0; i0 < NI; ++i0) {
       if (i0 % ipp != 0) continue;
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        if (ii >= ipp) continue;
+      for (int ii = 0; ii < NI; ++ii) {
+        if (ii >= ipp || i0 + ii >= NI) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int r = 32 * ii + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5), c = 32 * j + (lane & 31);
             const float val = C[i0 + ii][j][e];
-            if (bf) ((uint16_t *)s_c)[r * 128 + c] = f32_to_bf16_bits(val);
-            else ((float *)s_c)[r * 128 + c] = val;
+            if (bf) ((uint16_t *)s_c)[r * TN + c] = f32_to_bf16_bits(val);
+            else ((float *)s_c)[r * TN + c] = val;
           }
       }
       __syncthreads();
       for (int q = lane; q < 32 * ipp * cpr; q += 64) {
         const int r = q / cpr, ch = q % cpr;
-        const int mm = m0 + 128 * wm + 32 * i0 + r;
-        const int n0 = rt0 * UNIT_ROWS + 128 * wn + ch * per;
+        const int mm = m0 + TM * wm + 32 * i0 + r;
+        const int n0 = rt0 * UNIT_ROWS + TN * wn + ch * per;
         if (mm >= J.m) continue;
-        const u4 v = *(const u4 *)(s_c + r * 128 * esz + ch * 16);
-        char *dst = (char *)J.y + ((size_t)mm * J.ldy + n0) * esz;
-        if (b.yvec && n0 + per <= w.n) {
+        const u4 v = *(const u4 *)(s_c + r * TN * esz + ch * 16);
+        char *dst = (char *)ybase + ((size_t)mm * yld + n0) * esz;
+        if (yv && n0 + per <= nlim) {
           *(u4 *)dst = v;
         } else {
           for (int l = 0; l < per; ++l) {
-            if (n0 + l >= w.n) break;
+            if (n0 + l >= nlim) break;
             if (bf) ((uint16_t *)dst)[l] = (uint16_t)(v[l >> 1] >> (16 * (l & 1)));
             else ((uint32_t *)dst)[l] = v[l];
           }
@@ -340,6 +357,34 @@ void prefill_batched_kernel(PrefillBatch b) {
       __syncthreads();
     }
   }
+}
+
+// Sum of the K-split partial tiles of every split job, in split order:
+// y[row][n] = sum_s part[s][row][n], four columns per thread.
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillBatch b) {
+  int jn = 0;
+  while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].red_begin) ++jn;
+  const PrefillJob &J = b.job[jn];
+  if (J.splits <= 1) return;
+  const int per_row = (J.w.n + 1023) / 1024;  // blocks per output row
+  const int lb = (int)blockIdx.x - J.red_begin;
+  const int row = lb / per_row, n = (lb % per_row) * 1024 + 4 * (int)threadIdx.x;
+  if (row >= J.m || n >= J.w.n) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < J.splits; ++sp) {
+    const float4 v = *(const float4 *)(J.part + ((size_t)sp * J.m_pad + row) * J.n_pad + n);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  const float o[4] = {acc.x, acc.y, acc.z, acc.w};
+  for (int l = 0; l < 4 && n + l < J.w.n; ++l) store_out(J.y, (size_t)row * J.ldy + n + l, o[l], b.ydt);
+}
+
+hipError_t launch_prefill_reduce(PrefillBatch &b, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(prefill_reduce_kernel, dim3(blocks), dim3(256), 0, s, b);
+  return hipGetLastError();
 }
 
 // Prep for the prefill launch: the permuted activations of every job in
@@ -431,14 +476,25 @@ hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, int rpb, int k_max, 
   return hipGetLastError();
 }
 
-int prefill_m_pad(int m) { return ((m + P_BM - 1) / P_BM) * P_BM; }
+int prefill_bm(int m) { return m >= PREFILL_MIN_M ? 256 : 64; }
+
+int prefill_m_pad(int m) {
+  const int bm = prefill_bm(m);
+  return ((m + bm - 1) / bm) * bm;
+}
 
 int prefill_tiles_n(int n_tiles) { return (n_tiles + P_BN / UNIT_ROWS - 1) / (P_BN / UNIT_ROWS); }
 
-hipError_t launch_prefill_batched(PrefillBatch &b, int blocks, hipStream_t s) {
-  hipError_t e = allow_smem(prefill_batched_kernel, P_SMEM);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_batched_kernel, dim3(blocks), dim3(256), P_SMEM, s, b);
+hipError_t launch_prefill_batched(PrefillBatch &b, int bm, int blocks, hipStream_t s) {
+  if (bm == 256) {
+    hipError_t e = allow_smem(prefill_batched_kernel<256>, P_SMEM);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prefill_batched_kernel<256>, dim3(blocks), dim3(256), P_SMEM, s, b);
+  } else {
+    hipError_t e = allow_smem(prefill_batched_kernel<64>, P_SMEM);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prefill_batched_kernel<64>, dim3(blocks), dim3(256), P_SMEM, s, b);
+  }
   return hipGetLastError();
 }
 

@@ -268,6 +268,37 @@ class BatchedCall:
         _check(st, "svq_linear_batched")
 
 
+class MoeCall:
+    """Pre-marshalled arguments of one svq_moe_linear call (device tensors and
+    the packed experts are owned by the caller and must outlive the object)."""
+
+    def __init__(self, pms: Sequence[PackedMatrix], x, expert_ids, topk: int, x_per_slot: bool,
+                 y, workspace=None, stream=None):
+        import torch
+        self.keep = (list(pms), x, expert_ids, y)
+        self.handles = handle_array(pms)
+        self.n_exp = len(pms)
+        self.topk = topk
+        self.m = expert_ids.numel() // topk
+        self.x_per_slot = int(x_per_slot)
+        self.args_x = (x.data_ptr(), x.stride(0))
+        self.ids = expert_ids.data_ptr()
+        self.args_y = (y.data_ptr(), y.stride(0))
+        self.ydt = SVQ_F32 if y.dtype == torch.float32 else SVQ_BF16
+        need = moe_workspace_bytes(self.handles, self.n_exp, self.m, topk, self.x_per_slot)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        self.workspace = workspace
+        self.stream = _stream_handle(stream)
+
+    def __call__(self) -> None:
+        st, _ = svq_moe_linear(self.handles, self.n_exp, self.args_x[0], self.args_x[1],
+                               self.x_per_slot, self.ids, self.m, self.topk, self.args_y[0],
+                               self.args_y[1], self.ydt, self.workspace.data_ptr(),
+                               self.workspace.numel(), self.stream)
+        _check(st, "svq_moe_linear")
+
+
 def linear_batched(pms: Sequence[PackedMatrix], xs, outs=None, out_dtype=None, stream=None):
     """svq_linear over several matrices sharing m in one call."""
     import torch

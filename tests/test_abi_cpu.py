@@ -134,9 +134,35 @@ def _fake_handle(n, k, bd):
     return h
 
 
+def _dequant_gemm_need(shapes, m, cus=256):
+    """Workspace of the m > 4 path: permuted activations padded to the block
+    height (64 rows below m = 256, else 256), plus fp32 partial tiles of the
+    K splits taken when the output tiles give fewer than 2 blocks per compute
+    unit (no device here: 256 compute units assumed)."""
+    a = lambda v: (v + 255) // 256 * 256
+    cdiv = lambda p, q: -(-p // q)
+    bm = 256 if m >= 256 else 64
+    m_pad = cdiv(m, bm) * bm
+    tiles = [cdiv(cdiv(n, 16), 16) for n, _ in shapes]
+    units = [cdiv(k, 512) for _, k in shapes]
+    need = sum(a(m_pad * u * 512 * 2) for u in units)
+    blocks = sum(t * (m_pad // bm) for t in tiles)
+    if blocks < 2 * cus:
+        per = cdiv(sum(t * (m_pad // bm) * u for t, u in zip(tiles, units)), 2 * cus)
+        for t, u in zip(tiles, units):
+            sp = max(1, cdiv(u, per))
+            ups = cdiv(u, sp)
+            sp = cdiv(u, ups)
+            if sp > 1:
+                need += a(sp * m_pad * t * 256 * 4)
+    return need
+
+
 def test_linear_workspace_query_and_validation():
     h = _fake_handle(512, 1024, 8)
-    for m, expect in [(1, 256), (4, 256), (5, 64 * 2048), (64, 64 * 2048), (65, 128 * 2048)]:
+    dq = lambda m: _dequant_gemm_need([(512, 1024)], m)
+    assert dq(5) == 64 * 2048 + 2 * 64 * 512 * 4  # two K splits of one unit each
+    for m, expect in [(1, 256), (4, 256), (5, dq(5)), (64, dq(64)), (65, dq(65)), (300, dq(300))]:
         st, need = svq.svq_linear(h, None, m, 1024, None, 512, svq.SVQ_BF16, None, 0, 0)
         assert st == svq.SVQ_OK and need == expect, (m, need)
     # bad arguments
@@ -186,7 +212,7 @@ def test_linear_batched_query_and_validation():
     assert st == svq.SVQ_OK and need == 256
     st, need = svq.svq_linear_batched(hs, 3, None, None, 16, None, None, 0, None, 0, 0)
     a = lambda v: (v + 255) // 256 * 256
-    assert st == svq.SVQ_OK and need == a(64 * 1024 * 2) + a(64 * 2560 * 2) + a(64 * 1024 * 2)
+    assert st == svq.SVQ_OK and need == _dequant_gemm_need([(512, 1024), (64, 2560), (300, 768)], 16)
     assert svq.svq_linear_batched(hs, 0, None, None, 1, None, None, 0, None, 0, 0)[0] == \
         svq.SVQ_ERR_INVALID_ARG
     assert svq.svq_linear_batched(hs, 9, None, None, 1, None, None, 0, None, 0, 0)[0] == \
