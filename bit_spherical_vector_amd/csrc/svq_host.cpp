@@ -434,12 +434,21 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
     // job's blocks with one m-tile share an XCD; the padding blocks exit at
     // once
     int blocks = 0, prep_blocks = 0, red_blocks = 0;
+    // prep: row groups of rpb rows; with few of them, each job's chunks are
+    // also cut into ranges (at least 64 chunks each) for about 512 blocks
+    const int row_groups = count * (m_pad / rpb);
+    const int want = (512 + row_groups - 1) / row_groups;
+    for (int j = 0; j < b.count; ++j) {
+      const int nch = b.job[j].w.units * UNIT_SLOTS / 8;
+      int cs = want < nch / 64 ? want : nch / 64;
+      b.job[j].prep_csplit = cs < 1 ? 1 : cs;
+    }
     for (int j = 0; j < b.count; ++j) {
       b.job[j].tiles_m = m_pad / prefill_bm((int)m);
       b.job[j].block_begin = blocks;
       blocks += (b.job[j].tiles_n * b.job[j].tiles_m * b.job[j].splits + 7) / 8 * 8;
       b.job[j].prep_begin = prep_blocks;
-      prep_blocks += m_pad / rpb;
+      prep_blocks += (m_pad / rpb) * b.job[j].prep_csplit;
       b.job[j].red_begin = red_blocks;
       if (b.job[j].splits > 1) red_blocks += (int)m * ((b.job[j].w.n + 1023) / 1024);
     }

@@ -106,6 +106,7 @@ struct PrefillJob {
   int32_t tiles_m;      // output tiles along m
   int32_t block_begin;  // first GEMM block of this job
   int32_t prep_begin;   // first prep block of this job
+  int32_t prep_csplit;  // prep blocks per row group (chunk ranges)
   // K split (small m): GEMM block (mt, nt, sp) covers units
   // [sp * units_per_split, ...); with splits > 1 each writes an fp32 partial
   // tile to part[sp][m_pad][n_pad] and the reduce launch sums them into y

@@ -389,10 +389,11 @@ hipError_t launch_prefill_reduce(PrefillBatch &b, int blocks, hipStream_t s) {
 
 // Prep for the prefill launch: the permuted activations of every job in
 // fragment order (xb_frag_offset), rows >= m and slots >= k zero.  A block
-// takes `rpb` consecutive activation rows of one job and stages them in LDS
-// (rpb * k bf16); thread tau handles row tau % rpb and every (256 / rpb)-th
-// 8-slot chunk, so the rpb threads of one chunk write rpb * 16 contiguous
-// bytes.
+// takes `rpb` consecutive activation rows of one job and one of the job's
+// prep_csplit ranges of 8-slot chunks (several when the rows alone give few
+// blocks); it stages the live rows in LDS (rpb * k bf16), and thread tau
+// handles row tau % rpb and every (256 / rpb)-th chunk of the range, so the
+// rpb threads of one chunk write rpb * 16 contiguous bytes.
 template <bool XVEC>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int rpb) {
   extern __shared__ __attribute__((aligned(16))) uint16_t s_rows[];
@@ -401,15 +402,19 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int r
   const PrefillJob &J = b.job[jn];
   const MatView &w = J.w;
   const int K = w.k, Kp = w.units * UNIT_SLOTS, S = Kp / P_BK;
-  const int r0 = ((int)blockIdx.x - J.prep_begin) * rpb;
+  const int lb = (int)blockIdx.x - J.prep_begin;
+  const int r0 = (lb / J.prep_csplit) * rpb, cs = lb % J.prep_csplit;
+  const int nch = Kp / 8, cpb = (nch + J.prep_csplit - 1) / J.prep_csplit;
+  const int c_lo = cs * cpb, c_hi = min(nch, c_lo + cpb);
+  const int nlive = max(0, min(rpb, J.m - r0));  // rows of the group below m
   const int tid = threadIdx.x;
-  // Stage the rows (rows >= m read row m - 1 and are zeroed below), LDS row
+  // Stage the live rows (rows >= m are written as zeros below), LDS row
   // stride k + 8: the rpb threads of one chunk read one column of rpb rows,
   // and the 16-byte pad puts those rows in different banks.  Eight 16-byte
   // loads per thread are in flight at a time.
   const int ks_ = K + 8;
   if (XVEC) {
-    const int n8 = K / 8, tot = rpb * n8;
+    const int n8 = K / 8, tot = nlive * n8;
     constexpr int B = 8;
     for (int q0 = tid; q0 < tot; q0 += 256 * B) {
       u4 v[B];
@@ -429,8 +434,8 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int r
       }
     }
   } else {
-    for (int rr = 0; rr < rpb; ++rr) {
-      const uint16_t *xr = J.x + (int64_t)min(r0 + rr, J.m - 1) * J.ldx;
+    for (int rr = 0; rr < nlive; ++rr) {
+      const uint16_t *xr = J.x + (int64_t)(r0 + rr) * J.ldx;
       uint16_t *dst = s_rows + (size_t)rr * ks_;
       for (int j = tid; j < K; j += 256) dst[j] = xr[j];
     }
@@ -440,17 +445,27 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int r
   const int rr = tid % rpb, r = r0 + rr;
   const uint16_t *row = s_rows + (size_t)rr * ks_;
   const bool live = r < J.m;
-  for (int c = tid / rpb; c < Kp / 8; c += 256 / rpb) {
-    // perm is zero padded to the unit width, so every index is < k
-    const u4 pv = *(const u4 *)(perm + 8 * c);
-    u4 v;
+  // eight chunks at a time: their permutation vectors are loaded together
+  const int cstep = 256 / rpb;
+  for (int cb = c_lo + tid / rpb; cb < c_hi; cb += 8 * cstep) {
+    u4 pv[8];
 #pragma unroll
-    for (int l = 0; l < 4; ++l) {
-      const uint32_t lo = live && 8 * c + 2 * l < K ? row[pv[l] & 0xFFFFu] : 0u;
-      const uint32_t hi = live && 8 * c + 2 * l + 1 < K ? row[pv[l] >> 16] : 0u;
-      v[l] = lo | (hi << 16);
+    for (int bb = 0; bb < 8; ++bb)
+      pv[bb] = *(const u4 *)(perm + 8 * min(cb + bb * cstep, c_hi - 1));
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      const int c = cb + bb * cstep;
+      if (c >= c_hi) break;
+      // perm is zero padded to the unit width, so every index is < k
+      u4 v;
+#pragma unroll
+      for (int l = 0; l < 4; ++l) {
+        const uint32_t lo = live && 8 * c + 2 * l < K ? row[pv[bb][l] & 0xFFFFu] : 0u;
+        const uint32_t hi = live && 8 * c + 2 * l + 1 < K ? row[pv[bb][l] >> 16] : 0u;
+        v[l] = lo | (hi << 16);
+      }
+      *(u4 *)(J.xb + xb_frag_offset(r, 8 * c, S)) = v;
     }
-    *(u4 *)(J.xb + xb_frag_offset(r, 8 * c, S)) = v;
   }
 }
 
