@@ -46,6 +46,23 @@ __device__ __forceinline__ ItemCodes load_item(const uint8_t *ub, int rec) {
   return c;
 }
 
+// Matrix view of expert e of a MoE projection.
+__device__ __forceinline__ MatView expert_view(const MoeShape &sh, const ExpertTable &tab, int e) {
+  MatView v;
+  v.base = tab.base[e];
+  v.off_dtab = sh.off_dtab;
+  v.off_rtab = sh.off_rtab;
+  v.off_btab = sh.off_btab;
+  v.off_perm = sh.off_perm;
+  v.off_codes = sh.off_codes;
+  v.n = sh.n;
+  v.k = sh.k;
+  v.bd = tab.bd[e];
+  v.n_tiles = sh.n_tiles;
+  v.units = sh.units;
+  return v;
+}
+
 // Opt a kernel into more than 64 KB of dynamic LDS.
 template <typename Kern>
 static hipError_t allow_smem(Kern k, size_t bytes) {

@@ -513,108 +513,12 @@ hipError_t launch_gemv_batched(GemvBatch &b, int blocks, size_t smem, bool xvec,
 // bf16 path
 // ---------------------------------------------------------------------------
 
-// Block-level: xo[p] = xr[perm[p]] (bf16), zero for p >= k.  The row is
-// staged in LDS (s_row, K entries) when stage != 0.  blockDim.x == 256.
-__device__ void prep_bf16_row(const uint16_t *__restrict__ perm, int K, int Kp,
-                              const uint16_t *__restrict__ xr, uint16_t *__restrict__ xo,
-                              uint16_t *s_row, int stage) {
-  if (stage) {
-    for (int j = threadIdx.x; j < K; j += 256) s_row[j] = xr[j];
-    __syncthreads();
-    for (int p = threadIdx.x; p < Kp; p += 256) xo[p] = p < K ? s_row[perm[p]] : (uint16_t)0;
-  } else {
-    for (int p = threadIdx.x; p < Kp; p += 256) xo[p] = p < K ? xr[perm[p]] : (uint16_t)0;
-  }
-}
-
-constexpr int GEMM_BMT = 4;  // 64 activation rows per MoE GEMM block
-
-// GEMM tile: wave wv of the block owns row tile rt (16 output rows) and BMT
-// 16-row activation tiles starting at activation row m0 of xb (rows Kp
-// apart).  Each decoded code (B operand) is reused across the BMT activation
-// tiles.  Output row mm (m0 <= mm < m_end) goes to y row out_row(mm).
-//
-// v_mfma_f32_16x16x32_bf16 for K-block kb (code columns 4kb..4kb+3 of the
-// unit) takes from lane L the code in row L & 15, column 4kb + (L >> 4).  In
-// the unit layout that code is code 4c + (kb >> 2), c = (L >> 2) & 3, of lane
-// record 16(kb & 3) + 4(L >> 4) + (L & 3); so each lane reads four records
-// and decodes four codes from each.
-template <int BMT, typename RowMap>
-__device__ void gemm_bf16_tile(const MatView &w, int rt, const uint16_t *__restrict__ xb, int m0,
-                               int m_end, void *__restrict__ y, int64_t ldy, int ydt,
-                               const u4 *s_btab, RowMap out_row) {
-  const int lane = threadIdx.x & 63;
-  const int Kp = w.units * UNIT_SLOTS;
-  const uint8_t *tile = w.base + w.off_codes + (size_t)rt * w.units * UNIT_BYTES;
-  const u4 *xrow = (const u4 *)(xb + (size_t)(m0 + (lane & 15)) * Kp) + (lane >> 4);
-  const size_t xstride = (size_t)16 * Kp / 8;  // 16 rows, in u4 units
-  const int c = (lane >> 2) & 3;
-  const int rec0 = 4 * (lane >> 4) + (lane & 3);
-  const uint32_t SM = 0x80008000u;
-
-  f4 C[BMT];
-#pragma unroll
-  for (int t = 0; t < BMT; ++t) C[t] = (f4){0.f, 0.f, 0.f, 0.f};
-
-  for (int u = 0; u < w.units; ++u) {
-    const uint8_t *ub = tile + (size_t)u * UNIT_BYTES;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int rec = rec0 + 16 * t;
-      u4 S = *(const u4 *)(ub + PLANE_SIGN + 16 * rec);
-      const u4 L = *(const u4 *)(ub + PLANE_LOW + 16 * rec);
-      const uint32_t H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * rec) >> (8 * c);
-      const uint32_t Lc = c == 0 ? L[0] : c == 1 ? L[1] : c == 2 ? L[2] : L[3];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[j] <<= 4 * c;
-#pragma unroll
-      for (int sidx = 0; sidx < 4; ++sidx) {
-        const int kb = 4 * sidx + t;
-        const uint32_t idx = ((Lc >> (8 * sidx)) & 0xFFu) | (((H >> (2 * sidx)) & 3u) << 8);
-        u4 B = s_btab[idx];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) B[j] ^= (S[j] << sidx) & SM;
-#pragma unroll
-        for (int tt = 0; tt < BMT; ++tt) {
-          const u4 A = xrow[tt * xstride + 64 * u + 4 * kb];
-          C[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, A),
-                                                          __builtin_bit_cast(b8, B), C[tt], 0, 0, 0);
-        }
-      }
-    }
-  }
-  const int n = rt * 16 + (lane & 15);
-  if (n >= w.n) return;
-#pragma unroll
-  for (int t = 0; t < BMT; ++t) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int mm = m0 + 16 * t + 4 * (lane >> 4) + j;
-      if (mm < m_end) store_out(y, (size_t)out_row(mm) * ldy + n, C[t][j], ydt);
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Mixture of experts (grouped form; routing is not on the pages and follows
 // the usual top-k slot convention: slot q = t*topk + j)
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ MatView expert_view(const MoeShape &sh, const ExpertTable &tab, int e) {
-  MatView v;
-  v.base = tab.base[e];
-  v.off_dtab = sh.off_dtab;
-  v.off_rtab = sh.off_rtab;
-  v.off_btab = sh.off_btab;
-  v.off_perm = sh.off_perm;
-  v.off_codes = sh.off_codes;
-  v.n = sh.n;
-  v.k = sh.k;
-  v.bd = tab.bd[e];
-  v.n_tiles = sh.n_tiles;
-  v.units = sh.units;
-  return v;
-}
 
 // Per-slot fused GEMV (one activation row per slot): block (row tile, slot),
 // matrix = the slot's expert.
@@ -686,50 +590,6 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
   }
 }
 
-// bf16 grouped preparation: sorted row j holds slot sorted[j]'s activations
-// permuted by its expert's permutation.
-__global__ __launch_bounds__(256) void moe_prep_bf16_kernel(MoeShape sh, ExpertTable tab,
-                                                             const uint16_t *__restrict__ x,
-                                                             int64_t ldx, int x_per_slot, int topk,
-                                                             const int32_t *__restrict__ ids,
-                                                             const int32_t *__restrict__ sorted,
-                                                             uint16_t *__restrict__ xb, int stage) {
-  extern __shared__ uint16_t s_row[];
-  const int j = blockIdx.x;
-  const int q = sorted[j];
-  const int e = ids[q];
-  const int src = x_per_slot ? q : q / topk;
-  const int Kp = sh.units * UNIT_SLOTS;
-  prep_bf16_row((const uint16_t *)(tab.base[e] + sh.off_perm), sh.k, Kp, x + (int64_t)src * ldx,
-                xb + (size_t)j * Kp, s_row, stage);
-}
-
-struct SortedRows {
-  const int32_t *sorted;
-  __device__ int operator()(int mm) const { return sorted[mm]; }
-};
-
-template <int BMT>
-__global__ __launch_bounds__(256) void moe_gemm_bf16_kernel(MoeShape sh, ExpertTable tab,
-                                                            const int32_t *__restrict__ work,
-                                                            const int32_t *__restrict__ nwork,
-                                                            const int32_t *__restrict__ sorted,
-                                                            const uint16_t *__restrict__ xb,
-                                                            void *__restrict__ y, int64_t ldy,
-                                                            int ydt) {
-  __shared__ u4 s_btab[1024];
-  const int wi = blockIdx.y;
-  if (wi >= *nwork) return;
-  const int e = work[3 * wi + 0], r0 = work[3 * wi + 1], r1 = work[3 * wi + 2];
-  const MatView w = expert_view(sh, tab, e);
-  const u4 *btab_g = (const u4 *)(w.base + w.off_btab);
-  for (int j = threadIdx.x; j < 1024; j += 256) s_btab[j] = btab_g[j];
-  __syncthreads();
-  const int rt = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (rt >= w.n_tiles) return;
-  gemm_bf16_tile<BMT>(w, rt, xb, r0, r1, y, ldy, ydt, s_btab, SortedRows{sorted});
-}
-
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -784,7 +644,7 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
                          xp, ldx, x_per_slot, topk, y, ldy, ydt);
     return hipGetLastError();
   }
-  const int rows_per_item = 16 * GEMM_BMT;
+  const int rows_per_item = MOE_DQ_ROWS;
   const int max_work = (S + rows_per_item - 1) / rows_per_item + E;
   size_t off = 0;
   const size_t o_counts = off;
@@ -798,7 +658,7 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   const size_t o_nwork = off;
   off += 256;
   const size_t o_xb = off;
-  off += align256((size_t)(S + rows_per_item) * Kp * 2);
+  off += align256(moe_dq_xb_bytes(max_work, sh.units));
   *need = off;
   if (!ws) return hipSuccess;
   if (ws_bytes < *need) return hipErrorInvalidValue;
@@ -809,13 +669,10 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   uint16_t *xb = (uint16_t *)(b + o_xb);
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), 0, s, ids, S, E, rows_per_item, counts,
                      offsets, sorted, work, nwork);
-  const int stage = sh.k <= 32768 ? 1 : 0;
-  hipLaunchKernelGGL(moe_prep_bf16_kernel, dim3(S), dim3(256), stage ? (size_t)sh.k * 2 : 0, s, sh,
-                     tab, xp, ldx, x_per_slot, topk, ids, (const int32_t *)sorted, xb, stage);
-  hipLaunchKernelGGL(moe_gemm_bf16_kernel<GEMM_BMT>, dim3((sh.n_tiles + 3) / 4, max_work), dim3(256),
-                     0, s, sh, tab, (const int32_t *)work, (const int32_t *)nwork,
-                     (const int32_t *)sorted, (const uint16_t *)xb, y, ldy, ydt);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_moe_dq(sh, tab, xp, ldx, x_per_slot, topk, work, nwork, sorted, max_work, xb, y,
+                       ldy, ydt, s);
 }
 
 }  // namespace svq

@@ -47,6 +47,10 @@ constexpr int P_OFF_BTAB = 2 * P_STAGE;
 constexpr int P_SMEM = P_OFF_BTAB + BTAB_BYTES;  // 80 KB
 static_assert(P_SMEM <= 160 * 1024, "prefill LDS exceeds a workgroup's 160 KB");
 
+__host__ __device__ __forceinline__ int prefill_tiles_n_dev(int n_tiles) {
+  return (n_tiles + P_BN / UNIT_ROWS - 1) / (P_BN / UNIT_ROWS);
+}
+
 // Fragment order of the permuted activations xb (per job, m_pad x Kp bf16):
 // the 1 KB block F(rb, s, ks) holds, for 32-row block rb, K-step s and k
 // substep ks, lane L's eight values (row 32rb + (L & 31), slots
@@ -108,36 +112,37 @@ __device__ __forceinline__ void p_store(const ItemCodes &c, uint8_t *tile, int r
   }
 }
 
+// One output tile of the dequant-GEMM: activation rows m0 .. m0+BM-1 of a
+// fragment-ordered copy xb (rows >= m_valid past m0 are padding) times
+// weight rows 256 nt .. 256 nt + 255 of w, over units [u0, u1).  Output row
+// m0 + rr goes to row (ymap ? ymap[rr] : m0 + rr) of y (ld ldy, nlim
+// columns, bf16 when bf, else fp32; yvec: 16-byte aligned rows).
+struct DqTile {
+  MatView w;
+  const uint16_t *xb;
+  int m0, m_valid, nt, u0, u1;
+  void *y;
+  int64_t ldy;
+  int nlim;
+  bool bf, yvec;
+  const int32_t *ymap;
+};
+
 // BM = 256: four waves in a 2 x 2 grid of 128 x 128 tiles, one block per CU.
 // BM = 64 (activation row counts below 256): four waves side by side, each
 // 64 x 64, with a register budget for two blocks per CU.
 template <int BM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BM == 256 ? 1 : 2, BM == 256 ? 1 : 2)))
-void prefill_batched_kernel(PrefillBatch b) {
+__device__ __forceinline__ void dq_tile(const DqTile &T, uint8_t *smem) {
   constexpr int WM = BM == 256 ? 2 : 1, WN = 4 / WM;  // wave grid
   constexpr int TM = BM / WM, TN = P_BN / WN;         // wave tile
   constexpr int NI = TM / 32, NJ = TN / 32;           // 32 x 32 accumulator blocks
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int jn = 0;
-  while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].block_begin) ++jn;
-  const PrefillJob &J = b.job[jn];
-  const MatView &w = J.w;
-  // Blocks are dealt to the 8 XCDs round-robin (block i on XCD i % 8) and
-  // each XCD has its own L2: with m-tile = local % tiles_m, the blocks that
-  // share one 256-row activation tile run on the same XCD (when tiles_m
-  // divides 8 or is a multiple of it and jobs start on multiples of 8), so
-  // that tile is fetched into one L2 and reused there.
-  const int local = (int)blockIdx.x - J.block_begin;
-  if (local >= J.tiles_n * J.tiles_m * J.splits) return;  // padding block (uniform, before any barrier)
-  const int mt = local % J.tiles_m, nt = (local / J.tiles_m) % J.tiles_n;
-  const int sp = local / (J.tiles_m * J.tiles_n);  // K split: units [u0, u1)
+  const MatView &w = T.w;
+  const int nt = T.nt, u0 = T.u0, u1 = T.u1, m0 = T.m0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv / WN, wn = wv % WN;
   const int U = w.units, Kp = U * UNIT_SLOTS;
-  const int u0 = sp * J.units_per_split, u1 = min(U, u0 + J.units_per_split);
   const int rt0 = nt * (P_BN / UNIT_ROWS);
-  const int m0 = mt * BM;
 
   uint8_t *s_btab = smem + P_OFF_BTAB;
   for (int j = tid; j < 1024; j += 256) ((u4 *)s_btab)[j] = ((const u4 *)(w.base + w.off_btab))[j];
@@ -148,7 +153,7 @@ void prefill_batched_kernel(PrefillBatch b) {
   const uint16_t *a_ptr[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i)
-    a_ptr[i] = J.xb + ((size_t)((m0 >> 5) + NI * wm + i) * S * 4 * 64 + lane) * 8;
+    a_ptr[i] = T.xb + ((size_t)((m0 >> 5) + NI * wm + i) * S * 4 * 64 + lane) * 8;
   // weight tile: row tiles rtl and rtl + 8 (clamped to the matrix; rows past
   // n are decoded from the last tile and never stored)
   const int rtl = tid >> 5, bl = (tid & 31) >> 2, jr = tid & 3;
@@ -308,14 +313,11 @@ void prefill_batched_kernel(PrefillBatch b) {
   __syncthreads();
   {
     uint8_t *s_c = smem + wv * 16384;
-    // destination: y, or this split's fp32 partial tile (summed by the
-    // reduce launch) when K is split
-    const bool split = J.splits > 1;
-    void *const ybase = split ? (void *)(J.part + (size_t)sp * J.m_pad * J.n_pad) : J.y;
-    const int64_t yld = split ? J.n_pad : J.ldy;
-    const int nlim = split ? J.n_pad : w.n;
-    const bool yv = split || b.yvec;
-    const bool bf = !split && b.ydt == 0;
+    void *const ybase = T.y;
+    const int64_t yld = T.ldy;
+    const int nlim = T.nlim;
+    const bool yv = T.yvec;
+    const bool bf = T.bf;
     const int esz = bf ? 2 : 4;
     const int ipp = min(NI, 16384 / (32 * TN * esz));  // 32-row blocks per pass
     const int cpr = TN * esz / 16;                      // 16-byte pieces per row
@@ -339,11 +341,12 @@ void prefill_batched_kernel(PrefillBatch b) {
       __syncthreads();
       for (int q = lane; q < 32 * ipp * cpr; q += 64) {
         const int r = q / cpr, ch = q % cpr;
-        const int mm = m0 + TM * wm + 32 * i0 + r;
+        const int rr = TM * wm + 32 * i0 + r;  // row of the tile
         const int n0 = rt0 * UNIT_ROWS + TN * wn + ch * per;
-        if (mm >= J.m) continue;
+        if (rr >= T.m_valid) continue;
+        const int orow = T.ymap ? T.ymap[rr] : m0 + rr;
         const u4 v = *(const u4 *)(s_c + r * TN * esz + ch * 16);
-        char *dst = (char *)ybase + ((size_t)mm * yld + n0) * esz;
+        char *dst = (char *)ybase + ((size_t)orow * yld + n0) * esz;
         if (yv && n0 + per <= nlim) {
           *(u4 *)dst = v;
         } else {
@@ -357,6 +360,46 @@ void prefill_batched_kernel(PrefillBatch b) {
       __syncthreads();
     }
   }
+}
+
+// Dense calls: block (mt, nt, sp) of job J (m-tile fastest, so that the
+// blocks sharing one activation tile fall on one XCD: blocks are dealt to
+// the 8 XCDs round-robin and jobs start on multiples of 8).  With K splits
+// the block writes its fp32 partial tile to J.part[sp] for the reduce launch.
+template <int BM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BM == 256 ? 1 : 2, BM == 256 ? 1 : 2)))
+void prefill_batched_kernel(PrefillBatch b) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int jn = 0;
+  while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].block_begin) ++jn;
+  const PrefillJob &J = b.job[jn];
+  const int local = (int)blockIdx.x - J.block_begin;
+  if (local >= J.tiles_n * J.tiles_m * J.splits) return;  // padding block (uniform, before any barrier)
+  const int mt = local % J.tiles_m, nt = (local / J.tiles_m) % J.tiles_n;
+  const int sp = local / (J.tiles_m * J.tiles_n);
+  DqTile T;
+  T.w = J.w;
+  T.xb = J.xb;
+  T.m0 = mt * BM;
+  T.m_valid = J.m - T.m0;
+  T.nt = nt;
+  T.u0 = sp * J.units_per_split;
+  T.u1 = min(J.w.units, T.u0 + J.units_per_split);
+  T.ymap = nullptr;
+  if (J.splits > 1) {
+    T.y = J.part + (size_t)sp * J.m_pad * J.n_pad;
+    T.ldy = J.n_pad;
+    T.nlim = J.n_pad;
+    T.bf = false;
+    T.yvec = true;
+  } else {
+    T.y = J.y;
+    T.ldy = J.ldy;
+    T.nlim = J.w.n;
+    T.bf = b.ydt == 0;
+    T.yvec = b.yvec != 0;
+  }
+  dq_tile<BM>(T, smem);
 }
 
 // Sum of the K-split partial tiles of every split job, in split order:
@@ -394,27 +437,23 @@ hipError_t launch_prefill_reduce(PrefillBatch &b, int blocks, hipStream_t s) {
 // blocks); it stages the live rows in LDS (rpb * k bf16), and thread tau
 // handles row tau % rpb and every (256 / rpb)-th chunk of the range, so the
 // rpb threads of one chunk write rpb * 16 contiguous bytes.
+// Gather of up to rpb activation rows into fragment order: src[rr] is the
+// bf16 row (nullptr: padding row, written as zeros) that becomes xb row
+// xrow0 + rr, permuted by perm (k values, zero padded to Kp); this block
+// handles 8-slot chunks [c_lo, c_hi).  Rows are staged in LDS with stride
+// k + 8: the rpb threads of one chunk read one column of rpb rows, and the
+// 16-byte pad puts those rows in different banks; thread tau handles row
+// tau % rpb, so the rpb threads of one chunk write rpb * 16 contiguous
+// bytes.
 template <bool XVEC>
-__global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int rpb) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t s_rows[];
-  int jn = 0;
-  while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].prep_begin) ++jn;
-  const PrefillJob &J = b.job[jn];
-  const MatView &w = J.w;
-  const int K = w.k, Kp = w.units * UNIT_SLOTS, S = Kp / P_BK;
-  const int lb = (int)blockIdx.x - J.prep_begin;
-  const int r0 = (lb / J.prep_csplit) * rpb, cs = lb % J.prep_csplit;
-  const int nch = Kp / 8, cpb = (nch + J.prep_csplit - 1) / J.prep_csplit;
-  const int c_lo = cs * cpb, c_hi = min(nch, c_lo + cpb);
-  const int nlive = max(0, min(rpb, J.m - r0));  // rows of the group below m
-  const int tid = threadIdx.x;
-  // Stage the live rows (rows >= m are written as zeros below), LDS row
-  // stride k + 8: the rpb threads of one chunk read one column of rpb rows,
-  // and the 16-byte pad puts those rows in different banks.  Eight 16-byte
-  // loads per thread are in flight at a time.
+__device__ __forceinline__ void dq_gather_rows(const uint16_t *const *src, int rpb, int K, int Kp,
+                                               const uint16_t *perm, uint16_t *xb, int xrow0,
+                                               int c_lo, int c_hi, uint16_t *s_rows) {
+  const int S = Kp / P_BK, tid = threadIdx.x;
   const int ks_ = K + 8;
   if (XVEC) {
-    const int n8 = K / 8, tot = nlive * n8;
+    // eight 16-byte loads per thread in flight at a time
+    const int n8 = K / 8, tot = rpb * n8;
     constexpr int B = 8;
     for (int q0 = tid; q0 < tot; q0 += 256 * B) {
       u4 v[B];
@@ -422,7 +461,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int r
       for (int bb = 0; bb < B; ++bb) {
         const int q = min(q0 + 256 * bb, tot - 1);
         const int rr = q / n8, c = q - rr * n8;
-        v[bb] = *(const u4 *)(J.x + (int64_t)min(r0 + rr, J.m - 1) * J.ldx + 8 * c);
+        v[bb] = src[rr] ? *(const u4 *)(src[rr] + 8 * c) : (u4){0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
@@ -434,17 +473,16 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int r
       }
     }
   } else {
-    for (int rr = 0; rr < nlive; ++rr) {
-      const uint16_t *xr = J.x + (int64_t)(r0 + rr) * J.ldx;
+    for (int rr = 0; rr < rpb; ++rr) {
+      if (!src[rr]) continue;
       uint16_t *dst = s_rows + (size_t)rr * ks_;
-      for (int j = tid; j < K; j += 256) dst[j] = xr[j];
+      for (int j = tid; j < K; j += 256) dst[j] = src[rr][j];
     }
   }
   __syncthreads();
-  const uint16_t *perm = (const uint16_t *)(w.base + w.off_perm);
-  const int rr = tid % rpb, r = r0 + rr;
+  const int rr = tid % rpb;
   const uint16_t *row = s_rows + (size_t)rr * ks_;
-  const bool live = r < J.m;
+  const bool live = src[rr] != nullptr;
   // eight chunks at a time: their permutation vectors are loaded together
   const int cstep = 256 / rpb;
   for (int cb = c_lo + tid / rpb; cb < c_hi; cb += 8 * cstep) {
@@ -464,9 +502,32 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int r
         const uint32_t hi = live && 8 * c + 2 * l + 1 < K ? row[pv[bb][l] >> 16] : 0u;
         v[l] = lo | (hi << 16);
       }
-      *(u4 *)(J.xb + xb_frag_offset(r, 8 * c, S)) = v;
+      *(u4 *)(xb + xb_frag_offset(xrow0 + rr, 8 * c, S)) = v;
     }
   }
+}
+
+// Prep for dense calls: the permuted activations of every job in fragment
+// order (xb_frag_offset), rows >= m and slots >= k zero.  A block takes
+// `rpb` consecutive activation rows of one job and one of the job's
+// prep_csplit ranges of 8-slot chunks (several when the rows alone give few
+// blocks).
+template <bool XVEC>
+__global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int rpb) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_rows[];
+  int jn = 0;
+  while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].prep_begin) ++jn;
+  const PrefillJob &J = b.job[jn];
+  const MatView &w = J.w;
+  const int K = w.k, Kp = w.units * UNIT_SLOTS;
+  const int lb = (int)blockIdx.x - J.prep_begin;
+  const int r0 = (lb / J.prep_csplit) * rpb, cs = lb % J.prep_csplit;
+  const int nch = Kp / 8, cpb = (nch + J.prep_csplit - 1) / J.prep_csplit;
+  const uint16_t *src[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) src[rr] = rr < rpb && r0 + rr < J.m ? J.x + (int64_t)(r0 + rr) * J.ldx : nullptr;
+  dq_gather_rows<XVEC>(src, rpb, K, Kp, (const uint16_t *)(w.base + w.off_perm), J.xb, r0,
+                       cs * cpb, min(nch, cs * cpb + cpb), s_rows);
 }
 
 // LDS of a prep block: rpb staged rows of k + 8 values.
@@ -491,6 +552,102 @@ hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, int rpb, int k_max, 
   return hipGetLastError();
 }
 
+// MoE grouped dequant-GEMM (routed slots beyond the exact path): work item
+// wi = (expert, sorted rows r0 .. r1 <= r0 + 64) of the routing; its
+// activations are xb rows 64 wi .. 64 wi + 63 (fragment order, padding rows
+// zero), and its output rows go to the slots sorted[r0 ..].
+__global__ __launch_bounds__(256) void moe_dq_prep_kernel(MoeShape sh, ExpertTable tab,
+                                                          const uint16_t *__restrict__ x, int64_t ldx,
+                                                          int x_per_slot, int topk,
+                                                          const int32_t *__restrict__ work,
+                                                          const int32_t *__restrict__ nwork,
+                                                          const int32_t *__restrict__ sorted,
+                                                          uint16_t *__restrict__ xb, int rpb,
+                                                          int csplit, int xvec) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_rows[];
+  const int groups = MOE_DQ_ROWS / rpb;
+  const int lb = (int)blockIdx.x;
+  const int wi = lb / (groups * csplit), rg = (lb / csplit) % groups, cs = lb % csplit;
+  if (wi >= *nwork) return;  // uniform, before any barrier
+  const int e = work[3 * wi], r0 = work[3 * wi + 1], r1 = work[3 * wi + 2];
+  const int Kp = sh.units * UNIT_SLOTS, nch = Kp / 8, cpb = (nch + csplit - 1) / csplit;
+  const uint16_t *src[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    const int j = r0 + rg * rpb + rr;
+    src[rr] = nullptr;
+    if (rr < rpb && j < r1) {
+      const int q = sorted[j];
+      src[rr] = x + (int64_t)(x_per_slot ? q : q / topk) * ldx;
+    }
+  }
+  const uint16_t *perm = (const uint16_t *)(tab.base[e] + sh.off_perm);
+  if (xvec)
+    dq_gather_rows<true>(src, rpb, sh.k, Kp, perm, xb, MOE_DQ_ROWS * wi + rg * rpb, cs * cpb,
+                         min(nch, cs * cpb + cpb), s_rows);
+  else
+    dq_gather_rows<false>(src, rpb, sh.k, Kp, perm, xb, MOE_DQ_ROWS * wi + rg * rpb, cs * cpb,
+                          min(nch, cs * cpb + cpb), s_rows);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void moe_dq_kernel(MoeShape sh, ExpertTable tab, const int32_t *__restrict__ work,
+                   const int32_t *__restrict__ nwork, const int32_t *__restrict__ sorted,
+                   const uint16_t *__restrict__ xb, void *__restrict__ y, int64_t ldy, int ydt,
+                   int yvec) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tiles_n = prefill_tiles_n_dev(sh.n_tiles);
+  const int wi = (int)blockIdx.x / tiles_n, nt = (int)blockIdx.x % tiles_n;
+  if (wi >= *nwork) return;  // uniform, before any barrier
+  const int e = work[3 * wi], r0 = work[3 * wi + 1], r1 = work[3 * wi + 2];
+  DqTile T;
+  T.w = expert_view(sh, tab, e);
+  T.xb = xb;
+  T.m0 = MOE_DQ_ROWS * wi;
+  T.m_valid = r1 - r0;
+  T.nt = nt;
+  T.u0 = 0;
+  T.u1 = sh.units;
+  T.y = y;
+  T.ldy = ldy;
+  T.nlim = sh.n;
+  T.bf = ydt == 0;
+  T.yvec = yvec != 0;
+  T.ymap = sorted + r0;
+  dq_tile<MOE_DQ_ROWS>(T, smem);
+}
+
+size_t moe_dq_xb_bytes(int max_work, int units) {
+  return (size_t)max_work * MOE_DQ_ROWS * units * UNIT_SLOTS * 2;
+}
+
+hipError_t launch_moe_dq(const MoeShape &sh, const ExpertTable &tab, const uint16_t *x, int64_t ldx,
+                         int x_per_slot, int topk, const int32_t *work, const int32_t *nwork,
+                         const int32_t *sorted, int max_work, uint16_t *xb, void *y, int64_t ldy,
+                         int ydt, hipStream_t s) {
+  const int rpb = prefill_prep_rows(sh.k);
+  const int nch = sh.units * UNIT_SLOTS / 8;
+  const int groups = max_work * (MOE_DQ_ROWS / rpb);
+  int csplit = (512 + groups - 1) / groups;
+  csplit = csplit < nch / 64 ? csplit : nch / 64;
+  csplit = csplit < 1 ? 1 : csplit;
+  const bool xvec = ((((uintptr_t)x) | ((uintptr_t)ldx * 2)) & 15) == 0;
+  const size_t lds = prep_lds(rpb, sh.k);
+  hipError_t e = allow_smem(moe_dq_prep_kernel, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_dq_prep_kernel, dim3(groups * csplit), dim3(256), lds, s, sh, tab, x, ldx,
+                     x_per_slot, topk, work, nwork, sorted, xb, rpb, csplit, xvec ? 1 : 0);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t esz = ydt == 0 ? 2 : 4;
+  const int yvec = ((((uintptr_t)y) | ((uintptr_t)ldy * esz)) & 15) == 0;
+  e = allow_smem(moe_dq_kernel, P_SMEM);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_dq_kernel, dim3(max_work * prefill_tiles_n(sh.n_tiles)), dim3(256), P_SMEM,
+                     s, sh, tab, work, nwork, sorted, xb, y, ldy, ydt, yvec);
+  return hipGetLastError();
+}
+
 int prefill_bm(int m) { return m >= PREFILL_MIN_M ? 256 : 64; }
 
 int prefill_m_pad(int m) {
@@ -498,7 +655,7 @@ int prefill_m_pad(int m) {
   return ((m + bm - 1) / bm) * bm;
 }
 
-int prefill_tiles_n(int n_tiles) { return (n_tiles + P_BN / UNIT_ROWS - 1) / (P_BN / UNIT_ROWS); }
+int prefill_tiles_n(int n_tiles) { return prefill_tiles_n_dev(n_tiles); }
 
 hipError_t launch_prefill_batched(PrefillBatch &b, int bm, int blocks, hipStream_t s) {
   if (bm == 256) {
