@@ -552,23 +552,51 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
   __shared__ int32_t s_off[MAX_EXPERTS + 1];
   __shared__ int32_t s_fill[MAX_EXPERTS];
   __shared__ int32_t s_items[MAX_EXPERTS + 1];
+  __shared__ int32_t s_wsum[2][MAX_EXPERTS / 64];
   const int t = threadIdx.x;
   for (int e = t; e < E; e += 1024) s_cnt[e] = 0;
   __syncthreads();
   for (int q = t; q < S; q += 1024) atomicAdd(&s_cnt[ids[q]], 1);
   __syncthreads();
-  if (t == 0) {
-    int off = 0, items = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = off;
-      s_items[e] = items;
-      off += s_cnt[e];
-      items += (s_cnt[e] + rows_per_item - 1) / rows_per_item;
-      s_fill[e] = 0;
+  // exclusive scans of the slot counts and of the work items per expert
+  // (threads 0 .. MAX_EXPERTS-1, one expert each: a scan within each wave,
+  // then the wave totals)
+  int c = 0, it = 0, ci = 0, ii = 0;
+  if (t < MAX_EXPERTS) {
+    c = t < E ? s_cnt[t] : 0;
+    it = (c + rows_per_item - 1) / rows_per_item;
+    ci = c;
+    ii = it;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int uc = __shfl_up(ci, d), ui = __shfl_up(ii, d);
+      if ((t & 63) >= d) {
+        ci += uc;
+        ii += ui;
+      }
     }
-    s_off[E] = off;
-    s_items[E] = items;
-    *nwork = items;
+    if ((t & 63) == 63) {
+      s_wsum[0][t >> 6] = ci;
+      s_wsum[1][t >> 6] = ii;
+    }
+  }
+  __syncthreads();
+  if (t < MAX_EXPERTS) {
+    int bc = 0, bi = 0;
+    for (int w = 0; w < (t >> 6); ++w) {
+      bc += s_wsum[0][w];
+      bi += s_wsum[1][w];
+    }
+    if (t < E) {
+      s_off[t] = bc + ci - c;
+      s_items[t] = bi + ii - it;
+      s_fill[t] = 0;
+    }
+    if (t == E - 1) {
+      s_off[E] = bc + ci;
+      s_items[E] = bi + ii;
+      *nwork = bi + ii;
+    }
   }
   __syncthreads();
   for (int e = t; e < E; e += 1024) counts[e] = s_cnt[e];
