@@ -527,14 +527,16 @@ __global__ __launch_bounds__(256) SVQ_GEMV_OCCUPANCY(1) void moe_gemv_kernel(Moe
                                                        const int32_t *__restrict__ ids,
                                                        const uint16_t *__restrict__ x, int64_t ldx,
                                                        int x_per_slot, int topk,
-                                                       void *__restrict__ y, int64_t ldy, int ydt) {
+                                                       void *__restrict__ y, int64_t ldy, int ydt,
+                                                       int R) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int q = blockIdx.y;
   const MatView w = expert_view(sh, tab, ids[q]);
   const int src = x_per_slot ? q : q / topk;
-  const int rt0 = blockIdx.x;
+  const int rt0 = blockIdx.x * R;
   char *yq = (char *)y + (size_t)q * ldy * (ydt == 0 ? 2 : 4);
-  gemv_fused_block<1, XVEC>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, 1, 1, smem);
+  gemv_fused_block<1, XVEC>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, min(R, w.n_tiles - rt0),
+                            smem);
 }
 
 // Routing for the grouped GEMM: counting sort of slots by expert and a list
@@ -664,12 +666,17 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
     if ((xvec ? lds_ok_t : lds_ok_f) != hipSuccess) return xvec ? lds_ok_t : lds_ok_f;
     hipError_t e = xvec ? allow_smem(moe_gemv_kernel<true>, smem) : allow_smem(moe_gemv_kernel<false>, smem);
     if (e != hipSuccess) return e;
+    // row tiles per block: as in the dense planner, enough units per wave
+    // to amortise the gather, while the launch keeps >= 256 blocks
+    int R = sh.units <= GV_ITEMS_PER_WAVE ? 4 : (sh.units <= 2 * GV_ITEMS_PER_WAVE ? 2 : 1);
+    while (R > 1 && ((sh.n_tiles + R - 1) / R) * S < 256) R /= 2;
+    const dim3 grid((sh.n_tiles + R - 1) / R, S);
     if (xvec)
-      hipLaunchKernelGGL(moe_gemv_kernel<true>, dim3(sh.n_tiles, S), dim3(256), smem, s, sh, tab, ids,
-                         xp, ldx, x_per_slot, topk, y, ldy, ydt);
+      hipLaunchKernelGGL(moe_gemv_kernel<true>, grid, dim3(256), smem, s, sh, tab, ids, xp, ldx,
+                         x_per_slot, topk, y, ldy, ydt, R);
     else
-      hipLaunchKernelGGL(moe_gemv_kernel<false>, dim3(sh.n_tiles, S), dim3(256), smem, s, sh, tab, ids,
-                         xp, ldx, x_per_slot, topk, y, ldy, ydt);
+      hipLaunchKernelGGL(moe_gemv_kernel<false>, grid, dim3(256), smem, s, sh, tab, ids, xp, ldx,
+                         x_per_slot, topk, y, ldy, ydt, R);
     return hipGetLastError();
   }
   const int rows_per_item = MOE_DQ_ROWS;
