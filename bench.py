@@ -42,17 +42,21 @@ COLD_BYTES = 600 << 20  # > 2 x 256 MB MALL
 # only holds for the kernel source it was taken on (sha256 prefix below);
 # after any change of that source the traffic is reported as null.
 TRAFFIC = {
-    "layer4b_m1": {"kernel_src_sha256": "b31dd7ff600c7fa0",
-                   "fetch_kib": 14581.8, "fetch_factor": 2.0,
+    "layer4b_m1": {"kernel_src_sha256": "9b021ec005d631f3",
+                   "fetch_kib": 14587.9, "fetch_factor": 2.0,
                    "write_kib": 60.0, "write_factor": 1.0},
 }
 
 
 def kernel_source_hash() -> str:
+    """sha256 prefix of the exact-path kernel sources (translation unit and
+    the device header it includes)."""
     import hashlib
-    path = os.path.join(ROOT, "bit_spherical_vector_amd", "csrc", "svq_kernels.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ("svq_kernels.hip", "svq_device.h"):
+        with open(os.path.join(ROOT, "bit_spherical_vector_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_bytes(workload):
@@ -320,7 +324,9 @@ def main():
     ms_per_step = ms_total / args.steps
 
     flops = sum(2.0 * m * mat.n * mat.k for mat in mats)
-    launches = 1 if m <= 4 else 2 * len(mats)
+    # m <= 4: one exact-path launch; else prep + GEMM, plus the K-split
+    # reduce below 256 rows
+    launches = 1 if m <= 4 else (2 if m >= 256 else 3)
     # roofline.achieved: algorithmic work of one step over the mean step
     # duration of the timed region.  For m <= 4 a step is exactly one launch
     # of the dominant kernel (gemv_batched_kernel); for m > 4 it also holds

@@ -7,19 +7,22 @@
 // product is a dense contraction, so the decoded tile feeds the matrix cores.
 //
 // One launch covers every matrix of a call ("jobs", longest k first).  A
-// block computes a P_BM x P_BN output tile (activation rows x weight rows)
-// over K in steps of P_BK = 64 permuted slots (8 codes per weight row).  The
+// block computes a BM x 256 output tile (activation rows x weight rows) over
+// K in steps of P_BK = 64 permuted slots (8 codes per weight row).  The
 // decoded weight tile of each step, RNE_bf16(R*D) with the signs applied,
 // goes through LDS (two stages: the next step's decode overlaps the current
 // step's MFMAs, one barrier per step).  The activations never touch LDS: a
 // prep launch writes the permuted activations in MFMA fragment order (see
-// prefill_prep_kernel), so each wave loads its A fragments straight into
-// registers with fully coalesced 1 KB loads, one step ahead.  Four waves in
-// a 2 x 2 grid each own a 128 x 128 tile: 16 accumulators of
-// v_mfma_f32_32x32x16_bf16 (held in accumulation registers; this
-// translation unit is built without the VGPR-form MFMA option of the
-// exact-path kernels).  B fragments of the next 16-wide k substep are read
-// while the current one's MFMAs run.
+// xb_frag_offset), so each wave loads its A fragments straight into
+// registers with fully coalesced 1 KB loads, one step ahead.  BM = 256:
+// four waves in a 2 x 2 grid, each 128 x 128 (16 accumulators of
+// v_mfma_f32_32x32x16_bf16 in accumulation registers; this translation unit
+// is built without the VGPR-form MFMA option of the exact-path kernels).
+// BM = 64 (fewer activation rows): four 64 x 64 waves side by side, two
+// blocks per CU, and K splits summed by a reduce launch when the output
+// tiles alone give few blocks.  B fragments of the next 16-wide k substep
+// are read while the current one's MFMAs run.  The same tile serves the
+// grouped MoE product (moe_dq_kernel).
 //
 // 32x32x16 operands: lane L holds row L & 31 of a 32-row fragment and
 // k = 8(L >> 5)..+7; accumulator element e of lane L is row
