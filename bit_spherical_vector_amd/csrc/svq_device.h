@@ -37,13 +37,32 @@ struct ItemCodes {
   uint32_t H;
 };
 
-// Lane record `rec` of the coded unit at ub.
+// Lane record `rec` of the coded unit at ub.  NT: non-temporal loads, for
+// codes that are read exactly once (a streaming hint; on MI355X it raises
+// the HBM rate of a launch that streams all of its codes about twofold).
+template <bool NT = false>
 __device__ __forceinline__ ItemCodes load_item(const uint8_t *ub, int rec) {
   ItemCodes c;
-  c.S = *(const u4 *)(ub + PLANE_SIGN + 16 * rec);
-  c.L = *(const u4 *)(ub + PLANE_LOW + 16 * rec);
-  c.H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * rec);
+  if constexpr (NT) {
+    c.S = __builtin_nontemporal_load((const u4 *)(ub + PLANE_SIGN + 16 * rec));
+    c.L = __builtin_nontemporal_load((const u4 *)(ub + PLANE_LOW + 16 * rec));
+    c.H = __builtin_nontemporal_load((const uint32_t *)(ub + PLANE_HIGH + 4 * rec));
+  } else {
+    c.S = *(const u4 *)(ub + PLANE_SIGN + 16 * rec);
+    c.L = *(const u4 *)(ub + PLANE_LOW + 16 * rec);
+    c.H = *(const uint32_t *)(ub + PLANE_HIGH + 4 * rec);
+  }
   return c;
+}
+
+// The job of a batched launch that owns this block (see JobStarts): the
+// number of later job starts at or below blockIdx.x.
+__device__ __forceinline__ int find_job(const JobStarts &st, int count) {
+  const int blk = (int)blockIdx.x;
+  int j = 0;
+#pragma unroll
+  for (int t = 1; t < GV_MAX_JOBS; ++t) j += (t < count && blk >= st.first[t]) ? 1 : 0;
+  return j;
 }
 
 // Matrix view of expert e of a MoE projection.

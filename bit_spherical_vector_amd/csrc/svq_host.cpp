@@ -238,12 +238,42 @@ svq_status svq_pack(const svq_matrix_desc *src, void *dst_dev, size_t *dst_bytes
   return SVQ_OK;
 }
 
-// Exact path (m <= 4): plan the blocks of one fused launch over `count`
-// matrices.  R (row tiles per block, 1, 2 or 4) is the largest that keeps
-// every wave's work items (one 512-slot unit of one row tile each) within
-// GV_ITEMS_PER_WAVE; R halves while the launch has fewer than 512 blocks.  Jobs with the largest k come first (their
-// blocks run longest).
-static int plan_gemv(GemvBatch &b) {
+// Exact path (m <= 4): plan the blocks of the gather and main launches over
+// `count` matrices.  R (row tiles per main block) is the largest that keeps
+// the block's units (R*U, split evenly between its 4 waves) near
+// GV_UNITS_PER_WAVE per wave, at most GV_MAX_R.  Jobs with the largest k
+// come first (their blocks run longest).  Returns the main launch's blocks.
+static int plan_gemv(GemvBatch &b, int *gather_blocks) {
+  for (int i = 1; i < b.count; ++i)
+    for (int j = i; j > 0 && b.job[j].w.k > b.job[j - 1].w.k; --j) {
+      const GemvJob t = b.job[j];
+      b.job[j] = b.job[j - 1];
+      b.job[j - 1] = t;
+    }
+  int begin = 0, gbegin = 0;
+  for (int j = 0; j < b.count; ++j) {
+    const int U = b.job[j].w.units;
+    int R = 4 * GV_UNITS_PER_WAVE / U;
+    R = R < 1 ? 1 : (R > GV_MAX_R ? GV_MAX_R : R);
+    b.job[j].R = R;
+    b.job[j].block_begin = begin;
+    b.starts.first[j] = begin;
+    begin += (b.job[j].w.n_tiles + R - 1) / R;
+    b.gather_starts.first[j] = gbegin;
+    gbegin += b.m * ((U + 3) / 4);
+  }
+  // table-touch blocks start on a multiple of 8 (block i runs on XCD i % 8)
+  b.touch_begin = (gbegin + 7) / 8 * 8;
+  *gather_blocks = b.touch_begin + 8 * b.count;
+  return begin;
+}
+
+// Exact path, m = 1 (one fused launch): R (row tiles per block, 1, 2 or 4)
+// is the largest that keeps every wave's work items (one 512-slot unit of one
+// row tile each) within GF_ITEMS_PER_WAVE; R halves while the launch has
+// fewer than 512 blocks.  Jobs with the largest k come first (their blocks
+// run longest).  Returns the launch's blocks.
+static int plan_fused(GemvBatch &b) {
   for (int i = 1; i < b.count; ++i)
     for (int j = i; j > 0 && b.job[j].w.k > b.job[j - 1].w.k; --j) {
       const GemvJob t = b.job[j];
@@ -253,7 +283,7 @@ static int plan_gemv(GemvBatch &b) {
   int R[GV_MAX_JOBS];
   for (int j = 0; j < b.count; ++j) {
     const int U = b.job[j].w.units;
-    R[j] = U <= GV_ITEMS_PER_WAVE ? 4 : (U <= 2 * GV_ITEMS_PER_WAVE ? 2 : 1);
+    R[j] = U <= GF_ITEMS_PER_WAVE ? 4 : (U <= 2 * GF_ITEMS_PER_WAVE ? 2 : 1);
   }
   auto total = [&]() {
     int t = 0;
@@ -271,6 +301,7 @@ static int plan_gemv(GemvBatch &b) {
   for (int j = 0; j < b.count; ++j) {
     b.job[j].R = R[j];
     b.job[j].block_begin = begin;
+    b.starts.first[j] = begin;
     begin += (b.job[j].w.n_tiles + R[j] - 1) / R[j];
   }
   return begin;
@@ -336,17 +367,24 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
     const svq_status st = validate_handle(&w[j]);
     if (st != SVQ_OK) return st;
   }
-  // the exact path keeps the permuted activations of a block in LDS
-  int k_max = 0, u_max = 0;
+  int k_max = 0, bd_max = 0, u_max = 0;
   for (int32_t j = 0; j < count; ++j) {
     k_max = w[j].k > k_max ? w[j].k : k_max;
+    bd_max = w[j].bd > bd_max ? w[j].bd : bd_max;
     u_max = w[j].units > u_max ? w[j].units : u_max;
   }
-  const bool exact = m <= EXACT_MAX_M && gemv_smem_bytes((int)m, k_max, u_max) <= GV_LDS_LIMIT;
-  size_t need = 256;
+  const bool exact = m <= EXACT_MAX_M;
+  // m = 1: the fused launch, when the activation row and its permuted copy
+  // fit in LDS beside the tables
+  const bool fused = m == 1 && gemv_fused_smem_bytes(k_max, u_max) <= GV_LDS_LIMIT;
+  size_t need = 0;
   int m_pad = 0;
   int splits[GV_MAX_JOBS], ups[GV_MAX_JOBS];
-  if (!exact) {
+  if (fused) {
+    need = 256;  // unused: the fused launch gathers in LDS
+  } else if (exact) {
+    for (int32_t j = 0; j < count; ++j) need += gemv_ws_bytes((int)m, w[j].units);
+  } else {
     m_pad = prefill_m_pad((int)m);
     need = plan_splits(w, count, m_pad, prefill_bm((int)m), splits, ups);
     for (int32_t j = 0; j < count; ++j)
@@ -373,18 +411,34 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
     b.count = count;
     b.m = (int)m;
     b.ydt = (int)ydt;
+    uint8_t *ws = (uint8_t *)workspace;
     for (int32_t j = 0; j < count; ++j) {
       b.job[j].w = view_of(&w[j]);
       b.job[j].x = (const uint16_t *)xs[j];
       b.job[j].ldx = ldx[j];
+      if (!fused) {
+        b.job[j].xg = ws;
+        b.job[j].xs = (float *)(ws + align256((size_t)m * w[j].units * GV_XG_UNIT_BYTES));
+        ws += gemv_ws_bytes((int)m, w[j].units);
+      }
       b.job[j].y = ys[j];
       b.job[j].ldy = ldy[j];
     }
-    bool xvec = true;
+    b.xvec = 1;
     for (int32_t j = 0; j < count; ++j)
-      if ((((uintptr_t)xs[j]) | ((uintptr_t)ldx[j] * 2)) & 15) xvec = false;
-    const int blocks = plan_gemv(b);
-    e = launch_gemv_batched(b, blocks, gemv_smem_bytes((int)m, k_max, u_max), xvec, s);
+      if ((((uintptr_t)xs[j]) | ((uintptr_t)ldx[j] * 2)) & 15) b.xvec = 0;
+    if (fused) {
+      const int blocks = plan_fused(b);
+      e = launch_gemv_fused(b, blocks, gemv_fused_smem_bytes(k_max, u_max), s);
+      return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+    }
+    int gather_blocks = 0;
+    const int blocks = plan_gemv(b, &gather_blocks);
+    int r_max = 1;
+    for (int32_t j = 0; j < count; ++j) r_max = b.job[j].R > r_max ? b.job[j].R : r_max;
+    const size_t smem = gemv_smem_bytes((int)m, bd_max, r_max);
+    b.red_off = (int32_t)gemv_smem_bytes((int)m, bd_max, 0);
+    e = launch_gemv_batched(b, gather_blocks, k_max, blocks, smem, s);
   } else {
     // permuted activations of every matrix in fragment order (one prep
     // launch), then one GEMM launch over all of them, longest k first
@@ -451,6 +505,9 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
       prep_blocks += (m_pad / rpb) * b.job[j].prep_csplit;
       b.job[j].red_begin = red_blocks;
       if (b.job[j].splits > 1) red_blocks += (int)m * ((b.job[j].w.n + 1023) / 1024);
+      b.gemm_starts.first[j] = b.job[j].block_begin;
+      b.prep_starts.first[j] = b.job[j].prep_begin;
+      b.red_starts.first[j] = b.job[j].red_begin;
     }
     e = launch_prefill_prep(b, prep_blocks, rpb, k_max, xvec, s);
     if (e == hipSuccess) e = launch_prefill_batched(b, prefill_bm((int)m), blocks, s);

@@ -65,28 +65,57 @@ struct MatView {
 };
 
 // ---- dense path ---------------------------------------------------------
-// Exact path (m <= 4): one fused kernel per call (gather, scale, decode and
-// multiply) over up to GV_MAX_JOBS matrices; a block owns R in {1, 2, 4} row
-// tiles of one matrix ("job").
+// Exact path, m = 2..4: a gather launch writes every matrix's permuted,
+// per-unit scaled fp16 activations to the workspace (xg: row a of unit u at
+// xg + (a*units + u) * GV_XG_UNIT_BYTES, 64 code columns x 8 slots; xs: the
+// unit's 2^-e per row at xs[4*u + a]); one main launch then covers up to
+// GV_MAX_JOBS matrices ("jobs"), a block owning R consecutive row tiles of
+// one job.
 constexpr int GV_MAX_JOBS = 8;
+constexpr int GV_XG_UNIT_BYTES = UNIT_SLOTS * 2;  // one unit of one row, fp16
+constexpr int GV_MAX_R = 4;                       // row tiles per main block
+// First block of each job of one launch (job t owns blocks
+// [first[t], first[t + 1])).  The starts sit in one 32-byte array at the
+// head of the launch arguments, so a block finds its job with a single
+// scalar load rather than a chain of dependent loads through the job records.
+struct JobStarts {
+  int32_t first[GV_MAX_JOBS];
+};
 struct GemvJob {
   MatView w;
   const uint16_t *x;
   int64_t ldx;
+  uint8_t *xg;          // gathered activations (workspace)
+  float *xs;            // their scales, [units][4]
   void *y;
   int64_t ldy;
-  int32_t R;            // row tiles per block
-  int32_t block_begin;  // first block of this job
+  int32_t R;            // row tiles per main block
+  int32_t block_begin;  // first main block of this job
 };
 struct GemvBatch {
+  JobStarts starts;         // main launch
+  JobStarts gather_starts;  // gather launch (4 waves per block, one per (row, unit))
   GemvJob job[GV_MAX_JOBS];
   int32_t count, m, ydt;
+  int32_t red_off;          // LDS offset of the partial sums (after the tables)
+  int32_t touch_begin;      // gather launch: first of the 8*count table-touch blocks
+  int32_t xvec;             // every activation row starts 16-byte aligned
 };
 constexpr size_t GV_LDS_LIMIT = 160 * 1024;  // LDS per workgroup on gfx950
-size_t gemv_smem_bytes(int m, int k_max, int units_max);
-// xvec: every activation row of every job starts 16-byte aligned.
-hipError_t launch_gemv_batched(GemvBatch &b, int blocks, size_t smem, bool xvec, hipStream_t s);
-constexpr int GV_ITEMS_PER_WAVE = 5;  // work items per wave the planner aims for
+// Workspace of the exact path for one matrix of `units` units.
+inline size_t gemv_ws_bytes(int m, int units) {
+  return align256((size_t)m * units * GV_XG_UNIT_BYTES) + align256((size_t)units * 16);
+}
+// LDS of the main launch for the largest bd of its jobs and R <= r_max.
+size_t gemv_smem_bytes(int m, int bd_max, int r_max);
+hipError_t launch_gemv_batched(GemvBatch &b, int gather_blocks, int k_max, int blocks, size_t smem,
+                               hipStream_t s);
+constexpr int GV_UNITS_PER_WAVE = 4;  // units per wave the planner aims for
+// m = 1: one fused launch (gather in the block); R in {1, 2, 4} row tiles
+// per block, each wave near GF_ITEMS_PER_WAVE units.
+constexpr int GF_ITEMS_PER_WAVE = 5;
+size_t gemv_fused_smem_bytes(int k_max, int units_max);
+hipError_t launch_gemv_fused(GemvBatch &b, int blocks, size_t smem, hipStream_t s);
 
 // Dequant-GEMM path (m > EXACT_MAX_M; "prefill" for m >= PREFILL_MIN_M, with
 // 64-row block tiles below that): a prep launch writes the permuted
@@ -116,6 +145,7 @@ struct PrefillJob {
   int32_t red_begin;    // first reduce block of this job
 };
 struct PrefillBatch {
+  JobStarts gemm_starts, prep_starts, red_starts;  // copies of block/prep/red_begin
   PrefillJob job[GV_MAX_JOBS];
   int32_t count, ydt;
   int32_t yvec;  // every output row of every job starts 16-byte aligned

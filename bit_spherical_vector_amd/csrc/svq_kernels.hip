@@ -31,54 +31,57 @@
 namespace svq {
 
 // ---------------------------------------------------------------------------
-// Exact path (m <= 4), fused: gather + scale + decode-and-multiply in one
-// kernel.
+// Exact path (m <= 4): two launches.
 // ---------------------------------------------------------------------------
 //
-// A block owns R in {1, 2, 4} consecutive 16-row tiles of one matrix and all
-// of its K; each tile gets 4/R of the block's 4 waves, which split its 512-slot
-// units between them.
-// Prologue: the block stages each activation row in LDS and gathers the
-// permuted slots (Fig. 6 caption: a subvector multiplies eight reordered
-// activations) unit by unit.  Each unit u gets its own exact power-of-two
-// scale 2^e_u with max|x_u| * 2^e_u in [2^14, 2^15), so the fp16 copy is
-// exact for every bf16 value above 2^-17 * max|x_u|; the scale is undone once
-// per (row tile, unit) in fp32.
+// Gather launch: one wave per (matrix, activation row a, coded unit u).  Lane
+// c takes code column c of the unit (permuted slots 8c .. 8c+7; Fig. 6
+// caption: a subvector multiplies eight reordered activations), loads the
+// eight activations x[a][perm[p]] and the wave writes the unit's fp16 copy
+// with an exact power-of-two scale 2^e (max|x_au| * 2^e in [2^14, 2^15)), so
+// the copy is exact for every bf16 value above 2^-17 * max|x_au|; 2^-e is
+// stored beside it and undone once per (row tile, unit) in fp32.
 //
-// Main loop: one work item is one coded unit (16 rows x 64 codes, 2304
-// contiguous bytes, 36 per lane).  The codes of up to GV_PIPE items are in
-// flight per wave, issued before the prologue so that their HBM latency
-// overlaps it.  MFMA mapping (v_mfma_f32_4x4x4_16b_f16: 16 blocks of 4 lanes,
-// lane 4b + j):
+// Main launch: a block of 4 waves owns R consecutive 16-row tiles of one
+// matrix and all of its K; the block's R*U coded units are split evenly
+// between the waves in tile-major order (a wave's range may cross a tile
+// boundary: its partial sums are flushed to LDS at every tile end).  One work
+// item is one coded unit (16 rows x 64 codes, 2304 contiguous bytes, 36 per
+// lane) together with the lane's four 16-byte activation fragments and the
+// unit's scales, all loaded straight into registers GV_PIPE items ahead.
+// MFMA mapping (v_mfma_f32_4x4x4_16b_f16: 16 blocks of 4 lanes, lane 4b + j):
 //   B: lane 4b + j holds 4 signed direction values of its code (one half of
 //      the code's 8), column j of block b;
 //   A: lane 4b + j holds the matching 4 scaled activations of activation row
 //      j (rows >= m repeat row 0), row j of block b; all four lanes of a
-//      block share the code column, so A is read once per column group and
-//      reused for the 4 codes of that column;
+//      block share the code column;
 //   C: lane 4b + j receives, for activation row a, the dot product of its
 //      own code's half with row a; two chained halves give the code's 8-term
 //      dot product.
 // The radius multiply R[r] * dot is an fp32 FMA per code, so R*D is never
-// rounded.  Partial sums meet across lanes (shuffles) and waves (LDS).
+// rounded.
+//
+// Direction rows are read from LDS at random (one row per code), which is
+// the main loop's most frequent LDS access.  A ds_read_b128 serves 16 lanes
+// per pass, one 16-byte bank group each, so the table is stored C times,
+// lane-interleaved: copy c of row d sits at d*16C + c*16 and lane l reads
+// copy l % C.  With C = 16 (bd <= 7) the 16 lanes of a pass always hit 16
+// different bank groups; the 256-row tables of bd = 8 keep C = 8 (32 KB, so
+// that four blocks fit in a compute unit), two lanes per bank group.
 
 constexpr int GV_WAVES = 4;
 #ifndef SVQ_GV_PIPE
 #define SVQ_GV_PIPE 2
 #endif
-// Work items whose codes are in flight per wave.  A CU can only keep a
-// limited number of requests in flight; a wave that asks for more stalls at
-// issue and cannot do other work meanwhile, so the ring is kept short and
-// refilled after each item's compute.
+// Work items whose loads are in flight per wave.
 constexpr int GV_PIPE = SVQ_GV_PIPE;
-constexpr int GV_PRE_UNITS = 5;   // permutation vectors prefetched per wave (gather)
-constexpr int GV_STAGE_BATCH = 5; // 16-byte activation loads per thread per staging pass
-// LDS: direction table, radius table by 10-bit index, unit scales, cross-wave
-// partial sums, then the permuted activations and the staging row.
-constexpr int GV_OFF_RTAB = DTAB_BYTES;
-constexpr int GV_OFF_SCALE = GV_OFF_RTAB + RTAB_BYTES;
-constexpr int GV_OFF_RED = GV_OFF_SCALE + 128 * 4 * 4;  // [U <= 128][M <= 4] scales
-constexpr int GV_SMEM_FIXED = GV_OFF_RED + GV_WAVES * 4 * 4 * 4 * 4;
+// lane-interleaved copies of a direction table of 2^bd rows (at most 32 KB)
+__host__ __device__ constexpr int gv_copies(int bd) { return bd >= 8 ? 8 : 16; }
+// LDS (absolute addresses, see lds_u4): radius by 10-bit index, then the
+// direction copies (2^bd rows of 256 bytes), then the cross-wave partial sums
+// [R][GV_WAVES][4][4][4][M] fp32 at GemvBatch::red_off.
+constexpr int GV_OFF_RTAB = 0;
+constexpr int GV_OFF_D = RTAB_BYTES;
 
 // Maximum over the 64 lanes of a non-negative float (returned in every
 // lane): DPP row shifts within the 16-lane rows, row broadcasts across rows,
@@ -132,19 +135,178 @@ typedef __attribute__((address_space(3))) const _Float16 lds_f16_t;
 __device__ __forceinline__ u4 lds_u4(uint32_t addr) { return *(lds_u4_t *)(size_t)addr; }
 __device__ __forceinline__ _Float16 lds_f16(uint32_t addr) { return *(lds_f16_t *)(size_t)addr; }
 
+// Gather of one block: activation row xr (K bf16) is staged in LDS with
+// coalesced loads while each wave loads the permutation vector of its unit
+// u0 + w (one memory round trip for both); then wave w writes the unit's
+// permuted fp16 copy (64 x 16 bytes at xg_row + u * 1 KB, lane c = code
+// column c) with its exact power-of-two scale (see the gather launch above),
+// and 2^-e to xs_row[4u].  xvec: xr is 16-byte aligned.
+constexpr int GV_STAGE_BATCH = 8;  // staging loads in flight per thread
+__device__ __forceinline__ void gather_block(const uint16_t *__restrict__ perm,
+                                             const uint16_t *__restrict__ xr, int K, int U, int u0,
+                                             bool xvec, uint8_t *__restrict__ xg_row,
+                                             float *__restrict__ xs_row, uint8_t *smem) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int u = min(u0 + wv, U - 1);  // clamped: every wave reaches the barrier
+  const int p0 = u * UNIT_SLOTS + 8 * lane;
+  const u4 pv = __builtin_nontemporal_load((const u4 *)(perm + p0));
+  uint16_t *s_x = (uint16_t *)smem;
+  if (xvec) {
+    const int n8 = K / 8;
+    for (int base = 0; base < n8; base += 256 * GV_STAGE_BATCH) {
+      u4 v[GV_STAGE_BATCH];
+#pragma unroll
+      for (int g = 0; g < GV_STAGE_BATCH; ++g) {
+        const int idx = base + g * 256 + tid;
+        v[g] = ((const u4 *)xr)[min(idx, n8 - 1)];
+      }
+#pragma unroll
+      for (int g = 0; g < GV_STAGE_BATCH; ++g) {
+        const int idx = base + g * 256 + tid;
+        if (idx < n8) ((u4 *)s_x)[idx] = v[g];
+      }
+    }
+  } else {
+    for (int base = 0; base < K; base += 256 * 2 * GV_STAGE_BATCH) {
+      uint16_t v[2 * GV_STAGE_BATCH];
+#pragma unroll
+      for (int g = 0; g < 2 * GV_STAGE_BATCH; ++g) v[g] = xr[min(base + g * 256 + tid, K - 1)];
+#pragma unroll
+      for (int g = 0; g < 2 * GV_STAGE_BATCH; ++g)
+        if (base + g * 256 + tid < K) s_x[base + g * 256 + tid] = v[g];
+    }
+  }
+  __syncthreads();
+  if (u0 + wv >= U) return;  // wave-uniform, after the only barrier
+  float v[8], mx = 0.f;
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {  // perm is zero padded to the unit width: every channel < K
+    v[2 * l] = (p0 + 2 * l < K) ? bf16_bits_to_f32(s_x[pv[l] & 0xFFFFu]) : 0.f;
+    v[2 * l + 1] = (p0 + 2 * l + 1 < K) ? bf16_bits_to_f32(s_x[pv[l] >> 16]) : 0.f;
+  }
+#pragma unroll
+  for (int l = 0; l < 8; ++l) mx = fmaxf(mx, fabsf(v[l]));
+  mx = wave_max(mx);
+  const int e = mx > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
+  u4 h;
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {
+    const _Float16 lo = (_Float16)ldexpf(v[2 * l], e), hi = (_Float16)ldexpf(v[2 * l + 1], e);
+    h[l] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  ((u4 *)(xg_row + (size_t)u * GV_XG_UNIT_BYTES))[lane] = h;
+  if (lane == 0) xs_row[4 * u] = ldexpf(1.f, -e);
+}
+
+// Gather launch of the dense path: block = (job, activation row a, group of
+// 4 units), wave = unit.  The launch ends with 8 blocks per job (one per XCD:
+// blocks go to the XCDs round-robin) that only read the job's direction and
+// radius tables, so that the main launch finds them near.
+__global__ __launch_bounds__(256) void gemv_gather_kernel(GemvBatch b) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  if ((int)blockIdx.x >= b.touch_begin) {
+    const int jt = ((int)blockIdx.x - b.touch_begin) >> 3;
+    if (jt < b.count) {
+      const MatView &w = b.job[jt].w;
+      const u4 d = ((const u4 *)(w.base + w.off_dtab))[threadIdx.x];
+      const u2 r = ((const u2 *)(w.base + w.off_rtab))[threadIdx.x];
+      asm volatile("" ::"v"(d), "v"(r));  // keeps the loads
+    }
+    return;
+  }
+  const int j = find_job(b.gather_starts, b.count);
+  const GemvJob &jb = b.job[j];
+  const int U = jb.w.units, groups = (U + GV_WAVES - 1) / GV_WAVES;
+  const int local = (int)blockIdx.x - b.gather_starts.first[j];
+  const int a = local / groups, u0 = (local - a * groups) * GV_WAVES;
+  if (a >= b.m) return;  // block-uniform, before the barrier
+  gather_block((const uint16_t *)(jb.w.base + jb.w.off_perm), jb.x + (int64_t)a * jb.ldx, jb.w.k, U,
+               u0, b.xvec != 0, jb.xg + (size_t)a * U * GV_XG_UNIT_BYTES, jb.xs + a, smem);
+}
+
+// Activation fragments of one item, one per column group.  With a single
+// activation row the four lanes of an MFMA block need the same 16 bytes, so
+// each lane holds one dword of them (4 registers per item instead of 16) and
+// the block's lanes exchange them (DPP quad broadcasts) when the item is
+// used.
+template <int M>
+struct GvAct {
+  u4 A[4];
+  template <int CI>
+  __device__ __forceinline__ u4 get() const { return A[CI]; }
+};
+template <>
+struct GvAct<1> {
+  uint32_t q[4];
+  template <int CI>
+  __device__ __forceinline__ u4 get() const {
+    const int v = (int)q[CI];
+    return (u4){(uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x00, 0xF, 0xF, false),
+                (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x55, 0xF, 0xF, false),
+                (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0xAA, 0xF, 0xF, false),
+                (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0xFF, 0xF, 0xF, false)};
+  }
+};
+
+// One work item in registers: the lane's 36 code bytes, its activation
+// fragments and the unit's scales (one per activation row).
+template <int M>
+struct GvItem {
+  ItemCodes c;
+  GvAct<M> act;
+  float sc[M];
+};
+
+// Item f of a block (flat unit index, tile-major from the block's first
+// tile; u = f mod U): codes at codes + f*UNIT_BYTES, activations of unit u.
+template <int M>
+__device__ __forceinline__ GvItem<M> load_gv_item(const uint8_t *codes, const uint8_t *xa,
+                                                  const float *xs, int f, int u, int lane) {
+  GvItem<M> it;
+  it.c = load_item<true>(codes + (size_t)f * UNIT_BYTES, lane);
+  if constexpr (M == 1) {
+#pragma unroll
+    for (int ci = 0; ci < 4; ++ci)
+      it.act.q[ci] = *(const uint32_t *)(xa + (size_t)u * GV_XG_UNIT_BYTES + 256 * ci + 4 * (lane & 3));
+  } else {
+#pragma unroll
+    for (int ci = 0; ci < 4; ++ci) it.act.A[ci] = *(const u4 *)(xa + (size_t)u * GV_XG_UNIT_BYTES + 256 * ci);
+  }
+#pragma unroll
+  for (int a = 0; a < M; ++a) it.sc[a] = xs[4 * u + a];
+  return it;
+}
+
+// Sum over the four lanes of each 16-lane row that share lane & 3 (DPP row
+// rotations); every such lane receives the sum.
+__device__ __forceinline__ float row_sum4(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  return v;
+}
+
+// Direction-row address parts: index bits, log2 of the row stride (16
+// bytes per copy), the lane's copy offset.
+struct DirAddr {
+  uint32_t bd, rs, loff;
+};
+
 // Table reads of the four codes of column group ci: direction rows (signs
-// not yet applied) and radii.
+// not yet applied) from the lane's table copy, and radii.
 template <int CI>
-__device__ __forceinline__ void gemv_group_reads(const ItemCodes &c, u4 (&D)[4], _Float16 (&R)[4]) {
+__device__ __forceinline__ void gemv_group_reads(const ItemCodes &c, const DirAddr &da,
+                                                 uint32_t (&dad)[4], u4 (&D)[4], _Float16 (&R)[4]) {
 #pragma unroll
   for (int ri = 0; ri < 4; ++ri) {
     const int i = 4 * ri + CI;
-    const uint32_t lo16 = byte_shl<CI, 4>(c.L[ri]);  // low index byte * 16
-    const uint32_t lo2 = byte_shl<CI, 1>(c.L[ri]);   // low index byte * 2
+    // direction index * row stride + copy * 16
+    dad[ri] = (__builtin_amdgcn_ubfe(c.L[ri], 8 * CI, da.bd) << da.rs) | da.loff;
+    const uint32_t lo2 = byte_shl<CI, 1>(c.L[ri]);  // low index byte * 2
     const int sh = 9 - 2 * i;
     const uint32_t hs = sh >= 0 ? c.H << sh : c.H >> -sh;
-    const uint32_t idx2 = (hs & 0x600u) | lo2;       // 10-bit index * 2
-    D[ri] = lds_u4(lo16);
+    const uint32_t idx2 = (hs & 0x600u) | lo2;      // 10-bit index * 2
+    D[ri] = lds_u4(GV_OFF_D + dad[ri]);
     R[ri] = lds_f16(GV_OFF_RTAB + idx2);
   }
 }
@@ -211,7 +373,271 @@ __device__ __forceinline__ void gemv_group_mul(uint64_t S01, uint64_t S23, const
 // One work item: the lane's 16 codes, column group by column group, with
 // the table reads of the next group issued before the current one is used.
 template <int M>
-__device__ __forceinline__ void gemv_item(const ItemCodes &c, const uint8_t *xu,
+__device__ __forceinline__ void gemv_item(const GvItem<M> &it, const DirAddr &dmask, uint32_t (&dad0)[4],
+                                          uint32_t (&dad1)[4], float (&tmp)[4][M]) {
+  const ItemCodes &c = it.c;
+  const uint64_t S01 = (uint64_t)c.S[0] | ((uint64_t)c.S[1] << 32);
+  const uint64_t S23 = (uint64_t)c.S[2] | ((uint64_t)c.S[3] << 32);
+  u4 D0[4], D1[4];
+  _Float16 R0[4], R1[4];
+  // phases are kept in this order (scheduling barriers): the reads of group
+  // g + 1 are in flight while group g is decoded and multiplied
+  gemv_group_reads<0>(c, dmask, dad0, D0, R0);
+  gemv_group_reads<1>(c, dmask, dad1, D1, R1);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_group_mul<M, 0>(S01, S23, it.act.template get<0>(), D0, R0, tmp);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_group_reads<2>(c, dmask, dad0, D0, R0);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_group_mul<M, 1>(S01, S23, it.act.template get<1>(), D1, R1, tmp);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_group_reads<3>(c, dmask, dad1, D1, R1);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_group_mul<M, 2>(S01, S23, it.act.template get<2>(), D0, R0, tmp);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_group_mul<M, 3>(S01, S23, it.act.template get<3>(), D1, R1, tmp);
+}
+
+// Main launch, one block: tiles t0 .. t0+Reff-1 of matrix w (U units each),
+// activations gathered at xg / xs (row a of unit u at xg + (a*U + u) * 1 KB).
+template <int M>
+__device__ void gemv_main_block(const MatView &w, const uint8_t *__restrict__ xg,
+                                const float *__restrict__ xs, void *__restrict__ y, int64_t ldy,
+                                int ydt, int t0, int Reff, int red_off, uint8_t *smem) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int U = w.units, F = Reff * U;
+  // the wave's items: flat units f = wv + k*GV_WAVES < F, k < n_items (the
+  // block's waves step through its units side by side, so that at any time
+  // they read neighbouring units)
+  const int n_items = F > wv ? (F - wv + GV_WAVES - 1) / GV_WAVES : 0;
+  const uint8_t *codes = w.base + w.off_codes + (size_t)t0 * U * UNIT_BYTES;
+  // lane 4b + j reads activation row j (row 0 when j >= M) of code column
+  // 16*ci + b of each unit
+  const int jl = lane & 3, bl = lane >> 2;
+  const uint8_t *xa = xg + (size_t)(jl < M ? jl : 0) * U * GV_XG_UNIT_BYTES + 16 * bl;
+
+  // Tables first, and their LDS copies written before any code is
+  // requested: at the start of a launch every block asks for its tables at
+  // once, and behind the code stream of the blocks already running they
+  // would wait for the whole queue.
+  const int bd = w.bd, rows = 1 << bd;
+  const u4 drow = ((const u4 *)(w.base + w.off_dtab))[tid & (rows - 1)];
+  const u2 rrow = ((const u2 *)(w.base + w.off_rtab))[tid];
+  // LDS: radius table, 16 lane-interleaved copies of the direction table
+  // (each thread writes copies of row tid mod 2^bd; the copy index rotates
+  // with the row so that the lanes of one store hit different bank groups),
+  // zeroed partial sums [R][GV_WAVES][4 lane rows][j][ri][M] (tile, wave,
+  // 16-lane row of the wave, then output row 4*ri + j of the tile)
+  float *s_red = (float *)(smem + red_off);
+  for (int o = tid; o < Reff * GV_WAVES * 64 * M; o += 256) s_red[o] = 0.f;
+  ((u2 *)(smem + GV_OFF_RTAB))[tid] = rrow;
+  const int copies = gv_copies(bd);
+  for (int e = tid; e < rows * copies; e += 256) {
+    const int row = e & (rows - 1), cp = ((e >> bd) + row) & (copies - 1);
+    *(u4 *)(smem + GV_OFF_D + (row * copies + cp) * 16) = drow;
+  }
+
+  __syncthreads();  // before the code requests: a wave may stall while issuing them
+
+  // The first GV_PIPE items, all unconditional (clamped indexes) and in the
+  // order of the main loop's refills (scheduling barriers), which keeps its
+  // wait counts exact.
+  GvItem<M> ring[GV_PIPE];
+  int fl = wv, ul = wv % U;  // next item to load and its unit
+#pragma unroll
+  for (int s = 0; s < GV_PIPE; ++s) {
+    const bool in = fl < F;
+    __builtin_amdgcn_sched_barrier(0);
+    ring[s] = load_gv_item<M>(codes, xa, xs, in ? fl : F - 1, in ? ul : U - 1, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    fl += GV_WAVES;
+    for (ul += GV_WAVES; ul >= U; ul -= U) {}
+  }
+
+  DirAddr dmask;
+  dmask.bd = (uint32_t)bd;
+  dmask.rs = copies == 16 ? 8u : 7u;
+  dmask.loff = (uint32_t)(lane & (copies - 1)) << 4;
+  uint32_t dad0[4], dad1[4];  // direction addresses
+  float acc[4][M];
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+    for (int a = 0; a < M; ++a) acc[ri][a] = 0.f;
+
+  auto step = [&](const GvItem<M> &it) __attribute__((always_inline)) {
+    // items are scheduled one at a time: interleaving several items only
+    // raises register pressure
+    __builtin_amdgcn_sched_barrier(0);
+    float tmp[4][M];
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+      for (int a = 0; a < M; ++a) tmp[ri][a] = 0.f;
+    gemv_item<M>(it, dmask, dad0, dad1, tmp);
+#pragma unroll
+    for (int a = 0; a < M; ++a)
+#pragma unroll
+      for (int ri = 0; ri < 4; ++ri) acc[ri][a] = __builtin_fmaf(tmp[ri][a], it.sc[a], acc[ri][a]);
+  };
+  // partial sums of tile tl (block-local): sum over the 4 code columns of
+  // each 16-lane row that share j, then every lane stores its row's sums
+  // (the four lanes of equal j store equal values to one place: no lane
+  // mask, no cross-row traffic; the rows meet in the final sum)
+  auto flush = [&](int tl) __attribute__((always_inline)) {
+    float *dst = s_red + (((tl * GV_WAVES + wv) * 4 + (lane >> 4)) * 4 + (lane & 3)) * 4 * M;
+    float v[4 * M];
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+      for (int a = 0; a < M; ++a) {
+        v[ri * M + a] = row_sum4(acc[ri][a]);
+        acc[ri][a] = 0.f;
+      }
+#pragma unroll
+    for (int q = 0; q < M; ++q) ((u4 *)dst)[q] = (u4){__builtin_bit_cast(uint32_t, v[4 * q]),
+                                                    __builtin_bit_cast(uint32_t, v[4 * q + 1]),
+                                                    __builtin_bit_cast(uint32_t, v[4 * q + 2]),
+                                                    __builtin_bit_cast(uint32_t, v[4 * q + 3])};
+  };
+
+  // Items k = 0 .. n_items-1 (ring slot k % GV_PIPE).  While GV_PIPE more
+  // items follow, each processed slot is refilled at once (unconditional
+  // loads); the last GV_PIPE items have no refills.  The partial sums are
+  // flushed whenever the next item lies in another tile.
+  int k = 0, t = wv / U, u = wv % U;  // tile and unit of item k
+  auto advance = [&]() __attribute__((always_inline)) {
+    const int t_now = t;
+    for (u += GV_WAVES; u >= U; u -= U) ++t;
+    ++k;
+    if (k == n_items || t != t_now) flush(t_now);
+  };
+  while (k + GV_PIPE < n_items) {
+#pragma unroll
+    for (int s = 0; s < GV_PIPE; ++s) {
+      step(ring[s]);
+      ring[s] = load_gv_item<M>(codes, xa, xs, fl, ul, lane);  // fl < F: item k + GV_PIPE exists
+      fl += GV_WAVES;
+      for (ul += GV_WAVES; ul >= U; ul -= U) {}
+      advance();
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < GV_PIPE; ++s) {
+    if (k < n_items) {
+      step(ring[s]);
+      advance();
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < Reff * 16 * M; o += 256) {
+    const int t = o / (16 * M), rem = o - t * 16 * M, row = rem / M, a = rem - row * M;
+    const int ri = row >> 2, j = row & 3;
+    float sum = 0.f;
+#pragma unroll
+    for (int p = 0; p < GV_WAVES * 4; ++p) sum += s_red[((t * GV_WAVES * 4 + p) * 4 + j) * 4 * M + ri * M + a];
+    const int n = (t0 + t) * 16 + row;
+    if (n < w.n) store_out(y, (size_t)a * ldy + n, sum, ydt);
+  }
+}
+
+template <int M>
+__global__ __launch_bounds__(256) void gemv_batched_kernel(GemvBatch b) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int j = find_job(b.starts, b.count);
+  const GemvJob &jb = b.job[j];
+  const int t0 = ((int)blockIdx.x - b.starts.first[j]) * jb.R;
+  const int Reff = min(jb.R, jb.w.n_tiles - t0);
+  gemv_main_block<M>(jb.w, jb.xg, jb.xs, jb.y, jb.ldy, b.ydt, t0, Reff, b.red_off, smem);
+}
+
+// LDS of the main launch: radius table, direction copies of the largest bd,
+// partial sums of R tiles.
+size_t gemv_smem_bytes(int m, int bd_max, int r_max) {
+  return (size_t)GV_OFF_D + ((size_t)gv_copies(bd_max) << bd_max) * 16 +
+         (size_t)r_max * GV_WAVES * 64 * m * 4;
+}
+
+// The exact-path kernels address their LDS tables from 0 (see lds_u4), which
+// holds when they declare no static LDS.
+template <typename Kern>
+static hipError_t check_no_static_lds(Kern k) {
+  hipFuncAttributes attr;
+  hipError_t e = hipFuncGetAttributes(&attr, (const void *)k);
+  if (e != hipSuccess) return e;
+  return attr.sharedSizeBytes == 0 ? hipSuccess : hipErrorInvalidKernelFile;
+}
+
+template <int M>
+static hipError_t launch_gemv_m(GemvBatch &b, int blocks, size_t smem, hipStream_t s) {
+  static const hipError_t lds_ok = check_no_static_lds(gemv_batched_kernel<M>);
+  if (lds_ok != hipSuccess) return lds_ok;
+  hipError_t e = allow_smem(gemv_batched_kernel<M>, smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemv_batched_kernel<M>), dim3(blocks), dim3(256), smem, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_batched(GemvBatch &b, int gather_blocks, int k_max, int blocks, size_t smem,
+                               hipStream_t s) {
+  const size_t gsmem = align256((size_t)k_max * 2);
+  hipError_t e = allow_smem(gemv_gather_kernel, gsmem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemv_gather_kernel, dim3(gather_blocks), dim3(256), gsmem, s, b);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (b.m) {
+    case 1: return launch_gemv_m<1>(b, blocks, smem, s);
+    case 2: return launch_gemv_m<2>(b, blocks, smem, s);
+    case 3: return launch_gemv_m<3>(b, blocks, smem, s);
+    default: return launch_gemv_m<4>(b, blocks, smem, s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact path, m = 1: one fused launch (gather + scale + decode-and-multiply).
+// ---------------------------------------------------------------------------
+//
+// With a single activation row the gather costs less inside the block than
+// as a launch of its own.  A block owns R in {1, 2, 4} consecutive 16-row
+// tiles of one matrix and all of its K; each tile gets 4/R of the block's 4
+// waves, which split its 512-slot units between them.  Prologue: the block
+// stages the activation row in LDS and gathers the permuted slots unit by
+// unit, with the exact per-unit power-of-two scale described above.  Main
+// loop: the same work items and MFMA mapping as the main launch of m = 2..4,
+// with the activations read from LDS and the direction table stored once
+// (4 KB, direction row by the low index byte).
+constexpr int GF_PRE_UNITS = 5;    // permutation vectors prefetched per wave (gather)
+constexpr int GF_STAGE_BATCH = 5;  // 16-byte activation loads per thread per staging pass
+// LDS: direction table, radius table by 10-bit index, unit scales, cross-wave
+// partial sums, then the permuted activations and the staging row.
+constexpr int GF_OFF_RTAB = DTAB_BYTES;
+constexpr int GF_OFF_SCALE = GF_OFF_RTAB + RTAB_BYTES;
+constexpr int GF_OFF_RED = GF_OFF_SCALE + 128 * 4 * 4;  // [U <= 128][M <= 4] scales
+constexpr int GF_SMEM_FIXED = GF_OFF_RED + GV_WAVES * 4 * 4 * 4 * 4;
+
+// Table reads of the four codes of column group ci: direction rows (signs
+// not yet applied) and radii.
+template <int CI>
+__device__ __forceinline__ void gf_group_reads(const ItemCodes &c, u4 (&D)[4], _Float16 (&R)[4]) {
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri) {
+    const int i = 4 * ri + CI;
+    const uint32_t lo16 = byte_shl<CI, 4>(c.L[ri]);  // low index byte * 16
+    const uint32_t lo2 = byte_shl<CI, 1>(c.L[ri]);   // low index byte * 2
+    const int sh = 9 - 2 * i;
+    const uint32_t hs = sh >= 0 ? c.H << sh : c.H >> -sh;
+    const uint32_t idx2 = (hs & 0x600u) | lo2;       // 10-bit index * 2
+    D[ri] = lds_u4(lo16);
+    R[ri] = lds_f16(GF_OFF_RTAB + idx2);
+  }
+}
+
+// One work item: the lane's 16 codes, column group by column group, with
+// the table reads of the next group issued before the current one is used.
+template <int M>
+__device__ __forceinline__ void gf_item(const ItemCodes &c, const uint8_t *xu,
                                           float (&tmp)[4][M]) {
   const uint64_t S01 = (uint64_t)c.S[0] | ((uint64_t)c.S[1] << 32);
   const uint64_t S23 = (uint64_t)c.S[2] | ((uint64_t)c.S[3] << 32);
@@ -220,19 +646,19 @@ __device__ __forceinline__ void gemv_item(const ItemCodes &c, const uint8_t *xu,
   // phases are kept in this order (scheduling barriers): the reads of group
   // g + 1 are in flight while group g is decoded and multiplied
   u4 A0 = *(const u4 *)(xu);
-  gemv_group_reads<0>(c, D0, R0);
+  gf_group_reads<0>(c, D0, R0);
   u4 A1 = *(const u4 *)(xu + 256);
-  gemv_group_reads<1>(c, D1, R1);
+  gf_group_reads<1>(c, D1, R1);
   __builtin_amdgcn_sched_barrier(0);
   gemv_group_mul<M, 0>(S01, S23, A0, D0, R0, tmp);
   __builtin_amdgcn_sched_barrier(0);
   A0 = *(const u4 *)(xu + 512);
-  gemv_group_reads<2>(c, D0, R0);
+  gf_group_reads<2>(c, D0, R0);
   __builtin_amdgcn_sched_barrier(0);
   gemv_group_mul<M, 1>(S01, S23, A1, D1, R1, tmp);
   __builtin_amdgcn_sched_barrier(0);
   A1 = *(const u4 *)(xu + 768);
-  gemv_group_reads<3>(c, D1, R1);
+  gf_group_reads<3>(c, D1, R1);
   __builtin_amdgcn_sched_barrier(0);
   gemv_group_mul<M, 2>(S01, S23, A0, D0, R0, tmp);
   __builtin_amdgcn_sched_barrier(0);
@@ -245,10 +671,10 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
                                  void *__restrict__ y, int64_t ldy, int ydt, int rt0, int R,
                                  int Reff, uint8_t *smem) {
   u4 *s_dtab = (u4 *)smem;
-  _Float16 *s_rtab = (_Float16 *)(smem + GV_OFF_RTAB);
-  float *s_scale = (float *)(smem + GV_OFF_SCALE);        // [U][M] 2^-e per unit
-  float *s_red = (float *)(smem + GV_OFF_RED);            // [W][4][M][4]
-  uint16_t *s_xp = (uint16_t *)(smem + GV_SMEM_FIXED);    // [M][Kp] fp16
+  _Float16 *s_rtab = (_Float16 *)(smem + GF_OFF_RTAB);
+  float *s_scale = (float *)(smem + GF_OFF_SCALE);        // [U][M] 2^-e per unit
+  float *s_red = (float *)(smem + GF_OFF_RED);            // [W][4][M][4]
+  uint16_t *s_xp = (uint16_t *)(smem + GF_SMEM_FIXED);    // [M][Kp] fp16
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int U = w.units, Kp = U * UNIT_SLOTS, K = w.k;
@@ -274,16 +700,16 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   const u4 drow = ((const u4 *)(w.base + w.off_dtab))[tid];
   const u2 rrow = ((const u2 *)(w.base + w.off_rtab))[tid];
   const uint16_t *perm = (const uint16_t *)(w.base + w.off_perm);
-  u4 pvec[GV_PRE_UNITS];
+  u4 pvec[GF_PRE_UNITS];
 #pragma unroll
-  for (int j = 0; j < GV_PRE_UNITS; ++j)
+  for (int j = 0; j < GF_PRE_UNITS; ++j)
     pvec[j] = *(const u4 *)(perm + min(g_lo + j, U - 1) * UNIT_SLOTS + 8 * lane);
-  u4 xv[M][GV_STAGE_BATCH];
+  u4 xv[M][GF_STAGE_BATCH];
   if (XVEC) {
 #pragma unroll
     for (int a = 0; a < M; ++a)
 #pragma unroll
-      for (int b = 0; b < GV_STAGE_BATCH; ++b)
+      for (int b = 0; b < GF_STAGE_BATCH; ++b)
         xv[a][b] = ((const u4 *)(x + (int64_t)a * ldx))[min(tid + 256 * b, n8 - 1)];
   }
   ItemCodes ring[GV_PIPE];
@@ -315,11 +741,11 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
     if (a > 0) __syncthreads();  // previous row's gathers are done
     if (XVEC) {
 #pragma unroll
-      for (int b = 0; b < GV_STAGE_BATCH; ++b) {
+      for (int b = 0; b < GF_STAGE_BATCH; ++b) {
         const int j = tid + 256 * b;
         if (j < n8) ((u4 *)s_stage)[j] = xv[a][b];
       }
-      for (int j = tid + 256 * GV_STAGE_BATCH; j < n8; j += 256) ((u4 *)s_stage)[j] = ((const u4 *)xr)[j];
+      for (int j = tid + 256 * GF_STAGE_BATCH; j < n8; j += 256) ((u4 *)s_stage)[j] = ((const u4 *)xr)[j];
     } else {
       for (int j = tid; j < K; j += 256) s_stage[j] = xr[j];
     }
@@ -330,16 +756,16 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
 #pragma unroll
       for (int s = 0; s < GV_PIPE; ++s) {
         const uint8_t *ub = ul < u_end ? tile + (size_t)ul * UNIT_BYTES : w.base;
-        ring[s] = load_item(ub, lane);
+        ring[s] = load_item<true>(ub, lane);
         ++ul;
       }
     }
     __syncthreads();
-    // The wave's first GV_PRE_UNITS gather units side by side (unrolled, so
+    // The wave's first GF_PRE_UNITS gather units side by side (unrolled, so
     // that their LDS reads and wave reductions overlap), two at a time and
     // the remaining three together when the wave has them; slots past the
     // wave's units read a clamped unit and store nothing.
-    const int npre = min(g_hi - g_lo + 1, GV_PRE_UNITS);  // may be <= 0
+    const int npre = min(g_hi - g_lo + 1, GF_PRE_UNITS);  // may be <= 0
     auto gather_group = [&](auto J0, auto NJ) __attribute__((always_inline)) {
       constexpr int j0 = decltype(J0)::value, nj = decltype(NJ)::value;
       float v[nj][8], mx[nj];
@@ -363,11 +789,11 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
       for (int jj = 0; jj < nj; ++jj)
         if (j0 + jj < npre) gather_store(a, g_lo + j0 + jj, v[jj], mx[jj]);
     };
-    static_assert(GV_PRE_UNITS == 5, "gather groups cover 2 + 3 units");
+    static_assert(GF_PRE_UNITS == 5, "gather groups cover 2 + 3 units");
     if (npre > 0) gather_group(std::integral_constant<int, 0>(), std::integral_constant<int, 2>());
     if (npre > 2) gather_group(std::integral_constant<int, 2>(), std::integral_constant<int, 3>());
-    // units beyond the prefetched ones (k > 4 * GV_PRE_UNITS * 512 only)
-    for (int uu = g_lo + GV_PRE_UNITS; uu <= g_hi; ++uu) {
+    // units beyond the prefetched ones (k > 4 * GF_PRE_UNITS * 512 only)
+    for (int uu = g_lo + GF_PRE_UNITS; uu <= g_hi; ++uu) {
       const int p0 = uu * UNIT_SLOTS + 8 * lane;
       const u4 pv = *(const u4 *)(perm + p0);
       float w8[8];
@@ -404,7 +830,7 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
       for (int a = 0; a < M; ++a) tmp[ri][a] = 0.f;
-    gemv_item<M>(c, xa + (size_t)u * (UNIT_CODES * 16), tmp);
+    gf_item<M>(c, xa + (size_t)u * (UNIT_CODES * 16), tmp);
 #pragma unroll
     for (int a = 0; a < M; ++a) {
       const float sc = s_scale[u * M + a];
@@ -424,7 +850,7 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
       step(ring[s], u);
       ++u;
       const uint8_t *ub = ul < u_end ? tile + (size_t)ul * UNIT_BYTES : w.base;
-      ring[s] = load_item(ub, lane);
+      ring[s] = load_item<true>(ub, lane);
       ++ul;
     }
   }
@@ -465,65 +891,45 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
 // the register budget is relaxed accordingly.
 #define SVQ_GEMV_OCCUPANCY(M) \
   __attribute__((amdgpu_waves_per_eu((M) == 1 ? 3 : ((M) == 2 ? 2 : 1))))
-template <int M, bool XVEC>
-__global__ __launch_bounds__(256) SVQ_GEMV_OCCUPANCY(M) void gemv_batched_kernel(GemvBatch b) {
+// Occupancy: three 256-thread blocks per CU (the tables, activations and
+// staging row of a 2560..9728-wide matrix fit 3x in LDS).
+template <bool XVEC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void gemv_fused_kernel(GemvBatch b) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int j = 0;
-  while (j + 1 < b.count && (int)blockIdx.x >= b.job[j + 1].block_begin) ++j;
+  const int j = find_job(b.starts, b.count);
   const GemvJob &jb = b.job[j];
-  const int rt0 = ((int)blockIdx.x - jb.block_begin) * jb.R;
+  const int rt0 = ((int)blockIdx.x - b.starts.first[j]) * jb.R;
   const int Reff = min(jb.R, jb.w.n_tiles - rt0);
-  gemv_fused_block<M, XVEC>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
+  gemv_fused_block<1, XVEC>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
 }
 
-size_t gemv_smem_bytes(int m, int k_max, int units_max) {
-  return (size_t)GV_SMEM_FIXED + (size_t)m * units_max * UNIT_SLOTS * 2 + (size_t)k_max * 2;
+size_t gemv_fused_smem_bytes(int k_max, int units_max) {
+  return (size_t)GF_SMEM_FIXED + (size_t)units_max * UNIT_SLOTS * 2 + (size_t)k_max * 2;
 }
 
-// The exact-path kernels address their LDS tables from 0 (see lds_u4), which
-// holds when they declare no static LDS.
-template <typename Kern>
-static hipError_t check_no_static_lds(Kern k) {
-  hipFuncAttributes attr;
-  hipError_t e = hipFuncGetAttributes(&attr, (const void *)k);
-  if (e != hipSuccess) return e;
-  return attr.sharedSizeBytes == 0 ? hipSuccess : hipErrorInvalidKernelFile;
-}
-
-template <int M, bool XVEC>
-static hipError_t launch_gemv_m(GemvBatch &b, int blocks, size_t smem, hipStream_t s) {
-  static const hipError_t lds_ok = check_no_static_lds(gemv_batched_kernel<M, XVEC>);
+template <bool XVEC>
+static hipError_t launch_fused_x(GemvBatch &b, int blocks, size_t smem, hipStream_t s) {
+  static const hipError_t lds_ok = check_no_static_lds(gemv_fused_kernel<XVEC>);
   if (lds_ok != hipSuccess) return lds_ok;
-  hipError_t e = allow_smem(gemv_batched_kernel<M, XVEC>, smem);
+  hipError_t e = allow_smem(gemv_fused_kernel<XVEC>, smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemv_batched_kernel<M, XVEC>), dim3(blocks), dim3(256), smem, s, b);
+  hipLaunchKernelGGL((gemv_fused_kernel<XVEC>), dim3(blocks), dim3(256), smem, s, b);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_batched(GemvBatch &b, int blocks, size_t smem, bool xvec, hipStream_t s) {
-  switch (b.m) {
-    case 1: return xvec ? launch_gemv_m<1, true>(b, blocks, smem, s) : launch_gemv_m<1, false>(b, blocks, smem, s);
-    case 2: return xvec ? launch_gemv_m<2, true>(b, blocks, smem, s) : launch_gemv_m<2, false>(b, blocks, smem, s);
-    case 3: return xvec ? launch_gemv_m<3, true>(b, blocks, smem, s) : launch_gemv_m<3, false>(b, blocks, smem, s);
-    default: return xvec ? launch_gemv_m<4, true>(b, blocks, smem, s) : launch_gemv_m<4, false>(b, blocks, smem, s);
-  }
+hipError_t launch_gemv_fused(GemvBatch &b, int blocks, size_t smem, hipStream_t s) {
+  return b.xvec ? launch_fused_x<true>(b, blocks, smem, s) : launch_fused_x<false>(b, blocks, smem, s);
 }
-
-// ---------------------------------------------------------------------------
-// bf16 path
-// ---------------------------------------------------------------------------
-
 
 // ---------------------------------------------------------------------------
 // Mixture of experts (grouped form; routing is not on the pages and follows
 // the usual top-k slot convention: slot q = t*topk + j)
 // ---------------------------------------------------------------------------
 
-
 // Per-slot fused GEMV (one activation row per slot): block (row tile, slot),
 // matrix = the slot's expert.
 template <bool XVEC>
-__global__ __launch_bounds__(256) SVQ_GEMV_OCCUPANCY(1) void moe_gemv_kernel(MoeShape sh, ExpertTable tab,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_gemv_kernel(MoeShape sh, ExpertTable tab,
                                                        const int32_t *__restrict__ ids,
                                                        const uint16_t *__restrict__ x, int64_t ldx,
                                                        int x_per_slot, int topk,
@@ -627,7 +1033,7 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
 
 // ---------------------------------------------------------------------------
 // MoE launcher.  Workspace layout depends on the path:
-//   exact (m*topk <= MOE_EXACT_MAX_SLOTS): xw[S][Kp] fp16, escale[S]
+//   exact (m*topk <= MOE_EXACT_MAX_SLOTS): none (the fused per-slot launch)
 //   bf16: counts[E], offsets[E+1], sorted[S], work[3*max_work], nwork,
 //         xb[S + 16*BMT][Kp] bf16
 // ---------------------------------------------------------------------------
@@ -659,7 +1065,7 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   if (S <= MOE_EXACT_MAX_SLOTS) {
     *need = 256;
     if (!ws) return hipSuccess;
-    const size_t smem = gemv_smem_bytes(1, sh.k, sh.units);
+    const size_t smem = gemv_fused_smem_bytes(sh.k, sh.units);
     const bool xvec = ((((uintptr_t)x) | ((uintptr_t)ldx * 2)) & 15) == 0;
     static const hipError_t lds_ok_t = check_no_static_lds(moe_gemv_kernel<true>);
     static const hipError_t lds_ok_f = check_no_static_lds(moe_gemv_kernel<false>);
@@ -668,7 +1074,7 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
     if (e != hipSuccess) return e;
     // row tiles per block: as in the dense planner, enough units per wave
     // to amortise the gather, while the launch keeps >= 256 blocks
-    int R = sh.units <= GV_ITEMS_PER_WAVE ? 4 : (sh.units <= 2 * GV_ITEMS_PER_WAVE ? 2 : 1);
+    int R = sh.units <= GF_ITEMS_PER_WAVE ? 4 : (sh.units <= 2 * GF_ITEMS_PER_WAVE ? 2 : 1);
     while (R > 1 && ((sh.n_tiles + R - 1) / R) * S < 256) R /= 2;
     const dim3 grid((sh.n_tiles + R - 1) / R, S);
     if (xvec)

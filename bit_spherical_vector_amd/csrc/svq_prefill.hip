@@ -373,8 +373,7 @@ template <int BM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BM == 256 ? 1 : 2, BM == 256 ? 1 : 2)))
 void prefill_batched_kernel(PrefillBatch b) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int jn = 0;
-  while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].block_begin) ++jn;
+  const int jn = find_job(b.gemm_starts, b.count);
   const PrefillJob &J = b.job[jn];
   const int local = (int)blockIdx.x - J.block_begin;
   if (local >= J.tiles_n * J.tiles_m * J.splits) return;  // padding block (uniform, before any barrier)
@@ -408,8 +407,7 @@ void prefill_batched_kernel(PrefillBatch b) {
 // Sum of the K-split partial tiles of every split job, in split order:
 // y[row][n] = sum_s part[s][row][n], four columns per thread.
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillBatch b) {
-  int jn = 0;
-  while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].red_begin) ++jn;
+  const int jn = find_job(b.red_starts, b.count);
   const PrefillJob &J = b.job[jn];
   if (J.splits <= 1) return;
   const int per_row = (J.w.n + 1023) / 1024;  // blocks per output row
@@ -518,8 +516,7 @@ __device__ __forceinline__ void dq_gather_rows(const uint16_t *const *src, int r
 template <bool XVEC>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int rpb) {
   extern __shared__ __attribute__((aligned(16))) uint16_t s_rows[];
-  int jn = 0;
-  while (jn + 1 < b.count && (int)blockIdx.x >= b.job[jn + 1].prep_begin) ++jn;
+  const int jn = find_job(b.prep_starts, b.count);
   const PrefillJob &J = b.job[jn];
   const MatView &w = J.w;
   const int K = w.k, Kp = w.units * UNIT_SLOTS;

@@ -158,11 +158,24 @@ def _dequant_gemm_need(shapes, m, cus=256):
     return need
 
 
+def _exact_need(shapes, m):
+    """Workspace of the m <= 4 path: none for the fused m = 1 launch (256
+    bytes reported); for m = 2..4, per matrix, the gathered fp16 activations
+    (1 KB per unit and row) and the units' scales (16 bytes per unit)."""
+    if m == 1:
+        return 256
+    a = lambda v: (v + 255) // 256 * 256
+    units = [-(-k // 512) for _, k in shapes]
+    return sum(a(m * u * 1024) + a(u * 16) for u in units)
+
+
 def test_linear_workspace_query_and_validation():
     h = _fake_handle(512, 1024, 8)
     dq = lambda m: _dequant_gemm_need([(512, 1024)], m)
     assert dq(5) == 64 * 2048 + 2 * 64 * 512 * 4  # two K splits of one unit each
-    for m, expect in [(1, 256), (4, 256), (5, dq(5)), (64, dq(64)), (65, dq(65)), (300, dq(300))]:
+    assert _exact_need([(512, 1024)], 2) == 4096 + 256
+    for m, expect in [(1, _exact_need([(512, 1024)], 1)), (4, _exact_need([(512, 1024)], 4)),
+                      (5, dq(5)), (64, dq(64)), (65, dq(65)), (300, dq(300))]:
         st, need = svq.svq_linear(h, None, m, 1024, None, 512, svq.SVQ_BF16, None, 0, 0)
         assert st == svq.SVQ_OK and need == expect, (m, need)
     # bad arguments
@@ -209,7 +222,7 @@ def test_linear_batched_query_and_validation():
     hs = (svq.Handle * 3)(_fake_handle(512, 1024, 8), _fake_handle(64, 2560, 6),
                           _fake_handle(300, 768, 7))
     st, need = svq.svq_linear_batched(hs, 3, None, None, 1, None, None, 0, None, 0, 0)
-    assert st == svq.SVQ_OK and need == 256
+    assert st == svq.SVQ_OK and need == _exact_need([(512, 1024), (64, 2560), (300, 768)], 1)
     st, need = svq.svq_linear_batched(hs, 3, None, None, 16, None, None, 0, None, 0, 0)
     a = lambda v: (v + 255) // 256 * 256
     assert st == svq.SVQ_OK and need == _dequant_gemm_need([(512, 1024), (64, 2560), (300, 768)], 16)

@@ -123,6 +123,9 @@ EDGE = [
     (17, 520, 6, 64),
     (15, 2048, 8, 65),
     (64, 4096, 6, 1),
+    # m = 1 with a row too long for the fused launch's LDS: the two-launch path
+    (20, 53248, 8, 1),
+    (20, 53248, 7, 3),
 ]
 
 
