@@ -38,12 +38,12 @@ COLD_BYTES = 600 << 20  # > 2 x 256 MB MALL
 # by what the same counter reads for a plain 256 MiB device copy in the same
 # run (--copy-calibration): FETCH_SIZE reads half of the bytes a copy moves
 # (factor 2.0), WRITE_SIZE all of them (factor 1.0).  Commands and raw
-# figures: profiles/gemv_batched_kernel_layer4b_m1_counters.md.  An entry
+# figures: profiles/gemv_fused_kernel_layer4b_m1_counters.md.  An entry
 # only holds for the kernel source it was taken on (sha256 prefix below);
 # after any change of that source the traffic is reported as null.
 TRAFFIC = {
-    "layer4b_m1": {"kernel_src_sha256": "9b021ec005d631f3",
-                   "fetch_kib": 14587.9, "fetch_factor": 2.0,
+    "layer4b_m1": {"kernel_src_sha256": "55c2aebf31243e86",
+                   "fetch_kib": 14579.9, "fetch_factor": 2.0,
                    "write_kib": 60.0, "write_factor": 1.0},
 }
 
