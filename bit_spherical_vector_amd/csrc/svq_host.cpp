@@ -376,7 +376,12 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
   const bool exact = m <= EXACT_MAX_M;
   // m = 1: the fused launch, when the activation row and its permuted copy
   // fit in LDS beside the tables
-  const bool fused = m == 1 && gemv_fused_smem_bytes(k_max, u_max) <= GV_LDS_LIMIT;
+  size_t fused_smem = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const size_t b = gemv_fused_smem_bytes(w[j].k, w[j].units, w[j].bd);
+    fused_smem = b > fused_smem ? b : fused_smem;
+  }
+  const bool fused = m == 1 && fused_smem <= GV_LDS_LIMIT;
   size_t need = 0;
   int m_pad = 0;
   int splits[GV_MAX_JOBS], ups[GV_MAX_JOBS];
@@ -429,7 +434,7 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
       if ((((uintptr_t)xs[j]) | ((uintptr_t)ldx[j] * 2)) & 15) b.xvec = 0;
     if (fused) {
       const int blocks = plan_fused(b);
-      e = launch_gemv_fused(b, blocks, gemv_fused_smem_bytes(k_max, u_max), s);
+      e = launch_gemv_fused(b, blocks, fused_smem, s);
       return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
     }
     int gather_blocks = 0;

@@ -114,7 +114,7 @@ constexpr int GV_UNITS_PER_WAVE = 4;  // units per wave the planner aims for
 // m = 1: one fused launch (gather in the block); R in {1, 2, 4} row tiles
 // per block, each wave near GF_ITEMS_PER_WAVE units.
 constexpr int GF_ITEMS_PER_WAVE = 5;
-size_t gemv_fused_smem_bytes(int k_max, int units_max);
+size_t gemv_fused_smem_bytes(int k, int units, int bd);  // one matrix
 hipError_t launch_gemv_fused(GemvBatch &b, int blocks, size_t smem, hipStream_t s);
 
 // Dequant-GEMM path (m > EXACT_MAX_M; "prefill" for m >= PREFILL_MIN_M, with

@@ -116,6 +116,25 @@ __device__ __forceinline__ uint32_t byte_shl(uint32_t v) {
   return r;
 }
 
+// Byte 1 of dst := (byte k of v) & mask, the other bytes of dst kept (SDWA
+// destination select with preserve): one VALU op turns a code's low index
+// byte into the address of its direction row in the lane's table copy.
+template <int K>
+__device__ __forceinline__ void byte_and_to_b1(uint32_t &dst, uint32_t mask, uint32_t v) {
+  if (K == 0)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_0"
+        : "+v"(dst) : "v"(mask), "v"(v));
+  else if (K == 1)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_1"
+        : "+v"(dst) : "v"(mask), "v"(v));
+  else if (K == 2)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_2"
+        : "+v"(dst) : "v"(mask), "v"(v));
+  else
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_3"
+        : "+v"(dst) : "v"(mask), "v"(v));
+}
+
 // 64-bit left shift by a constant in one VALU op (the compiler otherwise
 // splits it into a shift and a funnel shift).
 template <int SH>
@@ -610,35 +629,63 @@ hipError_t launch_gemv_batched(GemvBatch &b, int gather_blocks, int k_max, int b
 // (4 KB, direction row by the low index byte).
 constexpr int GF_PRE_UNITS = 5;    // permutation vectors prefetched per wave (gather)
 constexpr int GF_STAGE_BATCH = 5;  // 16-byte activation loads per thread per staging pass
-// LDS: direction table, radius table by 10-bit index, unit scales, cross-wave
-// partial sums, then the permuted activations and the staging row.
-constexpr int GF_OFF_RTAB = DTAB_BYTES;
-constexpr int GF_OFF_SCALE = GF_OFF_RTAB + RTAB_BYTES;
-constexpr int GF_OFF_RED = GF_OFF_SCALE + 128 * 4 * 4;  // [U <= 128][M <= 4] scales
-constexpr int GF_SMEM_FIXED = GF_OFF_RED + GV_WAVES * 4 * 4 * 4 * 4;
+// Two table modes, chosen per block by the matrix's bd:
+// * mode 0 (bd <= 7): 16 lane-interleaved copies of the 2^bd direction rows
+//   (copy c of row d at d*256 + 16c, lane l reads copy l & 15: the 16 lanes
+//   of a ds_read_b128 pass hit 16 different bank groups), radii from the
+//   1024-entry table by 10-bit index;
+// * mode 1 (bd = 8): the 256 direction rows once (16 copies would take
+//   64 KB), and the four radii from two registers by v_perm_b32 (the radius
+//   index is then the code's two high index bits), which saves the radius
+//   read from LDS.
+// LDS: radius table [0, 2 KB), direction rows from 2 KB (GF_OFF_D), then at
+// per-block offsets: unit scales, cross-wave partial sums, the permuted
+// activations and the staging row.
+constexpr int GF_OFF_RTAB = 0;
+constexpr int GF_OFF_D = RTAB_BYTES;
+__host__ __device__ constexpr int gf_dir_bytes(int bd) { return bd >= 8 ? DTAB_BYTES : (16 << bd) * 16; }
+__host__ __device__ constexpr int gf_scale_off(int bd) { return GF_OFF_D + gf_dir_bytes(bd); }
+__host__ __device__ constexpr int gf_xp_off(int bd, int units, int m) {
+  return gf_scale_off(bd) + ((units * m * 4 + 15) & ~15) + GV_WAVES * 4 * 4 * 4 * m;
+}
 
 // Table reads of the four codes of column group ci: direction rows (signs
 // not yet applied) and radii.
-template <int CI>
-__device__ __forceinline__ void gf_group_reads(const ItemCodes &c, u4 (&D)[4], _Float16 (&R)[4]) {
+// Radii of mode 1: fp16 R0..R3 as {rhi:rlo} bytes 0..7.
+struct GfRad {
+  uint32_t lo, hi, dmask;
+};
+
+template <int CI, int MODE>
+__device__ __forceinline__ void gf_group_reads(const ItemCodes &c, const GfRad &rd, uint32_t (&dad)[4],
+                                               u4 (&D)[4], _Float16 (&R)[4]) {
 #pragma unroll
   for (int ri = 0; ri < 4; ++ri) {
     const int i = 4 * ri + CI;
-    const uint32_t lo16 = byte_shl<CI, 4>(c.L[ri]);  // low index byte * 16
-    const uint32_t lo2 = byte_shl<CI, 1>(c.L[ri]);   // low index byte * 2
-    const int sh = 9 - 2 * i;
-    const uint32_t hs = sh >= 0 ? c.H << sh : c.H >> -sh;
-    const uint32_t idx2 = (hs & 0x600u) | lo2;       // 10-bit index * 2
-    D[ri] = lds_u4(lo16);
-    R[ri] = lds_f16(GF_OFF_RTAB + idx2);
+    if constexpr (MODE == 0) {
+      byte_and_to_b1<CI>(dad[ri], rd.dmask, c.L[ri]);  // direction * 256 + copy * 16
+      const uint32_t lo2 = byte_shl<CI, 1>(c.L[ri]);    // low index byte * 2
+      const int sh = 9 - 2 * i;
+      const uint32_t hs = sh >= 0 ? c.H << sh : c.H >> -sh;
+      const uint32_t idx2 = (hs & 0x600u) | lo2;        // 10-bit index * 2
+      D[ri] = lds_u4(GF_OFF_D + dad[ri]);
+      R[ri] = lds_f16(GF_OFF_RTAB + idx2);
+    } else {
+      const uint32_t lo16 = byte_shl<CI, 4>(c.L[ri]);   // direction * 16
+      D[ri] = lds_u4(GF_OFF_D + lo16);
+      // radius index = index bits 8..9; bytes 2r, 2r+1 of {hi:lo}, zeros above
+      const uint32_t r = __builtin_amdgcn_ubfe(c.H, 2 * i, 2);
+      const uint32_t sel = r * 0x0202u + 0x0C0C0100u;
+      R[ri] = __builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_perm(rd.hi, rd.lo, sel));
+    }
   }
 }
 
 // One work item: the lane's 16 codes, column group by column group, with
 // the table reads of the next group issued before the current one is used.
-template <int M>
-__device__ __forceinline__ void gf_item(const ItemCodes &c, const uint8_t *xu,
-                                          float (&tmp)[4][M]) {
+template <int M, int MODE>
+__device__ __forceinline__ void gf_item(const ItemCodes &c, const uint8_t *xu, const GfRad &rd,
+                                        uint32_t (&dad0)[4], uint32_t (&dad1)[4], float (&tmp)[4][M]) {
   const uint64_t S01 = (uint64_t)c.S[0] | ((uint64_t)c.S[1] << 32);
   const uint64_t S23 = (uint64_t)c.S[2] | ((uint64_t)c.S[3] << 32);
   u4 D0[4], D1[4];
@@ -646,19 +693,19 @@ __device__ __forceinline__ void gf_item(const ItemCodes &c, const uint8_t *xu,
   // phases are kept in this order (scheduling barriers): the reads of group
   // g + 1 are in flight while group g is decoded and multiplied
   u4 A0 = *(const u4 *)(xu);
-  gf_group_reads<0>(c, D0, R0);
+  gf_group_reads<0, MODE>(c, rd, dad0, D0, R0);
   u4 A1 = *(const u4 *)(xu + 256);
-  gf_group_reads<1>(c, D1, R1);
+  gf_group_reads<1, MODE>(c, rd, dad1, D1, R1);
   __builtin_amdgcn_sched_barrier(0);
   gemv_group_mul<M, 0>(S01, S23, A0, D0, R0, tmp);
   __builtin_amdgcn_sched_barrier(0);
   A0 = *(const u4 *)(xu + 512);
-  gf_group_reads<2>(c, D0, R0);
+  gf_group_reads<2, MODE>(c, rd, dad0, D0, R0);
   __builtin_amdgcn_sched_barrier(0);
   gemv_group_mul<M, 1>(S01, S23, A1, D1, R1, tmp);
   __builtin_amdgcn_sched_barrier(0);
   A1 = *(const u4 *)(xu + 768);
-  gf_group_reads<3>(c, D1, R1);
+  gf_group_reads<3, MODE>(c, rd, dad1, D1, R1);
   __builtin_amdgcn_sched_barrier(0);
   gemv_group_mul<M, 2>(S01, S23, A0, D0, R0, tmp);
   __builtin_amdgcn_sched_barrier(0);
@@ -666,18 +713,19 @@ __device__ __forceinline__ void gf_item(const ItemCodes &c, const uint8_t *xu,
 }
 
 // XVEC: every activation row starts 16-byte aligned (vector staging loads).
-template <int M, bool XVEC>
+// MODE: table mode (see above), 1 for bd = 8.
+template <int M, bool XVEC, int MODE>
 __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ x, int64_t ldx,
                                  void *__restrict__ y, int64_t ldy, int ydt, int rt0, int R,
                                  int Reff, uint8_t *smem) {
-  u4 *s_dtab = (u4 *)smem;
-  _Float16 *s_rtab = (_Float16 *)(smem + GF_OFF_RTAB);
-  float *s_scale = (float *)(smem + GF_OFF_SCALE);        // [U][M] 2^-e per unit
-  float *s_red = (float *)(smem + GF_OFF_RED);            // [W][4][M][4]
-  uint16_t *s_xp = (uint16_t *)(smem + GF_SMEM_FIXED);    // [M][Kp] fp16
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int U = w.units, Kp = U * UNIT_SLOTS, K = w.k;
+  const int bd = w.bd, rows = 1 << bd;
+  _Float16 *s_rtab = (_Float16 *)(smem + GF_OFF_RTAB);
+  float *s_scale = (float *)(smem + gf_scale_off(bd));    // [U][M] 2^-e per unit
+  float *s_red = s_scale + ((U * M + 3) & ~3);            // [W][4][M][4]
+  uint16_t *s_xp = (uint16_t *)(smem + gf_xp_off(bd, U, M));  // [M][Kp] fp16
   uint16_t *s_stage = s_xp + (size_t)M * Kp;              // [K] bf16
   const int n8 = K / 8;
 
@@ -697,7 +745,7 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   // that the wait counts stay exact, in the order they are needed: tables,
   // permutation vectors of the wave's gather units and the first staging
   // pass of every activation row; the codes follow once row 0 is staged.
-  const u4 drow = ((const u4 *)(w.base + w.off_dtab))[tid];
+  const u4 drow = ((const u4 *)(w.base + w.off_dtab))[tid & (rows - 1)];
   const u2 rrow = ((const u2 *)(w.base + w.off_rtab))[tid];
   const uint16_t *perm = (const uint16_t *)(w.base + w.off_perm);
   u4 pvec[GF_PRE_UNITS];
@@ -714,8 +762,17 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   }
   ItemCodes ring[GV_PIPE];
   int ul = u_begin;  // next unit to load
-  s_dtab[tid] = drow;
-  ((u2 *)s_rtab)[tid] = rrow;
+  if constexpr (MODE == 0) {
+    // 16 copies of each row; the copy index rotates with the row so that the
+    // lanes of one store hit different bank groups
+    for (int e = tid; e < rows * 16; e += 256) {
+      const int row = e & (rows - 1), cp = ((e >> bd) + row) & 15;
+      *(u4 *)(smem + GF_OFF_D + (row * 16 + cp) * 16) = drow;
+    }
+    ((u2 *)s_rtab)[tid] = rrow;
+  } else {
+    *(u4 *)(smem + GF_OFF_D + tid * 16) = drow;
+  }
 
   // fp16 copy of gathered unit uu of activation row a with its exact
   // power-of-two scale: 2^e with max|x_unit| * 2^e in [2^14, 2^15), i.e.
@@ -820,6 +877,19 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
     for (int a = 0; a < M; ++a) acc[ri][a] = 0.f;
+  GfRad rd;
+  rd.dmask = (uint32_t)(rows - 1);
+  if constexpr (MODE == 1) {
+    // R[r] sits at 10-bit index r << 8 of the radius table
+    const uint16_t *rt = (const uint16_t *)(w.base + w.off_rtab);
+    rd.lo = (uint32_t)rt[0] | ((uint32_t)rt[256] << 16);
+    rd.hi = (uint32_t)rt[512] | ((uint32_t)rt[768] << 16);
+  } else {
+    rd.lo = rd.hi = 0;
+  }
+  uint32_t dad0[4], dad1[4];  // mode 0: byte 0 = the lane's copy * 16
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri) dad0[ri] = dad1[ri] = (uint32_t)(lane & 15) << 4;
 
   auto step = [&](const ItemCodes &c, int u) __attribute__((always_inline)) {
     // items are scheduled one at a time: interleaving several items only
@@ -830,7 +900,7 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
       for (int a = 0; a < M; ++a) tmp[ri][a] = 0.f;
-    gf_item<M>(c, xa + (size_t)u * (UNIT_CODES * 16), tmp);
+    gf_item<M, MODE>(c, xa + (size_t)u * (UNIT_CODES * 16), rd, dad0, dad1, tmp);
 #pragma unroll
     for (int a = 0; a < M; ++a) {
       const float sc = s_scale[u * M + a];
@@ -900,11 +970,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
   const GemvJob &jb = b.job[j];
   const int rt0 = ((int)blockIdx.x - b.starts.first[j]) * jb.R;
   const int Reff = min(jb.R, jb.w.n_tiles - rt0);
-  gemv_fused_block<1, XVEC>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
+  if (jb.w.bd >= 8)
+    gemv_fused_block<1, XVEC, 1>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
+  else
+    gemv_fused_block<1, XVEC, 0>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
 }
 
-size_t gemv_fused_smem_bytes(int k_max, int units_max) {
-  return (size_t)GF_SMEM_FIXED + (size_t)units_max * UNIT_SLOTS * 2 + (size_t)k_max * 2;
+// LDS of one fused block at m = 1 for a matrix of k channels, `units` units.
+size_t gemv_fused_smem_bytes(int k, int units, int bd) {
+  return (size_t)gf_xp_off(bd, units, 1) + (size_t)units * UNIT_SLOTS * 2 + (size_t)k * 2;
 }
 
 template <bool XVEC>
@@ -941,8 +1015,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   const int src = x_per_slot ? q : q / topk;
   const int rt0 = blockIdx.x * R;
   char *yq = (char *)y + (size_t)q * ldy * (ydt == 0 ? 2 : 4);
-  gemv_fused_block<1, XVEC>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, min(R, w.n_tiles - rt0),
-                            smem);
+  if (w.bd >= 8)
+    gemv_fused_block<1, XVEC, 1>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, min(R, w.n_tiles - rt0),
+                                 smem);
+  else
+    gemv_fused_block<1, XVEC, 0>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, min(R, w.n_tiles - rt0),
+                                 smem);
 }
 
 // Routing for the grouped GEMM: counting sort of slots by expert and a list
@@ -1065,7 +1143,11 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   if (S <= MOE_EXACT_MAX_SLOTS) {
     *need = 256;
     if (!ws) return hipSuccess;
-    const size_t smem = gemv_fused_smem_bytes(sh.k, sh.units);
+    size_t smem = 0;
+    for (int e = 0; e < E; ++e) {
+      const size_t b = gemv_fused_smem_bytes(sh.k, sh.units, experts[e].bd);
+      smem = b > smem ? b : smem;
+    }
     const bool xvec = ((((uintptr_t)x) | ((uintptr_t)ldx * 2)) & 15) == 0;
     static const hipError_t lds_ok_t = check_no_static_lds(moe_gemv_kernel<true>);
     static const hipError_t lds_ok_f = check_no_static_lds(moe_gemv_kernel<false>);
