@@ -625,8 +625,8 @@ hipError_t launch_gemv_batched(GemvBatch &b, int gather_blocks, int k_max, int b
 // stages the activation row in LDS and gathers the permuted slots unit by
 // unit, with the exact per-unit power-of-two scale described above.  Main
 // loop: the same work items and MFMA mapping as the main launch of m = 2..4,
-// with the activations read from LDS and the direction table stored once
-// (4 KB, direction row by the low index byte).
+// with the activations read from LDS and the tables in one of the two modes
+// below.
 constexpr int GF_PRE_UNITS = 5;    // permutation vectors prefetched per wave (gather)
 constexpr int GF_STAGE_BATCH = 5;  // 16-byte activation loads per thread per staging pass
 // Two table modes, chosen per block by the matrix's bd:
