@@ -325,8 +325,9 @@ def main():
 
     flops = sum(2.0 * m * mat.n * mat.k for mat in mats)
     # m = 1: one fused exact-path launch; m = 2..4: gather + exact-path GEMV;
-    # else prep + GEMM, plus the K-split reduce below 256 rows
-    launches = (1 if m == 1 else 2) if m <= 4 else (2 if m >= 256 else 3)
+    # m = 5..16: prep + small-batch GEMM; else prep + GEMM, plus the K-split
+    # reduce below 256 rows
+    launches = (1 if m == 1 else 2) if m <= 4 else (2 if m <= 16 or m >= 256 else 3)
     # roofline.achieved: algorithmic work of one step over the mean step
     # duration of the timed region.  For m = 1 a step is exactly one launch
     # of the dominant kernel; otherwise a step also holds the small

@@ -24,6 +24,7 @@ SOURCES = [
     ("csrc/svq_host.cpp", []),
     ("csrc/svq_kernels.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("csrc/svq_prefill.hip", []),
+    ("csrc/svq_small.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
 ]
 # kept for callers that list the flags of the exact-path kernels
 HIPCC_FLAGS = COMMON_FLAGS + ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]

@@ -374,6 +374,13 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
     u_max = w[j].units > u_max ? w[j].units : u_max;
   }
   const bool exact = m <= EXACT_MAX_M;
+  const bool small = !exact && m <= SB_MAX_M;
+  int sb_items = 0;
+  if (small) {
+    int64_t total = 0;
+    for (int32_t j = 0; j < count; ++j) total += (int64_t)w[j].n_tiles * w[j].units;
+    sb_items = sb_block_items(total, device_cus());
+  }
   // m = 1: the fused launch, when the activation row and its permuted copy
   // fit in LDS beside the tables
   size_t fused_smem = 0;
@@ -389,6 +396,8 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
     need = 256;  // unused: the fused launch gathers in LDS
   } else if (exact) {
     for (int32_t j = 0; j < count; ++j) need += gemv_ws_bytes((int)m, w[j].units);
+  } else if (small) {
+    for (int32_t j = 0; j < count; ++j) need += sb_ws_bytes(w[j].n_tiles, w[j].units, sb_items);
   } else {
     m_pad = prefill_m_pad((int)m);
     need = plan_splits(w, count, m_pad, prefill_bm((int)m), splits, ups);
@@ -444,6 +453,55 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
     const size_t smem = gemv_smem_bytes((int)m, bd_max, r_max);
     b.red_off = (int32_t)gemv_smem_bytes((int)m, bd_max, 0);
     e = launch_gemv_batched(b, gather_blocks, k_max, blocks, smem, s);
+  } else if (small) {
+    // fragment-ordered activations (one prep launch), then one launch over
+    // every (tile group, K range) of every matrix
+    SbBatch b;
+    std::memset(&b, 0, sizeof(b));
+    b.count = count;
+    b.m = (int)m;
+    b.ydt = (int)ydt;
+    uint8_t *ws = (uint8_t *)workspace;
+    int blocks = 0, prep_blocks = 0;
+    for (int32_t j = 0; j < count; ++j) {
+      SbJob &J = b.job[j];
+      J.w = view_of(&w[j]);
+      J.x = (const uint16_t *)xs[j];
+      J.ldx = ldx[j];
+      J.y = ys[j];
+      J.ldy = ldy[j];
+      const SbPlan pl = sb_plan(J.w.n_tiles, J.w.units, sb_items);
+      J.tiles = pl.tiles;
+      J.upr = pl.upr;
+      J.groups = pl.groups;
+      J.splits = pl.splits;
+      J.xa = ws;
+      uint8_t *p = ws + align256((size_t)J.w.units * SB_XA_UNIT_BYTES);
+      if (J.splits > 1) {
+        J.part = (float *)p;
+        p += align256((size_t)J.groups * J.tiles * J.splits * 1024);
+        J.cnt = (int32_t *)p;
+      }
+      ws += sb_ws_bytes(J.w.n_tiles, J.w.units, sb_items);
+    }
+    // matrices cut into K ranges first: the tail of their blocks (partial
+    // tiles, arrival counts) then overlaps the other matrices' blocks
+    for (int i = 1; i < b.count; ++i)
+      for (int j = i; j > 0 && b.job[j].splits > b.job[j - 1].splits; --j) {
+        const SbJob t = b.job[j];
+        b.job[j] = b.job[j - 1];
+        b.job[j - 1] = t;
+      }
+    for (int32_t j = 0; j < count; ++j) {
+      SbJob &J = b.job[j];
+      J.block_begin = blocks;
+      blocks += J.groups * J.splits;
+      J.prep_begin = prep_blocks;
+      prep_blocks += 4 * J.w.units;
+      b.starts.first[j] = J.block_begin;
+      b.prep_starts.first[j] = J.prep_begin;
+    }
+    e = launch_sb(b, prep_blocks, blocks, s);
   } else {
     // permuted activations of every matrix in fragment order (one prep
     // launch), then one GEMM launch over all of them, longest k first

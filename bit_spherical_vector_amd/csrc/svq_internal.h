@@ -117,6 +117,56 @@ constexpr int GF_ITEMS_PER_WAVE = 5;
 size_t gemv_fused_smem_bytes(int k, int units, int bd);  // one matrix
 hipError_t launch_gemv_fused(GemvBatch &b, int blocks, size_t smem, hipStream_t s);
 
+// Small-batch dequant path (EXACT_MAX_M < m <= SB_MAX_M): a prep launch
+// writes every matrix's permuted activations as 16-row MFMA fragments (xa:
+// unit u at xa + u * SB_XA_UNIT_BYTES), then one launch decodes each code
+// straight into a 16x16x32 bf16 MFMA operand.  Work item = one coded unit of
+// one row tile.  A block of SB_WAVES waves owns `tiles` consecutive row
+// tiles and one K range of `upr` units (block lb of a job: group
+// lb / splits, range lb % splits); its tiles x units items, unit-major, are
+// cut into SB_WAVES contiguous runs, one per wave.  Matrices of more than
+// SB_MAX_RANGE units are cut into `splits` K ranges whose fp32 partial
+// tiles (part: [groups * tiles][splits][256]) are summed by the last block
+// of the group to arrive (cnt: one arrival counter per group, cleared by the
+// prep launch).
+constexpr int SB_MAX_M = 16;
+constexpr int SB_WAVES = 4;
+constexpr int SB_TMAX = 6;       // row tiles per block, at most
+constexpr int SB_NMAX = 8;       // items per wave, at most
+constexpr int SB_ITEMS_MIN = 16; // items per block, at least (when the matrix allows)
+constexpr int SB_MAX_RANGE = 8;  // units a block covers without a K split
+constexpr int SB_XA_UNIT_BYTES = 16 * UNIT_SLOTS * 2;
+struct SbJob {
+  MatView w;
+  const uint16_t *x;    // activations, bf16 [m][ldx]
+  int64_t ldx;
+  uint8_t *xa;          // fragment-ordered activations (workspace)
+  float *part;          // splits > 1: partial tiles (workspace)
+  int32_t *cnt;         // splits > 1: arrival counters (workspace)
+  void *y;
+  int64_t ldy;
+  int32_t tiles, upr;   // row tiles per block, units per K range
+  int32_t groups, splits;
+  int32_t block_begin;  // first main block of this job
+  int32_t prep_begin;   // first prep block (4 per unit)
+};
+struct SbBatch {
+  JobStarts starts, prep_starts;
+  SbJob job[GV_MAX_JOBS];
+  int32_t count, m, ydt;
+};
+// Block shape of one matrix: tiles per block, units per range, ranges,
+// tile groups.  `items` = work items per block the call aims for
+// (sb_block_items over all matrices of the call).
+struct SbPlan {
+  int tiles, upr, splits, groups;
+};
+int sb_block_items(int64_t total_items, int cus);
+SbPlan sb_plan(int n_tiles, int units, int items);
+// Workspace of one matrix on the small-batch path.
+size_t sb_ws_bytes(int n_tiles, int units, int items);
+hipError_t launch_sb(SbBatch &b, int prep_blocks, int blocks, hipStream_t s);
+
 // Dequant-GEMM path (m > EXACT_MAX_M; "prefill" for m >= PREFILL_MIN_M, with
 // 64-row block tiles below that): a prep launch writes the permuted
 // activations of every matrix of the call ("jobs") in MFMA fragment order

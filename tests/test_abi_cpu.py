@@ -158,6 +158,45 @@ def _dequant_gemm_need(shapes, m, cus=256):
     return need
 
 
+def _small_items(shapes, cus=256):
+    """Items (row tile x unit) per block on the 4 < m <= 16 path: every block
+    resident at once at two blocks per compute unit, between 16 and 32."""
+    cdiv = lambda p, q: -(-p // q)
+    total = sum(cdiv(n, 16) * cdiv(k, 512) for n, k in shapes)
+    return max(16, min(32, cdiv(total, 2 * cus)))
+
+
+def _small_plan(n_tiles, units, items):
+    """Block shape of the 4 < m <= 16 path: up to 8 units in one K range,
+    else ranges of about 5 units; then as many row tiles per block (1..6) as
+    give about `items` items, at most 32."""
+    splits = 1 if units <= 8 else (units + 4) // 5
+    upr = -(-units // splits)
+    splits = -(-units // upr)
+    tiles = max(1, min(6, (items + upr // 2) // upr))
+    while tiles > 1 and tiles * upr > 32:
+        tiles -= 1
+    return tiles, upr, splits, -(-n_tiles // tiles)
+
+
+def _small_need(shapes):
+    """Workspace of the 4 < m <= 16 path, per matrix: the fragment-ordered
+    activations (16 rows x 512 slots bf16 = 16 KB per unit); with K ranges,
+    fp32 partial tiles for every (tile of the groups, range) and one
+    arrival counter per group."""
+    a = lambda v: (v + 255) // 256 * 256
+    cdiv = lambda p, q: -(-p // q)
+    items = _small_items(shapes)
+    need = 0
+    for n, k in shapes:
+        units = cdiv(k, 512)
+        tiles, _, splits, groups = _small_plan(cdiv(n, 16), units, items)
+        need += a(units * 16384)
+        if splits > 1:
+            need += a(groups * tiles * splits * 1024) + a(groups * 4)
+    return need
+
+
 def _exact_need(shapes, m):
     """Workspace of the m <= 4 path: none for the fused m = 1 launch (256
     bytes reported); for m = 2..4, per matrix, the gathered fp16 activations
@@ -172,10 +211,22 @@ def _exact_need(shapes, m):
 def test_linear_workspace_query_and_validation():
     h = _fake_handle(512, 1024, 8)
     dq = lambda m: _dequant_gemm_need([(512, 1024)], m)
-    assert dq(5) == 64 * 2048 + 2 * 64 * 512 * 4  # two K splits of one unit each
+    assert dq(17) == 64 * 2048 + 2 * 64 * 512 * 4  # two K splits of one unit each
     assert _exact_need([(512, 1024)], 2) == 4096 + 256
+    assert _small_need([(512, 1024)]) == 2 * 16384
+    assert _small_need([(100, 2560)]) == 5 * 16384
+    assert _small_plan(160, 19, 16) == (3, 5, 4, 54)
+    assert _small_need([(2560, 9728)]) == 19 * 16384 + 54 * 3 * 4 * 1024 + 256
+    layer = [(4096, 2560), (1024, 2560), (1024, 2560), (2560, 4096), (9728, 2560), (9728, 2560),
+             (2560, 9728)]
+    assert _small_items(layer) == 25
+    big = _fake_handle(2560, 9728, 7)  # 19 units: K ranges
+    for m in (5, 16):
+        st, need = svq.svq_linear(big, None, m, 9728, None, 2560, svq.SVQ_BF16, None, 0, 0)
+        assert st == svq.SVQ_OK and need == _small_need([(2560, 9728)]), (m, need)
     for m, expect in [(1, _exact_need([(512, 1024)], 1)), (4, _exact_need([(512, 1024)], 4)),
-                      (5, dq(5)), (64, dq(64)), (65, dq(65)), (300, dq(300))]:
+                      (5, _small_need([(512, 1024)])), (16, _small_need([(512, 1024)])),
+                      (17, dq(17)), (64, dq(64)), (65, dq(65)), (300, dq(300))]:
         st, need = svq.svq_linear(h, None, m, 1024, None, 512, svq.SVQ_BF16, None, 0, 0)
         assert st == svq.SVQ_OK and need == expect, (m, need)
     # bad arguments
@@ -224,8 +275,15 @@ def test_linear_batched_query_and_validation():
     st, need = svq.svq_linear_batched(hs, 3, None, None, 1, None, None, 0, None, 0, 0)
     assert st == svq.SVQ_OK and need == _exact_need([(512, 1024), (64, 2560), (300, 768)], 1)
     st, need = svq.svq_linear_batched(hs, 3, None, None, 16, None, None, 0, None, 0, 0)
-    a = lambda v: (v + 255) // 256 * 256
-    assert st == svq.SVQ_OK and need == _dequant_gemm_need([(512, 1024), (64, 2560), (300, 768)], 16)
+    assert st == svq.SVQ_OK and need == _small_need([(512, 1024), (64, 2560), (300, 768)])
+    # the whole 4B-class layer: the long-k matrix is cut into K ranges
+    layer = [(4096, 2560), (1024, 2560), (1024, 2560), (2560, 4096), (9728, 2560), (9728, 2560),
+             (2560, 9728)]
+    hl = (svq.Handle * 7)(*[_fake_handle(n, k, 7) for n, k in layer])
+    st, need = svq.svq_linear_batched(hl, 7, None, None, 16, None, None, 0, None, 0, 0)
+    assert st == svq.SVQ_OK and need == _small_need(layer)
+    st, need = svq.svq_linear_batched(hs, 3, None, None, 40, None, None, 0, None, 0, 0)
+    assert st == svq.SVQ_OK and need == _dequant_gemm_need([(512, 1024), (64, 2560), (300, 768)], 40)
     assert svq.svq_linear_batched(hs, 0, None, None, 1, None, None, 0, None, 0, 0)[0] == \
         svq.SVQ_ERR_INVALID_ARG
     assert svq.svq_linear_batched(hs, 9, None, None, 1, None, None, 0, None, 0, 0)[0] == \

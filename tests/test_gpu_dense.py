@@ -138,6 +138,32 @@ def test_edge_shapes(svq, n, k, bd, m):
     _one_hot_check(svq, pm, W, cols, 4 if m <= 4 else 16)
 
 
+SMALL_EDGE = [
+    # n, k, bd, m on the 4 < m <= 16 path: 1..19 units (more than 8: K
+    # ranges, the last one shorter), blocks of 1..4 row tiles with a partial
+    # last group, ragged rows and slots
+    (16, 512, 8, 5),
+    (40, 1000, 6, 16),
+    (70, 1536, 7, 12),
+    (64, 2048, 8, 8),
+    (100, 2560, 6, 16),
+    (260, 3000, 6, 16),
+    (33, 3584, 8, 13),
+    (130, 4600, 7, 9),
+    (50, 5600, 6, 16),
+    (70, 9728, 8, 7),
+]
+
+
+@pytest.mark.parametrize("n,k,bd,m", SMALL_EDGE)
+def test_small_batch_path_edges(svq, n, k, bd, m):
+    mat = synth.random_matrix(n, k, bd, seed=(38, n, k))
+    x = synth.random_activations(m, k, seed=(38, m, k))
+    pm, W = _check_outputs(svq, mat, x, f"small edge n={n} k={k} bd={bd} m={m}")
+    cols = sorted(set([0, k - 1] + list(range(0, k, max(1, k // 30)))))
+    _one_hot_check(svq, pm, W, cols, 16)
+
+
 PREFILL_EDGE = [
     # n, k, bd, m: ragged row tiles, a partial last unit, m not a multiple of 256
     (200, 1032, 8, 300),
@@ -188,7 +214,7 @@ def test_unaligned_activations(svq, m):
 
 def test_deterministic(svq):
     mat = synth.random_matrix(256, 2560, 8, seed=(32, 0, 0))
-    for m in (1, 4, 33):
+    for m in (1, 4, 16, 33):
         x = synth.random_activations(m, 2560, seed=(32, m, 0))
         pm = svq.pack(mat)
         a = _run(svq, pm, x, torch.float32)
