@@ -11,18 +11,19 @@
 // Two decode-and-multiply schemes share the coded-unit layout described in
 // svq_internal.h:
 //
-// * Exact (m <= 4).  The 8 signed fp16 direction values of a code are an
-//   MFMA B operand as they come out of LDS (sign flips are exact), the
-//   activations (fp16 after an exact power-of-two scale) sit in a
-//   block-diagonal A operand, so v_mfma_f32_16x16x32_f16 returns, in the very
-//   lane that decoded the code, the code's 8-term dot product per activation
-//   row.  The radius multiply is then applied per code in fp32 (fp16 radius
-//   x fp32 dot, fused multiply-add), so the decoded weight R*D is never
-//   rounded.
-// * bf16 (m > 4).  A code decodes to 8 bf16 weights RNE_bf16(R*D) with its
-//   signs from a 1024-row table (one row per direction/radius index), which
-//   is the B operand of v_mfma_f32_16x16x32_bf16; activations are the
-//   A operand.
+// * Exact (m <= 4, this file).  The 8 signed fp16 direction values of a
+//   code are MFMA B operands as they come out of LDS (sign flips are exact),
+//   4 values each for two chained v_mfma_f32_4x4x4_16b_f16; the activations
+//   (fp16 after an exact power-of-two scale) are the A operands, so the MFMA
+//   returns, in the very lane that decoded the code, the code's 8-term dot
+//   product per activation row.  The radius multiply is then applied per
+//   code in fp32 (fp16 radius x fp32 dot, fused multiply-add), so the
+//   decoded weight R*D is never rounded.
+// * bf16 (m > 4, svq_small.hip and svq_prefill.hip).  A code decodes to 8
+//   bf16 weights RNE_bf16(R*D) with its signs from a 1024-row table (one row
+//   per direction/radius index): straight into a v_mfma_f32_16x16x32_bf16
+//   operand up to m = 16, through an LDS weight tile for
+//   v_mfma_f32_32x32x16_bf16 above.
 #include <type_traits>
 
 #include "svq_device.h"
