@@ -546,14 +546,22 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
         b.job[j] = b.job[j - 1];
         b.job[j - 1] = t;
       }
-    const int rpb = prefill_prep_rows(k_max);
     // jobs start on multiples of 8 GEMM blocks (the XCD count) so that a
     // job's blocks with one m-tile share an XCD; the padding blocks exit at
     // once
     int blocks = 0, prep_blocks = 0, red_blocks = 0;
-    // prep: row groups of rpb rows; with few of them, each job's chunks are
-    // also cut into ranges (at least 64 chunks each) for about 512 blocks
-    const int row_groups = count * (m_pad / rpb);
+    // prep: row groups of prep_rpb rows (fewer rows for long k); with few
+    // groups, each job's chunks are also cut into ranges (at least 64 chunks
+    // each) for about 512 blocks
+    size_t prep_lds = 0;
+    int row_groups = 0;
+    for (int j = 0; j < b.count; ++j) {
+      const int rpb = prefill_prep_rows(b.job[j].w.k);
+      b.job[j].prep_rpb = rpb;
+      row_groups += m_pad / rpb;
+      const size_t l = prefill_prep_lds(rpb, b.job[j].w.k);
+      prep_lds = l > prep_lds ? l : prep_lds;
+    }
     const int want = (512 + row_groups - 1) / row_groups;
     for (int j = 0; j < b.count; ++j) {
       const int nch = b.job[j].w.units * UNIT_SLOTS / 8;
@@ -565,14 +573,14 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
       b.job[j].block_begin = blocks;
       blocks += (b.job[j].tiles_n * b.job[j].tiles_m * b.job[j].splits + 7) / 8 * 8;
       b.job[j].prep_begin = prep_blocks;
-      prep_blocks += (m_pad / rpb) * b.job[j].prep_csplit;
+      prep_blocks += (m_pad / b.job[j].prep_rpb) * b.job[j].prep_csplit;
       b.job[j].red_begin = red_blocks;
       if (b.job[j].splits > 1) red_blocks += (int)m * ((b.job[j].w.n + 1023) / 1024);
       b.gemm_starts.first[j] = b.job[j].block_begin;
       b.prep_starts.first[j] = b.job[j].prep_begin;
       b.red_starts.first[j] = b.job[j].red_begin;
     }
-    e = launch_prefill_prep(b, prep_blocks, rpb, k_max, xvec, s);
+    e = launch_prefill_prep(b, prep_blocks, prep_lds, xvec, s);
     if (e == hipSuccess) e = launch_prefill_batched(b, prefill_bm((int)m), blocks, s);
     if (e == hipSuccess && any_split) e = launch_prefill_reduce(b, red_blocks, s);
   }

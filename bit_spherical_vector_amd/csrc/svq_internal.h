@@ -186,6 +186,7 @@ struct PrefillJob {
   int32_t block_begin;  // first GEMM block of this job
   int32_t prep_begin;   // first prep block of this job
   int32_t prep_csplit;  // prep blocks per row group (chunk ranges)
+  int32_t prep_rpb;     // activation rows per prep block (prefill_prep_rows(k))
   // K split (small m): GEMM block (mt, nt, sp) covers units
   // [sp * units_per_split, ...); with splits > 1 each writes an fp32 partial
   // tile to part[sp][m_pad][n_pad] and the reduce launch sums them into y
@@ -203,9 +204,10 @@ struct PrefillBatch {
 int prefill_bm(int m);      // activation rows per block tile: 256 (m >= PREFILL_MIN_M) or 64
 int prefill_m_pad(int m);   // m rounded up to prefill_bm(m)
 int prefill_tiles_n(int n_tiles);
-int prefill_prep_rows(int k_max);  // activation rows per prep block
+int prefill_prep_rows(int k);  // activation rows per prep block for rows of k values
+size_t prefill_prep_lds(int rpb, int k);  // LDS of such a block
 // xvec: every activation row of every job starts 16-byte aligned.
-hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, int rpb, int k_max, bool xvec,
+hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, size_t lds, bool xvec,
                                hipStream_t s);
 hipError_t launch_prefill_batched(PrefillBatch &b, int bm, int blocks, hipStream_t s);
 hipError_t launch_prefill_reduce(PrefillBatch &b, int blocks, hipStream_t s);

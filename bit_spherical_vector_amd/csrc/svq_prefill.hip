@@ -11,18 +11,19 @@
 // K in steps of P_BK = 64 permuted slots (8 codes per weight row).  The
 // decoded weight tile of each step, RNE_bf16(R*D) with the signs applied,
 // goes through LDS (two stages: the next step's decode overlaps the current
-// step's MFMAs, one barrier per step).  The activations never touch LDS: a
-// prep launch writes the permuted activations in MFMA fragment order (see
-// xb_frag_offset), so each wave loads its A fragments straight into
-// registers with fully coalesced 1 KB loads, one step ahead.  BM = 256:
-// four waves in a 2 x 2 grid, each 128 x 128 (16 accumulators of
-// v_mfma_f32_32x32x16_bf16 in accumulation registers; this translation unit
-// is built without the VGPR-form MFMA option of the exact-path kernels).
-// BM = 64 (fewer activation rows): four 64 x 64 waves side by side, two
-// blocks per CU, and K splits summed by a reduce launch when the output
-// tiles alone give few blocks.  B fragments of the next 16-wide k substep
-// are read while the current one's MFMAs run.  The same tile serves the
-// grouped MoE product (moe_dq_kernel).
+// step's MFMAs, one barrier per step).  A prep launch writes the permuted
+// activations in MFMA fragment order (see xb_frag_offset).  Two tiles:
+// * BM = 256 (m >= PREFILL_MIN_M, dq_tile_w8): 8 waves in a 2 x 4 grid,
+//   each 128 x 64, two waves per SIMD; the activation fragments of a step
+//   are copied into LDS by direct-to-LDS loads, one step ahead;
+// * BM = 64 (dq_tile<64>, fewer rows, and the grouped MoE product in
+//   moe_dq_kernel): four 64 x 64 waves side by side, two blocks per CU, A
+//   fragments loaded straight into registers with coalesced 1 KB loads one
+//   step ahead, B fragments of the next 16-wide k substep read while the
+//   current one's MFMAs run; K splits summed by a reduce launch when the
+//   output tiles alone give few blocks.
+// Accumulators of v_mfma_f32_32x32x16_bf16 (this translation unit is built
+// without the VGPR-form MFMA option of the exact-path kernels).
 //
 // 32x32x16 operands: lane L holds row L & 31 of a 32-row fragment and
 // k = 8(L >> 5)..+7; accumulator element e of lane L is row
@@ -365,6 +366,260 @@ __device__ __forceinline__ void dq_tile(const DqTile &T, uint8_t *smem) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 output tile with 8 waves (two per SIMD), both operands in LDS.
+// ---------------------------------------------------------------------------
+//
+// With one wave per SIMD a wave has no partner to cover its LDS reads and
+// the step barrier, so the matrix cores idle.  Here a block of 8 waves
+// (2 x 4 grid, wave tile 128 activation rows x 64 weight rows, 8
+// accumulators of v_mfma_f32_32x32x16_bf16) computes the same 256 x 256
+// tile; per 64-slot K-step both operands sit in LDS in MFMA fragment order,
+// double-buffered:
+// * A (activations): the step's 32 fragments of 1 KB (8 row blocks x 4
+//   k substeps) are copied from the fragment-ordered activations by
+//   direct-to-LDS loads (wave w copies row block w), one step ahead;
+// * B (decoded weights): thread tau decodes, one step ahead, the four codes
+//   (rows 4ri + j of row tile tau >> 5) of one lane record of the step and
+//   stores each as the 16 bytes that lane L = 16(rt & 1) + 4ri + j +
+//   32(b' & 1) of fragment (rt >> 1, b' >> 1) reads (b' = code column in
+//   the step).  Slot L of a fragment is kept at L ^ 4h, h = ((L >> 5) & 1) |
+//   ((ks & 1) << 1): the 16 lanes of a write pass then hit 16 bank groups,
+//   and a read pass (16 lanes, one h) still does.
+constexpr int W8_THREADS = 512;
+constexpr int W8_STAGE = 32 * 1024;  // one operand of one step
+// B first: every fragment read then fits a base register plus the 16-bit
+// instruction offset
+constexpr int W8_OFF_B = 0;
+constexpr int W8_OFF_A = 2 * W8_STAGE;
+constexpr int W8_OFF_BTAB = 4 * W8_STAGE;
+constexpr int W8_SMEM = W8_OFF_BTAB + BTAB_BYTES;  // 144 KB
+static_assert(W8_SMEM <= 160 * 1024, "8-wave tile LDS exceeds a workgroup's 160 KB");
+
+typedef __attribute__((address_space(3))) void w8_lds_t;
+
+// Physical 16-byte slot of fragment lane L in k substep ks.
+__device__ __forceinline__ uint32_t w8_slot(uint32_t L, uint32_t ks) {
+  const uint32_t h = ((L >> 5) & 1u) | ((ks & 1u) << 1);
+  return L ^ (h << 2);
+}
+
+// Table rows of the four codes (rows 4ri + j) of column group CI of one
+// lane record, then the signed rows into the B stage at byte offsets
+// boff[ri].
+template <int CI>
+__device__ __forceinline__ void w8_decode(const ItemCodes &c, const uint8_t *s_btab, u4 (&v)[4]) {
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri) {
+    const int i = 4 * ri + CI;
+    const uint32_t idx = ((c.L[ri] >> (8 * CI)) & 0xFFu) | (((c.H >> (2 * i)) & 3u) << 8);
+    v[ri] = *(const u4 *)(s_btab + 16 * idx);
+  }
+}
+template <int CI>
+__device__ __forceinline__ void w8_store(const ItemCodes &c, uint8_t *bst, const uint32_t (&boff)[4],
+                                         u4 (&v)[4]) {
+  const uint32_t SM = 0x80008000u;
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t cr;
+      switch (ri) {
+        case 0: cr = carrier<CI>(c.S[q]); break;
+        case 1: cr = carrier<4 + CI>(c.S[q]); break;
+        case 2: cr = carrier<8 + CI>(c.S[q]); break;
+        default: cr = carrier<12 + CI>(c.S[q]); break;
+      }
+      v[ri][q] ^= cr & SM;
+    }
+    *(u4 *)(bst + boff[ri]) = v[ri];
+  }
+}
+
+__device__ void dq_tile_w8(const DqTile &T, uint8_t *smem) {
+  constexpr int NI = 4, NJ = 2, TM = 128, TN = 64;
+  const MatView &w = T.w;
+  const int nt = T.nt, u0 = T.u0, u1 = T.u1, m0 = T.m0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 2, wn = wv & 3;
+  const int U = w.units, S = U * (UNIT_SLOTS / P_BK);
+  const int rt0 = nt * (P_BN / UNIT_ROWS);
+
+  uint8_t *s_btab = smem + W8_OFF_BTAB;
+  for (int q = tid; q < 1024; q += W8_THREADS) ((u4 *)s_btab)[q] = ((const u4 *)(w.base + w.off_btab))[q];
+
+  // A: wave wv copies row block wv of each step (4 KB: substeps 0..3)
+  const uint16_t *a_src = T.xb + ((size_t)((m0 >> 5) + wv) * S * 4 * 64 + lane) * 8;
+  auto load_a = [&](int s, int stage) {
+    w8_lds_t *dst = (w8_lds_t *)(smem + W8_OFF_A + stage * W8_STAGE + wv * 4096);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      __builtin_amdgcn_global_load_lds(a_src + ((size_t)s * 4 + ks) * 512, (w8_lds_t *)((uint8_t __attribute__((address_space(3))) *)dst + ks * 1024), 16, 0, 0);
+  };
+
+  // decode: row tile rt = tid >> 5 of the block (clamped to the matrix; rows
+  // past n are decoded from the last tile and never stored), code column
+  // bq of the step, record lane j
+  const int rt = tid >> 5, bq = (tid & 31) >> 2, jr = tid & 3;
+  const int rtg = min(rt0 + rt, w.n_tiles - 1);
+  const uint8_t *codes = w.base + w.off_codes + (size_t)rtg * U * UNIT_BYTES;
+  const int recA = 4 * bq + jr, recB = recA + 32;  // b = bq (even steps), 8 + bq (odd steps)
+  uint32_t boff[4];
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri) {
+    const uint32_t L = 16 * (rt & 1) + 4 * ri + jr + 32 * (bq & 1), ks = bq >> 1;
+    boff[ri] = (((rt >> 1) * 4 + ks) * 64 + w8_slot(L, ks)) * 16;
+  }
+
+  f16x C[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) C[i][jj] = (f16x){};
+
+  const size_t cu0 = (size_t)u0 * UNIT_BYTES;
+  ItemCodes rA = load_item(codes + cu0, recA), rB = load_item(codes + cu0, recB);
+  load_a(u0 * 8, 0);
+  __syncthreads();  // btab
+  {
+    u4 v[4];
+    w8_decode<0>(rA, s_btab, v);
+    w8_store<0>(rA, smem + W8_OFF_B, boff, v);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // fragment addresses of the wave (stage 0): A row blocks 4wm + i, B column
+  // blocks 2wn + jj; substep ks adds ks KB, stage adds W8_STAGE
+  const uint32_t a_frag = W8_OFF_A + (4 * wm) * 4096 + 16 * lane;
+  uint32_t b_frag[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) b_frag[ks] = W8_OFF_B + (2 * wn) * 4096 + ks * 1024 + 16 * w8_slot(lane, ks);
+
+  for (int u = u0; u < u1; ++u) {
+    const size_t nu = (size_t)min(u + 1, u1 - 1) * UNIT_BYTES;
+    ItemCodes nA, nB;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t == 6) nA = load_item(codes + nu, recA);
+      if (t == 7) nB = load_item(codes + nu, recB);
+      const int st = t & 1;  // stage of this step (a unit has 8 steps)
+      const int sn = min(u * 8 + t + 1, 8 * u1 - 1);
+      // the next step's activations (clamped on the last step: a harmless
+      // reload into the stage no wave reads any more)
+      load_a(sn, st ^ 1);
+      u4 v[4];
+      // the next step's table rows
+      switch (t) {
+        case 0: w8_decode<0>(rB, s_btab, v); break;
+        case 1: w8_decode<1>(rA, s_btab, v); break;
+        case 2: w8_decode<1>(rB, s_btab, v); break;
+        case 3: w8_decode<2>(rA, s_btab, v); break;
+        case 4: w8_decode<2>(rB, s_btab, v); break;
+        case 5: w8_decode<3>(rA, s_btab, v); break;
+        case 6: w8_decode<3>(rB, s_btab, v); break;
+        default: w8_decode<0>(nA, s_btab, v); break;
+      }
+      const uint8_t *cur = smem + st * W8_STAGE;
+      u4 af[2][NI], bf[2][NJ];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) af[0][i] = *(const u4 *)(cur + a_frag + i * 4096);
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) bf[0][jj] = *(const u4 *)(cur + b_frag[0] + jj * 4096);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c = ks & 1;
+        if (ks + 1 < 4) {
+#pragma unroll
+          for (int i = 0; i < NI; ++i) af[c ^ 1][i] = *(const u4 *)(cur + a_frag + i * 4096 + (ks + 1) * 1024);
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj) bf[c ^ 1][jj] = *(const u4 *)(cur + b_frag[ks + 1] + jj * 4096);
+        }
+        if (ks == 2) {
+          uint8_t *nst = smem + W8_OFF_B + (st ^ 1) * W8_STAGE;
+          switch (t) {
+            case 0: w8_store<0>(rB, nst, boff, v); break;
+            case 1: w8_store<1>(rA, nst, boff, v); break;
+            case 2: w8_store<1>(rB, nst, boff, v); break;
+            case 3: w8_store<2>(rA, nst, boff, v); break;
+            case 4: w8_store<2>(rB, nst, boff, v); break;
+            case 5: w8_store<3>(rA, nst, boff, v); break;
+            case 6: w8_store<3>(rB, nst, boff, v); break;
+            default: w8_store<0>(nA, nst, boff, v); break;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+            C[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8, af[c][i]),
+                                                               __builtin_bit_cast(b8, bf[c][jj]),
+                                                               C[i][jj], 0, 0, 0);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    rA = nA;
+    rB = nB;
+  }
+
+  // Epilogue through LDS (the operand stages are free now): each wave turns
+  // its TM x TN accumulator tile into output-type rows in a private 16 KB
+  // region, as many 32-row blocks per pass as fit, and writes them back as
+  // whole 16-byte pieces of consecutive output columns.
+  {
+    uint8_t *s_c = smem + wv * 16384;
+    void *const ybase = T.y;
+    const int64_t yld = T.ldy;
+    const int nlim = T.nlim;
+    const bool yv = T.yvec;
+    const bool bf16o = T.bf;
+    const int esz = bf16o ? 2 : 4;
+    const int ipp = min(NI, 16384 / (32 * TN * esz));  // 32-row blocks per pass
+    const int cpr = TN * esz / 16;                      // 16-byte pieces per row
+    const int per = 16 / esz;                           // columns per piece
+#pragma unroll
+    for (int i0 = 0; i0 < NI; ++i0) {
+      if (i0 % ipp != 0) continue;
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) {
+        if (ii >= ipp || i0 + ii >= NI) continue;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = 32 * ii + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5), cc = 32 * jj + (lane & 31);
+            const float val = C[i0 + ii][jj][e];
+            if (bf16o) ((uint16_t *)s_c)[r * TN + cc] = f32_to_bf16_bits(val);
+            else ((float *)s_c)[r * TN + cc] = val;
+          }
+      }
+      __syncthreads();
+      for (int q = lane; q < 32 * ipp * cpr; q += 64) {
+        const int r = q / cpr, ch = q % cpr;
+        const int rr = TM * wm + 32 * i0 + r;  // row of the tile
+        const int n0 = rt0 * UNIT_ROWS + TN * wn + ch * per;
+        if (rr >= T.m_valid) continue;
+        const int orow = T.ymap ? T.ymap[rr] : m0 + rr;
+        const u4 vv = *(const u4 *)(s_c + r * TN * esz + ch * 16);
+        char *dst = (char *)ybase + ((size_t)orow * yld + n0) * esz;
+        if (yv && n0 + per <= nlim) {
+          *(u4 *)dst = vv;
+        } else {
+          for (int l = 0; l < per; ++l) {
+            if (n0 + l >= nlim) break;
+            if (bf16o) ((uint16_t *)dst)[l] = (uint16_t)(vv[l >> 1] >> (16 * (l & 1)));
+            else ((uint32_t *)dst)[l] = vv[l];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // Dense calls: block (mt, nt, sp) of job J (m-tile fastest, so that the
 // blocks sharing one activation tile fall on one XCD: blocks are dealt to
 // the 8 XCDs round-robin and jobs start on multiples of 8).  With K splits
@@ -402,6 +657,42 @@ void prefill_batched_kernel(PrefillBatch b) {
     T.yvec = b.yvec != 0;
   }
   dq_tile<BM>(T, smem);
+}
+
+// The same blocks as prefill_batched_kernel<256>, computed by the 8-wave
+// tile.
+__global__ __launch_bounds__(W8_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_w8_kernel(PrefillBatch b) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int jn = find_job(b.gemm_starts, b.count);
+  const PrefillJob &J = b.job[jn];
+  const int local = (int)blockIdx.x - J.block_begin;
+  if (local >= J.tiles_n * J.tiles_m * J.splits) return;  // padding block (uniform, before any barrier)
+  const int mt = local % J.tiles_m, nt = (local / J.tiles_m) % J.tiles_n;
+  const int sp = local / (J.tiles_m * J.tiles_n);
+  DqTile T;
+  T.w = J.w;
+  T.xb = J.xb;
+  T.m0 = mt * 256;
+  T.m_valid = J.m - T.m0;
+  T.nt = nt;
+  T.u0 = sp * J.units_per_split;
+  T.u1 = min(J.w.units, T.u0 + J.units_per_split);
+  T.ymap = nullptr;
+  if (J.splits > 1) {
+    T.y = J.part + (size_t)sp * J.m_pad * J.n_pad;
+    T.ldy = J.n_pad;
+    T.nlim = J.n_pad;
+    T.bf = false;
+    T.yvec = true;
+  } else {
+    T.y = J.y;
+    T.ldy = J.ldy;
+    T.nlim = J.w.n;
+    T.bf = b.ydt == 0;
+    T.yvec = b.yvec != 0;
+  }
+  dq_tile_w8(T, smem);
 }
 
 // Sum of the K-split partial tiles of every split job, in split order:
@@ -514,13 +805,14 @@ __device__ __forceinline__ void dq_gather_rows(const uint16_t *const *src, int r
 // prep_csplit ranges of 8-slot chunks (several when the rows alone give few
 // blocks).
 template <bool XVEC>
-__global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int rpb) {
+__global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b) {
   extern __shared__ __attribute__((aligned(16))) uint16_t s_rows[];
   const int jn = find_job(b.prep_starts, b.count);
   const PrefillJob &J = b.job[jn];
   const MatView &w = J.w;
   const int K = w.k, Kp = w.units * UNIT_SLOTS;
   const int lb = (int)blockIdx.x - J.prep_begin;
+  const int rpb = J.prep_rpb;
   const int r0 = (lb / J.prep_csplit) * rpb, cs = lb % J.prep_csplit;
   const int nch = Kp / 8, cpb = (nch + J.prep_csplit - 1) / J.prep_csplit;
   const uint16_t *src[8];
@@ -531,24 +823,27 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b, int r
 }
 
 // LDS of a prep block: rpb staged rows of k + 8 values.
-static size_t prep_lds(int rpb, int k_max) { return (size_t)rpb * (k_max + 8) * 2; }
+static size_t prep_lds(int rpb, int k) { return (size_t)rpb * (k + 8) * 2; }
+size_t prefill_prep_lds(int rpb, int k) { return prep_lds(rpb, k); }
 
-int prefill_prep_rows(int k_max) {
+// Up to 8 rows, fewer for long rows: a block's staging stays near 40 KB, so
+// that several prep blocks share a compute unit (with whole 156 KB of rows
+// per block, one block per unit waits out each row load alone).
+constexpr size_t PREP_LDS_TARGET = 40 * 1024;
+int prefill_prep_rows(int k) {
   int rpb = 8;
-  while (rpb > 1 && prep_lds(rpb, k_max) > GV_LDS_LIMIT) rpb /= 2;
+  while (rpb > 1 && prep_lds(rpb, k) > PREP_LDS_TARGET) rpb /= 2;
   return rpb;
 }
 
-hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, int rpb, int k_max, bool xvec,
-                               hipStream_t s) {
-  const size_t lds = prep_lds(rpb, k_max);
+hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, size_t lds, bool xvec, hipStream_t s) {
   if (lds > GV_LDS_LIMIT) return hipErrorInvalidValue;
   hipError_t e = xvec ? allow_smem(prefill_prep_kernel<true>, lds) : allow_smem(prefill_prep_kernel<false>, lds);
   if (e != hipSuccess) return e;
   if (xvec)
-    hipLaunchKernelGGL(prefill_prep_kernel<true>, dim3(blocks), dim3(256), lds, s, b, rpb);
+    hipLaunchKernelGGL(prefill_prep_kernel<true>, dim3(blocks), dim3(256), lds, s, b);
   else
-    hipLaunchKernelGGL(prefill_prep_kernel<false>, dim3(blocks), dim3(256), lds, s, b, rpb);
+    hipLaunchKernelGGL(prefill_prep_kernel<false>, dim3(blocks), dim3(256), lds, s, b);
   return hipGetLastError();
 }
 
@@ -659,9 +954,9 @@ int prefill_tiles_n(int n_tiles) { return prefill_tiles_n_dev(n_tiles); }
 
 hipError_t launch_prefill_batched(PrefillBatch &b, int bm, int blocks, hipStream_t s) {
   if (bm == 256) {
-    hipError_t e = allow_smem(prefill_batched_kernel<256>, P_SMEM);
+    hipError_t e = allow_smem(prefill_w8_kernel, W8_SMEM);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prefill_batched_kernel<256>, dim3(blocks), dim3(256), P_SMEM, s, b);
+    hipLaunchKernelGGL(prefill_w8_kernel, dim3(blocks), dim3(W8_THREADS), W8_SMEM, s, b);
   } else {
     hipError_t e = allow_smem(prefill_batched_kernel<64>, P_SMEM);
     if (e != hipSuccess) return e;
