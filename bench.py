@@ -42,8 +42,8 @@ COLD_BYTES = 600 << 20  # > 2 x 256 MB MALL
 # only holds for the kernel source it was taken on (sha256 prefix below);
 # after any change of that source the traffic is reported as null.
 TRAFFIC = {
-    "layer4b_m1": {"kernel_src_sha256": "ebb85f3c8269b860",
-                   "fetch_kib": 14649.7, "fetch_factor": 2.0,
+    "layer4b_m1": {"kernel_src_sha256": "64866f994be825d4",
+                   "fetch_kib": 14681.7, "fetch_factor": 2.0,
                    "write_kib": 60.0, "write_factor": 1.0},
 }
 

@@ -273,36 +273,61 @@ static int plan_gemv(GemvBatch &b, int *gather_blocks) {
 // row tile each) within GF_ITEMS_PER_WAVE; R halves while the launch has
 // fewer than 512 blocks.  Jobs with the largest k come first (their blocks
 // run longest).  Returns the launch's blocks.
+// Fused m = 1 launch: three 4-wave blocks share a compute unit (LDS and
+// registers allow it for every matrix shape this path takes), and the
+// dispatcher gives blocks i, i + CUs and i + 2 CUs to one unit when all of
+// them fit at once.  So: about total / (3 CUs) items per block (R tiles of
+// U units), at most 3 CUs blocks, and jobs ordered by items per block,
+// largest first, which puts a large block beside two small ones.
+static int device_cus();
 static int plan_fused(GemvBatch &b) {
-  for (int i = 1; i < b.count; ++i)
-    for (int j = i; j > 0 && b.job[j].w.k > b.job[j - 1].w.k; --j) {
-      const GemvJob t = b.job[j];
-      b.job[j] = b.job[j - 1];
-      b.job[j - 1] = t;
-    }
+  const int slots = 3 * device_cus();
+  int64_t total = 0;
+  for (int j = 0; j < b.count; ++j) total += (int64_t)b.job[j].w.n_tiles * b.job[j].w.units;
+  const int target = (int)((total + slots - 1) / slots);
   int R[GV_MAX_JOBS];
   for (int j = 0; j < b.count; ++j) {
     const int U = b.job[j].w.units;
-    R[j] = U <= GF_ITEMS_PER_WAVE ? 4 : (U <= 2 * GF_ITEMS_PER_WAVE ? 2 : 1);
+    int r = (target + U / 2) / U;
+    R[j] = r < 1 ? 1 : (r > GF_MAX_R ? GF_MAX_R : r);
   }
-  auto total = [&]() {
+  auto blocks_of = [&](int j) { return (b.job[j].w.n_tiles + R[j] - 1) / R[j]; };
+  auto total_blocks = [&]() {
     int t = 0;
-    for (int j = 0; j < b.count; ++j) t += (b.job[j].w.n_tiles + R[j] - 1) / R[j];
+    for (int j = 0; j < b.count; ++j) t += blocks_of(j);
     return t;
   };
-  while (total() < 512) {
+  // too many blocks for one round: grow the smallest blocks
+  while (total_blocks() > slots) {
     int best = -1;
     for (int j = 0; j < b.count; ++j)
-      if (R[j] > 1 && (best < 0 || R[j] > R[best])) best = j;
+      if (R[j] < GF_MAX_R && blocks_of(j) > 1 &&
+          (best < 0 || R[j] * b.job[j].w.units < R[best] * b.job[best].w.units))
+        best = j;
     if (best < 0) break;
-    R[best] /= 2;
+    ++R[best];
+  }
+  int order[GV_MAX_JOBS];
+  for (int j = 0; j < b.count; ++j) order[j] = j;
+  for (int i = 1; i < b.count; ++i)
+    for (int j = i; j > 0 && R[order[j]] * b.job[order[j]].w.units > R[order[j - 1]] * b.job[order[j - 1]].w.units; --j) {
+      const int t = order[j];
+      order[j] = order[j - 1];
+      order[j - 1] = t;
+    }
+  GemvJob sorted[GV_MAX_JOBS];
+  int Rs[GV_MAX_JOBS];
+  for (int j = 0; j < b.count; ++j) {
+    sorted[j] = b.job[order[j]];
+    Rs[j] = R[order[j]];
   }
   int begin = 0;
   for (int j = 0; j < b.count; ++j) {
-    b.job[j].R = R[j];
+    b.job[j] = sorted[j];
+    b.job[j].R = Rs[j];
     b.job[j].block_begin = begin;
     b.starts.first[j] = begin;
-    begin += (b.job[j].w.n_tiles + R[j] - 1) / R[j];
+    begin += (b.job[j].w.n_tiles + Rs[j] - 1) / Rs[j];
   }
   return begin;
 }

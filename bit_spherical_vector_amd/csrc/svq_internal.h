@@ -111,9 +111,9 @@ size_t gemv_smem_bytes(int m, int bd_max, int r_max);
 hipError_t launch_gemv_batched(GemvBatch &b, int gather_blocks, int k_max, int blocks, size_t smem,
                                hipStream_t s);
 constexpr int GV_UNITS_PER_WAVE = 4;  // units per wave the planner aims for
-// m = 1: one fused launch (gather in the block); R in {1, 2, 4} row tiles
-// per block, each wave near GF_ITEMS_PER_WAVE units.
-constexpr int GF_ITEMS_PER_WAVE = 5;
+// m = 1: one fused launch (gather in the block); R <= GF_MAX_R row tiles
+// per block, whose R x units items the 4 waves split into equal runs.
+constexpr int GF_MAX_R = 8;
 size_t gemv_fused_smem_bytes(int k, int units, int bd);  // one matrix
 hipError_t launch_gemv_fused(GemvBatch &b, int blocks, size_t smem, hipStream_t s);
 

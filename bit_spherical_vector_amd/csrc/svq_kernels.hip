@@ -620,9 +620,11 @@ hipError_t launch_gemv_batched(GemvBatch &b, int gather_blocks, int k_max, int b
 // ---------------------------------------------------------------------------
 //
 // With a single activation row the gather costs less inside the block than
-// as a launch of its own.  A block owns R in {1, 2, 4} consecutive 16-row
-// tiles of one matrix and all of its K; each tile gets 4/R of the block's 4
-// waves, which split its 512-slot units between them.  Prologue: the block
+// as a launch of its own.  A block owns R <= GF_MAX_R consecutive 16-row
+// tiles of one matrix and all of its K; its R x U items (unit u of tile t,
+// tile-major, which is their order in memory) are cut into 4 equal runs,
+// one per wave, and a wave flushes its sums to its LDS slot of a tile when
+// its run leaves the tile.  Prologue: the block
 // stages the activation row in LDS and gathers the permuted slots unit by
 // unit, with the exact per-unit power-of-two scale described above.  Main
 // loop: the same work items and MFMA mapping as the main launch of m = 2..4,
@@ -647,7 +649,7 @@ constexpr int GF_OFF_D = RTAB_BYTES;
 __host__ __device__ constexpr int gf_dir_bytes(int bd) { return bd >= 8 ? DTAB_BYTES : (16 << bd) * 16; }
 __host__ __device__ constexpr int gf_scale_off(int bd) { return GF_OFF_D + gf_dir_bytes(bd); }
 __host__ __device__ constexpr int gf_xp_off(int bd, int units, int m) {
-  return gf_scale_off(bd) + ((units * m * 4 + 15) & ~15) + GV_WAVES * 4 * 4 * 4 * m;
+  return gf_scale_off(bd) + ((units * m * 4 + 15) & ~15) + GF_MAX_R * GV_WAVES * 4 * 4 * 4 * m;
 }
 
 // Table reads of the four codes of column group ci: direction rows (signs
@@ -725,19 +727,17 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   const int bd = w.bd, rows = 1 << bd;
   _Float16 *s_rtab = (_Float16 *)(smem + GF_OFF_RTAB);
   float *s_scale = (float *)(smem + gf_scale_off(bd));    // [U][M] 2^-e per unit
-  float *s_red = s_scale + ((U * M + 3) & ~3);            // [W][4][M][4]
+  float *s_red = s_scale + ((U * M + 3) & ~3);            // [GF_MAX_R][W][4][M][4]
   uint16_t *s_xp = (uint16_t *)(smem + gf_xp_off(bd, U, M));  // [M][Kp] fp16
   uint16_t *s_stage = s_xp + (size_t)M * Kp;              // [K] bf16
   const int n8 = K / 8;
 
-  // this wave's work: tile rt0 + wt, units [u_begin, u_end)
-  const int wpt_log = R == 4 ? 0 : (R == 2 ? 1 : 2);  // log2 of waves per tile
-  const int wpt = 1 << wpt_log;
-  const int wt = wv >> wpt_log, part = wv & (wpt - 1);
-  const int uper = (U + wpt - 1) >> wpt_log;
-  const int u_begin = part * uper;
-  const int u_end = wt < Reff ? min(U, u_begin + uper) : u_begin;
-  const uint8_t *tile = w.base + w.off_codes + (size_t)(rt0 + wt) * U * UNIT_BYTES;
+  // this wave's work: items [i_begin, i_end) of the block's Reff x U items
+  // (item i = unit i % U of tile rt0 + i / U, at codes0 + i units)
+  const int n_items = Reff * U;
+  const int i_begin = wv * n_items / GV_WAVES, i_end = (wv + 1) * n_items / GV_WAVES;
+  const uint8_t *codes0 = w.base + w.off_codes + (size_t)rt0 * U * UNIT_BYTES;
+  (void)R;
   // this wave's share of the gather: units [g_lo, g_hi]
   const int gper = (U + GV_WAVES - 1) >> 2;
   const int g_lo = wv * gper, g_hi = min(U, g_lo + gper) - 1;
@@ -762,7 +762,10 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
         xv[a][b] = ((const u4 *)(x + (int64_t)a * ldx))[min(tid + 256 * b, n8 - 1)];
   }
   ItemCodes ring[GV_PIPE];
-  int ul = u_begin;  // next unit to load
+  int ul = i_begin;  // next item to load
+  // every (tile, wave) slot of the tile sums starts at zero: a wave adds
+  // only the tiles its run touches
+  for (int e = tid; e < GF_MAX_R * GV_WAVES * 4 * M * 4; e += 256) s_red[e] = 0.f;
   if constexpr (MODE == 0) {
     // 16 copies of each row; the copy index rotates with the row so that the
     // lanes of one store hit different bank groups
@@ -813,7 +816,7 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
       // the code latency then overlaps the gather.
 #pragma unroll
       for (int s = 0; s < GV_PIPE; ++s) {
-        const uint8_t *ub = ul < u_end ? tile + (size_t)ul * UNIT_BYTES : w.base;
+        const uint8_t *ub = ul < i_end ? codes0 + (size_t)ul * UNIT_BYTES : w.base;
         ring[s] = load_item<true>(ub, lane);
         ++ul;
       }
@@ -910,47 +913,65 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
     }
   };
 
-  // Items of the wave: units u_begin .. u_end-1 (slot (u - u_begin) % GV_PIPE).
-  // While a later chunk exists, every processed slot is refilled at once
-  // (unconditional loads, dummy address past the end); the last chunk has
-  // no refills.
-  int u = u_begin;
-  while (u + GV_PIPE < u_end) {
+  // The wave's sums of tile t: over the 16 code columns of each lane group
+  // (lanes with equal j) into the (t, wave) slot, then cleared.
+  auto flush = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri) {
+#pragma unroll
+      for (int a = 0; a < M; ++a) {
+        float v = acc[ri][a];
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (lane < 4) s_red[(((t * GV_WAVES + wv) * 4 + ri) * M + a) * 4 + lane] = v;
+        acc[ri][a] = 0.f;
+      }
+    }
+  };
+
+  // Items of the wave: i_begin .. i_end-1 (slot (i - i_begin) % GV_PIPE),
+  // unit cu of tile ct.  While a later chunk exists, every processed slot
+  // is refilled at once (unconditional loads, dummy address past the end);
+  // the last chunk has no refills.
+  int i = i_begin;
+  int ct = i_begin / U, cu = i_begin - ct * U;
+  auto advance = [&]() __attribute__((always_inline)) {
+    ++i;
+    if (++cu == U) {
+      flush(ct);
+      ++ct;
+      cu = 0;
+    }
+  };
+  while (i + GV_PIPE < i_end) {
 #pragma unroll
     for (int s = 0; s < GV_PIPE; ++s) {
-      step(ring[s], u);
-      ++u;
-      const uint8_t *ub = ul < u_end ? tile + (size_t)ul * UNIT_BYTES : w.base;
+      step(ring[s], cu);
+      advance();
+      const uint8_t *ub = ul < i_end ? codes0 + (size_t)ul * UNIT_BYTES : w.base;
       ring[s] = load_item<true>(ub, lane);
       ++ul;
     }
   }
 #pragma unroll
   for (int s = 0; s < GV_PIPE; ++s) {
-    if (u < u_end) step(ring[s], u);
-    ++u;
-  }
-
-  // sum over the 16 code columns of each lane group (lanes with equal j),
-  // then over the waves of the tile
-#pragma unroll
-  for (int ri = 0; ri < 4; ++ri) {
-#pragma unroll
-    for (int a = 0; a < M; ++a) {
-      float v = acc[ri][a];
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (lane < 4) s_red[((wv * 4 + ri) * M + a) * 4 + lane] = v;
+    if (i < i_end) {
+      step(ring[s], cu);
+      advance();
     }
   }
+  if (cu != 0) flush(ct);  // the run ends inside a tile
+
+  // sum over the waves of each tile, in wave order
   __syncthreads();
   for (int o = tid; o < Reff * 16 * M; o += 256) {
     const int t = o / (16 * M), a = (o / 16) % M, row = o & 15;
     const int ri = row >> 2, j = row & 3;
     float sum = 0.f;
-    for (int p = 0; p < wpt; ++p) sum += s_red[(((t * wpt + p) * 4 + ri) * M + a) * 4 + j];
+#pragma unroll
+    for (int p = 0; p < GV_WAVES; ++p) sum += s_red[(((t * GV_WAVES + p) * 4 + ri) * M + a) * 4 + j];
     const int n = (rt0 + t) * 16 + row;
     if (n < w.n) store_out(y, (size_t)a * ldy + n, sum, ydt);
   }
@@ -1155,9 +1176,10 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
     if ((xvec ? lds_ok_t : lds_ok_f) != hipSuccess) return xvec ? lds_ok_t : lds_ok_f;
     hipError_t e = xvec ? allow_smem(moe_gemv_kernel<true>, smem) : allow_smem(moe_gemv_kernel<false>, smem);
     if (e != hipSuccess) return e;
-    // row tiles per block: as in the dense planner, enough units per wave
-    // to amortise the gather, while the launch keeps >= 256 blocks
-    int R = sh.units <= GF_ITEMS_PER_WAVE ? 4 : (sh.units <= 2 * GF_ITEMS_PER_WAVE ? 2 : 1);
+    // row tiles per block: about 5 units per wave to amortise the gather,
+    // while the launch keeps >= 256 blocks
+    constexpr int ITEMS_PER_WAVE = 5;
+    int R = sh.units <= ITEMS_PER_WAVE ? 4 : (sh.units <= 2 * ITEMS_PER_WAVE ? 2 : 1);
     while (R > 1 && ((sh.n_tiles + R - 1) / R) * S < 256) R /= 2;
     const dim3 grid((sh.n_tiles + R - 1) / R, S);
     if (xvec)
