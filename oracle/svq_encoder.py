@@ -1,0 +1,106 @@
+"""CPU oracle for the SVQ encoder (float weights -> 18-bit codes).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this module.  The HIP
+library never calls it and it imports nothing from the library.
+
+What it computes.  "SAGE: Pushing 2-Bit Vector-Quantized LLMs toward
+Real-World Usability", Fig. 2 caption: spherical vector quantization codes
+each 8-weight subvector (taken along the channel permutation) by its signs,
+a direction index into a codebook of unit directions and a quantized radius,
+18 bits per subvector.  The pages do not spell out how a subvector is mapped
+to its code; the readings taken here (each is the library's contract too):
+
+* Subvector c of row i is ``v[l] = W[i, perm[8c + l]]`` (the same gather as
+  the decode side).
+* Sign bit l = the IEEE sign bit of ``v[l]`` (1 for negative numbers and for
+  -0.0), so that signs round-trip exactly through the decode.
+* Direction index d = the codebook row with the largest inner product with
+  ``|v|`` (the codebook directions lie in the positive orthant and have unit
+  norm, so this is the direction of largest cosine); ties go to the smaller
+  index.
+* Radius index r = the radius-table entry nearest to the Euclidean norm of
+  ``v``; ties go to the smaller index.  The table must be strictly
+  increasing, so "nearest" is "number of midpoints (R[t] + R[t+1]) / 2 that
+  lie strictly below the norm".
+
+Arithmetic (fixed so that a GPU implementation can take the same integer
+decisions bit for bit): float64 throughout.  The products ``|v_l| * D[j][l]``
+(float32 x fp16) and the squares ``v_l**2`` are exact in float64; the eight
+terms of each score and of the squared norm are added one at a time in lane
+order 0..7, with no fused multiply-add.  The radius decision compares the
+squared norm with the squared midpoints (both sides of each comparison are
+exact float64 values except for the rounding of the sequential sum), which
+avoids a square root.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle.svq_oracle import INDEX_BITS, SIGN_BITS, fp16_bits_to_f64, join_fields, pack_codes
+
+
+def gather_subvectors(w: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """Permuted weights, float64 [n, k/8, 8]: ``[i, c, l] = W[i, perm[8c + l]]``."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    perm = np.asarray(perm, dtype=np.int64)
+    if k % 8 or perm.shape != (k,) or not np.array_equal(np.sort(perm), np.arange(k)):
+        raise ValueError("perm must be a permutation of range(k), k a multiple of 8")
+    return w[:, perm].astype(np.float64).reshape(n, k // 8, 8)
+
+
+def radius_midpoints_sq(radius_bits: np.ndarray) -> np.ndarray:
+    """Squared midpoints between consecutive radii (exact in float64)."""
+    R = fp16_bits_to_f64(radius_bits)
+    if R.size < 2 or not np.all(np.isfinite(R)) or not np.all(np.diff(R) > 0) or R[0] < 0:
+        raise ValueError("radius table must be finite, non-negative and strictly increasing")
+    mid = (R[:-1] + R[1:]) / 2.0  # 12 significant bits at most: exact
+    return mid * mid              # 24 significant bits: exact
+
+
+def encode_fields(w: np.ndarray, perm: np.ndarray, bd: int, codebook_bits: np.ndarray,
+                  radius_bits: np.ndarray):
+    """(signs, direction index, radius index), each uint32 [n, k/8]."""
+    v = gather_subvectors(w, perm)
+    a = np.abs(v)
+    # signs: bit l set when v[l] carries a negative sign bit
+    neg = np.signbit(v).astype(np.uint32)
+    s = np.zeros(v.shape[:2], dtype=np.uint32)
+    for l in range(8):
+        s |= neg[:, :, l] << np.uint32(l)
+    # direction: sequential float64 sums of exact products, first maximum
+    D = fp16_bits_to_f64(np.asarray(codebook_bits).reshape(1 << bd, 8))
+    if not np.all(np.isfinite(D)):
+        raise ValueError("codebook entries must be finite")
+    score = a[:, :, 0, None] * D[None, None, :, 0]
+    for l in range(1, 8):
+        score = score + a[:, :, l, None] * D[None, None, :, l]
+    d = np.argmax(score, axis=2).astype(np.uint32)  # first index of the maximum
+    # radius: squared norm against squared midpoints
+    nsq = a[:, :, 0] * a[:, :, 0]
+    for l in range(1, 8):
+        nsq = nsq + a[:, :, l] * a[:, :, l]
+    msq = radius_midpoints_sq(np.asarray(radius_bits).reshape(1 << (INDEX_BITS - bd)))
+    r = np.zeros(nsq.shape, dtype=np.uint32)
+    for t in range(msq.size):
+        r += (nsq > msq[t]).astype(np.uint32)
+    return s, d, r
+
+
+def encode_matrix(w: np.ndarray, perm: np.ndarray, bd: int, codebook_bits: np.ndarray,
+                  radius_bits: np.ndarray) -> np.ndarray:
+    """uint32 codes [n, k/8] (bits 0-7 signs, then bd direction bits, then
+    the radius bits)."""
+    s, d, r = encode_fields(w, perm, bd, codebook_bits, radius_bits)
+    return join_fields(s, d, r, bd)
+
+
+def encode_stream(w: np.ndarray, perm: np.ndarray, bd: int, codebook_bits: np.ndarray,
+                  radius_bits: np.ndarray) -> np.ndarray:
+    """Canonical LSB-first bitstream of :func:`encode_matrix`."""
+    return pack_codes(encode_matrix(w, perm, bd, codebook_bits, radius_bits))
+
+
+__all__ = ["gather_subvectors", "radius_midpoints_sq", "encode_fields", "encode_matrix",
+           "encode_stream", "SIGN_BITS"]
