@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP64_VALU_PEAK_TFLOPS = 78.6  # MI355X published fp64 vector peak
 COLD_BYTES = 600 << 20  # > 2 x 256 MB MALL
 
 
@@ -73,7 +74,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="layer4b_m1",
                     choices=["layer4b_m1", "layer4b_m4", "layer4b_m16", "single_512x1024_m1",
-                             "prefill_m2048", "moe128_m1", "moe128_m512"])
+                             "prefill_m2048", "moe128_m1", "moe128_m512", "encode_gate_bd7"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
@@ -253,6 +254,92 @@ def bench_moe(args, wl, svq, synth, dev, stream):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_encode(w_rows, mat, bd, n_full, budget_s=12.0):
+    """The encoder oracle over row blocks of the workload's weights until
+    about budget_s of work is done; codes per second."""
+    from oracle import svq_encoder as se
+    t0 = time.perf_counter()
+    codes, blocks = 0, 0
+    while True:
+        se.encode_matrix(w_rows, mat.perm, bd, mat.codebook, mat.radius)
+        codes += w_rows.shape[0] * (w_rows.shape[1] // 8)
+        blocks += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(codes / dt / 1e6, 5), "unit": "Mcodes/s", "cores": 1, "kind": "oracle",
+            "sample": f"{blocks} x {w_rows.shape[0]} rows of the {n_full} x {mat.k} matrix, "
+                      f"{dt:.1f} s, single-threaded numpy float64"}
+
+
+def bench_encode(args, wl, svq, synth, stream):
+    """svq_encode on one gate-shaped float32 matrix (random weights whose
+    subvector norms span the radius table); a step is one whole call
+    (table staging, the kernel and the call's stream synchronisation)."""
+    import numpy as np
+    import torch
+
+    name, n, k = wl["shapes"][0]
+    bd = wl["bd"]
+    mat = synth.random_matrix(64, k, bd, seed=(60, n, k))  # tables and permutation
+    R = np.asarray(mat.radius, dtype=np.uint16).view(np.float16).astype(np.float64)
+    gen = torch.Generator(device="cuda").manual_seed(60)
+    # N(0, sigma) weights with sigma chosen so that subvector norms fall in
+    # the middle of the radius table
+    sigma = float(np.sqrt(R[0] * R[-1]) / np.sqrt(8.0))
+    w = torch.randn((n, k), device="cuda", generator=gen) * sigma
+    st, need = svq.svq_encode(None, k, n, k, bd, mat.codebook, mat.radius, mat.perm, None, None, 0, 0)
+    assert st == svq.SVQ_OK
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    codes = torch.zeros((n * (k // 8) * 18 + 7) // 8, dtype=torch.uint8, device="cuda")
+    sh = int(stream.cuda_stream)
+
+    def step():
+        st, _ = svq.svq_encode(w.data_ptr(), k, n, k, bd, mat.codebook, mat.radius, mat.perm,
+                               codes.data_ptr(), ws.data_ptr(), need, sh)
+        assert st == svq.SVQ_OK
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ncodes = n * (k // 8)
+    value = ncodes / (ms_per_step * 1e-3) / 1e6
+    # algorithmic double-precision operations per code: 2^bd scores and the
+    # squared norm, each 8 products and 7 additions
+    flops = ncodes * ((1 << bd) + 1) * 15.0
+    achieved = flops / (ms_per_step * 1e-3) / 1e12
+    roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": FP64_VALU_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / FP64_VALU_PEAK_TFLOPS, 4), "traffic": None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_encode(w[:64].cpu().numpy(), mat, bd, n)
+    out = {
+        "metric": "SVQ encode Mcodes/s",
+        "value": round(value, 3),
+        "unit": "Mcodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic (random fp32 weights, seeded codebook, radii, permutation)",
+        "config": {"workload": args.workload, "n": n, "k": k, "bd": bd, "codes": ncodes},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -274,6 +361,8 @@ def main():
 
     if wl["kind"] == "moe":
         return bench_moe(args, wl, svq, synth, dev, stream)
+    if wl["kind"] == "encode":
+        return bench_encode(args, wl, svq, synth, stream)
 
     if args.workload.startswith("layer4b"):
         mats, xs1 = synth.dense_layer()

@@ -656,3 +656,72 @@ svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts, const 
 }
 
 }  // extern "C"
+
+svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t bd,
+                      const uint16_t *codebook, const uint16_t *radius, const int32_t *perm,
+                      void *codes, void *workspace, size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes || !codebook || !radius || !perm) return SVQ_ERR_INVALID_ARG;
+  if (n <= 0 || k <= 0 || k % 8 != 0) return SVQ_ERR_INVALID_ARG;
+  if (bd < 6 || bd > 8) return SVQ_ERR_UNSUPPORTED;
+  if (k > SVQ_MAX_K || n > SVQ_MAX_N) return SVQ_ERR_UNSUPPORTED;
+  if (ldw < k) return SVQ_ERR_INVALID_ARG;
+  const int rows = 1 << bd, nrad = 1 << (10 - bd);
+  // tables: finite codebook; radii finite, >= 0, strictly increasing
+  std::vector<double> cb((size_t)rows * 8), msq((size_t)nrad - 1);
+  for (int e = 0; e < rows * 8; ++e) {
+    if (((codebook[e] >> 10) & 0x1F) == 0x1F) return SVQ_ERR_INVALID_ARG;
+    cb[(size_t)e] = (double)half_to_float(codebook[e]);
+  }
+  std::vector<double> R((size_t)nrad);
+  for (int t = 0; t < nrad; ++t) {
+    if (((radius[t] >> 10) & 0x1F) == 0x1F) return SVQ_ERR_INVALID_ARG;
+    R[(size_t)t] = (double)half_to_float(radius[t]);
+    if (R[(size_t)t] < 0.0 || (t > 0 && !(R[(size_t)t] > R[(size_t)t - 1]))) return SVQ_ERR_INVALID_ARG;
+  }
+  for (int t = 0; t + 1 < nrad; ++t) {
+    const double mid = (R[(size_t)t] + R[(size_t)t + 1]) / 2.0;  // exact (12 significant bits)
+    msq[(size_t)t] = mid * mid;                                   // exact (24 significant bits)
+  }
+  {
+    std::vector<uint8_t> seen((size_t)k, 0);
+    for (int32_t p = 0; p < k; ++p) {
+      const int32_t c = perm[p];
+      if (c < 0 || c >= k || seen[(size_t)c]) return SVQ_ERR_INVALID_ARG;
+      seen[(size_t)c] = 1;
+    }
+  }
+  const size_t cb_bytes = align256(cb.size() * sizeof(double));
+  const size_t msq_bytes = align256(msq.size() * sizeof(double));
+  const size_t perm_bytes = align256((size_t)k * sizeof(int32_t));
+  const size_t need = cb_bytes + msq_bytes + perm_bytes;
+  if (!workspace) {
+    *workspace_bytes = need;
+    return SVQ_OK;
+  }
+  if (!w || !codes) return SVQ_ERR_INVALID_ARG;
+  if (*workspace_bytes < need) return SVQ_ERR_BUFFER_TOO_SMALL;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  EncArgs a;
+  a.w = w;
+  a.ldw = ldw;
+  a.n = n;
+  a.k = k;
+  a.bd = bd;
+  a.n_mid = nrad - 1;
+  a.cb = (const double *)ws;
+  a.msq = (const double *)(ws + cb_bytes);
+  a.perm = (const int32_t *)(ws + cb_bytes + msq_bytes);
+  a.codes = (uint8_t *)codes;
+  a.count = (int64_t)n * (k / 8);
+  hipError_t e = hipMemcpyAsync(ws, cb.data(), cb.size() * sizeof(double), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(ws + cb_bytes, msq.data(), msq.size() * sizeof(double), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(ws + cb_bytes + msq_bytes, perm, (size_t)k * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = launch_encode(a, s);
+  // the staged host arrays must outlive the copies
+  const hipError_t e2 = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = e2;
+  return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+}

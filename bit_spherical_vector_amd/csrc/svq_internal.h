@@ -212,6 +212,22 @@ hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, size_t lds, bool xve
 hipError_t launch_prefill_batched(PrefillBatch &b, int bm, int blocks, hipStream_t s);
 hipError_t launch_prefill_reduce(PrefillBatch &b, int blocks, hipStream_t s);
 
+// ---- encoder ------------------------------------------------------------
+// Tables of svq_encode as staged in the workspace: the codebook in float64
+// (rows x 8), the squared midpoints of consecutive radii (float64) and the
+// permutation.
+struct EncArgs {
+  const float *w;
+  int64_t ldw;
+  int32_t n, k, bd, n_mid;
+  const double *cb;
+  const double *msq;
+  const int32_t *perm;
+  uint8_t *codes;  // canonical stream
+  int64_t count;   // n * k / 8 codes
+};
+hipError_t launch_encode(const EncArgs &a, hipStream_t s);
+
 // ---- MoE ----------------------------------------------------------------
 struct ExpertTable {
   const uint8_t *base[MAX_EXPERTS];

@@ -34,7 +34,7 @@ SVQ_BF16 = 0
 SVQ_F32 = 1
 
 EXPORTED = ("svq_pack", "svq_linear", "svq_linear_batched", "svq_moe_linear",
-            "svq_status_string")
+            "svq_encode", "svq_status_string")
 
 
 class SvqError(RuntimeError):
@@ -94,6 +94,11 @@ def _load() -> ctypes.CDLL:
                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                    ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
+    lib.svq_encode.restype = ctypes.c_int
+    lib.svq_encode.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
+                               ctypes.c_void_p]
     return lib
 
 
@@ -145,6 +150,20 @@ def svq_moe_linear(handles, num_experts: int, x_ptr: int, ldx: int, x_per_slot: 
     nbytes = ctypes.c_size_t(ws_bytes)
     st = LIB.svq_moe_linear(handles, num_experts, x_ptr, ldx, x_per_slot, ids_ptr, m, topk,
                             y_ptr, ldy, ydt, ws_ptr, ctypes.byref(nbytes), stream)
+    return st, nbytes.value
+
+
+def svq_encode(w_ptr: Optional[int], ldw: int, n: int, k: int, bd: int, codebook: np.ndarray,
+               radius: np.ndarray, perm: np.ndarray, codes_ptr: Optional[int],
+               ws_ptr: Optional[int], ws_bytes: int, stream: int) -> tuple:
+    """codebook / radius: host uint16 arrays (fp16 bit patterns); perm: host
+    int32 array."""
+    cb = np.ascontiguousarray(codebook, dtype=np.uint16)
+    rad = np.ascontiguousarray(radius, dtype=np.uint16)
+    pm = np.ascontiguousarray(perm, dtype=np.int32)
+    nbytes = ctypes.c_size_t(ws_bytes)
+    st = LIB.svq_encode(w_ptr, ldw, n, k, bd, cb.ctypes.data, rad.ctypes.data, pm.ctypes.data,
+                        codes_ptr, ws_ptr, ctypes.byref(nbytes), stream)
     return st, nbytes.value
 
 
@@ -344,3 +363,20 @@ def moe_linear(pms: Sequence[PackedMatrix], x, expert_ids, topk: int, x_per_slot
                            workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
     _check(st, "svq_moe_linear")
     return out
+
+
+def encode(w, perm, bd: int, codebook, radius, stream=None):
+    """Codes of a device fp32 weight matrix [n, k] (rows may be strided) as
+    the canonical stream, a device uint8 tensor of ceil(n*k*9/32) bytes."""
+    import torch
+    if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D float32 tensor with unit column stride")
+    n, k = w.shape
+    st, need = svq_encode(None, w.stride(0), n, k, bd, codebook, radius, perm, None, None, 0, 0)
+    _check(st, "svq_encode (size query)")
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+    codes = torch.zeros((n * (k // 8) * 18 + 7) // 8, dtype=torch.uint8, device=w.device)
+    st, _ = svq_encode(w.data_ptr(), w.stride(0), n, k, bd, codebook, radius, perm,
+                       codes.data_ptr(), ws.data_ptr(), need, _stream_handle(stream))
+    _check(st, "svq_encode")
+    return codes

@@ -166,6 +166,38 @@ svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts,
                           void *y, int64_t ldy, svq_dtype ydt,
                           void *workspace, size_t *workspace_bytes, void *stream);
 
+/* svq_encode: the codes of a float weight matrix for given tables -- the
+ * step before svq_pack (SAGE Fig. 2 caption: each 8-weight subvector, taken
+ * along the channel permutation, is coded by its signs, a direction index
+ * into the codebook and a quantized radius).  Subvector c of row i is
+ * v[l] = w[i][perm[8c + l]] and its code (bits 0-7 signs, then bd direction
+ * bits, then 10 - bd radius bits, as in svq_matrix_desc) is:
+ *   sign bit l  = the IEEE sign bit of v[l] (1 for negatives and -0.0);
+ *   direction   = the codebook row j with the largest
+ *                 sum_l |v[l]| * D[j][l], the first such row on ties;
+ *   radius      = the table entry nearest to the norm of v, the lower entry
+ *                 on ties.
+ * Scores and squared norms are formed in double precision, lane order
+ * 0..7, without fused multiply-adds; the radius is decided by the squared
+ * norm against the squared midpoints of consecutive radii.
+ *   w:          device fp32 [n][ldw], ldw >= k; every value finite.
+ *   n, k:       k a multiple of 8, limits as for svq_pack.
+ *   bd:         direction-index bits, 6..8 (radius bits 10 - bd).
+ *   codebook:   host, (1 << bd) x 8 fp16 bit patterns, finite.
+ *   radius:     host, 1 << (10 - bd) fp16 bit patterns, finite, >= 0 and
+ *               strictly increasing.
+ *   perm:       host, k entries, a permutation of [0, k).
+ *   codes:      device, out: the canonical LSB-first stream of the n*k/8
+ *               codes, ceil(n*k*9/32) bytes (the svq_matrix_desc format).
+ *   workspace:  device scratch of at least *workspace_bytes bytes (the
+ *               tables are staged there), or NULL to query the size.
+ * Validates every host argument before any device work; copies the tables
+ * on `stream` and synchronizes it before returning (the host arrays may be
+ * freed afterwards).  Non-finite weights make the codes undefined. */
+svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t bd,
+                      const uint16_t *codebook, const uint16_t *radius, const int32_t *perm,
+                      void *codes, void *workspace, size_t *workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *svq_status_string(svq_status s);
 

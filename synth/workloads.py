@@ -73,6 +73,8 @@ WORKLOADS: Dict[str, dict] = {
     "prefill_m2048": dict(kind="dense", shapes=PREFILL_SHAPES, m=2048, bd=7),
     "moe128_m1": dict(kind="moe", shapes=MOE_SHAPES, m=1),
     "moe128_m512": dict(kind="moe", shapes=MOE_SHAPES, m=512),
+    # the encoder (the step before the packed path): one gate-shaped matrix
+    "encode_gate_bd7": dict(kind="encode", shapes=[("gate", 9728, 2560)], m=0, bd=7),
 }
 
 

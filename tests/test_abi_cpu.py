@@ -23,7 +23,7 @@ def _declared_functions():
 def test_exports_every_declared_symbol():
     declared = _declared_functions()
     assert set(declared) == {"svq_pack", "svq_linear", "svq_linear_batched", "svq_moe_linear",
-                             "svq_status_string"}
+                             "svq_encode", "svq_status_string"}
     for name in declared:
         assert hasattr(svq.LIB, name), name
     assert set(declared) == set(svq.EXPORTED)
@@ -297,3 +297,36 @@ def test_linear_batched_query_and_validation():
     # missing pointer arrays with a workspace
     assert svq.svq_linear_batched(hs, 3, None, ldx, 1, None, ldy, 0, 0x1000, 4096, 0)[0] == \
         svq.SVQ_ERR_INVALID_ARG
+
+
+def test_encode_workspace_query_and_validation():
+    """svq_encode: size query without a GPU, and every host-side check
+    before any device work (the pointers below are never dereferenced)."""
+    import synth
+    mat = synth.random_matrix(16, 64, 7, seed=(45, 7, 0))
+    cb, rad, perm = mat.codebook, mat.radius, mat.perm
+    a = lambda v: (v + 255) // 256 * 256
+    st, need = svq.svq_encode(None, 64, 16, 64, 7, cb, rad, perm, None, None, 0, 0)
+    assert st == svq.SVQ_OK and need == a(128 * 8 * 8) + a(7 * 8) + a(64 * 4)
+    q = lambda **kw: svq.svq_encode(kw.get("w"), kw.get("ldw", 64), kw.get("n", 16), kw.get("k", 64),
+                                    kw.get("bd", 7), kw.get("cb", cb), kw.get("rad", rad),
+                                    kw.get("perm", perm), kw.get("codes"), kw.get("ws"),
+                                    kw.get("wsb", 0), 0)[0]
+    assert q(k=60) == svq.SVQ_ERR_INVALID_ARG          # k not a multiple of 8
+    assert q(n=0) == svq.SVQ_ERR_INVALID_ARG
+    assert q(ldw=32) == svq.SVQ_ERR_INVALID_ARG        # ldw < k
+    assert q(bd=5) == svq.SVQ_ERR_UNSUPPORTED
+    bad_perm = perm.copy()
+    bad_perm[1] = bad_perm[0]
+    assert q(perm=bad_perm) == svq.SVQ_ERR_INVALID_ARG
+    assert q(rad=rad[::-1].copy()) == svq.SVQ_ERR_INVALID_ARG   # not increasing
+    inf_cb = np.asarray(cb).copy()
+    inf_cb[3, 2] = 0x7C00
+    assert q(cb=inf_cb) == svq.SVQ_ERR_INVALID_ARG      # infinite codebook entry
+    neg = np.asarray(rad).copy()
+    neg[0] = 0xBC00                                     # -1.0
+    assert q(rad=neg) == svq.SVQ_ERR_INVALID_ARG
+    # a workspace without the weight or code pointers, then too small a one
+    assert q(ws=0x1000, wsb=1 << 20) == svq.SVQ_ERR_INVALID_ARG
+    assert q(w=0x2000, codes=0x3000, ws=0x1000, wsb=100) == svq.SVQ_ERR_BUFFER_TOO_SMALL
+
