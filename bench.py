@@ -74,7 +74,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="layer4b_m1",
                     choices=["layer4b_m1", "layer4b_m4", "layer4b_m16", "single_512x1024_m1",
-                             "prefill_m2048", "moe128_m1", "moe128_m512", "encode_gate_bd7"])
+                             "prefill_m2048", "moe128_m1", "moe128_m512", "encode_gate_bd7",
+                             "decode4b_36l"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
@@ -340,6 +341,98 @@ def bench_encode(args, wl, svq, synth, stream):
     print(json.dumps(out), flush=True)
 
 
+def bench_decode(args, wl, svq, synth, dev):
+    """The linears of one batch-1 decode step of a 36-layer 4B-class model:
+    per layer, four dependent svq_linear_batched calls (q/k/v, o, gate/up,
+    down), every layer with its own packed matrices (1.02 GB of codes in
+    all, four times the Infinity Cache, so each layer is read from HBM).
+    The step is timed twice: launched call by call from Python, and replayed
+    as one HIP graph captured from the same calls (the serving form: no host
+    work between launches).  ``value`` and ``ms_per_step`` are the graph
+    figures; the SAGE paper reports the same split of time per output token
+    (Table 3, Fig. 7) for whole models."""
+    import numpy as np
+    import torch
+
+    stack = synth.decode_stack(wl["layers"])
+    side = torch.cuda.Stream()  # graph capture needs a stream other than the legacy default
+    calls, ws, code_bytes = [], None, 0
+    for mats, xs in stack:
+        pms = [svq.pack(w) for w in mats]
+        code_bytes += sum(w.codes.size for w in mats)
+        for c, idx in enumerate(synth.DECODE_CALLS):
+            x = torch.from_numpy(xs[c].view(np.int16)).view(torch.bfloat16).to(dev)
+            ys = [torch.empty((1, mats[j].n), dtype=torch.bfloat16, device=dev) for j in idx]
+            call = svq.BatchedCall([pms[j] for j in idx], [x] * len(idx), ys, workspace=ws,
+                                   stream=side)
+            if ws is None or call.workspace.numel() > ws.numel():
+                ws = call.workspace
+            calls.append(call)
+    layer0 = stack[0]
+    del stack
+
+    def step():
+        for call in calls:
+            call()
+
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(side)
+    for _ in range(args.steps):
+        step()
+    ev[1].record(side)
+    torch.cuda.synchronize()
+    eager_ms = ev[0].elapsed_time(ev[1]) / args.steps
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        ev[2].record(side)
+        for _ in range(args.steps):
+            graph.replay()
+        ev[3].record(side)
+    torch.cuda.synchronize()
+    ms_per_step = ev[2].elapsed_time(ev[3]) / args.steps
+    value = code_bytes / (ms_per_step * 1e-3) / 1e9
+    # roofline.achieved: the step's code bytes over the mean step duration;
+    # a step is 144 back-to-back launches, so the gaps between them count
+    roof = {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        mats0, xs0 = layer0
+        cpu = cpu_baseline_dense(mats0, [xs0[c] for c, idx in enumerate(synth.DECODE_CALLS)
+                                         for _ in idx])
+    out = {
+        "metric": "packed-weight GB/s (batch-1 decode step, 36 layers)",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xf16->f32 (exact decode)",
+        "data": "synthetic (seeded codes, codebooks, radii, permutations, activations)",
+        "config": {"workload": args.workload, "layers": wl["layers"], "matrices": 7 * wl["layers"],
+                   "m": 1, "code_bytes": int(code_bytes), "launches_per_step": len(calls),
+                   "eager_ms_per_step": round(eager_ms, 5), "graph": True},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -363,6 +456,8 @@ def main():
         return bench_moe(args, wl, svq, synth, dev, stream)
     if wl["kind"] == "encode":
         return bench_encode(args, wl, svq, synth, stream)
+    if wl["kind"] == "decode":
+        return bench_decode(args, wl, svq, synth, dev)
 
     if args.workload.startswith("layer4b"):
         mats, xs1 = synth.dense_layer()

@@ -25,6 +25,9 @@ from .workloads import (  # noqa: F401
     single_matrix,
     dense_layer,
     dense_layer_activations,
+    DECODE_CALLS,
+    DECODE_LAYERS,
+    decode_stack,
     prefill_set,
     moe_expert_bd,
     moe_expert,

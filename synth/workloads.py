@@ -41,6 +41,7 @@ WL_LAYER = 1
 WL_LAYER_SMALL_BATCH = 2
 WL_PREFILL = 3
 WL_MOE = 4
+WL_DECODE = 5
 
 DENSE_LAYER_SHAPES: List[Tuple[str, int, int]] = [
     ("q", 4096, 2560),
@@ -75,6 +76,9 @@ WORKLOADS: Dict[str, dict] = {
     "moe128_m512": dict(kind="moe", shapes=MOE_SHAPES, m=512),
     # the encoder (the step before the packed path): one gate-shaped matrix
     "encode_gate_bd7": dict(kind="encode", shapes=[("gate", 9728, 2560)], m=0, bd=7),
+    # one decode step's linears: 36 layers of the seven 4B-class matrices at
+    # batch 1, four dependent calls per layer, each layer its own matrices
+    "decode4b_36l": dict(kind="decode", shapes=DENSE_LAYER_SHAPES, m=1, layers=36),
 }
 
 
@@ -198,6 +202,30 @@ def dense_layer(seed: int = 0) -> Tuple[List[MatrixInputs], List[np.ndarray]]:
         mats.append(w)
         xs.append(make_activations(rng, 1, k))
     return mats, xs
+
+
+# The linear calls of one decoder layer in their data-dependence order:
+# indices into DENSE_LAYER_SHAPES of the matrices that share one input
+# (q/k/v read the attention input, o the attention output, gate/up the MLP
+# input, down the gated product).
+DECODE_CALLS: Tuple[Tuple[int, ...], ...] = ((0, 1, 2), (3,), (4, 5), (6,))
+DECODE_LAYERS = 36
+
+
+def decode_stack(layers: int = DECODE_LAYERS, seed: int = 0
+                 ) -> List[Tuple[List[MatrixInputs], List[np.ndarray]]]:
+    """Per layer: its seven matrices (bd drawn per matrix, distinct codes,
+    codebooks and permutations in every layer) and one batch-1 input per
+    call of DECODE_CALLS."""
+    stack = []
+    for layer in range(layers):
+        mats = [make_matrix(WL_DECODE, 7 * layer + j, f"l{layer}.{name}", n, k, bd=None,
+                            seed=seed)[0]
+                for j, (name, n, k) in enumerate(DENSE_LAYER_SHAPES)]
+        xs = [make_activations(_rng(WL_DECODE, 1000 + 4 * layer + c, seed), 1, mats[call[0]].k)
+              for c, call in enumerate(DECODE_CALLS)]
+        stack.append((mats, xs))
+    return stack
 
 
 def dense_layer_activations(m: int) -> List[np.ndarray]:
