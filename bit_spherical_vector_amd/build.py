@@ -26,6 +26,7 @@ SOURCES = [
     ("csrc/svq_prefill.hip", []),
     ("csrc/svq_small.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("csrc/svq_encode.hip", []),
+    ("csrc/svq_calib.hip", []),
 ]
 # kept for callers that list the flags of the exact-path kernels
 HIPCC_FLAGS = COMMON_FLAGS + ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]

@@ -32,6 +32,9 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
   for (int e = threadIdx.x; e < rows * 8; e += 256) s_tab[e] = a.cb[e];
   double *s_msq = s_tab + rows * 8;
   for (int e = threadIdx.x; e < a.n_mid; e += 256) s_msq[e] = a.msq[e];
+  double *s_rad = s_msq + a.n_mid;  // radius values, used for the error only
+  if (a.err)
+    for (int e = threadIdx.x; e <= a.n_mid; e += 256) s_rad[e] = a.rad[e];
   __syncthreads();
 
   const int64_t grp = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -94,6 +97,23 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
     uint32_t r = 0;
     for (int t = 0; t < a.n_mid; ++t) r += nsq[q] > s_msq[t] ? 1u : 0u;
     const uint64_t code = q < nq ? (uint64_t)(sg[q] | ((uint32_t)bi[q] << 8) | (r << (8 + a.bd))) : 0;
+    if (a.err && q < nq) {
+      // (v[l] - w_hat[l])^2 * h[channel], lanes in order; w_hat = +-R[r] D[d][l]
+      // is exact in double, v[l] = +-|v[l]| from the sign bit
+      const int64_t cq = c0 + q;
+      const int c = (int)(cq % C);
+      const double R = s_rad[r];
+      double e = 0.0;
+#pragma unroll
+      for (int l = 0; l < 8; ++l) {
+        const bool neg = (sg[q] >> l) & 1u;
+        const double wh = R * s_tab[bi[q] * 8 + l];
+        const double d = neg ? wh - av[q][l] : av[q][l] - wh;  // v - w_hat, sign folded
+        const double t = (d * d) * a.h[a.perm[8 * c + l]];
+        e = l == 0 ? t : e + t;
+      }
+      a.err[cq] = e;
+    }
     lo |= code << (18 * q);                   // code 3 keeps its low 10 bits here
     if (q == 3) hi = (uint32_t)(code >> 10);  // and its high 8 bits here
   }
@@ -106,7 +126,7 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
 
 hipError_t launch_encode(const EncArgs &a, hipStream_t s) {
   const int64_t groups = (a.count + ENC_CODES - 1) / ENC_CODES;
-  const size_t lds = ((size_t)(8 << a.bd) + (size_t)a.n_mid) * sizeof(double);
+  const size_t lds = ((size_t)(8 << a.bd) + 2 * (size_t)a.n_mid + 1) * sizeof(double);
   hipLaunchKernelGGL(svq_encode_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), lds, s, a);
   return hipGetLastError();
 }

@@ -657,6 +657,68 @@ svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts, const 
 
 }  // extern "C"
 
+namespace {
+
+// Encoder tables in double precision: the codebook (rows x 8), the squared
+// midpoints of consecutive radii and the radii.  Rejects a non-finite
+// codebook and radii that are not finite, >= 0 and strictly increasing.
+struct EncTables {
+  std::vector<double> cb, msq, rad;
+};
+
+svq_status enc_tables(int32_t bd, const uint16_t *codebook, const uint16_t *radius, EncTables &t) {
+  if (!codebook || !radius) return SVQ_ERR_INVALID_ARG;
+  if (bd < 6 || bd > 8) return SVQ_ERR_UNSUPPORTED;
+  const int rows = 1 << bd, nrad = 1 << (10 - bd);
+  t.cb.assign((size_t)rows * 8, 0.0);
+  t.msq.assign((size_t)nrad - 1, 0.0);
+  t.rad.assign((size_t)nrad, 0.0);
+  for (int e = 0; e < rows * 8; ++e) {
+    if (((codebook[e] >> 10) & 0x1F) == 0x1F) return SVQ_ERR_INVALID_ARG;
+    t.cb[(size_t)e] = (double)half_to_float(codebook[e]);
+  }
+  for (int r = 0; r < nrad; ++r) {
+    if (((radius[r] >> 10) & 0x1F) == 0x1F) return SVQ_ERR_INVALID_ARG;
+    t.rad[(size_t)r] = (double)half_to_float(radius[r]);
+    if (t.rad[(size_t)r] < 0.0 || (r > 0 && !(t.rad[(size_t)r] > t.rad[(size_t)r - 1])))
+      return SVQ_ERR_INVALID_ARG;
+  }
+  for (int r = 0; r + 1 < nrad; ++r) {
+    const double mid = (t.rad[(size_t)r] + t.rad[(size_t)r + 1]) / 2.0;  // exact (12 significant bits)
+    t.msq[(size_t)r] = mid * mid;                                         // exact (24 significant bits)
+  }
+  return SVQ_OK;
+}
+
+bool valid_perm(const int32_t *perm, int32_t k) {
+  std::vector<uint8_t> seen((size_t)k, 0);
+  for (int32_t p = 0; p < k; ++p) {
+    const int32_t c = perm[p];
+    if (c < 0 || c >= k || seen[(size_t)c]) return false;
+    seen[(size_t)c] = 1;
+  }
+  return true;
+}
+
+// device copies of one candidate's tables: codebook, squared midpoints, radii
+constexpr size_t ENC_TAB_BYTES = 256 * 8 * sizeof(double) + 2 * 16 * sizeof(double);
+
+hipError_t stage_tables(const EncTables &t, uint8_t *dst, EncArgs &a, hipStream_t s) {
+  const size_t cb = t.cb.size() * sizeof(double), ms = t.msq.size() * sizeof(double);
+  a.cb = (const double *)dst;
+  a.msq = (const double *)(dst + cb);
+  a.rad = (const double *)(dst + cb + ms);
+  a.n_mid = (int32_t)t.msq.size();
+  hipError_t e = hipMemcpyAsync(dst, t.cb.data(), cb, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(dst + cb, t.msq.data(), ms, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(dst + cb + ms, t.rad.data(), t.rad.size() * sizeof(double),
+                       hipMemcpyHostToDevice, s);
+  return e;
+}
+
+}  // namespace
+
 svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t bd,
                       const uint16_t *codebook, const uint16_t *radius, const int32_t *perm,
                       void *codes, void *workspace, size_t *workspace_bytes, void *stream) {
@@ -665,35 +727,12 @@ svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t
   if (bd < 6 || bd > 8) return SVQ_ERR_UNSUPPORTED;
   if (k > SVQ_MAX_K || n > SVQ_MAX_N) return SVQ_ERR_UNSUPPORTED;
   if (ldw < k) return SVQ_ERR_INVALID_ARG;
-  const int rows = 1 << bd, nrad = 1 << (10 - bd);
-  // tables: finite codebook; radii finite, >= 0, strictly increasing
-  std::vector<double> cb((size_t)rows * 8), msq((size_t)nrad - 1);
-  for (int e = 0; e < rows * 8; ++e) {
-    if (((codebook[e] >> 10) & 0x1F) == 0x1F) return SVQ_ERR_INVALID_ARG;
-    cb[(size_t)e] = (double)half_to_float(codebook[e]);
-  }
-  std::vector<double> R((size_t)nrad);
-  for (int t = 0; t < nrad; ++t) {
-    if (((radius[t] >> 10) & 0x1F) == 0x1F) return SVQ_ERR_INVALID_ARG;
-    R[(size_t)t] = (double)half_to_float(radius[t]);
-    if (R[(size_t)t] < 0.0 || (t > 0 && !(R[(size_t)t] > R[(size_t)t - 1]))) return SVQ_ERR_INVALID_ARG;
-  }
-  for (int t = 0; t + 1 < nrad; ++t) {
-    const double mid = (R[(size_t)t] + R[(size_t)t + 1]) / 2.0;  // exact (12 significant bits)
-    msq[(size_t)t] = mid * mid;                                   // exact (24 significant bits)
-  }
-  {
-    std::vector<uint8_t> seen((size_t)k, 0);
-    for (int32_t p = 0; p < k; ++p) {
-      const int32_t c = perm[p];
-      if (c < 0 || c >= k || seen[(size_t)c]) return SVQ_ERR_INVALID_ARG;
-      seen[(size_t)c] = 1;
-    }
-  }
-  const size_t cb_bytes = align256(cb.size() * sizeof(double));
-  const size_t msq_bytes = align256(msq.size() * sizeof(double));
-  const size_t perm_bytes = align256((size_t)k * sizeof(int32_t));
-  const size_t need = cb_bytes + msq_bytes + perm_bytes;
+  EncTables tab;
+  const svq_status st = enc_tables(bd, codebook, radius, tab);
+  if (st != SVQ_OK) return st;
+  if (!valid_perm(perm, k)) return SVQ_ERR_INVALID_ARG;
+  const size_t tab_bytes = align256(ENC_TAB_BYTES);
+  const size_t need = tab_bytes + align256((size_t)k * sizeof(int32_t));
   if (!workspace) {
     *workspace_bytes = need;
     return SVQ_OK;
@@ -702,26 +741,115 @@ svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t
   if (*workspace_bytes < need) return SVQ_ERR_BUFFER_TOO_SMALL;
   hipStream_t s = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
-  EncArgs a;
+  EncArgs a{};
   a.w = w;
   a.ldw = ldw;
   a.n = n;
   a.k = k;
   a.bd = bd;
-  a.n_mid = nrad - 1;
-  a.cb = (const double *)ws;
-  a.msq = (const double *)(ws + cb_bytes);
-  a.perm = (const int32_t *)(ws + cb_bytes + msq_bytes);
+  a.perm = (const int32_t *)(ws + tab_bytes);
   a.codes = (uint8_t *)codes;
   a.count = (int64_t)n * (k / 8);
-  hipError_t e = hipMemcpyAsync(ws, cb.data(), cb.size() * sizeof(double), hipMemcpyHostToDevice, s);
+  hipError_t e = stage_tables(tab, ws, a, s);
   if (e == hipSuccess)
-    e = hipMemcpyAsync(ws + cb_bytes, msq.data(), msq.size() * sizeof(double), hipMemcpyHostToDevice, s);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(ws + cb_bytes + msq_bytes, perm, (size_t)k * sizeof(int32_t), hipMemcpyHostToDevice, s);
+    e = hipMemcpyAsync(ws + tab_bytes, perm, (size_t)k * sizeof(int32_t), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = launch_encode(a, s);
   // the staged host arrays must outlive the copies
   const hipError_t e2 = hipStreamSynchronize(s);
   if (e == hipSuccess) e = e2;
   return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+}
+
+svq_status svq_esg_perm(const void *x, int64_t t, int64_t ldx, int32_t k, double *energy,
+                        int32_t *perm, void *workspace, size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes) return SVQ_ERR_INVALID_ARG;
+  if (k <= 0 || k % 8 != 0 || t < 1 || ldx < k || ldx % 8 != 0) return SVQ_ERR_INVALID_ARG;
+  if (k > SVQ_MAX_K) return SVQ_ERR_UNSUPPORTED;
+  const size_t need = align256((size_t)k * sizeof(int32_t));
+  if (!workspace) {
+    *workspace_bytes = need;
+    return SVQ_OK;
+  }
+  if (!x || !energy || !perm || ((uintptr_t)x & 15) != 0) return SVQ_ERR_INVALID_ARG;
+  if (*workspace_bytes < need) return SVQ_ERR_BUFFER_TOO_SMALL;
+  EsgArgs a;
+  a.x = (const uint16_t *)x;
+  a.t = t;
+  a.ldx = ldx;
+  a.k = k;
+  a.energy = energy;
+  a.rank = (int32_t *)workspace;
+  a.perm = perm;
+  return launch_esg(a, (hipStream_t)stream) == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+}
+
+svq_status svq_abs_select(const float *w, int64_t ldw, int32_t n, int32_t k, const double *h,
+                          const int32_t *perm, int32_t n_cand, const int32_t *bd,
+                          const uint16_t *const *codebooks, const uint16_t *const *radii,
+                          void *codes, int32_t *chosen, double *errors, void *workspace,
+                          size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes || !perm || !bd || !codebooks || !radii) return SVQ_ERR_INVALID_ARG;
+  if (n <= 0 || k <= 0 || k % 8 != 0 || ldw < k) return SVQ_ERR_INVALID_ARG;
+  if (n_cand < 1 || n_cand > 8) return SVQ_ERR_INVALID_ARG;
+  if (k > SVQ_MAX_K || n > SVQ_MAX_N) return SVQ_ERR_UNSUPPORTED;
+  std::vector<EncTables> tabs((size_t)n_cand);
+  for (int c = 0; c < n_cand; ++c) {
+    const svq_status st = enc_tables(bd[c], codebooks[c], radii[c], tabs[(size_t)c]);
+    if (st != SVQ_OK) return st;
+  }
+  if (!valid_perm(perm, k)) return SVQ_ERR_INVALID_ARG;
+  const int64_t count = (int64_t)n * (k / 8);
+  const size_t stream_bytes = (size_t)((count * 18 + 7) / 8);
+  const size_t tab_bytes = align256(ENC_TAB_BYTES), perm_bytes = align256((size_t)k * sizeof(int32_t));
+  const size_t codes_slot = align256(stream_bytes), err_bytes = align256((size_t)count * sizeof(double));
+  const size_t rows_bytes = align256((size_t)n_cand * (size_t)n * sizeof(double));
+  const size_t off_perm = (size_t)n_cand * tab_bytes, off_codes = off_perm + perm_bytes;
+  const size_t off_err = off_codes + (size_t)n_cand * codes_slot, off_rows = off_err + err_bytes;
+  const size_t off_tot = off_rows + rows_bytes, need = off_tot + align256(8 * sizeof(double));
+  if (!workspace) {
+    *workspace_bytes = need;
+    return SVQ_OK;
+  }
+  if (!w || !h || !codes || !chosen || !errors) return SVQ_ERR_INVALID_ARG;
+  if (*workspace_bytes < need) return SVQ_ERR_BUFFER_TOO_SMALL;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  hipError_t e = hipMemcpyAsync(ws + off_perm, perm, (size_t)k * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  for (int c = 0; c < n_cand && e == hipSuccess; ++c) {
+    EncArgs a{};
+    a.w = w;
+    a.ldw = ldw;
+    a.n = n;
+    a.k = k;
+    a.bd = bd[c];
+    a.perm = (const int32_t *)(ws + off_perm);
+    a.codes = ws + off_codes + (size_t)c * codes_slot;
+    a.count = count;
+    a.h = h;
+    a.err = (double *)(ws + off_err);  // reused: the row sums of c run before c + 1 is coded
+    e = stage_tables(tabs[(size_t)c], ws + (size_t)c * tab_bytes, a, s);
+    if (e == hipSuccess) e = launch_encode(a, s);
+    if (e == hipSuccess)
+      e = launch_abs_rows(a.err, n, k / 8, (double *)(ws + off_rows) + (size_t)c * n, s);
+  }
+  if (e == hipSuccess) e = launch_abs_totals((const double *)(ws + off_rows), n, n_cand,
+                                             (double *)(ws + off_tot), s);
+  double tot[8] = {0};
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(tot, ws + off_tot, (size_t)n_cand * sizeof(double), hipMemcpyDeviceToHost, s);
+  // the staged host tables must outlive the copies; the totals decide
+  const hipError_t e2 = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) return SVQ_ERR_HIP;
+  int best = 0;
+  for (int c = 1; c < n_cand; ++c)
+    if (tot[c] < tot[best]) best = c;
+  e = hipMemcpyAsync(codes, ws + off_codes + (size_t)best * codes_slot, stream_bytes,
+                     hipMemcpyDeviceToDevice, s);
+  const hipError_t e3 = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = e3;
+  if (e != hipSuccess) return SVQ_ERR_HIP;
+  *chosen = best;
+  for (int c = 0; c < n_cand; ++c) errors[c] = tot[c];
+  return SVQ_OK;
 }

@@ -225,8 +225,30 @@ struct EncArgs {
   const int32_t *perm;
   uint8_t *codes;  // canonical stream
   int64_t count;   // n * k / 8 codes
+  // optional activation-weighted reconstruction error of every code (err
+  // non-null): the radius values (float64, n_mid + 1) and the per-channel
+  // weights h [k]; err[g] for code g
+  const double *rad;
+  const double *h;
+  double *err;
 };
 hipError_t launch_encode(const EncArgs &a, hipStream_t s);
+
+// ---- calibration: ESG energies and permutation, ABS error sums -----------
+struct EsgArgs {
+  const uint16_t *x;  // bf16 [t][ldx], 16-byte aligned rows
+  int64_t t, ldx;
+  int32_t k;
+  double *energy;     // [k] out
+  int32_t *rank;      // [k] scratch
+  int32_t *perm;      // [k] out
+};
+hipError_t launch_esg(const EsgArgs &a, hipStream_t s);
+// rows[c * n + i] = sequential sum over the C codes of row i of err (per
+// candidate c, launched per candidate); totals[c] = sequential sum over rows
+hipError_t launch_abs_rows(const double *err, int32_t n, int32_t C, double *rows, hipStream_t s);
+hipError_t launch_abs_totals(const double *rows, int32_t n, int32_t n_cand, double *totals,
+                             hipStream_t s);
 
 // ---- MoE ----------------------------------------------------------------
 struct ExpertTable {

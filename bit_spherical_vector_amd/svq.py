@@ -34,7 +34,7 @@ SVQ_BF16 = 0
 SVQ_F32 = 1
 
 EXPORTED = ("svq_pack", "svq_linear", "svq_linear_batched", "svq_moe_linear",
-            "svq_encode", "svq_status_string")
+            "svq_encode", "svq_esg_perm", "svq_abs_select", "svq_status_string")
 
 
 class SvqError(RuntimeError):
@@ -99,6 +99,16 @@ def _load() -> ctypes.CDLL:
                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
                                ctypes.c_void_p]
+    lib.svq_esg_perm.restype = ctypes.c_int
+    lib.svq_esg_perm.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
+    lib.svq_abs_select.restype = ctypes.c_int
+    lib.svq_abs_select.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
     return lib
 
 
@@ -165,6 +175,35 @@ def svq_encode(w_ptr: Optional[int], ldw: int, n: int, k: int, bd: int, codebook
     st = LIB.svq_encode(w_ptr, ldw, n, k, bd, cb.ctypes.data, rad.ctypes.data, pm.ctypes.data,
                         codes_ptr, ws_ptr, ctypes.byref(nbytes), stream)
     return st, nbytes.value
+
+
+def svq_esg_perm(x_ptr: Optional[int], t: int, ldx: int, k: int, energy_ptr: Optional[int],
+                 perm_ptr: Optional[int], ws_ptr: Optional[int], ws_bytes: int,
+                 stream: int) -> tuple:
+    nbytes = ctypes.c_size_t(ws_bytes)
+    st = LIB.svq_esg_perm(x_ptr, t, ldx, k, energy_ptr, perm_ptr, ws_ptr, ctypes.byref(nbytes), stream)
+    return st, nbytes.value
+
+
+def svq_abs_select(w_ptr: Optional[int], ldw: int, n: int, k: int, h_ptr: Optional[int],
+                   perm: np.ndarray, candidates, codes_ptr: Optional[int], ws_ptr: Optional[int],
+                   ws_bytes: int, stream: int) -> tuple:
+    """candidates: sequence of (bd, codebook bits, radius bits) host arrays.
+    Returns (status, workspace bytes, chosen index, errors)."""
+    nc = len(candidates)
+    pm = np.ascontiguousarray(perm, dtype=np.int32)
+    bds = np.array([int(c[0]) for c in candidates] or [0], dtype=np.int32)
+    cbs = [np.ascontiguousarray(c[1], dtype=np.uint16) for c in candidates]
+    rads = [np.ascontiguousarray(c[2], dtype=np.uint16) for c in candidates]
+    cb_ptrs = (ctypes.c_void_p * max(nc, 1))(*[a.ctypes.data for a in cbs])
+    rad_ptrs = (ctypes.c_void_p * max(nc, 1))(*[a.ctypes.data for a in rads])
+    errs = np.zeros(max(nc, 1), dtype=np.float64)
+    chosen = ctypes.c_int32(-1)
+    nbytes = ctypes.c_size_t(ws_bytes)
+    st = LIB.svq_abs_select(w_ptr, ldw, n, k, h_ptr, pm.ctypes.data, nc, bds.ctypes.data, cb_ptrs,
+                            rad_ptrs, codes_ptr, ctypes.byref(chosen), errs.ctypes.data, ws_ptr,
+                            ctypes.byref(nbytes), stream)
+    return st, nbytes.value, chosen.value, errs[:nc]
 
 
 # ---------------------------------------------------------------------------
@@ -363,6 +402,46 @@ def moe_linear(pms: Sequence[PackedMatrix], x, expert_ids, topk: int, x_per_slot
                            workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
     _check(st, "svq_moe_linear")
     return out
+
+
+def esg_perm(x, stream=None):
+    """ESG channel energies (device float64 [k]) and permutation (device
+    int32 [k]) from device bf16 calibration activations [t, k]."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bfloat16 tensor with unit column stride")
+    t, k = x.shape
+    st, need = svq_esg_perm(None, t, x.stride(0), k, None, None, None, 0, 0)
+    _check(st, "svq_esg_perm (size query)")
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    energy = torch.empty(k, dtype=torch.float64, device=x.device)
+    perm = torch.empty(k, dtype=torch.int32, device=x.device)
+    st, _ = svq_esg_perm(x.data_ptr(), t, x.stride(0), k, energy.data_ptr(), perm.data_ptr(),
+                         ws.data_ptr(), need, _stream_handle(stream))
+    _check(st, "svq_esg_perm")
+    return energy, perm
+
+
+def abs_select(w, perm, h, candidates, stream=None):
+    """ABS over ``candidates`` [(bd, codebook bits, radius bits)] for a device
+    fp32 weight matrix [n, k] with host permutation ``perm`` and device
+    float64 channel weights ``h`` [k].  Returns (chosen index, errors as a
+    host float64 array, the chosen codes as a device uint8 stream)."""
+    import torch
+    if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D float32 tensor with unit column stride")
+    if h.dtype != torch.float64 or not h.is_contiguous():
+        raise ValueError("h must be a contiguous float64 tensor")
+    n, k = w.shape
+    st, need, _, _ = svq_abs_select(None, w.stride(0), n, k, None, perm, candidates, None, None, 0, 0)
+    _check(st, "svq_abs_select (size query)")
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+    codes = torch.zeros((n * (k // 8) * 18 + 7) // 8, dtype=torch.uint8, device=w.device)
+    st, _, chosen, errs = svq_abs_select(w.data_ptr(), w.stride(0), n, k, h.data_ptr(), perm,
+                                         candidates, codes.data_ptr(), ws.data_ptr(), need,
+                                         _stream_handle(stream))
+    _check(st, "svq_abs_select")
+    return chosen, errs, codes
 
 
 def encode(w, perm, bd: int, codebook, radius, stream=None):

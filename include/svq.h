@@ -198,6 +198,57 @@ svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t
                       const uint16_t *codebook, const uint16_t *radius, const int32_t *perm,
                       void *codes, void *workspace, size_t *workspace_bytes, void *stream);
 
+/* svq_esg_perm: Energy-Stratified Grouping -- the channel permutation of a
+ * matrix from calibration activations of its input (SAGE abstract and
+ * Fig. 2 caption: channel energies from calibration activations; every
+ * subvector takes channels from different energy tiers).  Readings:
+ *   energy[j] = (x[0][j]^2 + x[1][j]^2 + ... + x[t-1][j]^2) / t, in double
+ *               precision, token order, one division at the end;
+ *   ranks:      channels by decreasing energy, equal energies by increasing
+ *               index; tier l = ranks [l*k/8, (l+1)*k/8);
+ *   perm:       slot 8c + l <- the channel of rank l*(k/8) + c, so lane l
+ *               of every subvector comes from tier l (the svq_matrix_desc
+ *               gather convention: slot p reads channel perm[p]).
+ *   x:          device bf16 [t][ldx], t >= 1; x and ldx*2 16-byte aligned
+ *               (ldx a multiple of 8, ldx >= k); every value finite.
+ *   k:          a multiple of 8, at most the svq_pack limit.
+ *   energy:     device double [k], out.
+ *   perm:       device int32 [k], out.
+ *   workspace:  device scratch of at least *workspace_bytes bytes (4k), or
+ *               NULL to query the size.
+ * Asynchronous on `stream`.  Non-finite activations make the outputs
+ * undefined (perm stays a map into [0, k)). */
+svq_status svq_esg_perm(const void *x, int64_t t, int64_t ldx, int32_t k, double *energy,
+                        int32_t *perm, void *workspace, size_t *workspace_bytes, void *stream);
+
+/* svq_abs_select: Adaptive Bit Split -- encode one matrix under each
+ * candidate split and keep the one with the lowest activation-weighted
+ * reconstruction error (SAGE abstract and Fig. 2 caption).  Every candidate
+ * is coded by the svq_encode rule; its error is
+ *   sum over rows i (row order) of
+ *     sum over subvectors c (code order) of
+ *       sum over lanes l (lane order) of (v[l] - w_hat[l])^2 * h[perm[8c+l]]
+ * with v[l] = w[i][perm[8c + l]] and w_hat the decoded weight, all in
+ * double precision without fused multiply-adds.  The first candidate with
+ * the smallest error wins.
+ *   w, ldw, n, k, perm:  as for svq_encode (perm on the host).
+ *   h:          device double [k]: the weight of input channel j (e.g. the
+ *               ESG energy raised to an exponent), finite, >= 0.
+ *   n_cand:     1..8 candidates: bd[c] (6..8), codebooks[c] and radii[c]
+ *               (host tables as for svq_encode).
+ *   codes:      device, out: the chosen candidate's code stream.
+ *   chosen:     host, out: index of the chosen candidate.
+ *   errors:     host, out: the error of every candidate [n_cand].
+ *   workspace:  device scratch of at least *workspace_bytes bytes (tables,
+ *               every candidate's codes and errors), or NULL to query.
+ * Validates every host argument before any device work, then synchronizes
+ * `stream` (the choice is made on the host from the device totals). */
+svq_status svq_abs_select(const float *w, int64_t ldw, int32_t n, int32_t k, const double *h,
+                          const int32_t *perm, int32_t n_cand, const int32_t *bd,
+                          const uint16_t *const *codebooks, const uint16_t *const *radii,
+                          void *codes, int32_t *chosen, double *errors, void *workspace,
+                          size_t *workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *svq_status_string(svq_status s);
 

@@ -23,7 +23,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol():
     declared = _declared_functions()
     assert set(declared) == {"svq_pack", "svq_linear", "svq_linear_batched", "svq_moe_linear",
-                             "svq_encode", "svq_status_string"}
+                             "svq_encode", "svq_esg_perm", "svq_abs_select",
+                             "svq_status_string"}
     for name in declared:
         assert hasattr(svq.LIB, name), name
     assert set(declared) == set(svq.EXPORTED)
@@ -307,7 +308,8 @@ def test_encode_workspace_query_and_validation():
     cb, rad, perm = mat.codebook, mat.radius, mat.perm
     a = lambda v: (v + 255) // 256 * 256
     st, need = svq.svq_encode(None, 64, 16, 64, 7, cb, rad, perm, None, None, 0, 0)
-    assert st == svq.SVQ_OK and need == a(128 * 8 * 8) + a(7 * 8) + a(64 * 4)
+    # every table slot is sized for bd = 8 (codebook 256 x 8, 16 radii, 15 midpoints)
+    assert st == svq.SVQ_OK and need == a(256 * 8 * 8 + 2 * 16 * 8) + a(64 * 4)
     q = lambda **kw: svq.svq_encode(kw.get("w"), kw.get("ldw", 64), kw.get("n", 16), kw.get("k", 64),
                                     kw.get("bd", 7), kw.get("cb", cb), kw.get("rad", rad),
                                     kw.get("perm", perm), kw.get("codes"), kw.get("ws"),
@@ -330,3 +332,47 @@ def test_encode_workspace_query_and_validation():
     assert q(ws=0x1000, wsb=1 << 20) == svq.SVQ_ERR_INVALID_ARG
     assert q(w=0x2000, codes=0x3000, ws=0x1000, wsb=100) == svq.SVQ_ERR_BUFFER_TOO_SMALL
 
+
+
+def test_esg_workspace_query_and_validation():
+    a = lambda v: (v + 255) // 256 * 256
+    q = lambda **kw: svq.svq_esg_perm(kw.get("x"), kw.get("t", 100), kw.get("ldx", 64),
+                                      kw.get("k", 64), kw.get("e"), kw.get("p"), kw.get("ws"),
+                                      kw.get("wsb", 0), 0)
+    st, need = q()
+    assert st == svq.SVQ_OK and need == a(64 * 4)
+    assert q(k=60)[0] == svq.SVQ_ERR_INVALID_ARG        # k not a multiple of 8
+    assert q(t=0)[0] == svq.SVQ_ERR_INVALID_ARG         # no calibration token
+    assert q(ldx=32)[0] == svq.SVQ_ERR_INVALID_ARG      # ldx < k
+    assert q(ldx=68)[0] == svq.SVQ_ERR_INVALID_ARG      # rows not 16-byte aligned
+    assert q(ws=0x1000, wsb=1 << 20)[0] == svq.SVQ_ERR_INVALID_ARG        # no x / outputs
+    assert q(x=0x2008, e=0x3000, p=0x4000, ws=0x1000, wsb=1 << 20)[0] == svq.SVQ_ERR_INVALID_ARG
+    assert q(x=0x2000, e=0x3000, p=0x4000, ws=0x1000, wsb=8)[0] == svq.SVQ_ERR_BUFFER_TOO_SMALL
+
+
+def test_abs_workspace_query_and_validation():
+    import synth
+    cands = [(bd, m.codebook, m.radius) for bd, m in
+             ((bd, synth.random_matrix(16, 64, bd, seed=(46, bd, 0))) for bd in (6, 7, 8))]
+    perm = synth.random_matrix(16, 64, 7, seed=(46, 7, 0)).perm
+    a = lambda v: (v + 255) // 256 * 256
+    q = lambda **kw: svq.svq_abs_select(kw.get("w"), kw.get("ldw", 64), kw.get("n", 16),
+                                        kw.get("k", 64), kw.get("h"), kw.get("perm", perm),
+                                        kw.get("cands", cands), kw.get("codes"), kw.get("ws"),
+                                        kw.get("wsb", 0), 0)
+    st, need, _, _ = q()
+    count = 16 * 8
+    tab = a(256 * 8 * 8 + 2 * 16 * 8)
+    assert st == svq.SVQ_OK
+    assert need == 3 * tab + a(64 * 4) + 3 * a(count * 18 // 8) + a(count * 8) + a(3 * 16 * 8) + a(64)
+    assert q(cands=[])[0] == svq.SVQ_ERR_INVALID_ARG
+    assert q(cands=cands * 3)[0] == svq.SVQ_ERR_INVALID_ARG          # more than 8
+    assert q(cands=[(5,) + cands[0][1:]])[0] == svq.SVQ_ERR_UNSUPPORTED
+    bad = np.asarray(cands[1][2]).copy()[::-1]
+    assert q(cands=[cands[0], (7, cands[1][1], bad)])[0] == svq.SVQ_ERR_INVALID_ARG
+    bad_perm = np.asarray(perm).copy()
+    bad_perm[0] = bad_perm[1]
+    assert q(perm=bad_perm)[0] == svq.SVQ_ERR_INVALID_ARG
+    assert q(ldw=8)[0] == svq.SVQ_ERR_INVALID_ARG
+    assert q(ws=0x1000, wsb=1 << 20)[0] == svq.SVQ_ERR_INVALID_ARG    # no w, h, codes
+    assert q(w=0x2000, h=0x3000, codes=0x4000, ws=0x1000, wsb=64)[0] == svq.SVQ_ERR_BUFFER_TOO_SMALL
