@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--workload", default="layer4b_m1",
                     choices=["layer4b_m1", "layer4b_m4", "layer4b_m16", "single_512x1024_m1",
                              "prefill_m2048", "moe128_m1", "moe128_m512", "encode_gate_bd7",
-                             "decode4b_36l"])
+                             "decode4b_36l", "esg_calib_t2048_k2560", "abs_gate_3splits"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
@@ -433,6 +433,104 @@ def bench_decode(args, wl, svq, synth, dev):
     print(json.dumps(out), flush=True)
 
 
+def _timed(args, stream, fn):
+    """Mean milliseconds of fn() over args.steps calls after args.warmup,
+    between HIP events on the launch stream."""
+    import torch
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / args.steps
+
+
+def bench_calib(args, wl, svq, synth, stream):
+    """The calibration steps before encoding.  ESG: channel energies and the
+    tiered permutation of 2048 synthetic calibration tokens (the activation
+    recipe of the dense workloads) over the 2560 input channels of the
+    q/k/v and gate/up matrices; value = activation bytes per second.  ABS:
+    the three direction/radius splits of one 9728 x 2560 gate matrix coded
+    and scored with h = the ESG energies of those tokens (one call codes all
+    three and synchronizes); value = candidate codes per second."""
+    import numpy as np
+    import torch
+
+    t, k = 2048, 2560
+    x = synth.random_activations(t, k, seed=(80, 0, 0))
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    if wl["kind"] == "esg":
+        ms = _timed(args, stream, lambda: svq.esg_perm(xd, stream))
+        nbytes = t * k * 2
+        value = nbytes / (ms * 1e-3) / 1e9
+        metric, unit = "ESG calibration GB/s (activation bytes)", "GB/s"
+        roof = {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None}
+        cpu = None
+        if not args.no_cpu_baseline:
+            from oracle import svq_calib as sc
+            t0 = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t0 < 10.0:
+                sc.esg_perm(sc.esg_energy(x))
+                reps += 1
+            dt = time.perf_counter() - t0
+            cpu = {"value": round(reps * nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": 1,
+                   "kind": "oracle", "sample": f"{reps} full run(s) of the workload, {dt:.1f} s"}
+        dtype, config = "f64 (energies), int32 (ranks)", {"workload": args.workload, "tokens": t, "k": k}
+        launches = 3
+    else:
+        energy, perm_d = svq.esg_perm(xd, stream)
+        perm = perm_d.cpu().numpy()
+        n = 9728
+        gen = torch.Generator(device="cuda").manual_seed(80)
+        w = torch.randn((n, k), device="cuda", generator=gen) * 0.05
+        cands = [(bd, m.codebook, m.radius) for bd, m in
+                 ((bd, synth.random_matrix(8, k, bd, seed=(80, bd, 1))) for bd in wl["bds"])]
+        ms = _timed(args, stream, lambda: svq.abs_select(w, perm, energy, cands, stream))
+        ncodes = n * (k // 8)
+        value = ncodes * len(cands) / (ms * 1e-3) / 1e6
+        metric, unit = "ABS candidate Mcodes/s (3 splits)", "Mcodes/s"
+        # fp64 operations per code: 2^bd scores and the squared norm (15
+        # each) and the weighted error (8 lanes x 4)
+        flops = sum(ncodes * (((1 << bd) + 1) * 15.0 + 32.0) for bd, _, _ in cands)
+        achieved = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": FP64_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP64_VALU_PEAK_TFLOPS, 4),
+                "traffic": None}
+        cpu = None
+        if not args.no_cpu_baseline:
+            from oracle import svq_calib as sc
+            rows = 32
+            w_rows = w[:rows].cpu().numpy()
+            h = energy.cpu().numpy()
+            t0 = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t0 < 10.0:
+                sc.abs_select(w_rows, perm, h, cands)
+                reps += 1
+            dt = time.perf_counter() - t0
+            cpu = {"value": round(reps * rows * (k // 8) * len(cands) / dt / 1e6, 5),
+                   "unit": "Mcodes/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{reps} run(s) over {rows} of {n} rows, 3 splits, {dt:.1f} s"}
+        dtype, config = "f64", {"workload": args.workload, "n": n, "k": k,
+                                "splits": list(wl["bds"])}
+        launches = 3 * 2 + 1
+    config["launches_per_step"] = launches
+    out = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded activations, weights, codebooks, radii)",
+        "config": config, "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -458,6 +556,8 @@ def main():
         return bench_encode(args, wl, svq, synth, stream)
     if wl["kind"] == "decode":
         return bench_decode(args, wl, svq, synth, dev)
+    if wl["kind"] in ("esg", "abs"):
+        return bench_calib(args, wl, svq, synth, stream)
 
     if args.workload.startswith("layer4b"):
         mats, xs1 = synth.dense_layer()

@@ -14,10 +14,12 @@
 // The energies decide an integer result (the permutation), so their
 // arithmetic is fixed: one float64 chain per channel in token order.  The
 // chain, not the memory, bounds the energy kernel; a block stages a tile of
-// 256 tokens x 32 channels in LDS (all 256 threads load, 16 bytes each)
-// while 32 threads run the chains over the previous tile.  Ranks are counts
+// 1024 tokens x 32 channels in LDS (all 256 threads load, 16 bytes at a
+// time) while 32 threads run the chains over the previous tile.  Ranks are counts
 // of strictly larger energies (ties: lower index first), accumulated with
-// integer atomics (order independent), so the permutation is exact.
+// integer atomics (order independent), so the permutation is exact.  The
+// error sums of ABS are chains too (lanes, codes of a row, rows), each
+// staged through LDS so that only the additions wait on one another.
 #include "svq_device.h"
 #include "../../include/svq.h"
 
@@ -26,8 +28,9 @@ namespace svq {
 #pragma clang fp contract(off)
 
 constexpr int ESG_CH = 32;       // channels per block
-constexpr int ESG_TOK = 256;     // tokens per staged tile
-constexpr int ESG_SPAN = 1024;   // energies compared per rank block
+constexpr int ESG_TOK = 1024;    // tokens per staged tile (64 KB)
+constexpr int ESG_LD = ESG_TOK / 64;  // 16-byte loads per thread and tile
+constexpr int ESG_SPAN = 256;    // energies compared per rank block
 
 __global__ __launch_bounds__(256) void esg_energy_kernel(EsgArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[ESG_TOK][ESG_CH];
@@ -36,10 +39,10 @@ __global__ __launch_bounds__(256) void esg_energy_kernel(EsgArgs a) {
   const int g = tid & 3, tr = tid >> 2;  // 8-channel group, token row 0..63
   const bool gok = c0 + 8 * g < a.k;     // k % 8 == 0: a group is all in or all out
   const int64_t T = a.t;
-  u4 nx[4];
+  u4 nx[ESG_LD];
   auto load = [&](int64_t t0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < ESG_LD; ++q) {
       const int64_t t = t0 + tr + 64 * q;
       u4 v = {0u, 0u, 0u, 0u};
       if (gok && t < T) v = *(const u4 *)(a.x + t * a.ldx + c0 + 8 * g);
@@ -51,12 +54,25 @@ __global__ __launch_bounds__(256) void esg_energy_kernel(EsgArgs a) {
   for (int64_t t0 = 0; t0 < T; t0 += ESG_TOK) {
     __syncthreads();  // the chains over the previous tile are done
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *(u4 *)&tile[tr + 64 * q][8 * g] = nx[q];
+    for (int q = 0; q < ESG_LD; ++q) *(u4 *)&tile[tr + 64 * q][8 * g] = nx[q];
     __syncthreads();
     if (t0 + ESG_TOK < T) load(t0 + ESG_TOK);
     if (tid < ESG_CH) {
       const int nt = (int)min((int64_t)ESG_TOK, T - t0);
-      for (int i = 0; i < nt; ++i) {
+      int i = 0;
+      // eight tokens at a time: the LDS reads and squares are independent,
+      // only the additions form the chain
+      for (; i + 8 <= nt; i += 8) {
+        double sq[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const double v = (double)bf16_bits_to_f32(tile[i + u][tid]);
+          sq[u] = v * v;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = acc + sq[u];
+      }
+      for (; i < nt; ++i) {
         const double v = (double)bf16_bits_to_f32(tile[i][tid]);
         acc = acc + v * v;
       }
@@ -68,20 +84,33 @@ __global__ __launch_bounds__(256) void esg_energy_kernel(EsgArgs a) {
   }
 }
 
-// rank[j] += #{i in this block's span: e_i > e_j, or e_i == e_j and i < j}
+// rank[j] += #{i in this block's span: e_i > e_j, or e_i == e_j and i < j}.
+// Energies are sums of squares divided by t: non-negative, so (for finite
+// values) their bit patterns order like the values and the tie rule becomes
+// one integer comparison of (bits, -index) keys.
 __global__ __launch_bounds__(256) void esg_count_kernel(EsgArgs a) {
-  __shared__ double s_e[ESG_SPAN];
+  __shared__ __attribute__((aligned(16))) uint64_t s_e[ESG_SPAN];
   const int i0 = blockIdx.y * ESG_SPAN;
-  for (int e = threadIdx.x; e < ESG_SPAN; e += 256) s_e[e] = i0 + e < a.k ? a.energy[i0 + e] : 0.0;
+  const uint64_t *bits = (const uint64_t *)a.energy;
+  // entries past the end are never read (hi stops at k - i0)
+  for (int e = threadIdx.x; e < ESG_SPAN; e += 256) s_e[e] = i0 + e < a.k ? bits[i0 + e] : 0;
   __syncthreads();
   const int j = blockIdx.x * 64 + (threadIdx.x & 63);
   if (j >= a.k) return;
-  const double ej = a.energy[j];
+  const uint64_t ej = bits[j];
   const int lo = (threadIdx.x >> 6) * (ESG_SPAN / 4);
   const int hi = min(lo + ESG_SPAN / 4, a.k - i0);
   int cnt = 0;
-  for (int e = lo; e < hi; ++e) {
-    const double ei = s_e[e];
+  int e = lo;
+  for (; e + 8 <= hi; e += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint64_t ei = s_e[e + u];
+      cnt += (ei > ej || (ei == ej && i0 + e + u < j)) ? 1 : 0;
+    }
+  }
+  for (; e < hi; ++e) {
+    const uint64_t ei = s_e[e];
     cnt += (ei > ej || (ei == ej && i0 + e < j)) ? 1 : 0;
   }
   if (cnt) atomicAdd(a.rank + j, cnt);
@@ -105,15 +134,34 @@ hipError_t launch_esg(const EsgArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// rows[i] = err[i][0] + err[i][1] + ... (code order)
+// rows[i] = err[i][0] + err[i][1] + ... (code order).  A block takes 64
+// rows; their errors pass through LDS 32 codes at a time (coalesced reads
+// by all 256 threads), and one thread per row runs the chain.
+constexpr int ABS_ROWS = 64, ABS_CODES = 32;
 __global__ __launch_bounds__(256) void abs_rows_kernel(const double *err, int32_t n, int32_t C,
                                                        double *rows) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const double *e = err + (int64_t)i * C;
-  double r = e[0];
-  for (int c = 1; c < C; ++c) r = r + e[c];
-  rows[i] = r;
+  __shared__ double s_e[ABS_ROWS][ABS_CODES + 1];
+  const int r0 = blockIdx.x * ABS_ROWS;
+  const int i = r0 + (int)threadIdx.x;
+  double r = 0.0;
+  for (int c0 = 0; c0 < C; c0 += ABS_CODES) {
+    const int nc = min(ABS_CODES, C - c0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < ABS_ROWS * ABS_CODES; e += 256) {
+      const int rr = e / ABS_CODES, cc = e % ABS_CODES;
+      if (r0 + rr < n && cc < nc) s_e[rr][cc] = err[(int64_t)(r0 + rr) * C + c0 + cc];
+    }
+    __syncthreads();
+    if (threadIdx.x < ABS_ROWS && i < n) {
+      int c = 0;
+      if (c0 == 0) {
+        r = s_e[threadIdx.x][0];
+        c = 1;
+      }
+      for (; c < nc; ++c) r = r + s_e[threadIdx.x][c];
+    }
+  }
+  if (threadIdx.x < ABS_ROWS && i < n) rows[i] = r;
 }
 
 // totals[c] = 0 + rows[c][0] + rows[c][1] + ... (row order), one block per
@@ -129,15 +177,24 @@ __global__ __launch_bounds__(256) void abs_totals_kernel(const double *rows, int
     __syncthreads();
     for (int e = threadIdx.x; e < cnt; e += 256) s_r[e] = r[i0 + e];
     __syncthreads();
-    if (threadIdx.x == 0)
-      for (int e = 0; e < cnt; ++e) tot = tot + s_r[e];
+    if (threadIdx.x == 0) {
+      int e = 0;
+      for (; e + 8 <= cnt; e += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = s_r[e + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tot = tot + v[u];
+      }
+      for (; e < cnt; ++e) tot = tot + s_r[e];
+    }
   }
   if (threadIdx.x == 0) totals[blockIdx.x] = tot;
 }
 
 hipError_t launch_abs_rows(const double *err, int32_t n, int32_t C, double *rows, hipStream_t s) {
-  hipLaunchKernelGGL(abs_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, err, n, C,
-                     rows);
+  hipLaunchKernelGGL(abs_rows_kernel, dim3((unsigned)((n + ABS_ROWS - 1) / ABS_ROWS)), dim3(256), 0, s,
+                     err, n, C, rows);
   return hipGetLastError();
 }
 

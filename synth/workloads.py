@@ -76,6 +76,10 @@ WORKLOADS: Dict[str, dict] = {
     "moe128_m512": dict(kind="moe", shapes=MOE_SHAPES, m=512),
     # the encoder (the step before the packed path): one gate-shaped matrix
     "encode_gate_bd7": dict(kind="encode", shapes=[("gate", 9728, 2560)], m=0, bd=7),
+    # calibration before encoding: ESG over 2048 tokens of the 2560-wide
+    # layer input; ABS over the three splits of one gate-shaped matrix
+    "esg_calib_t2048_k2560": dict(kind="esg", shapes=[("x", 2048, 2560)], m=2048),
+    "abs_gate_3splits": dict(kind="abs", shapes=[("gate", 9728, 2560)], m=0, bds=(6, 7, 8)),
     # one decode step's linears: 36 layers of the seven 4B-class matrices at
     # batch 1, four dependent calls per layer, each layer its own matrices
     "decode4b_36l": dict(kind="decode", shapes=DENSE_LAYER_SHAPES, m=1, layers=36),
