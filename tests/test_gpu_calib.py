@@ -32,14 +32,16 @@ def _x_dev(bits, pad=0):
 
 
 ESG_SHAPES = [
-    # t, k, row padding: one token and one subvector; ragged tiles of tokens
-    # (300 = 256 + 44) and channels (1032 = 32 * 32 + 8); strided rows; the
-    # gate/up input width with a calibration batch of 2048 tokens; the down
-    # input width (ranks across ten 1024-channel spans)
+    # t, k, row padding: one token and one subvector; a partial token tile
+    # (300, 257 of 1024) and a ragged channel block (1032 = 32 * 32 + 8);
+    # strided rows; the gate/up input width with 2048 calibration tokens
+    # (two full tiles); a full tile and a ragged second one; the down input
+    # width (ranks across 38 spans of 256 channels)
     (1, 8, 0),
     (300, 64, 0),
     (257, 1032, 8),
     (2048, 2560, 0),
+    (1100, 520, 0),
     (64, 9728, 0),
 ]
 
@@ -132,3 +134,19 @@ def test_abs_full_size_gate(svq):
     all_codes = so.unpack_codes(codes.cpu().numpy(), n, k)
     w_rows = wd[torch.from_numpy(rows).cuda()].cpu().numpy()
     assert np.array_equal(all_codes[rows], se.encode_matrix(w_rows, perm, bd, cb, rad))
+
+
+def test_abs_equal_candidates_pick_the_first(svq):
+    """The same split listed three times: equal errors, index 0 chosen
+    (first of equal smallest errors), codes equal to the oracle's."""
+    n, k = 16, 256
+    mat = synth.random_matrix(8, k, 7, seed=(75, 7, 0))
+    w = np.random.default_rng(75).standard_normal((n, k)).astype(np.float32) * 0.05
+    h = np.random.default_rng(76).exponential(size=k)
+    c = (7, mat.codebook, mat.radius)
+    chosen, errs, codes = svq.abs_select(torch.from_numpy(w).cuda(), mat.perm,
+                                         torch.from_numpy(h).cuda(), [c, c, c])
+    torch.cuda.synchronize()
+    c_ref, e_ref, codes_ref = sc.abs_select(w, mat.perm, h, [c, c, c])
+    assert chosen == 0 == c_ref and np.array_equal(errs, e_ref) and errs[0] == errs[1] == errs[2]
+    assert np.array_equal(codes.cpu().numpy(), so.pack_codes(codes_ref[0]))
