@@ -39,22 +39,34 @@ COLD_BYTES = 600 << 20  # > 2 x 256 MB MALL
 # by what the same counter reads for a plain 256 MiB device copy in the same
 # run (--copy-calibration): FETCH_SIZE reads half of the bytes a copy moves
 # (factor 2.0), WRITE_SIZE all of them (factor 1.0).  Commands and raw
-# figures: profiles/gemv_fused_kernel_layer4b_m1_counters.md.  An entry
-# only holds for the kernel source it was taken on (sha256 prefix below);
-# after any change of that source the traffic is reported as null.
+# figures: profiles/*_counters.md.  An entry only holds for the kernel
+# sources it was taken on (sha256 prefix below); after any change of those
+# sources the traffic is reported as null.
 TRAFFIC = {
-    "layer4b_m1": {"kernel_src_sha256": "64866f994be825d4",
+    # gemv_fused_kernel
+    "layer4b_m1": {"sources": ("svq_kernels.hip", "svq_device.h"),
+                   "kernel_src_sha256": "64866f994be825d4",
                    "fetch_kib": 14681.7, "fetch_factor": 2.0,
                    "write_kib": 60.0, "write_factor": 1.0},
+    # sb_gemm_kernel (profiles/sb_gemm_kernel_layer4b_m16_counters.md)
+    "layer4b_m16": {"sources": ("svq_small.hip", "svq_device.h"),
+                    "kernel_src_sha256": "ec5b0394a978c884",
+                    "fetch_kib": 17226.6, "fetch_factor": 2.0,
+                    "write_kib": 1604.0, "write_factor": 1.0},
+    # prefill_w8_kernel (profiles/prefill_w8_kernel_prefill_m2048_counters.md)
+    "prefill_m2048": {"sources": ("svq_prefill.hip", "svq_device.h"),
+                      "kernel_src_sha256": "ccd321bb9ce02b7f",
+                      "fetch_kib": 127740.6, "fetch_factor": 2.0,
+                      "write_kib": 88064.0, "write_factor": 1.0},
 }
 
 
-def kernel_source_hash() -> str:
-    """sha256 prefix of the exact-path kernel sources (translation unit and
-    the device header it includes)."""
+def kernel_source_hash(sources=("svq_kernels.hip", "svq_device.h")) -> str:
+    """sha256 prefix of a kernel's sources (translation unit and the device
+    header it includes)."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("svq_kernels.hip", "svq_device.h"):
+    for name in sources:
         with open(os.path.join(ROOT, "bit_spherical_vector_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -62,7 +74,7 @@ def kernel_source_hash() -> str:
 
 def traffic_bytes(workload):
     t = TRAFFIC.get(workload)
-    if t is None or t["kernel_src_sha256"] != kernel_source_hash():
+    if t is None or t["kernel_src_sha256"] != kernel_source_hash(t["sources"]):
         return None
     return int(round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024))
 
