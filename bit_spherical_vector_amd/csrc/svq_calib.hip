@@ -134,24 +134,36 @@ hipError_t launch_esg(const EsgArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// rows[i] = err[i][0] + err[i][1] + ... (code order).  A block takes 64
-// rows; their errors pass through LDS 32 codes at a time (coalesced reads
-// by all 256 threads), and one thread per row runs the chain.
-constexpr int ABS_ROWS = 64, ABS_CODES = 32;
+// rows[i] = err[i][0] + err[i][1] + ... (code order).  A block takes 32
+// rows; their errors pass through LDS 64 codes at a time (all 256 threads
+// load, the next chunk in flight while the current one is summed), and one
+// thread per row runs the chain.
+constexpr int ABS_ROWS = 32, ABS_CODES = 64, ABS_LD = ABS_ROWS * ABS_CODES / 256;
 __global__ __launch_bounds__(256) void abs_rows_kernel(const double *err, int32_t n, int32_t C,
                                                        double *rows) {
   __shared__ double s_e[ABS_ROWS][ABS_CODES + 1];
   const int r0 = blockIdx.x * ABS_ROWS;
   const int i = r0 + (int)threadIdx.x;
+  double nx[ABS_LD];
+  auto load = [&](int c0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < ABS_LD; ++q) {
+      const int e = (int)threadIdx.x + 256 * q, rr = e / ABS_CODES, cc = e % ABS_CODES;
+      nx[q] = (r0 + rr < n && c0 + cc < C) ? err[(int64_t)(r0 + rr) * C + c0 + cc] : 0.0;
+    }
+  };
+  load(0);
   double r = 0.0;
   for (int c0 = 0; c0 < C; c0 += ABS_CODES) {
     const int nc = min(ABS_CODES, C - c0);
-    __syncthreads();
-    for (int e = threadIdx.x; e < ABS_ROWS * ABS_CODES; e += 256) {
-      const int rr = e / ABS_CODES, cc = e % ABS_CODES;
-      if (r0 + rr < n && cc < nc) s_e[rr][cc] = err[(int64_t)(r0 + rr) * C + c0 + cc];
+    __syncthreads();  // the chains over the previous chunk are done
+#pragma unroll
+    for (int q = 0; q < ABS_LD; ++q) {
+      const int e = (int)threadIdx.x + 256 * q;
+      s_e[e / ABS_CODES][e % ABS_CODES] = nx[q];
     }
     __syncthreads();
+    if (c0 + ABS_CODES < C) load(c0 + ABS_CODES);
     if (threadIdx.x < ABS_ROWS && i < n) {
       int c = 0;
       if (c0 == 0) {
