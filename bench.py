@@ -89,6 +89,8 @@ def parse():
                              "prefill_m2048", "moe128_m1", "moe128_m512", "encode_gate_bd7",
                              "decode4b_36l", "esg_calib_t2048_k2560", "abs_gate_3splits"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only measure plain device copy and read rates (context for the HBM peak)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -543,12 +545,42 @@ def bench_calib(args, wl, svq, synth, stream):
     print(json.dumps(out), flush=True)
 
 
+def stream_ceiling():
+    """Rates of plain torch kernels over 2 GiB buffers, far beyond the
+    caches: a device-to-device copy (read + write bytes) and a sum (read
+    bytes).  Context for the published 8 TB/s; fractions always use the
+    published peak."""
+    import torch
+    n = 2 << 30
+    a = torch.ones(n // 8, dtype=torch.int64, device="cuda")
+    b = torch.empty_like(a)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for name, fn, nbytes in (("copy_read_write", lambda: b.copy_(a), 2 * n),
+                             ("sum_read", lambda: a.sum(), n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(10):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        out[name] = {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4)}
+    print(json.dumps({"stream_ceiling": out, "bytes": n, "peak_GB/s": HBM_PEAK_GBS}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path does not "
               "shard across GPUs in this build", file=sys.stderr)
         sys.exit(2)
+
+    if args.stream_ceiling:
+        return stream_ceiling()
 
     import numpy as np
     import torch
