@@ -376,3 +376,22 @@ def test_abs_workspace_query_and_validation():
     assert q(ldw=8)[0] == svq.SVQ_ERR_INVALID_ARG
     assert q(ws=0x1000, wsb=1 << 20)[0] == svq.SVQ_ERR_INVALID_ARG    # no w, h, codes
     assert q(w=0x2000, h=0x3000, codes=0x4000, ws=0x1000, wsb=64)[0] == svq.SVQ_ERR_BUFFER_TOO_SMALL
+
+
+def test_calibration_wrappers_reject_bad_tensors_before_any_device_work():
+    """The binding checks dtypes and layouts on the host (CPU tensors here:
+    nothing reaches the library or the device)."""
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        svq.esg_perm(torch.zeros((4, 8), dtype=torch.float32))          # not bf16
+    with pytest.raises(ValueError):
+        svq.esg_perm(torch.zeros((8, 4), dtype=torch.bfloat16).t())     # column stride != 1
+    w = torch.zeros((4, 8), dtype=torch.float32)
+    h = torch.zeros(8, dtype=torch.float64)
+    perm = np.arange(8, dtype=np.int32)
+    with pytest.raises(ValueError):
+        svq.abs_select(w.double(), perm, h, [])                          # weights not fp32
+    with pytest.raises(ValueError):
+        svq.abs_select(w, perm, h.float(), [])                           # h not fp64
+    with pytest.raises(ValueError):
+        svq.abs_select(w, perm, torch.zeros(16, dtype=torch.float64)[::2], [])  # h strided
