@@ -13,9 +13,10 @@
 //
 // The energies decide an integer result (the permutation), so their
 // arithmetic is fixed: one float64 chain per channel in token order.  The
-// chain, not the memory, bounds the energy kernel; a block stages a tile of
-// 1024 tokens x 32 channels in LDS (all 256 threads load, 16 bytes at a
-// time) while 32 threads run the chains over the previous tile.  Ranks are counts
+// chain, not the memory, bounds the energy kernel; all 256 threads of a
+// block load a tile of 256 tokens x 32 channels (16 bytes at a time, the
+// next tile in flight) and store its squares in LDS as doubles, and 32
+// threads run the chains of additions over them.  Ranks are counts
 // of strictly larger energies (ties: lower index first), accumulated with
 // integer atomics (order independent), so the permutation is exact.  The
 // error sums of ABS are chains too (lanes, codes of a row, rows), each
@@ -28,12 +29,12 @@ namespace svq {
 #pragma clang fp contract(off)
 
 constexpr int ESG_CH = 32;       // channels per block
-constexpr int ESG_TOK = 1024;    // tokens per staged tile (64 KB)
+constexpr int ESG_TOK = 256;     // tokens per staged tile (64 KB of squares)
 constexpr int ESG_LD = ESG_TOK / 64;  // 16-byte loads per thread and tile
 constexpr int ESG_SPAN = 256;    // energies compared per rank block
 
 __global__ __launch_bounds__(256) void esg_energy_kernel(EsgArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[ESG_TOK][ESG_CH];
+  __shared__ __attribute__((aligned(16))) double sq[ESG_TOK][ESG_CH];
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * ESG_CH;
   const int g = tid & 3, tr = tid >> 2;  // 8-channel group, token row 0..63
@@ -53,29 +54,32 @@ __global__ __launch_bounds__(256) void esg_energy_kernel(EsgArgs a) {
   double acc = 0.0;
   for (int64_t t0 = 0; t0 < T; t0 += ESG_TOK) {
     __syncthreads();  // the chains over the previous tile are done
+    // every thread squares its 8 x ESG_LD values (exact in double)
 #pragma unroll
-    for (int q = 0; q < ESG_LD; ++q) *(u4 *)&tile[tr + 64 * q][8 * g] = nx[q];
+    for (int q = 0; q < ESG_LD; ++q) {
+      double *dst = &sq[tr + 64 * q][8 * g];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const double lo = (double)bf16_bits_to_f32(nx[q][h] & 0xFFFFu);
+        const double hi = (double)bf16_bits_to_f32(nx[q][h] >> 16);
+        dst[2 * h] = lo * lo;
+        dst[2 * h + 1] = hi * hi;
+      }
+    }
     __syncthreads();
     if (t0 + ESG_TOK < T) load(t0 + ESG_TOK);
     if (tid < ESG_CH) {
       const int nt = (int)min((int64_t)ESG_TOK, T - t0);
       int i = 0;
-      // eight tokens at a time: the LDS reads and squares are independent,
-      // only the additions form the chain
+      // eight reads ahead of the additions, which alone form the chain
       for (; i + 8 <= nt; i += 8) {
-        double sq[8];
+        double v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const double v = (double)bf16_bits_to_f32(tile[i + u][tid]);
-          sq[u] = v * v;
-        }
+        for (int u = 0; u < 8; ++u) v[u] = sq[i + u][tid];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc = acc + sq[u];
+        for (int u = 0; u < 8; ++u) acc = acc + v[u];
       }
-      for (; i < nt; ++i) {
-        const double v = (double)bf16_bits_to_f32(tile[i][tid]);
-        acc = acc + v * v;
-      }
+      for (; i < nt; ++i) acc = acc + sq[i][tid];
     }
   }
   if (tid < ESG_CH && c0 + tid < a.k) {
