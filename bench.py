@@ -89,6 +89,8 @@ def parse():
                              "prefill_m2048", "moe128_m1", "moe128_m512", "encode_gate_bd7",
                              "decode4b_36l", "esg_calib_t2048_k2560", "abs_gate_3splits"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-matrix", action="store_true",
+                    help="dense workloads: also time every matrix alone (config.per_matrix)")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="only measure plain device copy and read rates (context for the HBM peak)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -674,6 +676,25 @@ def main():
         roof = {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(args.workload)}
 
+    per_matrix = None
+    if args.per_matrix:
+        # every matrix alone, same cold rotation and timing as the set
+        per_matrix = {}
+        for j, mat in enumerate(mats):
+            cj = [svq.BatchedCall([rot[c][j]], [x_dev[j]], [y_dev[j]], workspace=ws, stream=stream)
+                  for c in range(copies)]
+            for i in range(args.warmup):
+                cj[i % copies]()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(args.steps):
+                cj[(args.warmup + i) % copies]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / args.steps * 1e3
+            per_matrix[mat.name] = {"n": mat.n, "k": mat.k, "bd": mat.bd, "us": round(us, 3),
+                                    "GB/s": round(mat.codes.size / (us * 1e-6) / 1e9, 1)}
+
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -704,7 +725,8 @@ def main():
         "data": "synthetic (seeded codes, codebooks, radii, permutations, activations)",
         "config": {"workload": args.workload, "matrices": len(mats), "m": m,
                    "code_bytes": int(code_bytes), "cold_copies": int(copies),
-                   "launches_per_step": launches},
+                   "launches_per_step": launches,
+                   **({"per_matrix": per_matrix} if per_matrix else {})},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
