@@ -32,16 +32,18 @@ def _x_dev(bits, pad=0):
 
 
 ESG_SHAPES = [
-    # t, k, row padding: one token and one subvector; a partial token tile
-    # (300, 257 of 1024) and a ragged channel block (1032 = 32 * 32 + 8);
-    # strided rows; the gate/up input width with 2048 calibration tokens
-    # (two full tiles); a full tile and a ragged second one; the down input
+    # t, k, row padding (tiles of 256 tokens and 32 channels): one token and
+    # one subvector; a ragged last token tile (300 = 256 + 44, 257 = 256 + 1)
+    # and a ragged channel block (1032 = 32 * 32 + 8); strided rows; the
+    # gate/up input width with 2048 calibration tokens (eight full tiles);
+    # 1100 = 4 * 256 + 76; twenty tiles of one subvector; the down input
     # width (ranks across 38 spans of 256 channels)
     (1, 8, 0),
     (300, 64, 0),
     (257, 1032, 8),
     (2048, 2560, 0),
     (1100, 520, 0),
+    (5000, 8, 0),
     (64, 9728, 0),
 ]
 
@@ -77,7 +79,10 @@ def _cands(n, k, seed):
             ((bd, synth.random_matrix(8, k, bd, seed=(seed, bd, 0))) for bd in (6, 7, 8))]
 
 
-@pytest.mark.parametrize("n,k,pad", [(1, 8, 0), (33, 1032, 3), (256, 2560, 0)])
+# one row and one code; ragged row blocks (33 rows) and code chunks (129
+# codes); 256 full rows; more rows (4100) than the totals kernel stages at
+# once (4096)
+@pytest.mark.parametrize("n,k,pad", [(1, 8, 0), (33, 1032, 3), (256, 2560, 0), (4100, 64, 0)])
 def test_abs_matches_the_oracle(svq, n, k, pad):
     rng = np.random.default_rng(72 + n)
     cands = _cands(n, k, 72)
