@@ -39,9 +39,12 @@ namespace svq {
 // c takes code column c of the unit (permuted slots 8c .. 8c+7; Fig. 6
 // caption: a subvector multiplies eight reordered activations), loads the
 // eight activations x[a][perm[p]] and the wave writes the unit's fp16 copy
-// with an exact power-of-two scale 2^e (max|x_au| * 2^e in [2^14, 2^15)), so
-// the copy is exact for every bf16 value above 2^-17 * max|x_au|; 2^-e is
-// stored beside it and undone once per (row tile, unit) in fp32.
+// with a power-of-two scale 2^e (max|x_au| * 2^e in [2^14, 2^15)).  A bf16
+// value has 8 significant bits, so its scaled copy is exact down to a
+// scaled magnitude of 2^-17 (the fp16 subnormal quantum is 2^-24), i.e. for
+// every |x| >= 2^-31 * max|x_au|; smaller values round to fp16 subnormals.
+// 2^-e is stored beside the copy and undone once per (row tile, unit) in
+// fp32.
 //
 // Main launch: a block of 4 waves owns R consecutive 16-row tiles of one
 // matrix and all of its K; the block's R*U coded units are split evenly
@@ -537,7 +540,11 @@ __device__ void gemv_main_block(const MatView &w, const uint8_t *__restrict__ xg
 #pragma unroll
     for (int s = 0; s < GV_PIPE; ++s) {
       step(ring[s]);
-      ring[s] = load_gv_item<M>(codes, xa, xs, fl, ul, lane);  // fl < F: item k + GV_PIPE exists
+      // item k + GV_PIPE exists for s = 0 only when the loop is entered;
+      // a refill past the wave's run reads the block's last item instead
+      // (never used), so every address stays inside the matrix
+      const bool in = fl < F;
+      ring[s] = load_gv_item<M>(codes, xa, xs, in ? fl : F - 1, in ? ul : U - 1, lane);
       fl += GV_WAVES;
       for (ul += GV_WAVES; ul >= U; ul -= U) {}
       advance();

@@ -27,11 +27,16 @@
  *   - y[m, i] = sum_j What[i, j] * x[m, j]  with x bf16, y bf16 or fp32.
  *
  * Numerics.  For m <= 4 (the batch-1/small-batch GEMV path) each decoded
- * weight is the exact fp32 product R*D (fp16 x fp16 fits in 22 bits), the
- * activations enter the dot products as fp16 after an exact per-row power of
- * two scaling, and accumulation is fp32.  For m > 4 (skinny and prefill GEMM
- * on the matrix cores) a weight enters as RNE_bf16(R*D) with its sign, x as
- * bf16, accumulation fp32.  bf16 outputs are rounded to nearest even.
+ * weight is the exact fp32 product R*D (fp16 x fp16 fits in 22 bits) and
+ * accumulation is fp32.  The activations enter the dot products as fp16
+ * after a power-of-two scale chosen per 512-slot block of permuted inputs
+ * (per row of x): the block's largest magnitude is scaled into [2^14, 2^15),
+ * which keeps every bf16 value of magnitude at least 2^-31 times that
+ * largest one exact; smaller values round to fp16 subnormals (an absolute
+ * error of at most 2^-39 times the block's largest magnitude).  For m > 4
+ * (skinny and prefill GEMM on the matrix cores) a weight enters as
+ * RNE_bf16(R*D) with its sign, x as bf16, accumulation fp32.  bf16 outputs
+ * are rounded to nearest even.
  *
  * Ownership.  The caller owns every byte: the packed matrix buffer and the
  * workspace are device memory the caller allocates (size queries below);
@@ -121,7 +126,10 @@ svq_status svq_pack(const svq_matrix_desc *src, void *dst_dev, size_t *dst_bytes
 
 /* svq_linear: y = x * What^T for one packed matrix (SAGE Fig. 1 / Fig. 5
  * captions: weights reconstructed on demand; Fig. 6 caption: reordered
- * activations gathered per subvector).
+ * activations gathered per subvector).  Beside the operands the call takes a
+ * workspace pair: the library never allocates device memory, so the scratch
+ * some shapes need (permuted activations, K-split partial sums) comes from
+ * the caller, sized by a query call with workspace == NULL.
  *   w:          packed matrix.
  *   x:          device bf16 [m][ldx], ldx >= k.
  *   m:          rows of x, >= 1.
@@ -148,14 +156,20 @@ svq_status svq_linear_batched(const svq_handle *w, int32_t count, const void *co
                               void *stream);
 
 /* svq_moe_linear: one projection of a routed mixture of experts, one output
- * row per routed (token, expert) slot; the grouped form of svq_linear.
+ * row per routed (token, expert) slot; the grouped form of svq_linear.  The
+ * pages code dense linears only; this call applies the same per-matrix
+ * format to each expert's matrices (each expert with its own codebook,
+ * radius table, permutation and split) under the usual top-k slot
+ * convention below, which is this library's definition, not the pages'.
  *   experts:      host array of num_experts packed matrices, all with the
  *                 same n and k (bd may differ per expert).
  *   x:            device bf16; row t (token) when x_per_slot == 0, row
  *                 q = t*topk + j (slot) when x_per_slot == 1; stride ldx.
  *   expert_ids:   device int32 [m*topk]; slot q = t*topk + j uses expert
- *                 expert_ids[q], each in [0, num_experts).  Ids outside that
- *                 range make the results undefined.
+ *                 expert_ids[q], each in [0, num_experts).  A slot whose id
+ *                 is outside that range is skipped: its output row is
+ *                 written as zeros and no memory outside the arguments is
+ *                 touched.
  *   y:            device [m*topk][ldy] of type ydt, slot-major.
  *   workspace:    as for svq_linear (routing tables and permuted inputs).
  * Routing weights, the activation between projections and the combine over

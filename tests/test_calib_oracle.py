@@ -148,6 +148,18 @@ def test_abs_ties_go_to_the_first_candidate():
 
 # ---- planted mistakes (CPU only): every one must be caught by the pins above
 
+def test_total_in_order_is_sequential():
+    """total_in_order adds in index order, one rounding per addition.  The
+    values are chosen so that the order decides the result: the ulp of
+    1e16 is 2, so 1e16 + 1 rounds (ties to even) back to 1e16."""
+    # sixteen values: numpy's eight-way pairwise sum would give 1.0 here
+    assert sc.total_in_order(np.array([1e16, 1.0] + [0.0] * 6 + [-1e16] + [0.0] * 7)) == 0.0
+    assert sc.total_in_order(np.array([-1e16, 1e16, 1.0])) == 1.0
+    assert sc.total_in_order(np.array([1.0, 1e16, -1e16])) == 0.0
+    assert sc.total_in_order(np.array([0.25])) == 0.25
+    assert sc.total_in_order(np.array([], dtype=np.float64)) == 0.0
+
+
 def _mut_energy_abs(x_bits):
     x = np.abs(so.bf16_bits_to_f64(x_bits))
     return x.sum(axis=0) / x.shape[0]
@@ -176,7 +188,25 @@ def _mut_error_h_slot_order(w, perm, h, codes, bd, cb, rad):
     return _orig_rows(w, perm, np.asarray(h, dtype=np.float64)[np.argsort(perm)], codes, bd, cb, rad)
 
 
+def _mut_total_reversed(values):
+    tot = 0.0
+    for v in np.asarray(values, dtype=np.float64)[::-1]:
+        tot = tot + float(v)
+    return tot
+
+
+def _mut_total_pairwise(values):
+    return float(np.sum(np.asarray(values, dtype=np.float64)))
+
+
+def _mut_total_exact(values):
+    return math.fsum(np.asarray(values, dtype=np.float64).tolist())
+
+
 MUTANTS = {
+    "total_reversed": ("total_in_order", _mut_total_reversed),
+    "total_pairwise": ("total_in_order", _mut_total_pairwise),
+    "total_exact": ("total_in_order", _mut_total_exact),
     "energy_abs": ("esg_energy", _mut_energy_abs),
     "perm_contiguous": ("esg_perm", _mut_perm_contiguous),
     "perm_ascending": ("esg_perm", _mut_perm_ascending),
@@ -199,7 +229,8 @@ def test_pins_catch_calib_mutation(monkeypatch, name):
     pins = [test_golden_esg, test_energy_closed_forms, test_golden_weighted_error,
             lambda: test_perm_tier_structure(64),
             lambda: test_weighted_error_matches_the_dense_form(7),
-            test_abs_picks_the_split_that_reproduces_the_weights]
+            test_abs_picks_the_split_that_reproduces_the_weights,
+            test_total_in_order_is_sequential]
     caught = False
     for pin in pins:
         try:

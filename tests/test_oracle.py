@@ -58,6 +58,33 @@ def test_golden_worked_examples(name):
     assert [float(v) for v in yb[0]] == list(y)
 
 
+def _golden_bounds_ok(name):
+    """The parity bound of a hand-worked fixture: abs_bound equals the
+    fixture's hand sum of |W_ij||x_j| exactly (small dyadic values, so the
+    fp64 product is exact), and tolerance is 8e-3 times it plus 1e-6."""
+    g = load_golden(name)
+    n, k, bd, stream, cb, radius, perm, x, codes, y, w = _golden_case(name)
+    W = so.decode_matrix(stream, n, k, bd, cb, radius, perm)
+    cases = [(x, np.array([float(v) for v in g["bound"][0]]))]
+    if "x_signed" in g:
+        xs = np.array(_hex(g["x_signed"][0]), dtype=np.uint16).reshape(1, k)
+        ys = np.array([float(v) for v in g["y_signed"][0]])
+        if not np.array_equal(so.linear(xs, W).reshape(-1), ys):
+            return False
+        cases.append((xs, np.array([float(v) for v in g["bound_signed"][0]])))
+    for xb, bound in cases:
+        if not np.array_equal(so.abs_bound(xb, W).reshape(-1), bound):
+            return False
+        if not np.array_equal(so.tolerance(xb, W).reshape(-1), 8e-3 * bound + 1e-6):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("name", ["single_subvector.txt", "two_rows_bd6.txt"])
+def test_golden_parity_bound(name):
+    assert _golden_bounds_ok(name)
+
+
 def test_golden_two_codes_stream():
     g = load_golden("two_codes_stream.txt")
     codes = np.array(_hex(g["codes"][0]), dtype=np.uint32)

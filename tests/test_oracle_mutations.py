@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from oracle import svq_oracle as so
-from tests.test_oracle import _golden_case
+from tests.test_oracle import _golden_bounds_ok, _golden_case
 
 
 def _golden_ok(name):
@@ -82,3 +82,47 @@ def test_fixture_catches_mutation(monkeypatch, mutation):
         except (AssertionError, ValueError, IndexError):
             caught = True
     assert caught, f"mutation '{mutation}' slipped through the fixtures"
+
+
+# Planted mistakes in the parity bound itself: every GPU parity test passes
+# or fails on so.tolerance, so a slip that loosens it must not go unnoticed.
+ORIG_F64 = so.bf16_bits_to_f64
+
+
+def _mut_bound_signed_x(x_bits, w):
+    x = ORIG_F64(x_bits).reshape(-1, w.shape[1])  # |x| forgotten
+    return x @ np.abs(w).T
+
+
+def _mut_bound_signed_w(x_bits, w):
+    x = np.abs(ORIG_F64(x_bits).reshape(-1, w.shape[1]))
+    return x @ w.T  # |W| forgotten
+
+
+def _mut_tolerance_rel(x_bits, w, rel=8e-2, atol=1e-6):
+    return rel * so.abs_bound(x_bits, w) + atol
+
+
+def _mut_tolerance_atol(x_bits, w, rel=8e-3, atol=1e-3):
+    return rel * so.abs_bound(x_bits, w) + atol
+
+
+BOUND_MUTATIONS = {
+    "bound without |x|": ("abs_bound", _mut_bound_signed_x),
+    "bound without |W|": ("abs_bound", _mut_bound_signed_w),
+    "tolerance rel 8e-2": ("tolerance", _mut_tolerance_rel),
+    "tolerance atol 1e-3": ("tolerance", _mut_tolerance_atol),
+}
+
+
+def test_bound_fixtures_pass_unmutated():
+    assert _golden_bounds_ok("single_subvector.txt")
+    assert _golden_bounds_ok("two_rows_bd6.txt")
+
+
+@pytest.mark.parametrize("mutation", sorted(BOUND_MUTATIONS))
+def test_bound_fixture_catches_mutation(monkeypatch, mutation):
+    attr, fn = BOUND_MUTATIONS[mutation]
+    monkeypatch.setattr(so, attr, fn)
+    caught = not (_golden_bounds_ok("single_subvector.txt") and _golden_bounds_ok("two_rows_bd6.txt"))
+    assert caught, f"mutation '{mutation}' slipped through the bound fixtures"
