@@ -20,6 +20,8 @@ hipError_t launch_moe(const svq_handle *experts, int32_t num_experts, const void
 
 using namespace svq;
 
+static_assert(SCRATCH_BYTES == SVQ_SCRATCH_BYTES, "scratch size of svq.h and the library differ");
+
 namespace {
 
 constexpr uint32_t FIELD_MASK = (1u << 18) - 1;
@@ -629,6 +631,20 @@ svq_status svq_linear_batched(const svq_handle *w, int32_t count, const void *co
                               svq_dtype ydt, void *workspace, size_t *workspace_bytes,
                               void *stream) {
   return linear_impl(w, count, x, ldx, m, y, ldy, ydt, workspace, workspace_bytes, stream);
+}
+
+svq_status svq_linear_noalloc(const svq_handle *w, const void *x, int64_t m, int64_t ldx, void *y,
+                              int64_t ldy, svq_dtype ydt, void *stream) {
+  // the same plan as svq_linear; its workspace comes from the library's
+  // scratch, so the size is checked before anything touches the device
+  size_t need = 0;
+  svq_status st = svq_linear(w, nullptr, m, ldx, nullptr, ldy, ydt, nullptr, &need, stream);
+  if (st != SVQ_OK) return st;
+  if (need > SCRATCH_BYTES) return SVQ_ERR_UNSUPPORTED;
+  void *ws = nullptr;
+  if (scratch_ptr(&ws) != hipSuccess) return SVQ_ERR_HIP;
+  size_t cap = SCRATCH_BYTES;
+  return svq_linear(w, x, m, ldx, y, ldy, ydt, ws, &cap, stream);
 }
 
 svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts, const void *x,

@@ -55,6 +55,11 @@ constexpr int MAX_EXPERTS = 256;
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Scratch of svq_linear_noalloc: a file-scope device array of this size
+// (svq_scratch.hip); scratch_ptr returns the current device's address of it.
+constexpr size_t SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t scratch_ptr(void **ptr);
+
 // Matrix view passed to kernels by value.
 struct MatView {
   const uint8_t *base;  // packed buffer

@@ -33,8 +33,10 @@ SVQ_ERR_HIP = -4
 SVQ_BF16 = 0
 SVQ_F32 = 1
 
-EXPORTED = ("svq_pack", "svq_linear", "svq_linear_batched", "svq_moe_linear",
-            "svq_encode", "svq_esg_perm", "svq_abs_select", "svq_status_string")
+EXPORTED = ("svq_pack", "svq_linear", "svq_linear_batched", "svq_linear_noalloc",
+            "svq_moe_linear", "svq_encode", "svq_esg_perm", "svq_abs_select",
+            "svq_status_string")
+SVQ_SCRATCH_BYTES = 64 << 20
 
 
 class SvqError(RuntimeError):
@@ -88,6 +90,10 @@ def _load() -> ctypes.CDLL:
                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
                                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
                                        ctypes.c_void_p]
+    lib.svq_linear_noalloc.restype = ctypes.c_int
+    lib.svq_linear_noalloc.argtypes = [ctypes.POINTER(Handle), ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_void_p]
     lib.svq_moe_linear.restype = ctypes.c_int
     lib.svq_moe_linear.argtypes = [ctypes.POINTER(Handle), ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
@@ -142,6 +148,11 @@ def svq_linear(handle: Handle, x_ptr: int, m: int, ldx: int, y_ptr: int, ldy: in
     st = LIB.svq_linear(ctypes.byref(handle), x_ptr, m, ldx, y_ptr, ldy, ydt, ws_ptr,
                         ctypes.byref(nbytes), stream)
     return st, nbytes.value
+
+
+def svq_linear_noalloc(handle: Handle, x_ptr: int, m: int, ldx: int, y_ptr: int, ldy: int,
+                       ydt: int, stream: int) -> int:
+    return LIB.svq_linear_noalloc(ctypes.byref(handle), x_ptr, m, ldx, y_ptr, ldy, ydt, stream)
 
 
 def svq_linear_batched(handles, count: int, x_ptrs, ldx, m: int, y_ptrs, ldy, ydt: int,
@@ -292,6 +303,21 @@ def linear(pm: PackedMatrix, x, out=None, out_dtype=None, workspace=None, stream
     st, _ = svq_linear(pm.handle, x.data_ptr(), m, x.stride(0), out.data_ptr(), out.stride(0),
                        ydt, workspace.data_ptr(), workspace.numel(), _stream_handle(stream))
     _check(st, "svq_linear")
+    return out
+
+
+def linear_noalloc(pm: PackedMatrix, x, out, stream=None):
+    """y = x @ What^T into a caller-given ``out`` through svq_linear_noalloc
+    (no workspace: the library's own scratch is used)."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(1) != 1:
+        raise ValueError("out must be bf16 or fp32 with unit column stride")
+    ydt = SVQ_F32 if out.dtype == torch.float32 else SVQ_BF16
+    st = svq_linear_noalloc(pm.handle, x.data_ptr(), x.shape[0], x.stride(0), out.data_ptr(),
+                            out.stride(0), ydt, _stream_handle(stream))
+    _check(st, "svq_linear_noalloc")
     return out
 
 

@@ -155,6 +155,23 @@ svq_status svq_linear_batched(const svq_handle *w, int32_t count, const void *co
                               svq_dtype ydt, void *workspace, size_t *workspace_bytes,
                               void *stream);
 
+/* svq_linear_noalloc: svq_linear without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops, harnesses that forbid hipMalloc).  The scratch svq_linear would take
+ * from the caller comes from a file-scope device array of SVQ_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends; the
+ * call itself allocates nothing (no hipMalloc, no allocating library call).
+ *   w, x, m, ldx, y, ldy, ydt, stream:  as for svq_linear.
+ * Returns SVQ_ERR_UNSUPPORTED, before any device work, when the call would
+ * need more scratch than SVQ_SCRATCH_BYTES (svq_linear's workspace query
+ * gives the size).  Every call on one GPU shares that GPU's array and it
+ * keeps the last call's contents: calls that overlap on one GPU (different
+ * streams, different host threads without ordering) race and give undefined
+ * results.  Results equal svq_linear's for the same arguments. */
+#define SVQ_SCRATCH_BYTES ((size_t)64 << 20)
+svq_status svq_linear_noalloc(const svq_handle *w, const void *x, int64_t m, int64_t ldx,
+                              void *y, int64_t ldy, svq_dtype ydt, void *stream);
+
 /* svq_moe_linear: one projection of a routed mixture of experts, one output
  * row per routed (token, expert) slot; the grouped form of svq_linear.  The
  * pages code dense linears only; this call applies the same per-matrix

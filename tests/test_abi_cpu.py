@@ -22,8 +22,8 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol():
     declared = _declared_functions()
-    assert set(declared) == {"svq_pack", "svq_linear", "svq_linear_batched", "svq_moe_linear",
-                             "svq_encode", "svq_esg_perm", "svq_abs_select",
+    assert set(declared) == {"svq_pack", "svq_linear", "svq_linear_batched", "svq_linear_noalloc",
+                             "svq_moe_linear", "svq_encode", "svq_esg_perm", "svq_abs_select",
                              "svq_status_string"}
     for name in declared:
         assert hasattr(svq.LIB, name), name
@@ -395,3 +395,20 @@ def test_calibration_wrappers_reject_bad_tensors_before_any_device_work():
         svq.abs_select(w, perm, h.float(), [])                           # h not fp64
     with pytest.raises(ValueError):
         svq.abs_select(w, perm, torch.zeros(16, dtype=torch.float64)[::2], [])  # h strided
+
+
+def test_linear_noalloc_rejects_before_device_work():
+    """svq_linear_noalloc checks its arguments and the scratch size before it
+    looks up the device array, so a host without a GPU sees the errors."""
+    big = _fake_handle(2560, 9728, 7)
+    need = _dequant_gemm_need([(2560, 9728)], 4096)
+    assert need > svq.SVQ_SCRATCH_BYTES
+    assert svq.svq_linear_noalloc(big, 0x2000, 4096, 9728, 0x3000, 2560, 0, 0) == \
+        svq.SVQ_ERR_UNSUPPORTED
+    h = _fake_handle(512, 1024, 8)
+    assert svq.svq_linear_noalloc(h, 0x2000, 0, 1024, 0x3000, 512, 0, 0) == svq.SVQ_ERR_INVALID_ARG
+    assert svq.svq_linear_noalloc(h, 0x2000, 1, 1000, 0x3000, 512, 0, 0) == svq.SVQ_ERR_INVALID_ARG
+    assert svq.svq_linear_noalloc(h, 0x2000, 1, 1024, 0x3000, 512, 9, 0) == svq.SVQ_ERR_INVALID_ARG
+    bad = _fake_handle(512, 1024, 8)
+    bad.off_codes += 256
+    assert svq.svq_linear_noalloc(bad, 0x2000, 1, 1024, 0x3000, 512, 0, 0) == svq.SVQ_ERR_INVALID_ARG
