@@ -22,6 +22,7 @@ COMMON_FLAGS = [
 # 256 accumulators in accumulation registers.
 SOURCES = [
     ("csrc/svq_host.cpp", []),
+    ("csrc/svq_plan.cpp", []),
     ("csrc/svq_kernels.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("csrc/svq_prefill.hip", []),
     ("csrc/svq_small.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),

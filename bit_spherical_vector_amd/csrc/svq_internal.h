@@ -55,6 +55,19 @@ constexpr int MAX_EXPERTS = 256;
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// ---- per-wave load schedules, shared by the kernels and the host-side
+// launch checks (every code address a wave loads is derived from these) ----
+// Exact path, m = 2..4 (4-wave blocks): the wave's items are the flat units
+// f = wv + k*4 < F of its block; a load for f past the block's last item
+// reads the last item instead (never used), so loads stay inside the block.
+__host__ __device__ inline int gv_wave_items(int F, int wv) { return F > wv ? (F - wv + 3) / 4 : 0; }
+__host__ __device__ inline int gv_load_flat(int f, int F) { return f < F ? f : F - 1; }
+// Exact path, m = 1 (fused, `waves` waves per block): the wave's items are
+// [begin, end) of the block's n_items; a load past `end` reads the packed
+// buffer's first bytes instead (unit -1 here: never used).
+__host__ __device__ inline int gf_wave_begin(int n_items, int waves, int wv) { return wv * n_items / waves; }
+__host__ __device__ inline int gf_load_unit(int u, int end) { return u < end ? u : -1; }
+
 // Scratch of svq_linear_noalloc: a file-scope device array of this size
 // (svq_scratch.hip); scratch_ptr returns the current device's address of it.
 constexpr size_t SCRATCH_BYTES = (size_t)64 << 20;
@@ -107,6 +120,14 @@ struct GemvBatch {
   int32_t xvec;             // every activation row starts 16-byte aligned
 };
 constexpr size_t GV_LDS_LIMIT = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int GV_WAVES = 4;
+// lane-interleaved copies of a direction table of 2^bd rows (at most 32 KB)
+__host__ __device__ constexpr int gv_copies(int bd) { return bd >= 8 ? 8 : 16; }
+// LDS of the m = 2..4 main launch (absolute addresses): radius by 10-bit
+// index, then the direction copies (2^bd rows of 256 bytes), then the
+// cross-wave partial sums [R][GV_WAVES][4][4][4][M] fp32 at GemvBatch::red_off.
+constexpr int GV_OFF_RTAB = 0;
+constexpr int GV_OFF_D = RTAB_BYTES;
 // Workspace of the exact path for one matrix of `units` units.
 inline size_t gemv_ws_bytes(int m, int units) {
   return align256((size_t)m * units * GV_XG_UNIT_BYTES) + align256((size_t)units * 16);
@@ -119,6 +140,17 @@ constexpr int GV_UNITS_PER_WAVE = 4;  // units per wave the planner aims for
 // m = 1: one fused launch (gather in the block); R <= GF_MAX_R row tiles
 // per block, whose R x units items the 4 waves split into equal runs.
 constexpr int GF_MAX_R = 8;
+// LDS of the fused m = 1 block: radius table [0, 2 KB), direction rows from
+// 2 KB (16 lane-interleaved copies for bd <= 7, one copy for bd = 8), then
+// unit scales, cross-wave partial sums, the permuted activations and the
+// staging row.
+constexpr int GF_OFF_RTAB = 0;
+constexpr int GF_OFF_D = RTAB_BYTES;
+__host__ __device__ constexpr int gf_dir_bytes(int bd) { return bd >= 8 ? DTAB_BYTES : (16 << bd) * 16; }
+__host__ __device__ constexpr int gf_scale_off(int bd) { return GF_OFF_D + gf_dir_bytes(bd); }
+__host__ __device__ constexpr int gf_xp_off(int bd, int units, int m) {
+  return gf_scale_off(bd) + ((units * m * 4 + 15) & ~15) + GF_MAX_R * GV_WAVES * 4 * 4 * 4 * m;
+}
 size_t gemv_fused_smem_bytes(int k, int units, int bd);  // one matrix
 hipError_t launch_gemv_fused(GemvBatch &b, int blocks, size_t smem, hipStream_t s);
 
@@ -178,6 +210,7 @@ hipError_t launch_sb(SbBatch &b, int prep_blocks, int blocks, hipStream_t s);
 // (xb, padded to prefill_m_pad(m) rows), then one LDS-tiled dequant-GEMM
 // launch covers all jobs; a GEMM block owns one output tile of one job.
 constexpr int PREFILL_MIN_M = 256;
+constexpr int PREFILL_BN = 256;  // weight rows per GEMM block tile
 struct PrefillJob {
   MatView w;
   const uint16_t *x;    // activations, bf16 [m][ldx]
@@ -208,7 +241,9 @@ struct PrefillBatch {
 };
 int prefill_bm(int m);      // activation rows per block tile: 256 (m >= PREFILL_MIN_M) or 64
 int prefill_m_pad(int m);   // m rounded up to prefill_bm(m)
-int prefill_tiles_n(int n_tiles);
+__host__ __device__ inline int prefill_tiles_n(int n_tiles) {
+  return (n_tiles + PREFILL_BN / UNIT_ROWS - 1) / (PREFILL_BN / UNIT_ROWS);
+}
 int prefill_prep_rows(int k);  // activation rows per prep block for rows of k values
 size_t prefill_prep_lds(int rpb, int k);  // LDS of such a block
 // xvec: every activation row of every job starts 16-byte aligned.

@@ -73,19 +73,15 @@ namespace svq {
 // different bank groups; the 256-row tables of bd = 8 keep C = 8 (32 KB, so
 // that four blocks fit in a compute unit), two lanes per bank group.
 
-constexpr int GV_WAVES = 4;
 #ifndef SVQ_GV_PIPE
 #define SVQ_GV_PIPE 2
 #endif
 // Work items whose loads are in flight per wave.
 constexpr int GV_PIPE = SVQ_GV_PIPE;
 // lane-interleaved copies of a direction table of 2^bd rows (at most 32 KB)
-__host__ __device__ constexpr int gv_copies(int bd) { return bd >= 8 ? 8 : 16; }
 // LDS (absolute addresses, see lds_u4): radius by 10-bit index, then the
 // direction copies (2^bd rows of 256 bytes), then the cross-wave partial sums
 // [R][GV_WAVES][4][4][4][M] fp32 at GemvBatch::red_off.
-constexpr int GV_OFF_RTAB = 0;
-constexpr int GV_OFF_D = RTAB_BYTES;
 
 // Maximum over the 64 lanes of a non-negative float (returned in every
 // lane): DPP row shifts within the 16-lane rows, row broadcasts across rows,
@@ -433,7 +429,8 @@ __device__ void gemv_main_block(const MatView &w, const uint8_t *__restrict__ xg
   // the wave's items: flat units f = wv + k*GV_WAVES < F, k < n_items (the
   // block's waves step through its units side by side, so that at any time
   // they read neighbouring units)
-  const int n_items = F > wv ? (F - wv + GV_WAVES - 1) / GV_WAVES : 0;
+  static_assert(GV_WAVES == 4, "gv_wave_items assumes 4 waves per block");
+  const int n_items = gv_wave_items(F, wv);
   const uint8_t *codes = w.base + w.off_codes + (size_t)t0 * U * UNIT_BYTES;
   // lane 4b + j reads activation row j (row 0 when j >= M) of code column
   // 16*ci + b of each unit
@@ -472,7 +469,7 @@ __device__ void gemv_main_block(const MatView &w, const uint8_t *__restrict__ xg
   for (int s = 0; s < GV_PIPE; ++s) {
     const bool in = fl < F;
     __builtin_amdgcn_sched_barrier(0);
-    ring[s] = load_gv_item<M>(codes, xa, xs, in ? fl : F - 1, in ? ul : U - 1, lane);
+    ring[s] = load_gv_item<M>(codes, xa, xs, gv_load_flat(fl, F), in ? ul : U - 1, lane);
     __builtin_amdgcn_sched_barrier(0);
     fl += GV_WAVES;
     for (ul += GV_WAVES; ul >= U; ul -= U) {}
@@ -544,7 +541,7 @@ __device__ void gemv_main_block(const MatView &w, const uint8_t *__restrict__ xg
       // a refill past the wave's run reads the block's last item instead
       // (never used), so every address stays inside the matrix
       const bool in = fl < F;
-      ring[s] = load_gv_item<M>(codes, xa, xs, in ? fl : F - 1, in ? ul : U - 1, lane);
+      ring[s] = load_gv_item<M>(codes, xa, xs, gv_load_flat(fl, F), in ? ul : U - 1, lane);
       fl += GV_WAVES;
       for (ul += GV_WAVES; ul >= U; ul -= U) {}
       advance();
@@ -579,12 +576,6 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(GemvBatch b) {
   gemv_main_block<M>(jb.w, jb.xg, jb.xs, jb.y, jb.ldy, b.ydt, t0, Reff, b.red_off, smem);
 }
 
-// LDS of the main launch: radius table, direction copies of the largest bd,
-// partial sums of R tiles.
-size_t gemv_smem_bytes(int m, int bd_max, int r_max) {
-  return (size_t)GV_OFF_D + ((size_t)gv_copies(bd_max) << bd_max) * 16 +
-         (size_t)r_max * GV_WAVES * 64 * m * 4;
-}
 
 // The exact-path kernels address their LDS tables from 0 (see lds_u4), which
 // holds when they declare no static LDS.
@@ -651,13 +642,6 @@ constexpr int GF_STAGE_BATCH = 5;  // 16-byte activation loads per thread per st
 // LDS: radius table [0, 2 KB), direction rows from 2 KB (GF_OFF_D), then at
 // per-block offsets: unit scales, cross-wave partial sums, the permuted
 // activations and the staging row.
-constexpr int GF_OFF_RTAB = 0;
-constexpr int GF_OFF_D = RTAB_BYTES;
-__host__ __device__ constexpr int gf_dir_bytes(int bd) { return bd >= 8 ? DTAB_BYTES : (16 << bd) * 16; }
-__host__ __device__ constexpr int gf_scale_off(int bd) { return GF_OFF_D + gf_dir_bytes(bd); }
-__host__ __device__ constexpr int gf_xp_off(int bd, int units, int m) {
-  return gf_scale_off(bd) + ((units * m * 4 + 15) & ~15) + GF_MAX_R * GV_WAVES * 4 * 4 * 4 * m;
-}
 
 // Table reads of the four codes of column group ci: direction rows (signs
 // not yet applied) and radii.
@@ -742,7 +726,8 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   // this wave's work: items [i_begin, i_end) of the block's Reff x U items
   // (item i = unit i % U of tile rt0 + i / U, at codes0 + i units)
   const int n_items = Reff * U;
-  const int i_begin = wv * n_items / GV_WAVES, i_end = (wv + 1) * n_items / GV_WAVES;
+  const int i_begin = gf_wave_begin(n_items, GV_WAVES, wv);
+  const int i_end = gf_wave_begin(n_items, GV_WAVES, wv + 1);
   const uint8_t *codes0 = w.base + w.off_codes + (size_t)rt0 * U * UNIT_BYTES;
   (void)R;
   // this wave's share of the gather: units [g_lo, g_hi]
@@ -823,7 +808,8 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
       // the code latency then overlaps the gather.
 #pragma unroll
       for (int s = 0; s < GV_PIPE; ++s) {
-        const uint8_t *ub = ul < i_end ? codes0 + (size_t)ul * UNIT_BYTES : w.base;
+        const int lu = gf_load_unit(ul, i_end);
+        const uint8_t *ub = lu >= 0 ? codes0 + (size_t)lu * UNIT_BYTES : w.base;
         ring[s] = load_item<true>(ub, lane);
         ++ul;
       }
@@ -957,7 +943,8 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
     for (int s = 0; s < GV_PIPE; ++s) {
       step(ring[s], cu);
       advance();
-      const uint8_t *ub = ul < i_end ? codes0 + (size_t)ul * UNIT_BYTES : w.base;
+      const int lu = gf_load_unit(ul, i_end);
+      const uint8_t *ub = lu >= 0 ? codes0 + (size_t)lu * UNIT_BYTES : w.base;
       ring[s] = load_item<true>(ub, lane);
       ++ul;
     }
@@ -1005,10 +992,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
     gemv_fused_block<1, XVEC, 0>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
 }
 
-// LDS of one fused block at m = 1 for a matrix of k channels, `units` units.
-size_t gemv_fused_smem_bytes(int k, int units, int bd) {
-  return (size_t)gf_xp_off(bd, units, 1) + (size_t)units * UNIT_SLOTS * 2 + (size_t)k * 2;
-}
 
 template <bool XVEC>
 static hipError_t launch_fused_x(GemvBatch &b, int blocks, size_t smem, hipStream_t s) {
@@ -1040,10 +1023,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
                                                        int R) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int q = blockIdx.y;
-  const MatView w = expert_view(sh, tab, ids[q]);
-  const int src = x_per_slot ? q : q / topk;
+  const int e = ids[q];
   const int rt0 = blockIdx.x * R;
   char *yq = (char *)y + (size_t)q * ldy * (ydt == 0 ? 2 : 4);
+  if (e < 0 || e >= sh.num_experts) {  // block-uniform: the slot is skipped, its rows are zero
+    for (int r = rt0 * 16 + (int)threadIdx.x; r < min(sh.n, (rt0 + R) * 16); r += 256)
+      store_out(yq, (size_t)r, 0.f, ydt);
+    return;
+  }
+  const MatView w = expert_view(sh, tab, e);
+  const int src = x_per_slot ? q : q / topk;
   if (w.bd >= 8)
     gemv_fused_block<1, XVEC, 1>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, min(R, w.n_tiles - rt0),
                                  smem);
@@ -1056,13 +1045,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
 // of work items (expert, first sorted row, end row), at most 16*BMT rows
 // each.  Single block of 1024 threads.
 //   ws_counts[E], ws_offsets[E+1], ws_sorted[S], ws_work[3*max_work], ws_nwork[1]
+// Slots whose id is outside [0, E) are left out of the sort, and their output
+// rows (n values each, y of type ydt with row stride ldy) are written as zeros.
 __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restrict__ ids, int S,
                                                          int E, int rows_per_item,
                                                          int32_t *__restrict__ counts,
                                                          int32_t *__restrict__ offsets,
                                                          int32_t *__restrict__ sorted,
                                                          int32_t *__restrict__ work,
-                                                         int32_t *__restrict__ nwork) {
+                                                         int32_t *__restrict__ nwork, void *y,
+                                                         int64_t ldy, int n, int ydt) {
   __shared__ int32_t s_cnt[MAX_EXPERTS];
   __shared__ int32_t s_off[MAX_EXPERTS + 1];
   __shared__ int32_t s_fill[MAX_EXPERTS];
@@ -1071,7 +1063,10 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
   const int t = threadIdx.x;
   for (int e = t; e < E; e += 1024) s_cnt[e] = 0;
   __syncthreads();
-  for (int q = t; q < S; q += 1024) atomicAdd(&s_cnt[ids[q]], 1);
+  for (int q = t; q < S; q += 1024) {
+    const int e = ids[q];
+    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+  }
   __syncthreads();
   // exclusive scans of the slot counts and of the work items per expert
   // (threads 0 .. MAX_EXPERTS-1, one expert each: a scan within each wave,
@@ -1118,8 +1113,12 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
   for (int e = t; e <= E; e += 1024) offsets[e] = s_off[e];
   for (int q = t; q < S; q += 1024) {
     const int e = ids[q];
-    const int pos = s_off[e] + atomicAdd(&s_fill[e], 1);
-    sorted[pos] = q;
+    if (e >= 0 && e < E) {
+      const int pos = s_off[e] + atomicAdd(&s_fill[e], 1);
+      sorted[pos] = q;
+    } else {
+      for (int c = 0; c < n; ++c) store_out((char *)y + (size_t)q * ldy * (ydt == 0 ? 2 : 4), (size_t)c, 0.f, ydt);
+    }
   }
   for (int e = t; e < E; e += 1024) {
     const int n_items = s_items[e + 1] - s_items[e];
@@ -1221,7 +1220,7 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   int32_t *nwork = (int32_t *)(b + o_nwork);
   uint16_t *xb = (uint16_t *)(b + o_xb);
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), 0, s, ids, S, E, rows_per_item, counts,
-                     offsets, sorted, work, nwork);
+                     offsets, sorted, work, nwork, y, ldy, sh.n, ydt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_moe_dq(sh, tab, xp, ldx, x_per_slot, topk, work, nwork, sorted, max_work, xb, y,

@@ -43,7 +43,7 @@
 
 namespace svq {
 
-constexpr int P_BN = 256, P_BK = 64;
+constexpr int P_BN = PREFILL_BN, P_BK = 64;
 constexpr int P_ROW = P_BK * 2;                  // 128 bytes per LDS row
 constexpr int P_B = P_BN * P_ROW;                // weight tile, 32 KB
 constexpr int P_STAGE = P_B;
@@ -51,9 +51,6 @@ constexpr int P_OFF_BTAB = 2 * P_STAGE;
 constexpr int P_SMEM = P_OFF_BTAB + BTAB_BYTES;  // 80 KB
 static_assert(P_SMEM <= 160 * 1024, "prefill LDS exceeds a workgroup's 160 KB");
 
-__host__ __device__ __forceinline__ int prefill_tiles_n_dev(int n_tiles) {
-  return (n_tiles + P_BN / UNIT_ROWS - 1) / (P_BN / UNIT_ROWS);
-}
 
 // Fragment order of the permuted activations xb (per job, m_pad x Kp bf16):
 // the 1 KB block F(rb, s, ks) holds, for 32-row block rb, K-step s and k
@@ -822,19 +819,6 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillBatch b) {
                        cs * cpb, min(nch, cs * cpb + cpb), s_rows);
 }
 
-// LDS of a prep block: rpb staged rows of k + 8 values.
-static size_t prep_lds(int rpb, int k) { return (size_t)rpb * (k + 8) * 2; }
-size_t prefill_prep_lds(int rpb, int k) { return prep_lds(rpb, k); }
-
-// Up to 8 rows, fewer for long rows: a block's staging stays near 40 KB, so
-// that several prep blocks share a compute unit (with whole 156 KB of rows
-// per block, one block per unit waits out each row load alone).
-constexpr size_t PREP_LDS_TARGET = 40 * 1024;
-int prefill_prep_rows(int k) {
-  int rpb = 8;
-  while (rpb > 1 && prep_lds(rpb, k) > PREP_LDS_TARGET) rpb /= 2;
-  return rpb;
-}
 
 hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, size_t lds, bool xvec, hipStream_t s) {
   if (lds > GV_LDS_LIMIT) return hipErrorInvalidValue;
@@ -891,7 +875,7 @@ void moe_dq_kernel(MoeShape sh, ExpertTable tab, const int32_t *__restrict__ wor
                    const uint16_t *__restrict__ xb, void *__restrict__ y, int64_t ldy, int ydt,
                    int yvec) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tiles_n = prefill_tiles_n_dev(sh.n_tiles);
+  const int tiles_n = prefill_tiles_n(sh.n_tiles);
   const int wi = (int)blockIdx.x / tiles_n, nt = (int)blockIdx.x % tiles_n;
   if (wi >= *nwork) return;  // uniform, before any barrier
   const int e = work[3 * wi], r0 = work[3 * wi + 1], r1 = work[3 * wi + 2];
@@ -927,7 +911,7 @@ hipError_t launch_moe_dq(const MoeShape &sh, const ExpertTable &tab, const uint1
   csplit = csplit < nch / 64 ? csplit : nch / 64;
   csplit = csplit < 1 ? 1 : csplit;
   const bool xvec = ((((uintptr_t)x) | ((uintptr_t)ldx * 2)) & 15) == 0;
-  const size_t lds = prep_lds(rpb, sh.k);
+  const size_t lds = prefill_prep_lds(rpb, sh.k);
   hipError_t e = allow_smem(moe_dq_prep_kernel, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(moe_dq_prep_kernel, dim3(groups * csplit), dim3(256), lds, s, sh, tab, x, ldx,
@@ -943,14 +927,6 @@ hipError_t launch_moe_dq(const MoeShape &sh, const ExpertTable &tab, const uint1
   return hipGetLastError();
 }
 
-int prefill_bm(int m) { return m >= PREFILL_MIN_M ? 256 : 64; }
-
-int prefill_m_pad(int m) {
-  const int bm = prefill_bm(m);
-  return ((m + bm - 1) / bm) * bm;
-}
-
-int prefill_tiles_n(int n_tiles) { return prefill_tiles_n_dev(n_tiles); }
 
 hipError_t launch_prefill_batched(PrefillBatch &b, int bm, int blocks, hipStream_t s) {
   if (bm == 256) {

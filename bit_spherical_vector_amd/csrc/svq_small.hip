@@ -340,40 +340,6 @@ __global__ __launch_bounds__(256) void sb_prep_kernel(SbBatch b) {
   *(u4 *)(J.xa + ((size_t)u * 16 + f) * 1024 + 16 * L) = v;
 }
 
-// Items per block: all blocks of a call resident at once (two 4-wave
-// blocks per compute unit) when that takes at most SB_NMAX items per wave,
-// and at least SB_ITEMS_MIN.
-int sb_block_items(int64_t total_items, int cus) {
-  const int64_t slots = 2 * (int64_t)cus;
-  int64_t it = (total_items + slots - 1) / slots;
-  if (it < SB_ITEMS_MIN) it = SB_ITEMS_MIN;
-  if (it > SB_WAVES * SB_NMAX) it = SB_WAVES * SB_NMAX;
-  return (int)it;
-}
-
-// Matrices of up to SB_MAX_RANGE units keep all of K in one block, longer
-// ones are cut into ranges of about 5 units; then as many row tiles per
-// block (up to SB_TMAX) as give about `items` items, at most SB_NMAX per
-// wave.
-SbPlan sb_plan(int n_tiles, int units, int items) {
-  SbPlan p;
-  p.splits = units <= SB_MAX_RANGE ? 1 : (units + 4) / 5;
-  p.upr = (units + p.splits - 1) / p.splits;
-  p.splits = (units + p.upr - 1) / p.upr;
-  p.tiles = (items + p.upr / 2) / p.upr;
-  p.tiles = p.tiles < 1 ? 1 : (p.tiles > SB_TMAX ? SB_TMAX : p.tiles);
-  while (p.tiles > 1 && p.tiles * p.upr > SB_WAVES * SB_NMAX) --p.tiles;
-  p.groups = (n_tiles + p.tiles - 1) / p.tiles;
-  return p;
-}
-
-size_t sb_ws_bytes(int n_tiles, int units, int items) {
-  const SbPlan p = sb_plan(n_tiles, units, items);
-  size_t bytes = align256((size_t)units * SB_XA_UNIT_BYTES);
-  if (p.splits > 1)
-    bytes += align256((size_t)p.groups * p.tiles * p.splits * 1024) + align256((size_t)p.groups * 4);
-  return bytes;
-}
 
 hipError_t launch_sb(SbBatch &b, int prep_blocks, int blocks, hipStream_t s) {
   hipLaunchKernelGGL(sb_prep_kernel, dim3(prep_blocks), dim3(256), 0, s, b);

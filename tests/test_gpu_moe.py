@@ -52,9 +52,6 @@ def test_small_moe(svq, m, topk, x_per_slot):
         y = _run_moe(svq, pms, x, ids, topk, x_per_slot, dt)
         assert y.shape == (m * topk, n)
         _check_slots(y, x, ids, topk, x_per_slot, Ws, range(n_exp), f"small moe m={m}")
-        if dt == torch.float32 and m * topk <= 64:
-            # per-slot exact path: bit-exact decode through one-hot rows
-            pass
     # one-hot slots: decoded weights of the routed experts, exactly (exact
     # path) or as RNE_bf16 (grouped bf16 path)
     cols = np.arange(m * topk if x_per_slot else m) * 7 % k
@@ -91,8 +88,10 @@ def test_moe128_m1(svq, proj):
         _check_slots(y, x, ids, synth.MOE_TOPK, x_per_slot, Ws, Ws.keys(), f"moe128 m=1 p{proj}")
 
 
-@pytest.mark.parametrize("proj", [0, 2])
+@pytest.mark.parametrize("proj", [0, 1, 2])
 def test_moe128_m512(svq, proj):
+    """Every routed slot of all 128 experts, both output types, against the
+    oracle (each expert decoded once, then dropped)."""
     bd = synth.moe_expert_bd()
     all_mats = [synth.moe_expert(e, proj, int(bd[e])) for e in range(synth.MOE_EXPERTS)]
     pms = [svq.pack(w) for w in all_mats]
@@ -100,12 +99,38 @@ def test_moe128_m512(svq, proj):
     ids = synth.moe_routing(m)
     x = synth.moe_activations(m, proj)
     x_per_slot = 1 if proj == 2 else 0
-    y = _run_moe(svq, pms, x, ids, synth.MOE_TOPK, x_per_slot, torch.bfloat16)
-    assert y.shape == (m * synth.MOE_TOPK, all_mats[0].n)
-    assert np.isfinite(y).all()
-    sample = np.random.default_rng(50 + proj).choice(synth.MOE_EXPERTS, 10, replace=False)
-    Ws = {}
-    for e in sample:
+    ys = {dt: _run_moe(svq, pms, x, ids, synth.MOE_TOPK, x_per_slot, dt)
+          for dt in (torch.bfloat16, torch.float32)}
+    for y in ys.values():
+        assert y.shape == (m * synth.MOE_TOPK, all_mats[0].n)
+        assert np.isfinite(y).all()
+    assert set(np.unique(ids)) == set(range(synth.MOE_EXPERTS))
+    for e in range(synth.MOE_EXPERTS):
         w = all_mats[e]
-        Ws[e] = so.decode_matrix(w.codes, w.n, w.k, w.bd, w.codebook, w.radius, w.perm)
-    _check_slots(y, x, ids, synth.MOE_TOPK, x_per_slot, Ws, sample, f"moe128 m=512 p{proj}")
+        We = so.decode_matrix(w.codes, w.n, w.k, w.bd, w.codebook, w.radius, w.perm)
+        for dt, y in ys.items():
+            _check_slots(y, x, ids, synth.MOE_TOPK, x_per_slot, {e: We}, [e],
+                         f"moe128 m=512 p{proj} {dt}")
+
+
+@pytest.mark.parametrize("m,topk", [(3, 4), (40, 4)])
+def test_moe_out_of_range_ids_are_skipped(svq, m, topk):
+    """Slots whose expert id is outside [0, E) get zero rows (per-slot path
+    for 12 slots, grouped path for 160); every other slot is unaffected."""
+    n_exp, n, k = 6, 40, 520
+    mats = [synth.random_matrix(n, k, 6 + e % 3, seed=(43, e, 0)) for e in range(n_exp)]
+    Ws = [so.decode_matrix(w.codes, n, k, w.bd, w.codebook, w.radius, w.perm) for w in mats]
+    pms = [svq.pack(w) for w in mats]
+    ids = _ids(m, topk, n_exp, 44 + m)
+    bad = np.arange(1, ids.size, 5)
+    ids[bad] = np.where(bad % 2 == 0, -1, n_exp + 3)
+    x = synth.random_activations(m, k, seed=(45, m, 0))
+    for dt in (torch.float32, torch.bfloat16):
+        y = _run_moe(svq, pms, x, ids, topk, 0, dt)
+        assert np.all(y[bad] == 0)
+        good = np.setdiff1d(np.arange(ids.size), bad)
+        for e in range(n_exp):
+            slots = good[ids[good] == e]
+            if slots.size:
+                assert_within_tolerance(y[slots], so.linear(x[slots // topk], Ws[e]), x[slots // topk],
+                                        Ws[e], label=f"valid slots of expert {e}")
