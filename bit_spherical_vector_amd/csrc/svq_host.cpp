@@ -293,10 +293,16 @@ static int plan_fused(GemvBatch &b) {
   const int slots = (total < 8192 ? 2 : 3) * device_cus();
   const int target = (int)((total + slots - 1) / slots);
   int R[GV_MAX_JOBS];
+  // a block's LDS grows with its row tiles (partial sums): R stays where the
+  // block still fits (R = 1 always does: the caller checked)
+  auto fits = [&](int j, int r) {
+    return gemv_fused_smem_bytes(b.job[j].w.k, b.job[j].w.units, b.job[j].w.bd, r) <= GV_LDS_LIMIT;
+  };
   for (int j = 0; j < b.count; ++j) {
     const int U = b.job[j].w.units;
     int r = (target + U / 2) / U;
     R[j] = r < 1 ? 1 : (r > GF_MAX_R ? GF_MAX_R : r);
+    while (R[j] > 1 && !fits(j, R[j])) --R[j];
   }
   auto blocks_of = [&](int j) { return (b.job[j].w.n_tiles + R[j] - 1) / R[j]; };
   auto total_blocks = [&]() {
@@ -308,7 +314,7 @@ static int plan_fused(GemvBatch &b) {
   while (total_blocks() > slots) {
     int best = -1;
     for (int j = 0; j < b.count; ++j)
-      if (R[j] < GF_MAX_R && blocks_of(j) > 1 &&
+      if (R[j] < GF_MAX_R && blocks_of(j) > 1 && fits(j, R[j] + 1) &&
           (best < 0 || R[j] * b.job[j].w.units < R[best] * b.job[best].w.units))
         best = j;
     if (best < 0) break;
@@ -417,7 +423,7 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
   // fit in LDS beside the tables
   size_t fused_smem = 0;
   for (int32_t j = 0; j < count; ++j) {
-    const size_t b = gemv_fused_smem_bytes(w[j].k, w[j].units, w[j].bd);
+    const size_t b = gemv_fused_smem_bytes(w[j].k, w[j].units, w[j].bd, 1);
     fused_smem = b > fused_smem ? b : fused_smem;
   }
   const bool fused = m == 1 && fused_smem <= GV_LDS_LIMIT;
@@ -475,7 +481,15 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
       if ((((uintptr_t)xs[j]) | ((uintptr_t)ldx[j] * 2)) & 15) b.xvec = 0;
     if (fused) {
       const int blocks = plan_fused(b);
-      e = launch_gemv_fused(b, blocks, fused_smem, s);
+      // LDS of the launch: the largest block of the plan (the partial sums
+      // grow with the row tiles per block)
+      size_t smem = 0;
+      for (int32_t j = 0; j < count; ++j) {
+        const size_t bj = gemv_fused_smem_bytes(b.job[j].w.k, b.job[j].w.units, b.job[j].w.bd, b.job[j].R);
+        smem = bj > smem ? bj : smem;
+      }
+      if (smem > GV_LDS_LIMIT) return SVQ_ERR_UNSUPPORTED;
+      e = launch_gemv_fused(b, blocks, smem, s);
       return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
     }
     int gather_blocks = 0;

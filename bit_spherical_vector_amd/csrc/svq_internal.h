@@ -140,18 +140,39 @@ constexpr int GV_UNITS_PER_WAVE = 4;  // units per wave the planner aims for
 // m = 1: one fused launch (gather in the block); R <= GF_MAX_R row tiles
 // per block, whose R x units items the 4 waves split into equal runs.
 constexpr int GF_MAX_R = 8;
-// LDS of the fused m = 1 block: radius table [0, 2 KB), direction rows from
-// 2 KB (16 lane-interleaved copies for bd <= 7, one copy for bd = 8), then
-// unit scales, cross-wave partial sums, the permuted activations and the
-// staging row.
-constexpr int GF_OFF_RTAB = 0;
-constexpr int GF_OFF_D = RTAB_BYTES;
-__host__ __device__ constexpr int gf_dir_bytes(int bd) { return bd >= 8 ? DTAB_BYTES : (16 << bd) * 16; }
-__host__ __device__ constexpr int gf_scale_off(int bd) { return GF_OFF_D + gf_dir_bytes(bd); }
-__host__ __device__ constexpr int gf_xp_off(int bd, int units, int m) {
-  return gf_scale_off(bd) + ((units * m * 4 + 15) & ~15) + GF_MAX_R * GV_WAVES * 4 * 4 * 4 * m;
+// LDS of the fused m = 1 block: the radius table (64 lane copies of the
+// 2^(10-bd) fp32 radii) [0, gf_off_d(bd)); then the direction copies (bd <= 7: 16 copies
+// of 2^bd rows at a 256-byte stride; bd = 8: 8 copies of 256 rows at a
+// 128-byte stride, sharing their region with the activation staging row,
+// which is dead once the gather is done); then unit scales, cross-wave
+// partial sums, the permuted activations and (bd <= 7) the staging row.
+constexpr int GF_OFF_R = 0;
+__host__ __device__ constexpr int gf_off_d(int bd) { return 256 << (10 - bd); }  // after 2^(10-bd) radii x 64 lanes
+__host__ __device__ constexpr int gf_dir_bytes(int bd) { return bd >= 8 ? 256 * 8 * 16 : (16 << bd) * 16; }
+struct GfLds {
+  int scale, red, xp, stage, total;
+};
+// r: row tiles per block (the cross-wave partial sums hold r tiles)
+__host__ __device__ inline GfLds gf_lds(int bd, int k, int units, int m, int r) {
+  GfLds L;
+  const int stage = (k * 2 + 15) & ~15, dir = gf_dir_bytes(bd);
+  int off = gf_off_d(bd) + (bd >= 8 ? (dir > stage ? dir : stage) : dir);
+  L.scale = off;
+  off += (units * m * 4 + 15) & ~15;
+  L.red = off;
+  off += r * GV_WAVES * 4 * 4 * 4 * m;
+  L.xp = off;
+  off += units * UNIT_SLOTS * 2 * m;
+  if (bd >= 8) {
+    L.stage = gf_off_d(bd);
+  } else {
+    L.stage = off;
+    off += stage;
+  }
+  L.total = off;
+  return L;
 }
-size_t gemv_fused_smem_bytes(int k, int units, int bd);  // one matrix
+size_t gemv_fused_smem_bytes(int k, int units, int bd, int r);  // one matrix, r row tiles per block
 hipError_t launch_gemv_fused(GemvBatch &b, int blocks, size_t smem, hipStream_t s);
 
 // Small-batch dequant path (EXACT_MAX_M < m <= SB_MAX_M): a prep launch

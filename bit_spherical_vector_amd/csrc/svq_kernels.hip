@@ -345,9 +345,9 @@ __device__ __forceinline__ void sign_carriers(uint64_t S01, uint64_t S23, uint32
 // above): tmp[ri][a] += R * dot(code, activation row a).  The four codes go
 // through each phase together (signs, first-half MFMAs, second-half MFMAs,
 // radius FMAs), so that independent MFMAs cover each other's latency.
-template <int M, int CI>
+template <int M, int CI, typename RT>
 __device__ __forceinline__ void gemv_group_mul(uint64_t S01, uint64_t S23, const u4 &A,
-                                              const u4 (&Din)[4], const _Float16 (&R)[4],
+                                              const u4 (&Din)[4], const RT (&R)[4],
                                               float (&tmp)[4][M]) {
   const uint32_t SM = 0x80008000u;
   const h4 A0 = __builtin_bit_cast(h4, (u2){A[0], A[1]});
@@ -630,76 +630,100 @@ hipError_t launch_gemv_batched(GemvBatch &b, int gather_blocks, int k_max, int b
 // below.
 constexpr int GF_PRE_UNITS = 5;    // permutation vectors prefetched per wave (gather)
 constexpr int GF_STAGE_BATCH = 5;  // 16-byte activation loads per thread per staging pass
-// Two table modes, chosen per block by the matrix's bd:
-// * mode 0 (bd <= 7): 16 lane-interleaved copies of the 2^bd direction rows
-//   (copy c of row d at d*256 + 16c, lane l reads copy l & 15: the 16 lanes
-//   of a ds_read_b128 pass hit 16 different bank groups), radii from the
-//   1024-entry table by 10-bit index;
-// * mode 1 (bd = 8): the 256 direction rows once (16 copies would take
-//   64 KB), and the four radii from two registers by v_perm_b32 (the radius
-//   index is then the code's two high index bits), which saves the radius
-//   read from LDS.
-// LDS: radius table [0, 2 KB), direction rows from 2 KB (GF_OFF_D), then at
-// per-block offsets: unit scales, cross-wave partial sums, the permuted
-// activations and the staging row.
+// Tables, per block by the matrix's bd (a template parameter):
+// * direction rows, lane-interleaved copies so that the lanes of one
+//   ds_read_b128 pass spread over the bank groups: bd <= 7: 16 copies at a
+//   256-byte row stride (copy c of row d at d*256 + 16c, lane l reads copy
+//   l & 15: the 16 lanes of a pass hit 16 different bank groups; the row
+//   address is one SDWA op); bd = 8: 8 copies at a 128-byte stride (32 KB,
+//   written over the staging row once the gather is done; two lanes of a
+//   pass share a bank group);
+// * radii: the 2^(10-bd) values in fp32, one copy per lane (R[r] of lane l
+//   at r*256 + 4l: every lane reads its own bank, so the read never
+//   conflicts).  The address r*256 + 4l is formed in at most three ops from
+//   the code planes: the low index byte's top 8 - bd bits go into byte 1 of
+//   a register whose byte 0 holds 4l (SDWA destination select), the two
+//   high index bits are shifted into place and or-ed in.
+// LDS map: gf_lds (svq_internal.h).
 
 // Table reads of the four codes of column group ci: direction rows (signs
 // not yet applied) and radii.
-// Radii of mode 1: fp16 R0..R3 as {rhi:rlo} bytes 0..7.
-struct GfRad {
-  uint32_t lo, hi, dmask;
-};
+// byte 1 of dst := (byte K of v) >> SH, the other bytes kept
+template <int K, int SH>
+__device__ __forceinline__ void byte_shr_to_b1(uint32_t &dst, uint32_t v) {
+  if (K == 0)
+    asm("v_lshrrev_b32_sdwa %0, %2, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_0"
+        : "+v"(dst) : "v"(v), "i"(SH));
+  else if (K == 1)
+    asm("v_lshrrev_b32_sdwa %0, %2, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_1"
+        : "+v"(dst) : "v"(v), "i"(SH));
+  else if (K == 2)
+    asm("v_lshrrev_b32_sdwa %0, %2, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_2"
+        : "+v"(dst) : "v"(v), "i"(SH));
+  else
+    asm("v_lshrrev_b32_sdwa %0, %2, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_3"
+        : "+v"(dst) : "v"(v), "i"(SH));
+}
 
-template <int CI, int MODE>
-__device__ __forceinline__ void gf_group_reads(const ItemCodes &c, const GfRad &rd, uint32_t (&dad)[4],
-                                               u4 (&D)[4], _Float16 (&R)[4]) {
+typedef __attribute__((address_space(3))) const float lds_f32_t;
+__device__ __forceinline__ float lds_f32(uint32_t addr) { return *(lds_f32_t *)(size_t)addr; }
+
+// dad: direction addresses (bd <= 7: byte 0 = the lane's copy * 16, byte 1
+// rewritten per code); rad: radius addresses (bd <= 7: byte 0 = 4 * lane,
+// byte 1 rewritten per code); loff: the lane's copy offset (bd = 8) and 4 * lane.
+template <int CI, int BD>
+__device__ __forceinline__ void gf_group_reads(const ItemCodes &c, uint32_t (&dad)[4], uint32_t (&rad)[4],
+                                               uint32_t loff, uint32_t lane4, u4 (&D)[4], float (&R)[4]) {
 #pragma unroll
   for (int ri = 0; ri < 4; ++ri) {
     const int i = 4 * ri + CI;
-    if constexpr (MODE == 0) {
-      byte_and_to_b1<CI>(dad[ri], rd.dmask, c.L[ri]);  // direction * 256 + copy * 16
-      const uint32_t lo2 = byte_shl<CI, 1>(c.L[ri]);    // low index byte * 2
-      const int sh = 9 - 2 * i;
+    uint32_t raddr;
+    if constexpr (BD <= 7) {
+      byte_and_to_b1<CI>(dad[ri], (1u << BD) - 1u, c.L[ri]);  // direction * 256 + copy * 16
+      byte_shr_to_b1<CI, BD>(rad[ri], c.L[ri]);                 // radius bits of the low byte, * 256
+      // the two high index bits, r bits 8-BD..9-BD, to address bits 16-BD..17-BD
+      const int sh = 16 - BD - 2 * i;  // unrolled: a constant
       const uint32_t hs = sh >= 0 ? c.H << sh : c.H >> -sh;
-      const uint32_t idx2 = (hs & 0x600u) | lo2;        // 10-bit index * 2
-      D[ri] = lds_u4(GF_OFF_D + dad[ri]);
-      R[ri] = lds_f16(GF_OFF_RTAB + idx2);
+      raddr = (hs & (3u << (16 - BD))) | rad[ri];
+      D[ri] = lds_u4(gf_off_d(BD) + dad[ri]);
     } else {
-      const uint32_t lo16 = byte_shl<CI, 4>(c.L[ri]);   // direction * 16
-      D[ri] = lds_u4(GF_OFF_D + lo16);
-      // radius index = index bits 8..9; bytes 2r, 2r+1 of {hi:lo}, zeros above
-      const uint32_t r = __builtin_amdgcn_ubfe(c.H, 2 * i, 2);
-      const uint32_t sel = r * 0x0202u + 0x0C0C0100u;
-      R[ri] = __builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_perm(rd.hi, rd.lo, sel));
+      // direction * 128 + copy * 16; radius = the two high index bits
+      const uint32_t d128 = byte_shl<CI, 7>(c.L[ri]);
+      const int sh = 8 - 2 * i;  // unrolled: a constant
+      const uint32_t hs = sh >= 0 ? c.H << sh : c.H >> -sh;
+      raddr = (hs & 0x300u) | lane4;
+      D[ri] = lds_u4(gf_off_d(BD) + (d128 | loff));
     }
+    R[ri] = lds_f32(GF_OFF_R + raddr);
   }
 }
 
 // One work item: the lane's 16 codes, column group by column group, with
 // the table reads of the next group issued before the current one is used.
-template <int M, int MODE>
-__device__ __forceinline__ void gf_item(const ItemCodes &c, const uint8_t *xu, const GfRad &rd,
-                                        uint32_t (&dad0)[4], uint32_t (&dad1)[4], float (&tmp)[4][M]) {
+template <int M, int BD>
+__device__ __forceinline__ void gf_item(const ItemCodes &c, const uint8_t *xu, uint32_t (&dad0)[4],
+                                        uint32_t (&dad1)[4], uint32_t (&rad0)[4], uint32_t (&rad1)[4],
+                                        uint32_t loff, uint32_t lane4, float (&tmp)[4][M]) {
   const uint64_t S01 = (uint64_t)c.S[0] | ((uint64_t)c.S[1] << 32);
   const uint64_t S23 = (uint64_t)c.S[2] | ((uint64_t)c.S[3] << 32);
   u4 D0[4], D1[4];
-  _Float16 R0[4], R1[4];
+  float R0[4], R1[4];
   // phases are kept in this order (scheduling barriers): the reads of group
   // g + 1 are in flight while group g is decoded and multiplied
   u4 A0 = *(const u4 *)(xu);
-  gf_group_reads<0, MODE>(c, rd, dad0, D0, R0);
+  gf_group_reads<0, BD>(c, dad0, rad0, loff, lane4, D0, R0);
   u4 A1 = *(const u4 *)(xu + 256);
-  gf_group_reads<1, MODE>(c, rd, dad1, D1, R1);
+  gf_group_reads<1, BD>(c, dad1, rad1, loff, lane4, D1, R1);
   __builtin_amdgcn_sched_barrier(0);
   gemv_group_mul<M, 0>(S01, S23, A0, D0, R0, tmp);
   __builtin_amdgcn_sched_barrier(0);
   A0 = *(const u4 *)(xu + 512);
-  gf_group_reads<2, MODE>(c, rd, dad0, D0, R0);
+  gf_group_reads<2, BD>(c, dad0, rad0, loff, lane4, D0, R0);
   __builtin_amdgcn_sched_barrier(0);
   gemv_group_mul<M, 1>(S01, S23, A1, D1, R1, tmp);
   __builtin_amdgcn_sched_barrier(0);
   A1 = *(const u4 *)(xu + 768);
-  gf_group_reads<3, MODE>(c, rd, dad1, D1, R1);
+  gf_group_reads<3, BD>(c, dad1, rad1, loff, lane4, D1, R1);
   __builtin_amdgcn_sched_barrier(0);
   gemv_group_mul<M, 2>(S01, S23, A0, D0, R0, tmp);
   __builtin_amdgcn_sched_barrier(0);
@@ -707,20 +731,20 @@ __device__ __forceinline__ void gf_item(const ItemCodes &c, const uint8_t *xu, c
 }
 
 // XVEC: every activation row starts 16-byte aligned (vector staging loads).
-// MODE: table mode (see above), 1 for bd = 8.
-template <int M, bool XVEC, int MODE>
+// BD: the matrix's direction bits (table layout, see above).
+template <int M, bool XVEC, int BD>
 __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ x, int64_t ldx,
                                  void *__restrict__ y, int64_t ldy, int ydt, int rt0, int R,
                                  int Reff, uint8_t *smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int U = w.units, Kp = U * UNIT_SLOTS, K = w.k;
-  const int bd = w.bd, rows = 1 << bd;
-  _Float16 *s_rtab = (_Float16 *)(smem + GF_OFF_RTAB);
-  float *s_scale = (float *)(smem + gf_scale_off(bd));    // [U][M] 2^-e per unit
-  float *s_red = s_scale + ((U * M + 3) & ~3);            // [GF_MAX_R][W][4][M][4]
-  uint16_t *s_xp = (uint16_t *)(smem + gf_xp_off(bd, U, M));  // [M][Kp] fp16
-  uint16_t *s_stage = s_xp + (size_t)M * Kp;              // [K] bf16
+  constexpr int rows = 1 << BD;
+  const GfLds L = gf_lds(BD, K, U, M, R);
+  float *s_scale = (float *)(smem + L.scale);             // [U][M] 2^-e per unit
+  float *s_red = (float *)(smem + L.red);                 // [GF_MAX_R][W][4][M][4]
+  uint16_t *s_xp = (uint16_t *)(smem + L.xp);             // [M][Kp] fp16
+  uint16_t *s_stage = (uint16_t *)(smem + L.stage);       // [K] bf16
   const int n8 = K / 8;
 
   // this wave's work: items [i_begin, i_end) of the block's Reff x U items
@@ -729,7 +753,6 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   const int i_begin = gf_wave_begin(n_items, GV_WAVES, wv);
   const int i_end = gf_wave_begin(n_items, GV_WAVES, wv + 1);
   const uint8_t *codes0 = w.base + w.off_codes + (size_t)rt0 * U * UNIT_BYTES;
-  (void)R;
   // this wave's share of the gather: units [g_lo, g_hi]
   const int gper = (U + GV_WAVES - 1) >> 2;
   const int g_lo = wv * gper, g_hi = min(U, g_lo + gper) - 1;
@@ -739,7 +762,13 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   // permutation vectors of the wave's gather units and the first staging
   // pass of every activation row; the codes follow once row 0 is staged.
   const u4 drow = ((const u4 *)(w.base + w.off_dtab))[tid & (rows - 1)];
-  const u2 rrow = ((const u2 *)(w.base + w.off_rtab))[tid];
+  // radii for the lane-copy table: entry e = r * 64 + lane, R[r] at 10-bit
+  // index r << BD of the packed radius table
+  constexpr int nrad = 1 << (10 - BD);
+  _Float16 rv[(nrad * 64 + 255) / 256];
+  const _Float16 *rtab = (const _Float16 *)(w.base + w.off_rtab);
+#pragma unroll
+  for (int q = 0; q < (nrad * 64 + 255) / 256; ++q) rv[q] = rtab[((tid + 256 * q) >> 6) << BD];
   const uint16_t *perm = (const uint16_t *)(w.base + w.off_perm);
   u4 pvec[GF_PRE_UNITS];
 #pragma unroll
@@ -757,17 +786,17 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   int ul = i_begin;  // next item to load
   // every (tile, wave) slot of the tile sums starts at zero: a wave adds
   // only the tiles its run touches
-  for (int e = tid; e < GF_MAX_R * GV_WAVES * 4 * M * 4; e += 256) s_red[e] = 0.f;
-  if constexpr (MODE == 0) {
+  for (int e = tid; e < R * GV_WAVES * 4 * M * 4; e += 256) s_red[e] = 0.f;
+#pragma unroll
+  for (int q = 0; q < (nrad * 64 + 255) / 256; ++q)
+    if (tid + 256 * q < nrad * 64) ((float *)(smem + GF_OFF_R))[tid + 256 * q] = (float)rv[q];
+  if constexpr (BD <= 7) {
     // 16 copies of each row; the copy index rotates with the row so that the
     // lanes of one store hit different bank groups
     for (int e = tid; e < rows * 16; e += 256) {
-      const int row = e & (rows - 1), cp = ((e >> bd) + row) & 15;
-      *(u4 *)(smem + GF_OFF_D + (row * 16 + cp) * 16) = drow;
+      const int row = e & (rows - 1), cp = ((e >> BD) + row) & 15;
+      *(u4 *)(smem + gf_off_d(BD) + (row * 16 + cp) * 16) = drow;
     }
-    ((u2 *)s_rtab)[tid] = rrow;
-  } else {
-    *(u4 *)(smem + GF_OFF_D + tid * 16) = drow;
   }
 
   // fp16 copy of gathered unit uu of activation row a with its exact
@@ -863,6 +892,16 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
       gather_store(a, uu, w8, wave_max(m1));
     }
   }
+  if constexpr (BD == 8) {
+    // the 8 direction copies go over the staging row, now that every gather
+    // has read it
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = tid, cp = (q + row) & 7;
+      *(u4 *)(smem + gf_off_d(BD) + row * 128 + cp * 16) = drow;
+    }
+  }
   __syncthreads();  // gathered activations, scales and tables are visible
 
   // lane 4b + j reads activation row j (row 0 when j >= M) of code column
@@ -874,19 +913,15 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
   for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
     for (int a = 0; a < M; ++a) acc[ri][a] = 0.f;
-  GfRad rd;
-  rd.dmask = (uint32_t)(rows - 1);
-  if constexpr (MODE == 1) {
-    // R[r] sits at 10-bit index r << 8 of the radius table
-    const uint16_t *rt = (const uint16_t *)(w.base + w.off_rtab);
-    rd.lo = (uint32_t)rt[0] | ((uint32_t)rt[256] << 16);
-    rd.hi = (uint32_t)rt[512] | ((uint32_t)rt[768] << 16);
-  } else {
-    rd.lo = rd.hi = 0;
-  }
-  uint32_t dad0[4], dad1[4];  // mode 0: byte 0 = the lane's copy * 16
+  const uint32_t lane4 = (uint32_t)lane << 2;
+  const uint32_t loff = (uint32_t)(lane & 7) << 4;  // bd = 8: the lane's copy
+  uint32_t dad0[4], dad1[4];  // bd <= 7: byte 0 = the lane's copy * 16
+  uint32_t rad0[4], rad1[4];  // bd <= 7: byte 0 = 4 * lane
 #pragma unroll
-  for (int ri = 0; ri < 4; ++ri) dad0[ri] = dad1[ri] = (uint32_t)(lane & 15) << 4;
+  for (int ri = 0; ri < 4; ++ri) {
+    dad0[ri] = dad1[ri] = (uint32_t)(lane & 15) << 4;
+    rad0[ri] = rad1[ri] = lane4;
+  }
 
   auto step = [&](const ItemCodes &c, int u) __attribute__((always_inline)) {
     // items are scheduled one at a time: interleaving several items only
@@ -897,7 +932,7 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
       for (int a = 0; a < M; ++a) tmp[ri][a] = 0.f;
-    gf_item<M, MODE>(c, xa + (size_t)u * (UNIT_CODES * 16), rd, dad0, dad1, tmp);
+    gf_item<M, BD>(c, xa + (size_t)u * (UNIT_CODES * 16), dad0, dad1, rad0, rad1, loff, lane4, tmp);
 #pragma unroll
     for (int a = 0; a < M; ++a) {
       const float sc = s_scale[u * M + a];
@@ -987,9 +1022,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
   const int rt0 = ((int)blockIdx.x - b.starts.first[j]) * jb.R;
   const int Reff = min(jb.R, jb.w.n_tiles - rt0);
   if (jb.w.bd >= 8)
-    gemv_fused_block<1, XVEC, 1>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
+    gemv_fused_block<1, XVEC, 8>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
+  else if (jb.w.bd == 7)
+    gemv_fused_block<1, XVEC, 7>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
   else
-    gemv_fused_block<1, XVEC, 0>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
+    gemv_fused_block<1, XVEC, 6>(jb.w, jb.x, jb.ldx, jb.y, jb.ldy, b.ydt, rt0, jb.R, Reff, smem);
 }
 
 
@@ -1033,12 +1070,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   }
   const MatView w = expert_view(sh, tab, e);
   const int src = x_per_slot ? q : q / topk;
+  const int reff = min(R, w.n_tiles - rt0);
   if (w.bd >= 8)
-    gemv_fused_block<1, XVEC, 1>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, min(R, w.n_tiles - rt0),
-                                 smem);
+    gemv_fused_block<1, XVEC, 8>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, reff, smem);
+  else if (w.bd == 7)
+    gemv_fused_block<1, XVEC, 7>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, reff, smem);
   else
-    gemv_fused_block<1, XVEC, 0>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, min(R, w.n_tiles - rt0),
-                                 smem);
+    gemv_fused_block<1, XVEC, 6>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, reff, smem);
 }
 
 // Routing for the grouped GEMM: counting sort of slots by expert and a list
@@ -1171,22 +1209,23 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   if (S <= MOE_EXACT_MAX_SLOTS) {
     *need = 256;
     if (!ws) return hipSuccess;
+    // row tiles per block: about 5 units per wave to amortise the gather,
+    // while the launch keeps >= 256 blocks
+    constexpr int ITEMS_PER_WAVE = 5;
+    int R = sh.units <= ITEMS_PER_WAVE ? 4 : (sh.units <= 2 * ITEMS_PER_WAVE ? 2 : 1);
+    while (R > 1 && ((sh.n_tiles + R - 1) / R) * S < 256) R /= 2;
     size_t smem = 0;
     for (int e = 0; e < E; ++e) {
-      const size_t b = gemv_fused_smem_bytes(sh.k, sh.units, experts[e].bd);
+      const size_t b = gemv_fused_smem_bytes(sh.k, sh.units, experts[e].bd, R);
       smem = b > smem ? b : smem;
     }
+    if (smem > GV_LDS_LIMIT) return hipErrorInvalidValue;
     const bool xvec = ((((uintptr_t)x) | ((uintptr_t)ldx * 2)) & 15) == 0;
     static const hipError_t lds_ok_t = check_no_static_lds(moe_gemv_kernel<true>);
     static const hipError_t lds_ok_f = check_no_static_lds(moe_gemv_kernel<false>);
     if ((xvec ? lds_ok_t : lds_ok_f) != hipSuccess) return xvec ? lds_ok_t : lds_ok_f;
     hipError_t e = xvec ? allow_smem(moe_gemv_kernel<true>, smem) : allow_smem(moe_gemv_kernel<false>, smem);
     if (e != hipSuccess) return e;
-    // row tiles per block: about 5 units per wave to amortise the gather,
-    // while the launch keeps >= 256 blocks
-    constexpr int ITEMS_PER_WAVE = 5;
-    int R = sh.units <= ITEMS_PER_WAVE ? 4 : (sh.units <= 2 * ITEMS_PER_WAVE ? 2 : 1);
-    while (R > 1 && ((sh.n_tiles + R - 1) / R) * S < 256) R /= 2;
     const dim3 grid((sh.n_tiles + R - 1) / R, S);
     if (xvec)
       hipLaunchKernelGGL(moe_gemv_kernel<true>, grid, dim3(256), smem, s, sh, tab, ids, xp, ldx,

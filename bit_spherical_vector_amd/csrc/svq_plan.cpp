@@ -12,9 +12,10 @@ size_t gemv_smem_bytes(int m, int bd_max, int r_max) {
          (size_t)r_max * GV_WAVES * 64 * m * 4;
 }
 
-// LDS of one fused block at m = 1 for a matrix of k channels, `units` units.
-size_t gemv_fused_smem_bytes(int k, int units, int bd) {
-  return (size_t)gf_xp_off(bd, units, 1) + (size_t)units * UNIT_SLOTS * 2 + (size_t)k * 2;
+// LDS of one fused block at m = 1 for a matrix of k channels, `units` units,
+// r row tiles per block.
+size_t gemv_fused_smem_bytes(int k, int units, int bd, int r) {
+  return (size_t)gf_lds(bd, k, units, 1, r).total;
 }
 
 // Items per block: all blocks of a call resident at once (two 4-wave

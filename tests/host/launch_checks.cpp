@@ -75,7 +75,7 @@ hipError_t launch_gemv_fused(GemvBatch &b, int blocks, size_t smem, hipStream_t)
     const MatView &w = J.w;
     CHECK(b.starts.first[j] == next && J.block_begin == next, "job %d starts at %d", j, next);
     CHECK(J.R >= 1 && J.R <= GF_MAX_R, "R %d", J.R);
-    CHECK(gemv_fused_smem_bytes(w.k, w.units, w.bd) <= smem, "job %d LDS", j);
+    CHECK(gemv_fused_smem_bytes(w.k, w.units, w.bd, J.R) <= smem, "job %d LDS", j);
     const int nb = (w.n_tiles + J.R - 1) / J.R;
     for (int blk = 0; blk < nb; ++blk) {
       const int rt0 = blk * J.R, Reff = w.n_tiles - rt0 < J.R ? w.n_tiles - rt0 : J.R;
