@@ -72,6 +72,7 @@ __device__ __forceinline__ MatView expert_view(const MoeShape &sh, const ExpertT
   v.off_dtab = sh.off_dtab;
   v.off_rtab = sh.off_rtab;
   v.off_btab = sh.off_btab;
+  v.off_xtab = sh.off_xtab;
   v.off_perm = sh.off_perm;
   v.off_codes = sh.off_codes;
   v.n = sh.n;

@@ -5,6 +5,7 @@
 // Fig. 6 caption (subvectors multiply reordered activations).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 #include <vector>
 
@@ -53,6 +54,57 @@ float half_to_float(uint16_t h) {
   return f;
 }
 
+// double -> IEEE binary16 bits, round to nearest even; |v| below 65520.
+uint16_t double_to_half(double v) {
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  const double a = std::fabs(v);
+  if (a == 0.0) return sign;
+  int e = 0;
+  std::frexp(a, &e);                  // a = f * 2^e, f in [0.5, 1)
+  const int qexp = e - 11 < -24 ? -24 : e - 11;  // quantum: 11 significant bits, or subnormal
+  const double r = std::nearbyint(std::ldexp(a, -qexp)) * std::ldexp(1.0, qexp);  // ties to even
+  if (r < std::ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)std::ldexp(r, 24));
+  int re = 0;
+  const double rf = std::frexp(r, &re);  // r = rf * 2^re, rf in [0.5, 1)
+  const uint32_t mant = (uint32_t)std::ldexp(rf, 11) - 1024;
+  return (uint16_t)(sign | (uint16_t)((re - 1 + 15) << 10) | (uint16_t)mant);
+}
+
+// The exact split of a matrix's weights for the small-batch path: for the
+// 1024 index values (direction d, radius r) and lanes l, v = R[r]*D[d][l]
+// times 2^s is the sum of two fp16 values hi = RNE_fp16(v) and lo = v - hi.
+// s puts the largest |v| in [2^14, 2^15); the split exists when every lo is
+// itself an fp16 value (the low bits of v stay above the fp16 quantum).
+// Fills xtab (row idx: hi[8] then lo[8]) and returns s, or
+// SVQ_NO_EXACT_SPLIT.
+int32_t exact_split(const svq_matrix_desc *d, uint16_t *xtab) {
+  const uint32_t dmask = (1u << d->bd) - 1;
+  double vmax = 0.0;
+  for (int idx = 0; idx < 1024; ++idx)
+    for (int l = 0; l < 8; ++l) {
+      const double v = (double)half_to_float(d->radius_table[idx >> d->bd]) *
+                       (double)half_to_float(d->dir_codebook[(idx & dmask) * 8 + l]);
+      vmax = std::fabs(v) > vmax ? std::fabs(v) : vmax;
+    }
+  if (!(vmax > 0.0) || !std::isfinite(vmax)) return SVQ_NO_EXACT_SPLIT;
+  int e = 0;
+  std::frexp(vmax, &e);  // vmax in [2^(e-1), 2^e)
+  const int32_t sexp = 15 - e;
+  for (int idx = 0; idx < 1024; ++idx)
+    for (int l = 0; l < 8; ++l) {
+      const double v = std::ldexp((double)half_to_float(d->radius_table[idx >> d->bd]) *
+                                      (double)half_to_float(d->dir_codebook[(idx & dmask) * 8 + l]),
+                                  sexp);
+      const uint16_t hi = double_to_half(v);
+      const double lo = v - (double)half_to_float(hi);  // exact: both share v's quantum
+      const uint16_t lob = double_to_half(lo);
+      if ((double)half_to_float(lob) != lo) return SVQ_NO_EXACT_SPLIT;
+      xtab[idx * 16 + l] = hi;
+      xtab[idx * 16 + 8 + l] = lob;
+    }
+  return sexp;
+}
+
 // float -> bfloat16 bits, round to nearest even.
 uint16_t float_to_bf16(float f) {
   uint32_t u;
@@ -64,7 +116,7 @@ uint16_t float_to_bf16(float f) {
 
 struct Layout {
   int32_t n_tiles, units;
-  size_t off_dtab, off_rtab, off_btab, off_perm, off_codes, padded_code_bytes, bytes;
+  size_t off_dtab, off_rtab, off_btab, off_xtab, off_perm, off_codes, padded_code_bytes, bytes;
 };
 
 Layout make_layout(int32_t n, int32_t k) {
@@ -78,6 +130,8 @@ Layout make_layout(int32_t n, int32_t k) {
   off += align256(RTAB_BYTES);
   L.off_btab = off;
   off += align256(BTAB_BYTES);
+  L.off_xtab = off;
+  off += align256(XTAB_BYTES);
   L.off_perm = off;
   off += align256((size_t)L.units * UNIT_SLOTS * 2);  // zero padded to the unit width
   L.off_codes = off;
@@ -110,13 +164,15 @@ svq_status validate_handle(const svq_handle *w) {
   const Layout L = make_layout(w->n, w->k);
   if (w->n_tiles != L.n_tiles || w->units != L.units || w->off_codes != L.off_codes ||
       w->off_dtab != L.off_dtab || w->off_rtab != L.off_rtab || w->off_btab != L.off_btab ||
+      w->off_xtab != L.off_xtab ||
       w->off_perm != L.off_perm || w->bytes != L.bytes)
     return SVQ_ERR_INVALID_ARG;
   return SVQ_OK;
 }
 
-// Build the whole packed image on the host.
-void build_image(const svq_matrix_desc *d, const Layout &L, std::vector<uint8_t> &img) {
+// Build the whole packed image on the host; returns the exact split's power
+// of two (or SVQ_NO_EXACT_SPLIT).
+int32_t build_image(const svq_matrix_desc *d, const Layout &L, std::vector<uint8_t> &img) {
   img.assign(L.bytes, 0);
   const uint32_t dmask = (1u << d->bd) - 1;
   // direction rows by low index byte
@@ -133,6 +189,7 @@ void build_image(const svq_matrix_desc *d, const Layout &L, std::vector<uint8_t>
     for (int l = 0; l < 8; ++l)
       btab[idx * 8 + l] = float_to_bf16(R * half_to_float(d->dir_codebook[dd * 8 + l]));
   }
+  const int32_t xscale = exact_split(d, (uint16_t *)(img.data() + L.off_xtab));
   uint16_t *perm = (uint16_t *)(img.data() + L.off_perm);
   for (int p = 0; p < d->k; ++p) perm[p] = (uint16_t)d->perm[p];
 
@@ -166,6 +223,7 @@ void build_image(const svq_matrix_desc *d, const Layout &L, std::vector<uint8_t>
       *H |= (idx >> 8) << (2 * kb);
     }
   }
+  return xscale;
 }
 
 MatView view_of(const svq_handle *w) {
@@ -174,6 +232,7 @@ MatView view_of(const svq_handle *w) {
   v.off_dtab = (uint32_t)w->off_dtab;
   v.off_rtab = (uint32_t)w->off_rtab;
   v.off_btab = (uint32_t)w->off_btab;
+  v.off_xtab = (uint32_t)w->off_xtab;
   v.off_perm = (uint32_t)w->off_perm;
   v.off_codes = w->off_codes;
   v.n = w->n;
@@ -215,7 +274,7 @@ svq_status svq_pack(const svq_matrix_desc *src, void *dst_dev, size_t *dst_bytes
   }
   if (!out) return SVQ_ERR_INVALID_ARG;
   std::vector<uint8_t> img;
-  build_image(src, L, img);
+  const int32_t xscale = build_image(src, L, img);
   hipStream_t s = (hipStream_t)stream;
   if (hipMemcpyAsync(dst_dev, img.data(), L.bytes, hipMemcpyHostToDevice, s) != hipSuccess)
     return SVQ_ERR_HIP;
@@ -231,6 +290,8 @@ svq_status svq_pack(const svq_matrix_desc *src, void *dst_dev, size_t *dst_bytes
   out->off_dtab = L.off_dtab;
   out->off_rtab = L.off_rtab;
   out->off_btab = L.off_btab;
+  out->off_xtab = L.off_xtab;
+  out->xscale_log2 = xscale;
   out->off_perm = L.off_perm;
   out->off_codes = L.off_codes;
   out->code_bytes = ((uint64_t)src->n * (uint64_t)(src->k / 8) * 18 + 7) / 8;
@@ -412,6 +473,38 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
     u_max = w[j].units > u_max ? w[j].units : u_max;
   }
   const bool exact = m <= EXACT_MAX_M;
+  bool split_ok = true;
+  for (int32_t j = 0; j < count; ++j)
+    if (w[j].xscale_log2 == SVQ_NO_EXACT_SPLIT || w[j].xscale_log2 < -120 || w[j].xscale_log2 > 120)
+      split_ok = false;
+  if (!exact && m <= SB_MAX_M && !split_ok) {
+    // tables without an exact fp16 split: the m <= 4 kernels, four
+    // activation rows at a time (each chunk's workspace is the same size)
+    size_t need4 = 0;
+    svq_status st = linear_impl(w, count, nullptr, ldx, EXACT_MAX_M, nullptr, ldy, ydt, nullptr, &need4,
+                                stream);
+    if (st != SVQ_OK) return st;
+    if (!workspace) {
+      *workspace_bytes = need4;
+      return SVQ_OK;
+    }
+    if (!xs || !ys || !ldx || !ldy) return SVQ_ERR_INVALID_ARG;
+    const size_t esz = ydt == SVQ_BF16 ? 2 : 4;
+    for (int64_t r0 = 0; r0 < m; r0 += EXACT_MAX_M) {
+      const void *xc[GV_MAX_JOBS];
+      void *yc[GV_MAX_JOBS];
+      for (int32_t j = 0; j < count; ++j) {
+        if (!xs[j] || !ys[j]) return SVQ_ERR_INVALID_ARG;
+        xc[j] = (const uint16_t *)xs[j] + r0 * ldx[j];
+        yc[j] = (uint8_t *)ys[j] + (size_t)(r0 * ldy[j]) * esz;
+      }
+      size_t cap = *workspace_bytes;
+      const int64_t mc = m - r0 < EXACT_MAX_M ? m - r0 : EXACT_MAX_M;
+      st = linear_impl(w, count, xc, ldx, mc, yc, ldy, ydt, workspace, &cap, stream);
+      if (st != SVQ_OK) return st;
+    }
+    return SVQ_OK;
+  }
   const bool small = !exact && m <= SB_MAX_M;
   int sb_items = 0;
   if (small) {
@@ -522,7 +615,9 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
       J.groups = pl.groups;
       J.splits = pl.splits;
       J.xa = ws;
-      uint8_t *p = ws + align256((size_t)J.w.units * SB_XA_UNIT_BYTES);
+      J.xs = (float *)(ws + align256((size_t)J.w.units * SB_XA_UNIT_BYTES));
+      J.xinv = std::ldexp(1.0f, -w[j].xscale_log2);
+      uint8_t *p = (uint8_t *)J.xs + align256((size_t)J.w.units * 16 * 4);
       if (J.splits > 1) {
         J.part = (float *)p;
         p += align256((size_t)J.groups * J.tiles * J.splits * 1024);
@@ -543,7 +638,7 @@ static svq_status linear_impl(const svq_handle *w, int32_t count, const void *co
       J.block_begin = blocks;
       blocks += J.groups * J.splits;
       J.prep_begin = prep_blocks;
-      prep_blocks += 4 * J.w.units;
+      prep_blocks += J.w.units;
       b.starts.first[j] = J.block_begin;
       b.prep_starts.first[j] = J.prep_begin;
     }

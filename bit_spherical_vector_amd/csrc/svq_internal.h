@@ -50,6 +50,7 @@ constexpr int PLANE_HIGH = 2048;
 constexpr int DTAB_BYTES = 256 * 16;
 constexpr int RTAB_BYTES = 1024 * 2;  // radius by 10-bit index, fp16
 constexpr int BTAB_BYTES = 1024 * 16;
+constexpr int XTAB_BYTES = 1024 * 32;
 constexpr int EXACT_MAX_M = 4;    // m <= 4: exact fp32 decode path
 constexpr int MAX_EXPERTS = 256;
 
@@ -76,7 +77,7 @@ hipError_t scratch_ptr(void **ptr);
 // Matrix view passed to kernels by value.
 struct MatView {
   const uint8_t *base;  // packed buffer
-  uint32_t off_dtab, off_rtab, off_btab, off_perm;
+  uint32_t off_dtab, off_rtab, off_btab, off_xtab, off_perm;
   uint64_t off_codes;
   int32_t n, k, bd;
   int32_t n_tiles, units;
@@ -175,10 +176,12 @@ __host__ __device__ inline GfLds gf_lds(int bd, int k, int units, int m, int r) 
 size_t gemv_fused_smem_bytes(int k, int units, int bd, int r);  // one matrix, r row tiles per block
 hipError_t launch_gemv_fused(GemvBatch &b, int blocks, size_t smem, hipStream_t s);
 
-// Small-batch dequant path (EXACT_MAX_M < m <= SB_MAX_M): a prep launch
-// writes every matrix's permuted activations as 16-row MFMA fragments (xa:
-// unit u at xa + u * SB_XA_UNIT_BYTES), then one launch decodes each code
-// straight into a 16x16x32 bf16 MFMA operand.  Work item = one coded unit of
+// Small-batch path (EXACT_MAX_M < m <= SB_MAX_M): a prep launch writes
+// every matrix's permuted activations as 16-row fp16 MFMA fragments with a
+// power-of-two scale per (activation row, unit) (xa: unit u at
+// xa + u * SB_XA_UNIT_BYTES; xs: the unit's 16 inverse scales at
+// xs + 16 u), then one launch decodes each code straight into two 16x16x32
+// fp16 MFMA operands, the halves of the exact split of R*D (xtab).  Work item = one coded unit of
 // one row tile.  A block of SB_WAVES waves owns `tiles` consecutive row
 // tiles and one K range of `upr` units (block lb of a job: group
 // lb / splits, range lb % splits); its tiles x units items, unit-major, are
@@ -198,7 +201,9 @@ struct SbJob {
   MatView w;
   const uint16_t *x;    // activations, bf16 [m][ldx]
   int64_t ldx;
-  uint8_t *xa;          // fragment-ordered activations (workspace)
+  uint8_t *xa;          // fragment-ordered fp16 activations (workspace)
+  float *xs;            // their inverse scales, [units][16] (workspace)
+  float xinv;           // 2^-xscale_log2 of the matrix's exact split
   float *part;          // splits > 1: partial tiles (workspace)
   int32_t *cnt;         // splits > 1: arrival counters (workspace)
   void *y;
@@ -318,7 +323,7 @@ struct ExpertTable {
 };
 
 struct MoeShape {
-  uint32_t off_dtab, off_rtab, off_btab, off_perm;
+  uint32_t off_dtab, off_rtab, off_btab, off_xtab, off_perm;
   uint64_t off_codes;
   int32_t n, k, n_tiles, units;
   int32_t num_experts;

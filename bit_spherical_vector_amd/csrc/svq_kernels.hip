@@ -1192,6 +1192,7 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   sh.off_dtab = (uint32_t)h0.off_dtab;
   sh.off_rtab = (uint32_t)h0.off_rtab;
   sh.off_btab = (uint32_t)h0.off_btab;
+  sh.off_xtab = (uint32_t)h0.off_xtab;
   sh.off_perm = (uint32_t)h0.off_perm;
   sh.off_codes = h0.off_codes;
   sh.n = h0.n;

@@ -47,7 +47,7 @@ SbPlan sb_plan(int n_tiles, int units, int items) {
 
 size_t sb_ws_bytes(int n_tiles, int units, int items) {
   const SbPlan p = sb_plan(n_tiles, units, items);
-  size_t bytes = align256((size_t)units * SB_XA_UNIT_BYTES);
+  size_t bytes = align256((size_t)units * SB_XA_UNIT_BYTES) + align256((size_t)units * 16 * 4);
   if (p.splits > 1)
     bytes += align256((size_t)p.groups * p.tiles * p.splits * 1024) + align256((size_t)p.groups * 4);
   return bytes;

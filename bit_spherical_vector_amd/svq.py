@@ -37,6 +37,7 @@ EXPORTED = ("svq_pack", "svq_linear", "svq_linear_batched", "svq_linear_noalloc"
             "svq_moe_linear", "svq_encode", "svq_esg_perm", "svq_abs_select",
             "svq_status_string")
 SVQ_SCRATCH_BYTES = 64 << 20
+SVQ_NO_EXACT_SPLIT = -(1 << 31)
 
 
 class SvqError(RuntimeError):
@@ -61,9 +62,11 @@ class Handle(ctypes.Structure):
         ("bd", ctypes.c_int32), ("br", ctypes.c_int32),
         ("n_tiles", ctypes.c_int32), ("units", ctypes.c_int32),
         ("off_dtab", ctypes.c_uint64), ("off_rtab", ctypes.c_uint64),
-        ("off_btab", ctypes.c_uint64), ("off_perm", ctypes.c_uint64),
+        ("off_btab", ctypes.c_uint64), ("off_xtab", ctypes.c_uint64),
+        ("off_perm", ctypes.c_uint64),
         ("off_codes", ctypes.c_uint64), ("code_bytes", ctypes.c_uint64),
         ("padded_code_bytes", ctypes.c_uint64), ("bytes", ctypes.c_uint64),
+        ("xscale_log2", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 

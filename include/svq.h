@@ -26,17 +26,21 @@
  *     perm[p] (a gather permutation);
  *   - y[m, i] = sum_j What[i, j] * x[m, j]  with x bf16, y bf16 or fp32.
  *
- * Numerics.  For m <= 4 (the batch-1/small-batch GEMV path) each decoded
+ * Numerics.  For m <= 16 (the batch-1 and small-batch paths) each decoded
  * weight is the exact fp32 product R*D (fp16 x fp16 fits in 22 bits) and
- * accumulation is fp32.  The activations enter the dot products as fp16
+ * accumulation is fp32: for m <= 4 the radius multiplies an fp16 dot
+ * product in fp32; for 4 < m <= 16 the weight enters the matrix cores as
+ * two fp16 halves whose sum is R*D*2^s exactly (s per matrix, chosen and
+ * verified by svq_pack; tables that admit no such split are multiplied
+ * four activation rows at a time by the m <= 4 kernels instead).  The activations enter the dot products as fp16
  * after a power-of-two scale chosen per 512-slot block of permuted inputs
  * (per row of x): the block's largest magnitude is scaled into [2^14, 2^15),
  * which keeps every bf16 value of magnitude at least 2^-31 times that
  * largest one exact; smaller values round to fp16 subnormals (an absolute
- * error of at most 2^-39 times the block's largest magnitude).  For m > 4
- * (skinny and prefill GEMM on the matrix cores) a weight enters as
- * RNE_bf16(R*D) with its sign, x as bf16, accumulation fp32.  bf16 outputs
- * are rounded to nearest even.
+ * error of at most 2^-39 times the block's largest magnitude).  For m > 16
+ * (the dequant GEMM on the matrix cores) a weight enters as RNE_bf16(R*D)
+ * with its sign, x as bf16, accumulation fp32.  bf16 outputs are rounded to
+ * nearest even.
  *
  * Ownership.  The caller owns every byte: the packed matrix buffer and the
  * workspace are device memory the caller allocates (size queries below);
@@ -101,12 +105,17 @@ typedef struct {
   uint64_t off_dtab; /* 256 x 8 fp16: direction rows by low index byte  */
   uint64_t off_rtab; /* 16 fp16: radius by radius index (zero padded)   */
   uint64_t off_btab; /* 1024 x 8 bf16: RNE_bf16(R[r] * D[d][l]) by index */
+  uint64_t off_xtab; /* 1024 x (8 + 8) fp16: hi + lo = R[r]*D[d][l]*2^xscale_log2 exactly */
   uint64_t off_perm; /* k uint16 slots -> channels                      */
   uint64_t off_codes;/* n_tiles * units * 2304 bytes of coded units     */
   uint64_t code_bytes;    /* canonical code bytes: ceil(n*k*9/32)       */
   uint64_t padded_code_bytes; /* bytes of coded units including padding  */
   uint64_t bytes;    /* total packed buffer size                         */
+  int32_t xscale_log2; /* the power of two of the exact split, or
+                          SVQ_NO_EXACT_SPLIT when the tables admit none    */
+  int32_t reserved;
 } svq_handle;
+#define SVQ_NO_EXACT_SPLIT (-2147483647 - 1)
 
 /* svq_pack: one-time repack of a canonical matrix into the kernel layout
  * (SAGE Fig. 2 caption for what a code holds; the layout itself keeps the

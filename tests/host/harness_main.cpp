@@ -149,6 +149,18 @@ int main() {
     for (int m : {1, 3, 4, 5, 16, 64, 2048}) plan(sub, m);
   }
   for (auto &p : mats) std::free(p.buf);
+  // tables without an exact fp16 split: a radius of 60000 next to a
+  // direction entry of 2^-24 spans more than the split can hold
+  {
+    Canon c2 = make(70, 1536, 7, 77);
+    c2.rad[0] = 0x3C01;  // 1 + 2^-10
+    c2.rad[1] = 0x7B53;  // 60000
+    for (int l = 0; l < 8; ++l) c2.cb[l] = 0x0001;  // 2^-24
+    std::vector<Packed> one{pack(c2)};
+    EXPECT(one[0].h.xscale_log2 == SVQ_NO_EXACT_SPLIT, "expected no exact split");
+    for (int m : {5, 8, 13, 16}) plan(one, m);
+    std::free(one[0].buf);
+  }
   // malformed canonical inputs are rejected before any copy
   Canon c = make(32, 64, 7, 99);
   c.perm[3] = c.perm[4];

@@ -148,6 +148,8 @@ hipError_t launch_sb(SbBatch &b, int prep_blocks, int blocks, hipStream_t) {
     CHECK(b.starts.first[j] == next && J.block_begin == next, "start");
     CHECK(b.prep_starts.first[j] == pnext && J.prep_begin == pnext, "prep start");
     check::check_ws(J.xa, (size_t)w.units * SB_XA_UNIT_BYTES, "fragments");
+    check::check_ws(J.xs, (size_t)w.units * 16 * 4, "activation scales");
+    CHECK(J.xinv > 0.f, "split scale %g", (double)J.xinv);
     if (J.splits > 1) {
       check::check_ws(J.part, (size_t)J.groups * J.tiles * J.splits * 1024, "partial tiles");
       check::check_ws(J.cnt, (size_t)J.groups * 4, "arrival counters");
@@ -168,7 +170,7 @@ hipError_t launch_sb(SbBatch &b, int prep_blocks, int blocks, hipStream_t) {
         }
       }
     next += J.groups * J.splits;
-    pnext += 4 * w.units;
+    pnext += w.units;
   }
   CHECK(next == blocks && pnext == prep_blocks, "blocks");
   return hipSuccess;

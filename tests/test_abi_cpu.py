@@ -46,7 +46,7 @@ def _desc(mat, **over):
 def _expected_bytes(n, k):
     a = lambda v: (v + 255) // 256 * 256
     tiles, units = (n + 15) // 16, (k + 511) // 512
-    return a(4096) + a(2048) + a(16384) + a(2 * units * 512) + a(tiles * units * 2304)
+    return a(4096) + a(2048) + a(16384) + a(32768) + a(2 * units * 512) + a(tiles * units * 2304)
 
 
 @pytest.mark.parametrize("n,k,bd", [(512, 1024, 8), (37, 104, 6), (1, 8, 7), (2048, 768, 7)])
@@ -127,7 +127,9 @@ def _fake_handle(n, k, bd):
     h.off_dtab = 0
     h.off_rtab = a(4096)
     h.off_btab = h.off_rtab + a(2048)
-    h.off_perm = h.off_btab + a(16384)
+    h.off_xtab = h.off_btab + a(16384)
+    h.off_perm = h.off_xtab + a(32768)
+    h.xscale_log2 = 17
     h.off_codes = h.off_perm + a(2 * h.units * 512)
     h.padded_code_bytes = h.n_tiles * h.units * 2304
     h.bytes = h.off_codes + a(h.padded_code_bytes)
@@ -182,9 +184,9 @@ def _small_plan(n_tiles, units, items):
 
 def _small_need(shapes):
     """Workspace of the 4 < m <= 16 path, per matrix: the fragment-ordered
-    activations (16 rows x 512 slots bf16 = 16 KB per unit); with K ranges,
-    fp32 partial tiles for every (tile of the groups, range) and one
-    arrival counter per group."""
+    activations (16 rows x 512 slots fp16 = 16 KB per unit) and their
+    inverse scales (16 fp32 per unit); with K ranges, fp32 partial tiles for
+    every (tile of the groups, range) and one arrival counter per group."""
     a = lambda v: (v + 255) // 256 * 256
     cdiv = lambda p, q: -(-p // q)
     items = _small_items(shapes)
@@ -192,7 +194,7 @@ def _small_need(shapes):
     for n, k in shapes:
         units = cdiv(k, 512)
         tiles, _, splits, groups = _small_plan(cdiv(n, 16), units, items)
-        need += a(units * 16384)
+        need += a(units * 16384) + a(units * 64)
         if splits > 1:
             need += a(groups * tiles * splits * 1024) + a(groups * 4)
     return need
@@ -214,10 +216,10 @@ def test_linear_workspace_query_and_validation():
     dq = lambda m: _dequant_gemm_need([(512, 1024)], m)
     assert dq(17) == 64 * 2048 + 2 * 64 * 512 * 4  # two K splits of one unit each
     assert _exact_need([(512, 1024)], 2) == 4096 + 256
-    assert _small_need([(512, 1024)]) == 2 * 16384
-    assert _small_need([(100, 2560)]) == 5 * 16384
+    assert _small_need([(512, 1024)]) == 2 * 16384 + 256
+    assert _small_need([(100, 2560)]) == 5 * 16384 + 512
     assert _small_plan(160, 19, 16) == (3, 5, 4, 54)
-    assert _small_need([(2560, 9728)]) == 19 * 16384 + 54 * 3 * 4 * 1024 + 256
+    assert _small_need([(2560, 9728)]) == 19 * 16384 + 1280 + 54 * 3 * 4 * 1024 + 256
     layer = [(4096, 2560), (1024, 2560), (1024, 2560), (2560, 4096), (9728, 2560), (9728, 2560),
              (2560, 9728)]
     assert _small_items(layer) == 25
