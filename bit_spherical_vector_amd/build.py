@@ -26,6 +26,7 @@ SOURCES = [
     ("csrc/svq_kernels.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("csrc/svq_prefill.hip", []),
     ("csrc/svq_small.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
+    ("csrc/svq_moe.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("csrc/svq_encode.hip", []),
     ("csrc/svq_calib.hip", []),
     ("csrc/svq_scratch.hip", []),

@@ -55,6 +55,42 @@ __device__ __forceinline__ ItemCodes load_item(const uint8_t *ub, int rec) {
   return c;
 }
 
+// Record-crossing code loads of the 16x16x32 MFMA paths (small batch and
+// grouped MoE).  Lane L = 16s + 4b0 + j takes, for MFMA f = 4ci + q, the
+// code at row 4b0 + j, column 16ci + 4s + q of a unit: code 4b0 + ci of
+// lane record 16s + 4q + j.
+// The code bytes one lane needs for one unit:
+// for each q, the 16 sign bytes, index-low dword b0 and index-high dword of
+// lane record 16s + 4q + j.
+struct SbCodes {
+  u4 S[4];
+  uint32_t L[4], H[4];
+};
+
+// Lane offsets of those bytes within a unit, for q = 0: record 16s + j
+// (the records of q > 0 lie 4q records further).
+struct SbOffs {
+  uint32_t S, L, H;
+};
+
+__device__ __forceinline__ SbCodes sb_load_codes(const uint8_t *ub, const SbOffs &o) {
+  SbCodes c;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c.S[q] = __builtin_nontemporal_load((const u4 *)(ub + PLANE_SIGN + 64 * q + o.S));
+    c.L[q] = __builtin_nontemporal_load((const uint32_t *)(ub + PLANE_LOW + 64 * q + o.L));
+    c.H[q] = __builtin_nontemporal_load((const uint32_t *)(ub + PLANE_HIGH + 16 * q + o.H));
+  }
+  return c;
+}
+
+// Per-lane shift amounts of code 4b0 + ci (ci = 0..3): sign carriers
+// (S << (4b0 + ci) brings the code's pair signs to bits 15 and 31) and the
+// index-high bits (at 8b0 + 2ci of the record's high dword).
+struct SbShifts {
+  uint32_t sg[4], hi[4];
+};
+
 // The job of a batched launch that owns this block (see JobStarts): the
 // number of later job starts at or below blockIdx.x.
 __device__ __forceinline__ int find_job(const JobStarts &st, int count) {

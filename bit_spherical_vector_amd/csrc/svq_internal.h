@@ -329,14 +329,15 @@ struct MoeShape {
   int32_t num_experts;
 };
 
-// Grouped dequant-GEMM for routed slots: activation rows per work item,
-// workspace bytes of the fragment-ordered activations, and the prep + GEMM
-// launches over the routing's work list (expert, sorted rows r0..r1).
-constexpr int MOE_DQ_ROWS = 64;
-size_t moe_dq_xb_bytes(int max_work, int units);
-hipError_t launch_moe_dq(const MoeShape &sh, const ExpertTable &tab, const uint16_t *x, int64_t ldx,
+// Grouped MoE product (svq_moe.hip) for routed slots: activation rows per
+// work item, workspace bytes of the fragment-ordered activations, and the
+// prep + product launches over the routing's work list (expert, sorted rows
+// r0..r1).
+constexpr int MOE_SB_ROWS = 48;
+size_t moe_sb_xa_bytes(int max_work, int units);
+hipError_t launch_moe_sb(const MoeShape &sh, const ExpertTable &tab, const uint16_t *x, int64_t ldx,
                          int x_per_slot, int topk, const int32_t *work, const int32_t *nwork,
-                         const int32_t *sorted, int max_work, uint16_t *xb, void *y, int64_t ldy,
+                         const int32_t *sorted, int max_work, uint8_t *xa, void *y, int64_t ldy,
                          int ydt, hipStream_t s);
 
 }  // namespace svq

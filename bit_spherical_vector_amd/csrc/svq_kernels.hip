@@ -1158,14 +1158,15 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
       for (int c = 0; c < n; ++c) store_out((char *)y + (size_t)q * ldy * (ydt == 0 ? 2 : 4), (size_t)c, 0.f, ydt);
     }
   }
+  // an expert's rows split into its work items as evenly as possible (sizes
+  // differ by at most one, each <= rows_per_item)
   for (int e = t; e < E; e += 1024) {
-    const int n_items = s_items[e + 1] - s_items[e];
+    const int n_items = s_items[e + 1] - s_items[e], cnt = s_off[e + 1] - s_off[e];
     for (int c = 0; c < n_items; ++c) {
       const int wi = s_items[e] + c;
-      const int r0 = s_off[e] + c * rows_per_item;
       work[3 * wi + 0] = e;
-      work[3 * wi + 1] = r0;
-      work[3 * wi + 2] = min(r0 + rows_per_item, s_off[e + 1]);
+      work[3 * wi + 1] = s_off[e] + (int)((int64_t)c * cnt / n_items);
+      work[3 * wi + 2] = s_off[e] + (int)((int64_t)(c + 1) * cnt / n_items);
     }
   }
 }
@@ -1178,8 +1179,8 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
 // ---------------------------------------------------------------------------
 // MoE launcher.  Workspace layout depends on the path:
 //   exact (m*topk <= MOE_EXACT_MAX_SLOTS): none (the fused per-slot launch)
-//   bf16: counts[E], offsets[E+1], sorted[S], work[3*max_work], nwork,
-//         xb[S + 16*BMT][Kp] bf16
+//   grouped: counts[E], offsets[E+1], sorted[S], work[3*max_work], nwork,
+//            fragment-ordered activations (moe_sb_xa_bytes)
 // ---------------------------------------------------------------------------
 constexpr int MOE_EXACT_MAX_SLOTS = 64;
 
@@ -1236,7 +1237,7 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
                          x_per_slot, topk, y, ldy, ydt, R);
     return hipGetLastError();
   }
-  const int rows_per_item = MOE_DQ_ROWS;
+  const int rows_per_item = MOE_SB_ROWS;
   const int max_work = (S + rows_per_item - 1) / rows_per_item + E;
   size_t off = 0;
   const size_t o_counts = off;
@@ -1250,7 +1251,7 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   const size_t o_nwork = off;
   off += 256;
   const size_t o_xb = off;
-  off += align256(moe_dq_xb_bytes(max_work, sh.units));
+  off += align256(moe_sb_xa_bytes(max_work, sh.units));
   *need = off;
   if (!ws) return hipSuccess;
   if (ws_bytes < *need) return hipErrorInvalidValue;
@@ -1258,12 +1259,12 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   int32_t *counts = (int32_t *)(b + o_counts), *offsets = (int32_t *)(b + o_offsets);
   int32_t *sorted = (int32_t *)(b + o_sorted), *work = (int32_t *)(b + o_work);
   int32_t *nwork = (int32_t *)(b + o_nwork);
-  uint16_t *xb = (uint16_t *)(b + o_xb);
+  uint8_t *xb = b + o_xb;
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), 0, s, ids, S, E, rows_per_item, counts,
                      offsets, sorted, work, nwork, y, ldy, sh.n, ydt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_moe_dq(sh, tab, xp, ldx, x_per_slot, topk, work, nwork, sorted, max_work, xb, y,
+  return launch_moe_sb(sh, tab, xp, ldx, x_per_slot, topk, work, nwork, sorted, max_work, xb, y,
                        ldy, ydt, s);
 }
 

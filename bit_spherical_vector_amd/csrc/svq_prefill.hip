@@ -16,8 +16,8 @@
 // * BM = 256 (m >= PREFILL_MIN_M, dq_tile_w8): 8 waves in a 2 x 4 grid,
 //   each 128 x 64, two waves per SIMD; the activation fragments of a step
 //   are copied into LDS by direct-to-LDS loads, one step ahead;
-// * BM = 64 (dq_tile<64>, fewer rows, and the grouped MoE product in
-//   moe_dq_kernel): four 64 x 64 waves side by side, two blocks per CU, A
+// * BM = 64 (dq_tile<64>, 16 < m < PREFILL_MIN_M): four 64 x 64 waves
+//   side by side, two blocks per CU, A
 //   fragments loaded straight into registers with coalesced 1 KB loads one
 //   step ahead, B fragments of the next 16-wide k substep read while the
 //   current one's MFMAs run; K splits summed by a reduce launch when the
@@ -831,101 +831,6 @@ hipError_t launch_prefill_prep(PrefillBatch &b, int blocks, size_t lds, bool xve
   return hipGetLastError();
 }
 
-// MoE grouped dequant-GEMM (routed slots beyond the exact path): work item
-// wi = (expert, sorted rows r0 .. r1 <= r0 + 64) of the routing; its
-// activations are xb rows 64 wi .. 64 wi + 63 (fragment order, padding rows
-// zero), and its output rows go to the slots sorted[r0 ..].
-__global__ __launch_bounds__(256) void moe_dq_prep_kernel(MoeShape sh, ExpertTable tab,
-                                                          const uint16_t *__restrict__ x, int64_t ldx,
-                                                          int x_per_slot, int topk,
-                                                          const int32_t *__restrict__ work,
-                                                          const int32_t *__restrict__ nwork,
-                                                          const int32_t *__restrict__ sorted,
-                                                          uint16_t *__restrict__ xb, int rpb,
-                                                          int csplit, int xvec) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t s_rows[];
-  const int groups = MOE_DQ_ROWS / rpb;
-  const int lb = (int)blockIdx.x;
-  const int wi = lb / (groups * csplit), rg = (lb / csplit) % groups, cs = lb % csplit;
-  if (wi >= *nwork) return;  // uniform, before any barrier
-  const int e = work[3 * wi], r0 = work[3 * wi + 1], r1 = work[3 * wi + 2];
-  const int Kp = sh.units * UNIT_SLOTS, nch = Kp / 8, cpb = (nch + csplit - 1) / csplit;
-  const uint16_t *src[8];
-#pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    const int j = r0 + rg * rpb + rr;
-    src[rr] = nullptr;
-    if (rr < rpb && j < r1) {
-      const int q = sorted[j];
-      src[rr] = x + (int64_t)(x_per_slot ? q : q / topk) * ldx;
-    }
-  }
-  const uint16_t *perm = (const uint16_t *)(tab.base[e] + sh.off_perm);
-  if (xvec)
-    dq_gather_rows<true>(src, rpb, sh.k, Kp, perm, xb, MOE_DQ_ROWS * wi + rg * rpb, cs * cpb,
-                         min(nch, cs * cpb + cpb), s_rows);
-  else
-    dq_gather_rows<false>(src, rpb, sh.k, Kp, perm, xb, MOE_DQ_ROWS * wi + rg * rpb, cs * cpb,
-                          min(nch, cs * cpb + cpb), s_rows);
-}
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void moe_dq_kernel(MoeShape sh, ExpertTable tab, const int32_t *__restrict__ work,
-                   const int32_t *__restrict__ nwork, const int32_t *__restrict__ sorted,
-                   const uint16_t *__restrict__ xb, void *__restrict__ y, int64_t ldy, int ydt,
-                   int yvec) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tiles_n = prefill_tiles_n(sh.n_tiles);
-  const int wi = (int)blockIdx.x / tiles_n, nt = (int)blockIdx.x % tiles_n;
-  if (wi >= *nwork) return;  // uniform, before any barrier
-  const int e = work[3 * wi], r0 = work[3 * wi + 1], r1 = work[3 * wi + 2];
-  DqTile T;
-  T.w = expert_view(sh, tab, e);
-  T.xb = xb;
-  T.m0 = MOE_DQ_ROWS * wi;
-  T.m_valid = r1 - r0;
-  T.nt = nt;
-  T.u0 = 0;
-  T.u1 = sh.units;
-  T.y = y;
-  T.ldy = ldy;
-  T.nlim = sh.n;
-  T.bf = ydt == 0;
-  T.yvec = yvec != 0;
-  T.ymap = sorted + r0;
-  dq_tile<MOE_DQ_ROWS>(T, smem);
-}
-
-size_t moe_dq_xb_bytes(int max_work, int units) {
-  return (size_t)max_work * MOE_DQ_ROWS * units * UNIT_SLOTS * 2;
-}
-
-hipError_t launch_moe_dq(const MoeShape &sh, const ExpertTable &tab, const uint16_t *x, int64_t ldx,
-                         int x_per_slot, int topk, const int32_t *work, const int32_t *nwork,
-                         const int32_t *sorted, int max_work, uint16_t *xb, void *y, int64_t ldy,
-                         int ydt, hipStream_t s) {
-  const int rpb = prefill_prep_rows(sh.k);
-  const int nch = sh.units * UNIT_SLOTS / 8;
-  const int groups = max_work * (MOE_DQ_ROWS / rpb);
-  int csplit = (512 + groups - 1) / groups;
-  csplit = csplit < nch / 64 ? csplit : nch / 64;
-  csplit = csplit < 1 ? 1 : csplit;
-  const bool xvec = ((((uintptr_t)x) | ((uintptr_t)ldx * 2)) & 15) == 0;
-  const size_t lds = prefill_prep_lds(rpb, sh.k);
-  hipError_t e = allow_smem(moe_dq_prep_kernel, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_dq_prep_kernel, dim3(groups * csplit), dim3(256), lds, s, sh, tab, x, ldx,
-                     x_per_slot, topk, work, nwork, sorted, xb, rpb, csplit, xvec ? 1 : 0);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t esz = ydt == 0 ? 2 : 4;
-  const int yvec = ((((uintptr_t)y) | ((uintptr_t)ldy * esz)) & 15) == 0;
-  e = allow_smem(moe_dq_kernel, P_SMEM);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_dq_kernel, dim3(max_work * prefill_tiles_n(sh.n_tiles)), dim3(256), P_SMEM,
-                     s, sh, tab, work, nwork, sorted, xb, y, ldy, ydt, yvec);
-  return hipGetLastError();
-}
 
 
 hipError_t launch_prefill_batched(PrefillBatch &b, int bm, int blocks, hipStream_t s) {

@@ -75,38 +75,6 @@ static_assert(SB_SMEM <= 64 * 1024, "small-batch LDS");
 
 __device__ __forceinline__ u4 sb_lds(uint32_t addr) { return *(sb_lds_u4_t *)(size_t)addr; }
 
-// The code bytes one lane needs for one unit (see the code mapping above):
-// for each q, the 16 sign bytes, index-low dword b0 and index-high dword of
-// lane record 16s + 4q + j.
-struct SbCodes {
-  u4 S[4];
-  uint32_t L[4], H[4];
-};
-
-// Lane offsets of those bytes within a unit, for q = 0: record 16s + j
-// (the records of q > 0 lie 4q records further).
-struct SbOffs {
-  uint32_t S, L, H;
-};
-
-__device__ __forceinline__ SbCodes sb_load_codes(const uint8_t *ub, const SbOffs &o) {
-  SbCodes c;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    c.S[q] = __builtin_nontemporal_load((const u4 *)(ub + PLANE_SIGN + 64 * q + o.S));
-    c.L[q] = __builtin_nontemporal_load((const uint32_t *)(ub + PLANE_LOW + 64 * q + o.L));
-    c.H[q] = __builtin_nontemporal_load((const uint32_t *)(ub + PLANE_HIGH + 16 * q + o.H));
-  }
-  return c;
-}
-
-// Per-lane shift amounts of code 4b0 + ci (ci = 0..3): sign carriers
-// (S << (4b0 + ci) brings the code's pair signs to bits 15 and 31) and the
-// index-high bits (at 8b0 + 2ci of the record's high dword).
-struct SbShifts {
-  uint32_t sg[4], hi[4];
-};
-
 // Table rows of the four codes (ci = 0..3) of MFMA group q: the hi and lo
 // halves of each code's exact split (32-byte rows by 10-bit index).
 __device__ __forceinline__ void sb_reads(uint32_t Lw, uint32_t H, const SbShifts &sh, u4 (&Dh)[4],

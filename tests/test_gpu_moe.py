@@ -134,3 +134,30 @@ def test_moe_out_of_range_ids_are_skipped(svq, m, topk):
             if slots.size:
                 assert_within_tolerance(y[slots], so.linear(x[slots // topk], Ws[e]), x[slots // topk],
                                         Ws[e], label=f"valid slots of expert {e}")
+
+
+@pytest.mark.parametrize("x_per_slot", [0, 1])
+def test_moe_grouped_strided_unaligned(svq, x_per_slot):
+    """Grouped path (160 slots) with odd row strides for x and y (rows only
+    2-byte aligned, so the element-wise load and store forms run), n not a
+    multiple of 8 and k not a multiple of the unit width; the padding
+    columns of y are left untouched."""
+    n_exp, n, k, m, topk = 6, 44, 520, 40, 4
+    mats = [synth.random_matrix(n, k, 6 + e % 3, seed=(46, e, 0)) for e in range(n_exp)]
+    Ws = [so.decode_matrix(w.codes, n, k, w.bd, w.codebook, w.radius, w.perm) for w in mats]
+    pms = [svq.pack(w) for w in mats]
+    ids = _ids(m, topk, n_exp, 47)
+    rows = m * topk if x_per_slot else m
+    x = synth.random_activations(rows, k, seed=(48, x_per_slot, 0))
+    xb = torch.zeros((rows, k + 3), dtype=torch.int16)
+    xb[:, :k] = torch.from_numpy(x.view(np.int16))
+    xd = xb.cuda().view(torch.bfloat16)[:, :k]
+    d_ids = torch.from_numpy(ids).cuda()
+    for dt in (torch.float32, torch.bfloat16):
+        yb = torch.full((m * topk, n + 5), 7.0, dtype=dt, device="cuda")
+        y = yb[:, :n]
+        svq.moe_linear(pms, xd, d_ids, topk, bool(x_per_slot), out=y)
+        torch.cuda.synchronize()
+        assert torch.all(yb[:, n:] == 7.0)
+        y64 = out_to_f64(y)
+        _check_slots(y64, x, ids, topk, x_per_slot, Ws, range(n_exp), f"strided moe {dt}")
