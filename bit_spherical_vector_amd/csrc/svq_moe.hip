@@ -129,7 +129,8 @@ __global__ __launch_bounds__(MOE_SB_PREP_THREADS) void moe_sb_prep_kernel(
     for (int u = u0; u < U; u += USTEP) {
       u4 pv[4];
 #pragma unroll
-      for (int ci = 0; ci < 4; ++ci) pv[ci] = *(const u4 *)(perm + u * UNIT_SLOTS + 8 * (16 * ci + 4 * s + q));
+      for (int ci = 0; ci < 4; ++ci)
+        pv[ci] = *(const u4 *)(perm + u * UNIT_SLOTS + 8 * (16 * ci + 4 * s + q));
 #pragma unroll
       for (int ci = 0; ci < 4; ++ci) {
         const int p0 = u * UNIT_SLOTS + 8 * (16 * ci + 4 * s + q);
@@ -153,9 +154,10 @@ __device__ __forceinline__ void moe_reads(const uint8_t *smem, uint32_t Lw, uint
                                           u4 (&D)[4]) {
 #pragma unroll
   for (int ci = 0; ci < 4; ++ci) {
-    const uint32_t lo = __builtin_amdgcn_ubfe(Lw, 8 * ci, 8);
+    // byte address (hi << 12) | (lo << 4) of the 16-byte row (hi << 8) | lo
+    const uint32_t lo4 = __builtin_amdgcn_ubfe(Lw, 8 * ci, 8) << 4;
     const uint32_t hi = __builtin_amdgcn_ubfe(H, sh.hi[ci], 2);
-    D[ci] = *(const u4 *)(smem + MOE_SB_OFF_BTAB + ((lo | (hi << 8)) << 4));
+    D[ci] = *(const u4 *)(smem + MOE_SB_OFF_BTAB + ((hi << 12) | lo4));
   }
 }
 
