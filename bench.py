@@ -373,8 +373,10 @@ def bench_decode(args, wl, svq, synth, dev):
     stack = synth.decode_stack(wl["layers"])
     side = torch.cuda.Stream()  # graph capture needs a stream other than the legacy default
     calls, ws, code_bytes = [], None, 0
+    layers = []  # per layer: packed matrices and the input width of each call
     for mats, xs in stack:
         pms = [svq.pack(w) for w in mats]
+        layers.append((pms, synth.call_input_widths(mats)))
         code_bytes += sum(w.codes.size for w in mats)
         for c, idx in enumerate(synth.DECODE_CALLS):
             x = torch.from_numpy(xs[c].view(np.int16)).view(torch.bfloat16).to(dev)
@@ -417,6 +419,7 @@ def bench_decode(args, wl, svq, synth, dev):
         ev[3].record(side)
     torch.cuda.synchronize()
     ms_per_step = ev[2].elapsed_time(ev[3]) / args.steps
+    ttft = bench_first_token(args, wl, svq, synth, dev, side, layers)
     value = code_bytes / (ms_per_step * 1e-3) / 1e9
     # roofline.achieved: the step's code bytes over the mean step duration;
     # a step is 144 back-to-back launches, so the gaps between them count
@@ -442,11 +445,70 @@ def bench_decode(args, wl, svq, synth, dev):
         "data": "synthetic (seeded codes, codebooks, radii, permutations, activations)",
         "config": {"workload": args.workload, "layers": wl["layers"], "matrices": 7 * wl["layers"],
                    "m": 1, "code_bytes": int(code_bytes), "launches_per_step": len(calls),
-                   "eager_ms_per_step": round(eager_ms, 5), "graph": True},
+                   "eager_ms_per_step": round(eager_ms, 5), "graph": True,
+                   "tpot_ms": round(ms_per_step, 5), "first_token": ttft},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_first_token(args, wl, svq, synth, dev, side, layers):
+    """Time to first token of the decode stack's linears: the same layers'
+    calls over a P-token prompt (each call at m = P, the prefill path), run
+    once per step, eager and as a replayed HIP graph.  Reported beside the
+    per-token step (TPOT), the split of time the SAGE paper uses for whole
+    models (Table 3, Fig. 7)."""
+    import numpy as np
+    import torch
+
+    P = wl.get("prefill_tokens", 0)
+    if not P:
+        return None
+    calls, ws, flops = [], None, 0.0
+    for layer, (pms, ks) in enumerate(layers):
+        xs = synth.prompt_activations(layer, ks, P)
+        for c, idx in enumerate(synth.DECODE_CALLS):
+            x = torch.from_numpy(xs[c].view(np.int16)).view(torch.bfloat16).to(dev)
+            ys = [torch.empty((P, pms[j].handle.n), dtype=torch.bfloat16, device=dev) for j in idx]
+            call = svq.BatchedCall([pms[j] for j in idx], [x] * len(idx), ys, workspace=ws, stream=side)
+            if ws is None or call.workspace.numel() > ws.numel():
+                ws = call.workspace
+            calls.append(call)
+            flops += sum(2.0 * P * pms[j].handle.n * pms[j].handle.k for j in idx)
+
+    def step():
+        for call in calls:
+            call()
+
+    reps = max(1, min(args.steps, 10))
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(1, args.warmup)):
+            step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(side)
+    for _ in range(reps):
+        step()
+    ev[1].record(side)
+    torch.cuda.synchronize()
+    eager_ms = ev[0].elapsed_time(ev[1]) / reps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        graph.replay()
+        torch.cuda.synchronize()
+        ev[2].record(side)
+        for _ in range(reps):
+            graph.replay()
+        ev[3].record(side)
+    torch.cuda.synchronize()
+    ms = ev[2].elapsed_time(ev[3]) / reps
+    return {"tokens": P, "ttft_ms": round(ms, 4), "eager_ms": round(eager_ms, 4), "launch_calls": len(calls),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "reps": reps}
 
 
 def _timed(args, stream, fn):

@@ -28,6 +28,9 @@ from .workloads import (  # noqa: F401
     DECODE_CALLS,
     DECODE_LAYERS,
     decode_stack,
+    PREFILL_TOKENS,
+    prompt_activations,
+    call_input_widths,
     prefill_set,
     moe_expert_bd,
     moe_expert,

@@ -81,8 +81,10 @@ WORKLOADS: Dict[str, dict] = {
     "esg_calib_t2048_k2560": dict(kind="esg", shapes=[("x", 2048, 2560)], m=2048),
     "abs_gate_3splits": dict(kind="abs", shapes=[("gate", 9728, 2560)], m=0, bds=(6, 7, 8)),
     # one decode step's linears: 36 layers of the seven 4B-class matrices at
-    # batch 1, four dependent calls per layer, each layer its own matrices
-    "decode4b_36l": dict(kind="decode", shapes=DENSE_LAYER_SHAPES, m=1, layers=36),
+    # batch 1, four dependent calls per layer, each layer its own matrices;
+    # beside it the first-token pass: the same calls over a 128-token prompt
+    "decode4b_36l": dict(kind="decode", shapes=DENSE_LAYER_SHAPES, m=1, layers=36,
+                         prefill_tokens=128),
 }
 
 
@@ -230,6 +232,23 @@ def decode_stack(layers: int = DECODE_LAYERS, seed: int = 0
               for c, call in enumerate(DECODE_CALLS)]
         stack.append((mats, xs))
     return stack
+
+
+PREFILL_TOKENS = 128
+
+
+def prompt_activations(layer: int, ks: Sequence[int], tokens: int = PREFILL_TOKENS,
+                       seed: int = 0) -> List[np.ndarray]:
+    """The first-token (prompt) pass of the decode stack: one [tokens, k]
+    input per call of DECODE_CALLS of ``layer``, ``ks[c]`` the input width of
+    call c (same distribution as every other activation here)."""
+    return [make_activations(_rng(WL_DECODE, 5000 + 4 * layer + c, seed * 65536 + tokens), tokens, ks[c])
+            for c in range(len(DECODE_CALLS))]
+
+
+def call_input_widths(mats: Sequence["MatrixInputs"]) -> List[int]:
+    """Input width k of each call of DECODE_CALLS for one layer's matrices."""
+    return [mats[call[0]].k for call in DECODE_CALLS]
 
 
 def dense_layer_activations(m: int) -> List[np.ndarray]:
