@@ -34,8 +34,9 @@ What they leave open, and the readings taken here (the library's contract):
   w_hat the decoded weight (exact in float64), all in float64 without fused
   multiply-adds; the matrix error is the sum of the row errors in row order.
 * ABS: the candidate (in the caller's order) with the smallest matrix
-  error, the first one on ties.  Every candidate is coded by the encoder
-  rule of ``oracle/svq_encoder.py``.
+  error, the first one on ties.  Every candidate is coded by the plain
+  encoder rule of ``oracle/svq_encoder.py`` or, on request, by its
+  activation-weighted fitting rule with the same h.
 """
 from __future__ import annotations
 
@@ -43,7 +44,7 @@ from typing import Sequence, Tuple
 
 import numpy as np
 
-from oracle.svq_encoder import encode_matrix, gather_subvectors
+from oracle.svq_encoder import encode_matrix, encode_matrix_weighted, gather_subvectors
 from oracle.svq_oracle import bf16_bits_to_f64, decode_permuted
 
 
@@ -108,13 +109,18 @@ def total_in_order(values: np.ndarray) -> float:
 
 
 def abs_select(w: np.ndarray, perm: np.ndarray, h: np.ndarray,
-               candidates: Sequence[Tuple[int, np.ndarray, np.ndarray]]):
+               candidates: Sequence[Tuple[int, np.ndarray, np.ndarray]], weighted_fit: bool = False):
     """(chosen index, errors [len(candidates)], codes of every candidate):
-    each candidate (bd, codebook bits, radius bits) is encoded and scored by
-    its activation-weighted reconstruction error."""
+    each candidate (bd, codebook bits, radius bits) is encoded -- by the
+    plain rule, or by activation-weighted fitting with the same h when
+    ``weighted_fit`` -- and scored by its activation-weighted reconstruction
+    error."""
     errs, all_codes = [], []
     for bd, cb, rad in candidates:
-        codes = encode_matrix(w, perm, bd, cb, rad)
+        if weighted_fit:
+            codes = encode_matrix_weighted(w, perm, h, bd, cb, rad)
+        else:
+            codes = encode_matrix(w, perm, bd, cb, rad)
         errs.append(total_in_order(weighted_error_rows(w, perm, h, codes, bd, cb, rad)))
         all_codes.append(codes)
     errs = np.array(errs, dtype=np.float64)

@@ -102,5 +102,116 @@ def encode_stream(w: np.ndarray, perm: np.ndarray, bd: int, codebook_bits: np.nd
     return pack_codes(encode_matrix(w, perm, bd, codebook_bits, radius_bits))
 
 
+def _fit_weights(h: np.ndarray, perm: np.ndarray, C: int) -> np.ndarray:
+    """Per-slot fitting weights, float64 [C, 8]: ``[c, l] = h[perm[8c + l]]``
+    (the weight of the input channel that lane l of subvector c reads)."""
+    h = np.asarray(h, dtype=np.float64)
+    if h.shape != (8 * C,) or not np.all(np.isfinite(h)) or np.any(h < 0):
+        raise ValueError("h must hold k finite, non-negative channel weights")
+    return h[np.asarray(perm, dtype=np.int64)].reshape(C, 8)
+
+
+def _weighted_magnitudes(hp: np.ndarray, a: np.ndarray) -> np.ndarray:
+    """h_l |v_l|, float64 [n, C, 8], one rounding each."""
+    return hp[None, :, :] * a
+
+
+def _direction_sums(hw: np.ndarray, hp: np.ndarray, Dd: np.ndarray):
+    """A_d = sum_l (h_l |v_l|) D_dl [n, C] and B_d = sum_l (h_l D_dl) D_dl
+    [C] for one direction row Dd, lanes added in order 0..7."""
+    A = hw[:, :, 0] * Dd[0]
+    B = (hp[:, 0] * Dd[0]) * Dd[0]
+    for l in range(1, 8):
+        A = A + hw[:, :, l] * Dd[l]
+        B = B + (hp[:, l] * Dd[l]) * Dd[l]
+    return A, B
+
+
+def _reduced_error(Rr: float, A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """The code-dependent part of the weighted error of (d, r):
+    (R_r R_r) B_d - (R_r + R_r) A_d."""
+    return (Rr * Rr) * B[None, :] - (Rr + Rr) * A
+
+
+def _improves(E: np.ndarray, best: np.ndarray) -> np.ndarray:
+    """A later pair replaces the best one only when strictly smaller, so the
+    first minimum in (d, r) order wins."""
+    return E < best
+
+
+def encode_fields_weighted(w: np.ndarray, perm: np.ndarray, h: np.ndarray, bd: int,
+                           codebook_bits: np.ndarray, radius_bits: np.ndarray):
+    """(signs, direction index, radius index), each uint32 [n, k/8], by
+    activation-weighted fitting.
+
+    What it follows: "SAGE: Pushing 2-Bit Vector-Quantized LLMs toward
+    Real-World Usability", Abstract and Fig. 2 caption: ESG protects
+    sensitive channels through fitting weighted by calibration activations.
+    The pages give no formula; the reading taken here: with the weight
+    h_l = h[perm[8c + l]] of each lane (h[j] e.g. the ESG energy of input
+    channel j raised to an exponent), the code of subvector v is the one
+    whose decoded weights w_hat minimise the weighted squared error
+    sum_l h_l (v_l - w_hat_l)^2.
+
+    * Signs: the IEEE sign bits of v, as in :func:`encode_fields`.  The
+      directions and radii are non-negative, so a decoded weight with the
+      sign of v_l is never farther from it than one with the other sign.
+    * Direction d and radius r, searched jointly over every pair: with
+      a_l = |v_l|, the error of (d, r) is
+      sum_l h_l a_l^2 - 2 R_r A_d + R_r^2 B_d, where
+      A_d = sum_l (h_l a_l) D_dl and B_d = sum_l (h_l D_dl) D_dl.  The first
+      term does not depend on the code, so the pair minimising the reduced
+      error E = (R_r R_r) B_d - (R_r + R_r) A_d is chosen; pairs are taken
+      in order (d ascending, then r ascending) and the first minimum wins.
+
+    Arithmetic (fixed so that the GPU takes the same decisions): float64;
+    h_l a_l, A_d and B_d with one rounding per product and per addition,
+    lanes added in order 0..7; E as written, no fused multiply-adds."""
+    v = gather_subvectors(w, perm)                       # [n, C, 8]
+    n, C, _ = v.shape
+    a = np.abs(v)
+    neg = np.signbit(v).astype(np.uint32)
+    s = np.zeros((n, C), dtype=np.uint32)
+    for l in range(8):
+        s |= neg[:, :, l] << np.uint32(l)
+    hp = _fit_weights(h, perm, C)                        # [C, 8]
+    D = fp16_bits_to_f64(np.asarray(codebook_bits).reshape(1 << bd, 8))
+    if not np.all(np.isfinite(D)):
+        raise ValueError("codebook entries must be finite")
+    rad = np.asarray(radius_bits).reshape(1 << (INDEX_BITS - bd))
+    radius_midpoints_sq(rad)                             # same table checks as the plain rule
+    R = fp16_bits_to_f64(rad)
+    hw = _weighted_magnitudes(hp, a)
+    best = None
+    d_best = np.zeros((n, C), dtype=np.uint32)
+    r_best = np.zeros((n, C), dtype=np.uint32)
+    for d in range(1 << bd):
+        A, B = _direction_sums(hw, hp, D[d])
+        for r in range(R.size):
+            E = _reduced_error(float(R[r]), A, B)
+            if best is None:
+                best = E
+                continue
+            better = _improves(E, best)
+            best = np.where(better, E, best)
+            d_best = np.where(better, np.uint32(d), d_best)
+            r_best = np.where(better, np.uint32(r), r_best)
+    return s, d_best, r_best
+
+
+def encode_matrix_weighted(w: np.ndarray, perm: np.ndarray, h: np.ndarray, bd: int,
+                           codebook_bits: np.ndarray, radius_bits: np.ndarray) -> np.ndarray:
+    """uint32 codes [n, k/8] of :func:`encode_fields_weighted`."""
+    s, d, r = encode_fields_weighted(w, perm, h, bd, codebook_bits, radius_bits)
+    return join_fields(s, d, r, bd)
+
+
+def encode_stream_weighted(w: np.ndarray, perm: np.ndarray, h: np.ndarray, bd: int,
+                           codebook_bits: np.ndarray, radius_bits: np.ndarray) -> np.ndarray:
+    """Canonical LSB-first bitstream of :func:`encode_matrix_weighted`."""
+    return pack_codes(encode_matrix_weighted(w, perm, h, bd, codebook_bits, radius_bits))
+
+
 __all__ = ["gather_subvectors", "radius_midpoints_sq", "encode_fields", "encode_matrix",
-           "encode_stream", "SIGN_BITS"]
+           "encode_stream", "encode_fields_weighted", "encode_matrix_weighted",
+           "encode_stream_weighted", "SIGN_BITS"]
