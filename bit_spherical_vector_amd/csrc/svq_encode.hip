@@ -7,7 +7,9 @@
 // direction index into a codebook of unit directions and a quantized
 // radius.  The coding rule (largest inner product of |v| with a direction,
 // nearest radius to the norm, first index on ties) and its arithmetic are
-// stated in include/svq.h (svq_encode).
+// stated in include/svq.h (svq_encode); the activation-weighted fit (the
+// pair of direction and radius with the smallest weighted squared error,
+// SAGE Abstract and Fig. 2 caption) in include/svq.h (svq_encode_weighted).
 //
 // Every choice is an integer decided by floating-point comparisons, so the
 // arithmetic is fixed to the last bit: float64 products (exact: float32 x
@@ -16,7 +18,8 @@
 // the matrix cores here (their accumulation order is not specified); the
 // scores run on the double-precision VALU, one thread per group of four
 // codes, the codebook broadcast from LDS (every lane of a wave reads the
-// same row).  Per code: 2^bd x 15 double operations (bd = 8: 3840).
+// same row).  Per code: 2^bd x 15 double operations (bd = 8: 3840); the
+// weighted fit 2^bd x (31 + 5 x 2^br) (bd = 8: 13 000).
 #include "svq_device.h"
 #include "../../include/svq.h"
 
@@ -32,8 +35,8 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
   for (int e = threadIdx.x; e < rows * 8; e += 256) s_tab[e] = a.cb[e];
   double *s_msq = s_tab + rows * 8;
   for (int e = threadIdx.x; e < a.n_mid; e += 256) s_msq[e] = a.msq[e];
-  double *s_rad = s_msq + a.n_mid;  // radius values, used for the error only
-  if (a.err)
+  double *s_rad = s_msq + a.n_mid;  // radius values: the error, and the weighted fit
+  if (a.err || a.fit_h)
     for (int e = threadIdx.x; e <= a.n_mid; e += 256) s_rad[e] = a.rad[e];
   __syncthreads();
 
@@ -65,11 +68,57 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
     nsq[q] = n2;
   }
 
-  // direction: the first row with the largest score
+  // direction (and, for the weighted fit, radius) of every code
   double best[ENC_CODES];
   int bi[ENC_CODES];
+  uint32_t rw[ENC_CODES];
 #pragma unroll
-  for (int q = 0; q < ENC_CODES; ++q) bi[q] = 0;
+  for (int q = 0; q < ENC_CODES; ++q) {
+    bi[q] = 0;
+    rw[q] = 0;
+  }
+  if (a.fit_h) {
+    // Weighted fit: the (d, r) pair with the smallest reduced error
+    // (R R) B_d - (R + R) A_d, A_d = sum_l (h_l |v_l|) D_dl,
+    // B_d = sum_l (h_l D_dl) D_dl, lanes in order, pairs in (d, r) order,
+    // the first minimum kept.  One code at a time.
+    const int nR = a.n_mid + 1;
+#pragma unroll
+    for (int q = 0; q < ENC_CODES; ++q) {
+      const int64_t cq = min(c0 + q, a.count - 1);
+      const int c = (int)(cq % C);
+      double hl[8], hw[8];
+#pragma unroll
+      for (int l = 0; l < 8; ++l) {
+        hl[l] = a.fit_h[a.perm[8 * c + l]];
+        hw[l] = hl[l] * av[q][l];
+      }
+      double eb = 0.0;
+      int db = 0;
+      uint32_t rb = 0;
+      for (int j = 0; j < rows; ++j) {
+        const double *D = s_tab + j * 8;
+        double A = hw[0] * D[0];
+        double B = (hl[0] * D[0]) * D[0];
+#pragma unroll
+        for (int l = 1; l < 8; ++l) {
+          A = A + hw[l] * D[l];
+          B = B + (hl[l] * D[l]) * D[l];
+        }
+        for (int t = 0; t < nR; ++t) {
+          const double R = s_rad[t];
+          const double E = (R * R) * B - (R + R) * A;
+          if ((j == 0 && t == 0) || E < eb) {
+            eb = E;
+            db = j;
+            rb = (uint32_t)t;
+          }
+        }
+      }
+      bi[q] = db;
+      rw[q] = rb;
+    }
+  } else {
   for (int j = 0; j < rows; ++j) {
     double D[8];
 #pragma unroll
@@ -85,6 +134,7 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
       }
     }
   }
+  }
 
   // radius: number of squared midpoints strictly below the squared norm.
   // A partial last group packs only its own codes (the stream's trailing
@@ -94,8 +144,9 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
   uint32_t hi = 0;
 #pragma unroll
   for (int q = 0; q < ENC_CODES; ++q) {
-    uint32_t r = 0;
-    for (int t = 0; t < a.n_mid; ++t) r += nsq[q] > s_msq[t] ? 1u : 0u;
+    uint32_t r = rw[q];
+    if (!a.fit_h)
+      for (int t = 0; t < a.n_mid; ++t) r += nsq[q] > s_msq[t] ? 1u : 0u;
     const uint64_t code = q < nq ? (uint64_t)(sg[q] | ((uint32_t)bi[q] << 8) | (r << (8 + a.bd))) : 0;
     if (a.err && q < nq) {
       // (v[l] - w_hat[l])^2 * h[channel], lanes in order; w_hat = +-R[r] D[d][l]

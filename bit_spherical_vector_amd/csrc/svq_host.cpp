@@ -849,9 +849,13 @@ hipError_t stage_tables(const EncTables &t, uint8_t *dst, EncArgs &a, hipStream_
 
 }  // namespace
 
-svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t bd,
-                      const uint16_t *codebook, const uint16_t *radius, const int32_t *perm,
-                      void *codes, void *workspace, size_t *workspace_bytes, void *stream) {
+namespace {
+
+// svq_encode and svq_encode_weighted: fit_h null selects the plain rule.
+svq_status encode_impl(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t bd,
+                       const uint16_t *codebook, const uint16_t *radius, const int32_t *perm,
+                       const double *fit_h, bool weighted, void *codes, void *workspace,
+                       size_t *workspace_bytes, void *stream) {
   if (!workspace_bytes || !codebook || !radius || !perm) return SVQ_ERR_INVALID_ARG;
   if (n <= 0 || k <= 0 || k % 8 != 0) return SVQ_ERR_INVALID_ARG;
   if (bd < 6 || bd > 8) return SVQ_ERR_UNSUPPORTED;
@@ -867,7 +871,7 @@ svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t
     *workspace_bytes = need;
     return SVQ_OK;
   }
-  if (!w || !codes) return SVQ_ERR_INVALID_ARG;
+  if (!w || !codes || (weighted && !fit_h)) return SVQ_ERR_INVALID_ARG;
   if (*workspace_bytes < need) return SVQ_ERR_BUFFER_TOO_SMALL;
   hipStream_t s = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
@@ -880,6 +884,7 @@ svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t
   a.perm = (const int32_t *)(ws + tab_bytes);
   a.codes = (uint8_t *)codes;
   a.count = (int64_t)n * (k / 8);
+  a.fit_h = weighted ? fit_h : nullptr;
   hipError_t e = stage_tables(tab, ws, a, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(ws + tab_bytes, perm, (size_t)k * sizeof(int32_t), hipMemcpyHostToDevice, s);
@@ -888,6 +893,23 @@ svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t
   const hipError_t e2 = hipStreamSynchronize(s);
   if (e == hipSuccess) e = e2;
   return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+}
+
+}  // namespace
+
+svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t bd,
+                      const uint16_t *codebook, const uint16_t *radius, const int32_t *perm,
+                      void *codes, void *workspace, size_t *workspace_bytes, void *stream) {
+  return encode_impl(w, ldw, n, k, bd, codebook, radius, perm, nullptr, false, codes, workspace,
+                     workspace_bytes, stream);
+}
+
+svq_status svq_encode_weighted(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t bd,
+                               const uint16_t *codebook, const uint16_t *radius, const int32_t *perm,
+                               const double *h, void *codes, void *workspace, size_t *workspace_bytes,
+                               void *stream) {
+  return encode_impl(w, ldw, n, k, bd, codebook, radius, perm, h, true, codes, workspace,
+                     workspace_bytes, stream);
 }
 
 svq_status svq_esg_perm(const void *x, int64_t t, int64_t ldx, int32_t k, double *energy,
@@ -916,9 +938,10 @@ svq_status svq_esg_perm(const void *x, int64_t t, int64_t ldx, int32_t k, double
 svq_status svq_abs_select(const float *w, int64_t ldw, int32_t n, int32_t k, const double *h,
                           const int32_t *perm, int32_t n_cand, const int32_t *bd,
                           const uint16_t *const *codebooks, const uint16_t *const *radii,
-                          void *codes, int32_t *chosen, double *errors, void *workspace,
-                          size_t *workspace_bytes, void *stream) {
+                          int32_t weighted_fit, void *codes, int32_t *chosen, double *errors,
+                          void *workspace, size_t *workspace_bytes, void *stream) {
   if (!workspace_bytes || !perm || !bd || !codebooks || !radii) return SVQ_ERR_INVALID_ARG;
+  if (weighted_fit != 0 && weighted_fit != 1) return SVQ_ERR_INVALID_ARG;
   if (n <= 0 || k <= 0 || k % 8 != 0 || ldw < k) return SVQ_ERR_INVALID_ARG;
   if (n_cand < 1 || n_cand > 8) return SVQ_ERR_INVALID_ARG;
   if (k > SVQ_MAX_K || n > SVQ_MAX_N) return SVQ_ERR_UNSUPPORTED;
@@ -956,6 +979,7 @@ svq_status svq_abs_select(const float *w, int64_t ldw, int32_t n, int32_t k, con
     a.codes = ws + off_codes + (size_t)c * codes_slot;
     a.count = count;
     a.h = h;
+    a.fit_h = weighted_fit ? h : nullptr;
     a.err = (double *)(ws + off_err);  // reused: the row sums of c run before c + 1 is coded
     e = stage_tables(tabs[(size_t)c], ws + (size_t)c * tab_bytes, a, s);
     if (e == hipSuccess) e = launch_encode(a, s);

@@ -297,6 +297,9 @@ struct EncArgs {
   const double *rad;
   const double *h;
   double *err;
+  // activation-weighted fit (non-null): the per-channel weights h [k] that
+  // choose direction and radius jointly (rad must then be staged too)
+  const double *fit_h;
 };
 hipError_t launch_encode(const EncArgs &a, hipStream_t s);
 

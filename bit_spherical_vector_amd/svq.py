@@ -34,7 +34,7 @@ SVQ_BF16 = 0
 SVQ_F32 = 1
 
 EXPORTED = ("svq_pack", "svq_linear", "svq_linear_batched", "svq_linear_noalloc",
-            "svq_moe_linear", "svq_encode", "svq_esg_perm", "svq_abs_select",
+            "svq_moe_linear", "svq_encode", "svq_encode_weighted", "svq_esg_perm", "svq_abs_select",
             "svq_status_string")
 SVQ_SCRATCH_BYTES = 64 << 20
 SVQ_NO_EXACT_SPLIT = -(1 << 31)
@@ -108,6 +108,11 @@ def _load() -> ctypes.CDLL:
                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
                                ctypes.c_void_p]
+    lib.svq_encode_weighted.restype = ctypes.c_int
+    lib.svq_encode_weighted.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
     lib.svq_esg_perm.restype = ctypes.c_int
     lib.svq_esg_perm.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -115,7 +120,7 @@ def _load() -> ctypes.CDLL:
     lib.svq_abs_select.restype = ctypes.c_int
     lib.svq_abs_select.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
-                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
     return lib
@@ -191,6 +196,21 @@ def svq_encode(w_ptr: Optional[int], ldw: int, n: int, k: int, bd: int, codebook
     return st, nbytes.value
 
 
+def svq_encode_weighted(w_ptr: Optional[int], ldw: int, n: int, k: int, bd: int, codebook: np.ndarray,
+                        radius: np.ndarray, perm: np.ndarray, h_ptr: Optional[int],
+                        codes_ptr: Optional[int], ws_ptr: Optional[int], ws_bytes: int,
+                        stream: int) -> tuple:
+    """As :func:`svq_encode`, the code chosen by activation-weighted fitting
+    with the device float64 channel weights at ``h_ptr``."""
+    cb = np.ascontiguousarray(codebook, dtype=np.uint16)
+    rad = np.ascontiguousarray(radius, dtype=np.uint16)
+    pm = np.ascontiguousarray(perm, dtype=np.int32)
+    nbytes = ctypes.c_size_t(ws_bytes)
+    st = LIB.svq_encode_weighted(w_ptr, ldw, n, k, bd, cb.ctypes.data, rad.ctypes.data, pm.ctypes.data,
+                                 h_ptr, codes_ptr, ws_ptr, ctypes.byref(nbytes), stream)
+    return st, nbytes.value
+
+
 def svq_esg_perm(x_ptr: Optional[int], t: int, ldx: int, k: int, energy_ptr: Optional[int],
                  perm_ptr: Optional[int], ws_ptr: Optional[int], ws_bytes: int,
                  stream: int) -> tuple:
@@ -201,7 +221,7 @@ def svq_esg_perm(x_ptr: Optional[int], t: int, ldx: int, k: int, energy_ptr: Opt
 
 def svq_abs_select(w_ptr: Optional[int], ldw: int, n: int, k: int, h_ptr: Optional[int],
                    perm: np.ndarray, candidates, codes_ptr: Optional[int], ws_ptr: Optional[int],
-                   ws_bytes: int, stream: int) -> tuple:
+                   ws_bytes: int, stream: int, weighted_fit: int = 0) -> tuple:
     """candidates: sequence of (bd, codebook bits, radius bits) host arrays.
     Returns (status, workspace bytes, chosen index, errors)."""
     nc = len(candidates)
@@ -215,8 +235,8 @@ def svq_abs_select(w_ptr: Optional[int], ldw: int, n: int, k: int, h_ptr: Option
     chosen = ctypes.c_int32(-1)
     nbytes = ctypes.c_size_t(ws_bytes)
     st = LIB.svq_abs_select(w_ptr, ldw, n, k, h_ptr, pm.ctypes.data, nc, bds.ctypes.data, cb_ptrs,
-                            rad_ptrs, codes_ptr, ctypes.byref(chosen), errs.ctypes.data, ws_ptr,
-                            ctypes.byref(nbytes), stream)
+                            rad_ptrs, weighted_fit, codes_ptr, ctypes.byref(chosen), errs.ctypes.data,
+                            ws_ptr, ctypes.byref(nbytes), stream)
     return st, nbytes.value, chosen.value, errs[:nc]
 
 
@@ -451,11 +471,13 @@ def esg_perm(x, stream=None):
     return energy, perm
 
 
-def abs_select(w, perm, h, candidates, stream=None):
+def abs_select(w, perm, h, candidates, stream=None, weighted_fit: bool = False):
     """ABS over ``candidates`` [(bd, codebook bits, radius bits)] for a device
     fp32 weight matrix [n, k] with host permutation ``perm`` and device
-    float64 channel weights ``h`` [k].  Returns (chosen index, errors as a
-    host float64 array, the chosen codes as a device uint8 stream)."""
+    float64 channel weights ``h`` [k]; ``weighted_fit`` codes every candidate
+    by activation-weighted fitting with the same h.  Returns (chosen index,
+    errors as a host float64 array, the chosen codes as a device uint8
+    stream)."""
     import torch
     if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
         raise ValueError("w must be a 2-D float32 tensor with unit column stride")
@@ -468,9 +490,30 @@ def abs_select(w, perm, h, candidates, stream=None):
     codes = torch.zeros((n * (k // 8) * 18 + 7) // 8, dtype=torch.uint8, device=w.device)
     st, _, chosen, errs = svq_abs_select(w.data_ptr(), w.stride(0), n, k, h.data_ptr(), perm,
                                          candidates, codes.data_ptr(), ws.data_ptr(), need,
-                                         _stream_handle(stream))
+                                         _stream_handle(stream), int(bool(weighted_fit)))
     _check(st, "svq_abs_select")
     return chosen, errs, codes
+
+
+def encode_weighted(w, perm, h, bd: int, codebook, radius, stream=None):
+    """As :func:`encode`, each code chosen by activation-weighted fitting with
+    the device float64 channel weights ``h`` [k]."""
+    import torch
+    if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D float32 tensor with unit column stride")
+    if h.dtype != torch.float64 or not h.is_contiguous() or h.numel() != w.shape[1]:
+        raise ValueError("h must be a contiguous float64 tensor of k entries")
+    n, k = w.shape
+    st, need = svq_encode_weighted(None, w.stride(0), n, k, bd, codebook, radius, perm, None, None,
+                                   None, 0, 0)
+    _check(st, "svq_encode_weighted (size query)")
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+    codes = torch.zeros((n * (k // 8) * 18 + 7) // 8, dtype=torch.uint8, device=w.device)
+    st, _ = svq_encode_weighted(w.data_ptr(), w.stride(0), n, k, bd, codebook, radius, perm,
+                                h.data_ptr(), codes.data_ptr(), ws.data_ptr(), need,
+                                _stream_handle(stream))
+    _check(st, "svq_encode_weighted")
+    return codes
 
 
 def encode(w, perm, bd: int, codebook, radius, stream=None):

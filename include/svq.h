@@ -238,6 +238,32 @@ svq_status svq_encode(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t
                       const uint16_t *codebook, const uint16_t *radius, const int32_t *perm,
                       void *codes, void *workspace, size_t *workspace_bytes, void *stream);
 
+/* svq_encode_weighted: as svq_encode, but each code is chosen by
+ * activation-weighted fitting (SAGE abstract and Fig. 2 caption: ESG
+ * protects sensitive channels through fitting weighted by calibration
+ * activations).  The pages give no formula; this library's reading: with
+ * h_l = h[perm[8c + l]] the weight of the input channel at lane l, the code
+ * minimises sum_l h_l (v[l] - w_hat[l])^2 over every (direction, radius)
+ * pair.  Signs are those of svq_encode (a decoded weight with the sign of
+ * v[l] is never farther from it).  With a_l = |v[l]|, the pair (d, r)
+ * minimising the code-dependent part
+ *   E = (R[r] * R[r]) * B_d - (R[r] + R[r]) * A_d,
+ *   A_d = sum_l (h_l * a_l) * D[d][l],  B_d = sum_l (h_l * D[d][l]) * D[d][l]
+ * is chosen, pairs in order (d ascending, then r ascending), the first
+ * minimum on ties; double precision, lanes added in order 0..7, no fused
+ * multiply-adds.
+ *   w, ldw, n, k, bd, codebook, radius, perm, codes, workspace, stream:
+ *               as for svq_encode (the radius table is checked the same way).
+ *   h:          device double [k]: the weight of input channel j (e.g. the
+ *               ESG energy raised to an exponent), finite and >= 0 (other
+ *               values make the codes undefined); NULL only in a size query.
+ * Validates every host argument before any device work and synchronizes
+ * `stream` before returning. */
+svq_status svq_encode_weighted(const float *w, int64_t ldw, int32_t n, int32_t k, int32_t bd,
+                               const uint16_t *codebook, const uint16_t *radius,
+                               const int32_t *perm, const double *h, void *codes,
+                               void *workspace, size_t *workspace_bytes, void *stream);
+
 /* svq_esg_perm: Energy-Stratified Grouping -- the channel permutation of a
  * matrix from calibration activations of its input (SAGE abstract and
  * Fig. 2 caption: channel energies from calibration activations; every
@@ -264,7 +290,8 @@ svq_status svq_esg_perm(const void *x, int64_t t, int64_t ldx, int32_t k, double
 /* svq_abs_select: Adaptive Bit Split -- encode one matrix under each
  * candidate split and keep the one with the lowest activation-weighted
  * reconstruction error (SAGE abstract and Fig. 2 caption).  Every candidate
- * is coded by the svq_encode rule; its error is
+ * is coded by the svq_encode rule, or by the svq_encode_weighted rule with
+ * the same h when weighted_fit is 1; its error is
  *   sum over rows i (row order) of
  *     sum over subvectors c (code order) of
  *       sum over lanes l (lane order) of (v[l] - w_hat[l])^2 * h[perm[8c+l]]
@@ -276,6 +303,7 @@ svq_status svq_esg_perm(const void *x, int64_t t, int64_t ldx, int32_t k, double
  *               ESG energy raised to an exponent), finite, >= 0.
  *   n_cand:     1..8 candidates: bd[c] (6..8), codebooks[c] and radii[c]
  *               (host tables as for svq_encode).
+ *   weighted_fit: 0 (plain coding rule) or 1 (activation-weighted fit).
  *   codes:      device, out: the chosen candidate's code stream.
  *   chosen:     host, out: index of the chosen candidate.
  *   errors:     host, out: the error of every candidate [n_cand].
@@ -286,8 +314,8 @@ svq_status svq_esg_perm(const void *x, int64_t t, int64_t ldx, int32_t k, double
 svq_status svq_abs_select(const float *w, int64_t ldw, int32_t n, int32_t k, const double *h,
                           const int32_t *perm, int32_t n_cand, const int32_t *bd,
                           const uint16_t *const *codebooks, const uint16_t *const *radii,
-                          void *codes, int32_t *chosen, double *errors, void *workspace,
-                          size_t *workspace_bytes, void *stream);
+                          int32_t weighted_fit, void *codes, int32_t *chosen, double *errors,
+                          void *workspace, size_t *workspace_bytes, void *stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *svq_status_string(svq_status s);

@@ -23,8 +23,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol():
     declared = _declared_functions()
     assert set(declared) == {"svq_pack", "svq_linear", "svq_linear_batched", "svq_linear_noalloc",
-                             "svq_moe_linear", "svq_encode", "svq_esg_perm", "svq_abs_select",
-                             "svq_status_string"}
+                             "svq_moe_linear", "svq_encode", "svq_encode_weighted", "svq_esg_perm",
+                             "svq_abs_select", "svq_status_string"}
     for name in declared:
         assert hasattr(svq.LIB, name), name
     assert set(declared) == set(svq.EXPORTED)
@@ -336,6 +336,31 @@ def test_encode_workspace_query_and_validation():
 
 
 
+def test_encode_weighted_workspace_query_and_validation():
+    """svq_encode_weighted: the size query and host checks of svq_encode, and
+    a workspace call without the channel weights is refused before any
+    device work (the pointers below are never dereferenced)."""
+    import synth
+    mat = synth.random_matrix(16, 64, 7, seed=(45, 7, 0))
+    cb, rad, perm = mat.codebook, mat.radius, mat.perm
+    st_plain, need_plain = svq.svq_encode(None, 64, 16, 64, 7, cb, rad, perm, None, None, 0, 0)
+    q = lambda **kw: svq.svq_encode_weighted(kw.get("w"), kw.get("ldw", 64), kw.get("n", 16),
+                                             kw.get("k", 64), kw.get("bd", 7), kw.get("cb", cb),
+                                             kw.get("rad", rad), kw.get("perm", perm), kw.get("h"),
+                                             kw.get("codes"), kw.get("ws"), kw.get("wsb", 0), 0)
+    st, need = q()
+    assert st == svq.SVQ_OK == st_plain and need == need_plain
+    assert q(k=60)[0] == svq.SVQ_ERR_INVALID_ARG
+    assert q(bd=9)[0] == svq.SVQ_ERR_UNSUPPORTED
+    assert q(rad=np.asarray(rad)[::-1].copy())[0] == svq.SVQ_ERR_INVALID_ARG
+    bad_perm = np.asarray(perm).copy()
+    bad_perm[2] = bad_perm[3]
+    assert q(perm=bad_perm)[0] == svq.SVQ_ERR_INVALID_ARG
+    # weights, codes and workspace present but no h: refused
+    assert q(w=0x2000, codes=0x3000, ws=0x1000, wsb=need)[0] == svq.SVQ_ERR_INVALID_ARG
+    assert q(w=0x2000, h=0x4000, codes=0x3000, ws=0x1000, wsb=100)[0] == svq.SVQ_ERR_BUFFER_TOO_SMALL
+
+
 def test_esg_workspace_query_and_validation():
     a = lambda v: (v + 255) // 256 * 256
     q = lambda **kw: svq.svq_esg_perm(kw.get("x"), kw.get("t", 100), kw.get("ldx", 64),
@@ -378,6 +403,11 @@ def test_abs_workspace_query_and_validation():
     assert q(ldw=8)[0] == svq.SVQ_ERR_INVALID_ARG
     assert q(ws=0x1000, wsb=1 << 20)[0] == svq.SVQ_ERR_INVALID_ARG    # no w, h, codes
     assert q(w=0x2000, h=0x3000, codes=0x4000, ws=0x1000, wsb=64)[0] == svq.SVQ_ERR_BUFFER_TOO_SMALL
+    # the fit selector is 0 or 1
+    fit = lambda v: svq.svq_abs_select(None, 64, 16, 64, None, perm, cands, None, None, 0, 0,
+                                       weighted_fit=v)[0]
+    assert fit(1) == svq.SVQ_OK
+    assert fit(2) == svq.SVQ_ERR_INVALID_ARG
 
 
 def test_calibration_wrappers_reject_bad_tensors_before_any_device_work():
