@@ -98,6 +98,40 @@ def parse():
     return ap.parse_args()
 
 
+def _host_facts():
+    """Cores this process may run on (its affinity mask) and the CPU model."""
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cores": int(cores), "cpu_model": model}
+
+
+def _with_one_thread(res, rerun=None):
+    """Add the host facts to a cpu_baseline dict and the same measurement
+    with the BLAS / OpenMP pools limited to one thread (``rerun``: a
+    zero-argument callable returning a baseline dict).  A baseline that is
+    single-threaded already reports its own figure."""
+    if res is None:
+        return None
+    res.update(_host_facts())
+    if rerun is None or res.get("cores", 1) == 1:
+        res["value_1thread"] = res["value"]
+        return res
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        one = rerun()
+    res["value_1thread"] = one["value"]
+    res["sample_1thread"] = one["sample"]
+    return res
+
+
 def cpu_baseline_dense(mats, xs, budget_s=12.0):
     """Time the CPU oracle (unpack, exact decode, un-permute, fp64 product)
     over whole passes of the workload's matrices until about budget_s of
@@ -248,7 +282,8 @@ def bench_moe(args, wl, svq, synth, dev, stream):
         value = flops / (ms_per_step * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(value, 3), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(value / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
-    cpu = None if args.no_cpu_baseline else cpu_baseline_moe(mats, xs, ids, m)
+    cpu = None if args.no_cpu_baseline else _with_one_thread(
+        cpu_baseline_moe(mats, xs, ids, m), lambda: cpu_baseline_moe(mats, xs, ids, m, budget_s=6.0))
     out = {
         "metric": metric,
         "value": round(value, 3),
@@ -336,7 +371,7 @@ def bench_encode(args, wl, svq, synth, stream):
             "unit": "TFLOP/s", "frac": round(achieved / FP64_VALU_PEAK_TFLOPS, 4), "traffic": None}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_encode(w[:64].cpu().numpy(), mat, bd, n)
+        cpu = _with_one_thread(cpu_baseline_encode(w[:64].cpu().numpy(), mat, bd, n))
     out = {
         "metric": "SVQ encode Mcodes/s",
         "value": round(value, 3),
@@ -428,8 +463,9 @@ def bench_decode(args, wl, svq, synth, dev):
     cpu = None
     if not args.no_cpu_baseline:
         mats0, xs0 = layer0
-        cpu = cpu_baseline_dense(mats0, [xs0[c] for c, idx in enumerate(synth.DECODE_CALLS)
-                                         for _ in idx])
+        xs_calls = [xs0[c] for c, idx in enumerate(synth.DECODE_CALLS) for _ in idx]
+        cpu = _with_one_thread(cpu_baseline_dense(mats0, xs_calls),
+                               lambda: cpu_baseline_dense(mats0, xs_calls, budget_s=6.0))
     out = {
         "metric": "packed-weight GB/s (batch-1 decode step, 36 layers)",
         "value": round(value, 3),
@@ -557,8 +593,9 @@ def bench_calib(args, wl, svq, synth, stream):
                 sc.esg_perm(sc.esg_energy(x))
                 reps += 1
             dt = time.perf_counter() - t0
-            cpu = {"value": round(reps * nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": 1,
-                   "kind": "oracle", "sample": f"{reps} full run(s) of the workload, {dt:.1f} s"}
+            cpu = _with_one_thread({"value": round(reps * nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": 1,
+                                    "kind": "oracle",
+                                    "sample": f"{reps} full run(s) of the workload, {dt:.1f} s"})
         dtype, config = "f64 (energies), int32 (ranks)", {"workload": args.workload, "tokens": t, "k": k}
         launches = 3
     else:
@@ -592,9 +629,9 @@ def bench_calib(args, wl, svq, synth, stream):
                 sc.abs_select(w_rows, perm, h, cands)
                 reps += 1
             dt = time.perf_counter() - t0
-            cpu = {"value": round(reps * rows * (k // 8) * len(cands) / dt / 1e6, 5),
-                   "unit": "Mcodes/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{reps} run(s) over {rows} of {n} rows, 3 splits, {dt:.1f} s"}
+            cpu = _with_one_thread({"value": round(reps * rows * (k // 8) * len(cands) / dt / 1e6, 5),
+                                    "unit": "Mcodes/s", "cores": 1, "kind": "oracle",
+                                    "sample": f"{reps} run(s) over {rows} of {n} rows, 3 splits, {dt:.1f} s"})
         dtype, config = "f64", {"workload": args.workload, "n": n, "k": k,
                                 "splits": list(wl["bds"])}
         launches = 3 * 2 + 1
@@ -768,9 +805,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         if m >= 64:
-            cpu = cpu_baseline_prefill(mats, xs)
+            cpu = _with_one_thread(cpu_baseline_prefill(mats, xs), lambda: cpu_baseline_prefill(mats, xs))
         else:
-            cpu = cpu_baseline_dense(mats, xs)
+            cpu = _with_one_thread(cpu_baseline_dense(mats, xs),
+                                   lambda: cpu_baseline_dense(mats, xs, budget_s=6.0))
 
     out = {
         "metric": metric,
