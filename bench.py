@@ -43,21 +43,27 @@ COLD_BYTES = 600 << 20  # > 2 x 256 MB MALL
 # sources it was taken on (sha256 prefix below); after any change of those
 # sources the traffic is reported as null.
 TRAFFIC = {
-    # gemv_fused_kernel
+    # gemv_fused_kernel (profiles/gemv_fused_kernel_layer4b_m1_counters.md)
     "layer4b_m1": {"sources": ("svq_kernels.hip", "svq_device.h"),
-                   "kernel_src_sha256": "64866f994be825d4",
-                   "fetch_kib": 14681.7, "fetch_factor": 2.0,
+                   "kernel_src_sha256": "061290236f436d7a",
+                   "fetch_kib": 14671.0, "fetch_factor": 2.0,
                    "write_kib": 60.0, "write_factor": 1.0},
     # sb_gemm_kernel (profiles/sb_gemm_kernel_layer4b_m16_counters.md)
     "layer4b_m16": {"sources": ("svq_small.hip", "svq_device.h"),
-                    "kernel_src_sha256": "ec5b0394a978c884",
-                    "fetch_kib": 17226.6, "fetch_factor": 2.0,
+                    "kernel_src_sha256": "974c4e39f679f926",
+                    "fetch_kib": 17732.6, "fetch_factor": 2.0,
                     "write_kib": 1604.0, "write_factor": 1.0},
     # prefill_w8_kernel (profiles/prefill_w8_kernel_prefill_m2048_counters.md)
     "prefill_m2048": {"sources": ("svq_prefill.hip", "svq_device.h"),
-                      "kernel_src_sha256": "ccd321bb9ce02b7f",
-                      "fetch_kib": 127740.6, "fetch_factor": 2.0,
+                      "kernel_src_sha256": "875da4cd24cf768d",
+                      "fetch_kib": 127723.4, "fetch_factor": 2.0,
                       "write_kib": 88064.0, "write_factor": 1.0},
+    # moe_sb_kernel, mean over the step's three launches (gate, up, down;
+    # profiles/moe_sb_kernel_moe128_m512_counters.md)
+    "moe128_m512": {"sources": ("svq_moe.hip", "svq_device.h"),
+                    "kernel_src_sha256": "b035c8e2f061fb76",
+                    "fetch_kib": 63428.2, "fetch_factor": 2.0,
+                    "write_kib": 9557.3, "write_factor": 1.0},
 }
 
 
@@ -87,6 +93,7 @@ def parse():
     ap.add_argument("--workload", default="layer4b_m1",
                     choices=["layer4b_m1", "layer4b_m4", "layer4b_m16", "single_512x1024_m1",
                              "prefill_m2048", "moe128_m1", "moe128_m512", "encode_gate_bd7",
+                             "encode_weighted_gate_bd7",
                              "decode4b_36l", "esg_calib_t2048_k2560", "abs_gate_3splits"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-matrix", action="store_true",
@@ -281,7 +288,8 @@ def bench_moe(args, wl, svq, synth, dev, stream):
         metric, unit = "MoE grouped dequant-GEMM TFLOP/s", "TFLOP/s"
         value = flops / (ms_per_step * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(value, 3), "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(value / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(value / BF16_MFMA_PEAK_TFLOPS, 4),
+                "traffic": traffic_bytes(args.workload)}
     cpu = None if args.no_cpu_baseline else _with_one_thread(
         cpu_baseline_moe(mats, xs, ids, m), lambda: cpu_baseline_moe(mats, xs, ids, m, budget_s=6.0))
     out = {
@@ -306,14 +314,18 @@ def bench_moe(args, wl, svq, synth, dev, stream):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_encode(w_rows, mat, bd, n_full, budget_s=12.0):
-    """The encoder oracle over row blocks of the workload's weights until
-    about budget_s of work is done; codes per second."""
+def cpu_baseline_encode(w_rows, mat, bd, n_full, budget_s=12.0, h=None):
+    """The encoder oracle (the weighted fit when h is given) over row blocks
+    of the workload's weights until about budget_s of work is done; codes
+    per second."""
     from oracle import svq_encoder as se
     t0 = time.perf_counter()
     codes, blocks = 0, 0
     while True:
-        se.encode_matrix(w_rows, mat.perm, bd, mat.codebook, mat.radius)
+        if h is None:
+            se.encode_matrix(w_rows, mat.perm, bd, mat.codebook, mat.radius)
+        else:
+            se.encode_matrix_weighted(w_rows, mat.perm, h, bd, mat.codebook, mat.radius)
         codes += w_rows.shape[0] * (w_rows.shape[1] // 8)
         blocks += 1
         if time.perf_counter() - t0 > budget_s:
@@ -340,6 +352,14 @@ def bench_encode(args, wl, svq, synth, stream):
     # the middle of the radius table
     sigma = float(np.sqrt(R[0] * R[-1]) / np.sqrt(8.0))
     w = torch.randn((n, k), device="cuda", generator=gen) * sigma
+    weighted = bool(wl.get("weighted", False))
+    h = None
+    if weighted:
+        # channel weights: the ESG energies of 2048 calibration tokens
+        xc = synth.random_activations(2048, k, seed=(60, 1, 0))
+        xcd = torch.from_numpy(xc.view(np.int16)).view(torch.bfloat16).to("cuda")
+        h, _ = svq.esg_perm(xcd, stream)
+        torch.cuda.synchronize()
     st, need = svq.svq_encode(None, k, n, k, bd, mat.codebook, mat.radius, mat.perm, None, None, 0, 0)
     assert st == svq.SVQ_OK
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
@@ -347,8 +367,12 @@ def bench_encode(args, wl, svq, synth, stream):
     sh = int(stream.cuda_stream)
 
     def step():
-        st, _ = svq.svq_encode(w.data_ptr(), k, n, k, bd, mat.codebook, mat.radius, mat.perm,
-                               codes.data_ptr(), ws.data_ptr(), need, sh)
+        if weighted:
+            st, _ = svq.svq_encode_weighted(w.data_ptr(), k, n, k, bd, mat.codebook, mat.radius, mat.perm,
+                                            h.data_ptr(), codes.data_ptr(), ws.data_ptr(), need, sh)
+        else:
+            st, _ = svq.svq_encode(w.data_ptr(), k, n, k, bd, mat.codebook, mat.radius, mat.perm,
+                                   codes.data_ptr(), ws.data_ptr(), need, sh)
         assert st == svq.SVQ_OK
 
     for _ in range(args.warmup):
@@ -364,16 +388,22 @@ def bench_encode(args, wl, svq, synth, stream):
     ncodes = n * (k // 8)
     value = ncodes / (ms_per_step * 1e-3) / 1e6
     # algorithmic double-precision operations per code: 2^bd scores and the
-    # squared norm, each 8 products and 7 additions
-    flops = ncodes * ((1 << bd) + 1) * 15.0
+    # squared norm, each 8 products and 7 additions; the weighted fit: 8
+    # products h_l |v_l|, then per direction A_d (15) and B_d (23) and per
+    # radius the reduced error (5)
+    if weighted:
+        flops = ncodes * (8.0 + (1 << bd) * (38.0 + 5.0 * (1 << (10 - bd))))
+    else:
+        flops = ncodes * ((1 << bd) + 1) * 15.0
     achieved = flops / (ms_per_step * 1e-3) / 1e12
     roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": FP64_VALU_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / FP64_VALU_PEAK_TFLOPS, 4), "traffic": None}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = _with_one_thread(cpu_baseline_encode(w[:64].cpu().numpy(), mat, bd, n))
+        cpu = _with_one_thread(cpu_baseline_encode(w[:64].cpu().numpy(), mat, bd, n,
+                                                   h=None if h is None else h.cpu().numpy()))
     out = {
-        "metric": "SVQ encode Mcodes/s",
+        "metric": "SVQ encode Mcodes/s" + (" (activation-weighted fit)" if weighted else ""),
         "value": round(value, 3),
         "unit": "Mcodes/s",
         "n_gpus": 1,
@@ -695,6 +725,17 @@ def main():
     m = wl["m"]
     stream = torch.cuda.current_stream()
 
+    if args.copy_calibration:
+        # a plain 256 MiB fill and three device copies, before the workload:
+        # the reference for scaling the HBM byte counters
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     if wl["kind"] == "moe":
         return bench_moe(args, wl, svq, synth, dev, stream)
     if wl["kind"] == "encode":
@@ -793,14 +834,6 @@ def main():
             us = e0.elapsed_time(e1) / args.steps * 1e3
             per_matrix[mat.name] = {"n": mat.n, "k": mat.k, "bd": mat.bd, "us": round(us, 3),
                                     "GB/s": round(mat.codes.size / (us * 1e-6) / 1e9, 1)}
-
-    if args.copy_calibration:
-        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        a.fill_(1)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:

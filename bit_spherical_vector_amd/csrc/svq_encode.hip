@@ -29,6 +29,9 @@ namespace svq {
 
 constexpr int ENC_CODES = 4;  // codes per thread: 4 x 18 bits = 9 whole bytes
 
+// FIT: activation-weighted fit (a.fit_h non-null); the plain rule otherwise.
+// Two instantiations, so that the plain rule keeps its own register budget.
+template <bool FIT>
 __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
   extern __shared__ __attribute__((aligned(16))) double s_tab[];  // codebook rows x 8, midpoints
   const int rows = 1 << a.bd;
@@ -36,7 +39,7 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
   double *s_msq = s_tab + rows * 8;
   for (int e = threadIdx.x; e < a.n_mid; e += 256) s_msq[e] = a.msq[e];
   double *s_rad = s_msq + a.n_mid;  // radius values: the error, and the weighted fit
-  if (a.err || a.fit_h)
+  if (a.err || FIT)
     for (int e = threadIdx.x; e <= a.n_mid; e += 256) s_rad[e] = a.rad[e];
   __syncthreads();
 
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
     bi[q] = 0;
     rw[q] = 0;
   }
-  if (a.fit_h) {
+  if constexpr (FIT) {
     // Weighted fit: the (d, r) pair with the smallest reduced error
     // (R R) B_d - (R + R) A_d, A_d = sum_l (h_l |v_l|) D_dl,
     // B_d = sum_l (h_l D_dl) D_dl, lanes in order, pairs in (d, r) order,
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
 #pragma unroll
   for (int q = 0; q < ENC_CODES; ++q) {
     uint32_t r = rw[q];
-    if (!a.fit_h)
+    if constexpr (!FIT)
       for (int t = 0; t < a.n_mid; ++t) r += nsq[q] > s_msq[t] ? 1u : 0u;
     const uint64_t code = q < nq ? (uint64_t)(sg[q] | ((uint32_t)bi[q] << 8) | (r << (8 + a.bd))) : 0;
     if (a.err && q < nq) {
@@ -178,7 +181,10 @@ __global__ __launch_bounds__(256) void svq_encode_kernel(EncArgs a) {
 hipError_t launch_encode(const EncArgs &a, hipStream_t s) {
   const int64_t groups = (a.count + ENC_CODES - 1) / ENC_CODES;
   const size_t lds = ((size_t)(8 << a.bd) + 2 * (size_t)a.n_mid + 1) * sizeof(double);
-  hipLaunchKernelGGL(svq_encode_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), lds, s, a);
+  if (a.fit_h)
+    hipLaunchKernelGGL(svq_encode_kernel<true>, dim3((unsigned)((groups + 255) / 256)), dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL(svq_encode_kernel<false>, dim3((unsigned)((groups + 255) / 256)), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

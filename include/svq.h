@@ -45,7 +45,9 @@
  * Ownership.  The caller owns every byte: the packed matrix buffer and the
  * workspace are device memory the caller allocates (size queries below);
  * handles are plain structs held by the caller.  The library allocates no
- * device memory and keeps no global state, so there is nothing to free.
+ * device memory and keeps no state, with one exception: the fixed scratch
+ * array of svq_linear_noalloc (SVQ_SCRATCH_BYTES per device, held until the
+ * process ends).  There is nothing to free.
  *
  * Errors.  Every call returns an svq_status and never aborts.  Arguments are
  * validated before any device work.  HIP errors map to SVQ_ERR_HIP.  All
@@ -198,6 +200,11 @@ svq_status svq_linear_noalloc(const svq_handle *w, const void *x, int64_t m, int
  *                 touched.
  *   y:            device [m*topk][ldy] of type ydt, slot-major.
  *   workspace:    as for svq_linear (routing tables and permuted inputs).
+ * Numerics: up to 64 slots (m*topk <= 64) every slot runs the exact batch-1
+ * product of its expert (the m <= 4 numerics above); beyond that the slots
+ * are grouped by expert (work items of at most 48 rows) and each weight
+ * enters the matrix cores as RNE_bf16(R*D) with its sign, x as bf16,
+ * accumulation fp32 (the m > 16 numerics).
  * Routing weights, the activation between projections and the combine over
  * a token's experts are the caller's. */
 svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts,

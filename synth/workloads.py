@@ -76,6 +76,10 @@ WORKLOADS: Dict[str, dict] = {
     "moe128_m512": dict(kind="moe", shapes=MOE_SHAPES, m=512),
     # the encoder (the step before the packed path): one gate-shaped matrix
     "encode_gate_bd7": dict(kind="encode", shapes=[("gate", 9728, 2560)], m=0, bd=7),
+    # the same with activation-weighted fitting, h = ESG energies of 2048
+    # calibration tokens of the layer input
+    "encode_weighted_gate_bd7": dict(kind="encode", shapes=[("gate", 9728, 2560)], m=0, bd=7,
+                                     weighted=True),
     # calibration before encoding: ESG over 2048 tokens of the 2560-wide
     # layer input; ABS over the three splits of one gate-shaped matrix
     "esg_calib_t2048_k2560": dict(kind="esg", shapes=[("x", 2048, 2560)], m=2048),
