@@ -26,7 +26,8 @@
 //   expert's 1024-row table of RNE_bf16(R*D) rows, signs by XOR), and
 //   multiplied with all G row groups.  The activation fragments stream
 //   through a three-slot LDS ring, a quarter unit (fragments 4ci + q) per
-//   slot, filled by direct global-to-LDS loads two slices ahead.  A wave owns
+//   slot, filled by direct global-to-LDS loads two slices ahead; the last
+//   unit's padded half (k = 768) is skipped.  A wave owns
 //   two row tiles and reads each activation fragment once for both.  The
 //   block's outputs are staged in LDS and leave as 16-byte row pieces.
 //   Blocks are mapped so that the column groups of one item share an XCD
@@ -35,6 +36,7 @@
 // Numerics as the dequant GEMM for many rows: weights RNE_bf16(R*D), bf16
 // activations, fp32 accumulation, bf16 (RNE) or fp32 output.
 #include <algorithm>
+#include <type_traits>
 
 #include "svq_device.h"
 #include "../../include/svq.h"
@@ -148,12 +150,13 @@ __global__ __launch_bounds__(MOE_SB_PREP_THREADS) void moe_sb_prep_kernel(
   }
 }
 
-// Table rows (RNE_bf16(R*D), 16 bytes by 10-bit index) of the four codes
-// ci = 0..3 of fragment group q.
+// Table rows (RNE_bf16(R*D), 16 bytes by 10-bit index) of the codes
+// ci = 0..NCI-1 of fragment group q.
+template <int NCI>
 __device__ __forceinline__ void moe_reads(const uint8_t *smem, uint32_t Lw, uint32_t H, const SbShifts &sh,
                                           u4 (&D)[4]) {
 #pragma unroll
-  for (int ci = 0; ci < 4; ++ci) {
+  for (int ci = 0; ci < NCI; ++ci) {
     // byte address (hi << 12) | (lo << 4) of the 16-byte row (hi << 8) | lo
     const uint32_t lo4 = __builtin_amdgcn_ubfe(Lw, 8 * ci, 8) << 4;
     const uint32_t hi = __builtin_amdgcn_ubfe(H, sh.hi[ci], 2);
@@ -178,10 +181,9 @@ typedef __attribute__((address_space(3))) void moe_lds_t;
 constexpr int moe_vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Workgroup barrier for the slice loop: this wave's LDS operations are
-// complete, then s_barrier.  Unlike __syncthreads() it does not wait for the
-// wave's outstanding global loads (the code prefetches stay in flight); the
-// slice's direct-to-LDS loads are waited for explicitly before it.  The
-// memory clobber keeps every memory access on its side of the barrier.
+// complete, then s_barrier (the slice's direct-to-LDS loads are waited for
+// explicitly before it).  The memory clobber keeps every memory access on
+// its side of the barrier.
 __device__ __forceinline__ void moe_slice_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // One block's product over G row groups (see moe_sb_kernel).  The unit
@@ -218,7 +220,6 @@ __device__ __forceinline__ void moe_sb_block(const MatView &w, int tg, int wi, i
     shf.hi[ci] = 8 * b0 + 2 * ci;
   }
   // the record-q part of a unit's codes (what slice q reads): three loads per tile
-  constexpr int CODE_LOADS = 3 * MOE_SB_TW;
   auto unit_codes_q = [&](SbCodes &c, int t, int u, int q) __attribute__((always_inline)) {
     const uint8_t *ub = w.base + w.off_codes + ((size_t)tl[t] * U + u) * UNIT_BYTES;
     c.S[q] = __builtin_nontemporal_load((const u4 *)(ub + PLANE_SIGN + 64 * q + offs.S));
@@ -258,50 +259,66 @@ __device__ __forceinline__ void moe_sb_block(const MatView &w, int tg, int wi, i
 #pragma unroll
     for (int g = 0; g < G; ++g) C[t][g] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  for (int u = 0; u < U; ++u) {
+  // One slice (unit u, fragment group q) with NCI of the unit's four column
+  // groups: code columns 16ci .. 16ci + 15 hold input slots 512u + 128ci on,
+  // so when the last unit's real slots end within its first half (k = 768:
+  // 512 + 256) its groups 2 and 3 are padding (zero inputs) and are skipped.
+  auto slice = [&](int u, auto Q, auto NCI) __attribute__((always_inline)) {
+    constexpr int q = decltype(Q)::value, nci = decltype(NCI)::value;
+    const int i = 4 * u + q;
     const int un = min(u + 1, U - 1);
+    // this wave's part of slice i has landed.  A count above zero would
+    // rely on the direct-to-LDS loads completing in order with the later
+    // (non-temporal) code loads, which does not hold: every outstanding load
+    // is waited for.
+    __builtin_amdgcn_s_waitcnt(moe_vmcnt_imm(0));
+    // every wave's part has landed, and every wave is done with slice
+    // i - 1, whose slot (i + 2) % 3 is refilled next
+    moe_slice_barrier();
+    if (i + 2 < NS) dma_slice(i + 2);
+    const uint8_t *ab = smem + MOE_SB_OFF_A + (i % MOE_SB_RING) * MOE_SB_SLICE_BYTES;
+    u4 D[MOE_SB_TW][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = 4 * u + q;
-      // this wave's part of slice i has landed: at step i >= 1, the loads
-      // known to be issued after it are those of step i - 1 (the DMA of
-      // slice i + 1 when it exists, then the codes), all after barrier i - 1
-      if (i == 0)
-        __builtin_amdgcn_s_waitcnt(moe_vmcnt_imm(0));
-      else if (i + 1 < NS)
-        __builtin_amdgcn_s_waitcnt(moe_vmcnt_imm(G + CODE_LOADS));
-      else
-        __builtin_amdgcn_s_waitcnt(moe_vmcnt_imm(CODE_LOADS));
-      // every wave's part has landed, and every wave is done with slice
-      // i - 1, whose slot (i + 2) % 3 is refilled next
-      moe_slice_barrier();
-      if (i + 2 < NS) dma_slice(i + 2);
-      const uint8_t *ab = smem + MOE_SB_OFF_A + (i % MOE_SB_RING) * MOE_SB_SLICE_BYTES;
-      u4 D[MOE_SB_TW][4];
+    for (int t = 0; t < MOE_SB_TW; ++t) moe_reads<nci>(smem, cd[t].L[q], cd[t].H[q], shf, D[t]);
+    uint64_t S01[MOE_SB_TW], S23[MOE_SB_TW];
 #pragma unroll
-      for (int t = 0; t < MOE_SB_TW; ++t) moe_reads(smem, cd[t].L[q], cd[t].H[q], shf, D[t]);
-      uint64_t S01[MOE_SB_TW], S23[MOE_SB_TW];
+    for (int t = 0; t < MOE_SB_TW; ++t) {
+      S01[t] = (uint64_t)cd[t].S[q][0] | ((uint64_t)cd[t].S[q][1] << 32);
+      S23[t] = (uint64_t)cd[t].S[q][2] | ((uint64_t)cd[t].S[q][3] << 32);
+      unit_codes_q(cd[t], t, un, q);
+    }
+#pragma unroll
+    for (int ci = 0; ci < nci; ++ci) {
+      u4 A[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) A[g] = *(const u4 *)(ab + (4 * g + ci) * 1024 + lane * 16);
 #pragma unroll
       for (int t = 0; t < MOE_SB_TW; ++t) {
-        S01[t] = (uint64_t)cd[t].S[q][0] | ((uint64_t)cd[t].S[q][1] << 32);
-        S23[t] = (uint64_t)cd[t].S[q][2] | ((uint64_t)cd[t].S[q][3] << 32);
-        unit_codes_q(cd[t], t, un, q);
-      }
+        const u4 B = moe_signed(D[t][ci], S01[t], S23[t], shf.sg[ci]);
 #pragma unroll
-      for (int ci = 0; ci < 4; ++ci) {
-        u4 A[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) A[g] = *(const u4 *)(ab + (4 * g + ci) * 1024 + lane * 16);
-#pragma unroll
-        for (int t = 0; t < MOE_SB_TW; ++t) {
-          const u4 B = moe_signed(D[t][ci], S01[t], S23[t], shf.sg[ci]);
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-            C[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, A[g]),
-                                                              __builtin_bit_cast(b8, B), C[t][g], 0, 0, 0);
-        }
+        for (int g = 0; g < G; ++g)
+          C[t][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, A[g]),
+                                                            __builtin_bit_cast(b8, B), C[t][g], 0, 0, 0);
       }
     }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  const bool half_last = w.k - (U - 1) * UNIT_SLOTS <= UNIT_SLOTS / 2;  // block-uniform
+  for (int u = 0; u < U - (half_last ? 1 : 0); ++u) {
+    slice(u, I0(), I4());
+    slice(u, I1(), I4());
+    slice(u, I2(), I4());
+    slice(u, I3(), I4());
+  }
+  if (half_last) {
+    slice(U - 1, I0(), I2());
+    slice(U - 1, I1(), I2());
+    slice(U - 1, I2(), I2());
+    slice(U - 1, I3(), I2());
   }
 
   // The outputs leave through LDS: the block's item rows x its 128 columns
