@@ -61,9 +61,9 @@ TRAFFIC = {
     # moe_sb_kernel, mean over the step's three launches (gate, up, down;
     # profiles/moe_sb_kernel_moe128_m512_counters.md)
     "moe128_m512": {"sources": ("svq_moe.hip", "svq_device.h"),
-                    "kernel_src_sha256": "b035c8e2f061fb76",
-                    "fetch_kib": 63428.2, "fetch_factor": 2.0,
-                    "write_kib": 9557.3, "write_factor": 1.0},
+                    "kernel_src_sha256": "93191ad44b63ec23",
+                    "fetch_kib": 63432.1, "fetch_factor": 2.0,
+                    "write_kib": 11320.4, "write_factor": 1.0},
 }
 
 
@@ -100,6 +100,9 @@ def parse():
                     help="dense workloads: also time every matrix alone (config.per_matrix)")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="only measure plain device copy and read rates (context for the HBM peak)")
+    ap.add_argument("--matmul-ceiling", action="store_true",
+                    help="only time torch's dense bf16 matmul on the prefill shapes (context for the "
+                         "MFMA peak)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -703,6 +706,40 @@ def stream_ceiling():
     print(json.dumps({"stream_ceiling": out, "bytes": n, "peak_GB/s": HBM_PEAK_GBS}), flush=True)
 
 
+def matmul_ceiling():
+    """torch's dense bf16 matmul (the vendor GEMM library) on the shapes of
+    the prefill workload: y = x @ W^T with plain bf16 weights, W^T stored
+    contiguous, 2048 tokens, the three products back to back.  Context for
+    the 2.5 PFLOP/s peak: the same flops with no weight decode at all."""
+    import torch
+
+    import synth
+    m = synth.WORKLOADS["prefill_m2048"]["m"]
+    shapes = synth.PREFILL_SHAPES
+    g = torch.Generator(device="cuda").manual_seed(0)
+    xs = [torch.randn(m, k, device="cuda", dtype=torch.bfloat16, generator=g) for _, n, k in shapes]
+    wts = [torch.randn(k, n, device="cuda", dtype=torch.bfloat16, generator=g) for _, n, k in shapes]
+    flops = sum(2.0 * m * n * k for _, n, k in shapes)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(10):
+        ys = [x @ wt for x, wt in zip(xs, wts)]
+    torch.cuda.synchronize()
+    e0.record(s)
+    reps = 50
+    for _ in range(reps):
+        ys = [x @ wt for x, wt in zip(xs, wts)]
+    e1.record(s)
+    torch.cuda.synchronize()
+    del ys
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"matmul_ceiling": {"workload": "prefill_m2048 shapes, dense bf16 weights",
+                                         "us_per_step": round(ms * 1e3, 1),
+                                         "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+                                         "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 3)},
+                      "shapes": [[m, n, k] for _, n, k in shapes]}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -712,6 +749,8 @@ def main():
 
     if args.stream_ceiling:
         return stream_ceiling()
+    if args.matmul_ceiling:
+        return matmul_ceiling()
 
     import numpy as np
     import torch
