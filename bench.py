@@ -61,9 +61,9 @@ TRAFFIC = {
     # moe_sb_kernel, mean over the step's three launches (gate, up, down;
     # profiles/moe_sb_kernel_moe128_m512_counters.md)
     "moe128_m512": {"sources": ("svq_moe.hip", "svq_device.h"),
-                    "kernel_src_sha256": "93191ad44b63ec23",
-                    "fetch_kib": 63432.1, "fetch_factor": 2.0,
-                    "write_kib": 11320.4, "write_factor": 1.0},
+                    "kernel_src_sha256": "9cad67bccdd9f870",
+                    "fetch_kib": 63408.5, "fetch_factor": 2.0,
+                    "write_kib": 11327.6, "write_factor": 1.0},
 }
 
 

@@ -335,12 +335,24 @@ struct MoeShape {
 // Grouped MoE product (svq_moe.hip) for routed slots: activation rows per
 // work item, workspace bytes of the fragment-ordered activations, and the
 // prep + product launches over the routing's work list (expert, sorted rows
-// r0..r1).
+// r0..r1).  Up to MOE_FUSED_MAX_SLOTS slots the prep launch also does the
+// routing (route.ids set): every prep block sorts the slots itself and
+// writes the work list, the sorted slots and the zero rows of slots with
+// invalid ids; beyond that moe_route_kernel has written them (route.ids
+// null).
 constexpr int MOE_SB_ROWS = 48;
+constexpr int MOE_FUSED_MAX_SLOTS = 8192;
+struct MoeRoute {
+  const int32_t *ids;  // expert id per slot, or null when the work list is given
+  int32_t slots;       // S = m * topk
+  void *y;             // output rows of invalid slots are zeroed here
+  int64_t ldy;
+  int32_t ydt;
+};
 size_t moe_sb_xa_bytes(int max_work, int units);
 hipError_t launch_moe_sb(const MoeShape &sh, const ExpertTable &tab, const uint16_t *x, int64_t ldx,
-                         int x_per_slot, int topk, const int32_t *work, const int32_t *nwork,
-                         const int32_t *sorted, int max_work, uint8_t *xa, void *y, int64_t ldy,
-                         int ydt, hipStream_t s);
+                         int x_per_slot, int topk, const MoeRoute &route, int32_t *work,
+                         int32_t *nwork, int32_t *sorted, int max_work, uint8_t *xa, void *y,
+                         int64_t ldy, int ydt, hipStream_t s);
 
 }  // namespace svq

@@ -1180,7 +1180,9 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
 // MoE launcher.  Workspace layout depends on the path:
 //   exact (m*topk <= MOE_EXACT_MAX_SLOTS): none (the fused per-slot launch)
 //   grouped: counts[E], offsets[E+1], sorted[S], work[3*max_work], nwork,
-//            fragment-ordered activations (moe_sb_xa_bytes)
+//            fragment-ordered activations (moe_sb_xa_bytes); the routing
+//            is done by the prep launch up to MOE_FUSED_MAX_SLOTS slots
+//            (counts and offsets unused), by moe_route_kernel beyond
 // ---------------------------------------------------------------------------
 constexpr int MOE_EXACT_MAX_SLOTS = 64;
 
@@ -1260,12 +1262,22 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   int32_t *sorted = (int32_t *)(b + o_sorted), *work = (int32_t *)(b + o_work);
   int32_t *nwork = (int32_t *)(b + o_nwork);
   uint8_t *xb = b + o_xb;
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), 0, s, ids, S, E, rows_per_item, counts,
-                     offsets, sorted, work, nwork, y, ldy, sh.n, ydt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_moe_sb(sh, tab, xp, ldx, x_per_slot, topk, work, nwork, sorted, max_work, xb, y,
-                       ldy, ydt, s);
+  MoeRoute route;
+  route.ids = nullptr;
+  route.slots = S;
+  route.y = y;
+  route.ldy = ldy;
+  route.ydt = ydt;
+  if (S <= MOE_FUSED_MAX_SLOTS) {
+    route.ids = ids;  // the prep launch does the routing
+  } else {
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), 0, s, ids, S, E, rows_per_item, counts,
+                       offsets, sorted, work, nwork, y, ldy, sh.n, ydt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_moe_sb(sh, tab, xp, ldx, x_per_slot, topk, route, work, nwork, sorted, max_work, xb,
+                       y, ldy, ydt, s);
 }
 
 }  // namespace svq

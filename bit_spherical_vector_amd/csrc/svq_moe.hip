@@ -9,9 +9,10 @@
 // reordered activations (Fig. 6 caption).  The routing itself (top-k slots
 // per token, slot q = t*topk + j) is this library's convention.
 //
-// After the routing launch has sorted the slots by expert into work items
-// (each expert's rows split evenly into items of at most MOE_SB_ROWS rows,
-// moe_route_kernel), two launches per call:
+// The slots are sorted by expert into work items (each expert's rows split
+// evenly into items of at most MOE_SB_ROWS rows): up to MOE_FUSED_MAX_SLOTS
+// slots by every block of the prep launch for itself, beyond that by the
+// separate moe_route_kernel.  Then two launches per call:
 //
 // * moe_sb_prep_kernel, block (work item, row group g of 16 rows): the
 //   group's input rows are staged whole in LDS, then gathered through the
@@ -70,6 +71,24 @@ __host__ __device__ __forceinline__ size_t moe_sb_xa_off(int wi, int units, int 
   return (((size_t)wi * units + u) * MOE_SB_G + g) * MOE_SB_GROUP_BYTES;
 }
 
+// Routing inside the prep launch (ROUTE): every block sorts the slots by
+// expert itself, in the order moe_route_kernel's work list defines (experts
+// ascending, each expert's rows split evenly into items of at most
+// MOE_SB_ROWS rows) and, within an expert, by slot index, so that all blocks
+// of an item find the same rows without talking to each other.  Thread t
+// holds the ids of slots t*C .. t*C + C - 1 (C = ceil(S / threads) <=
+// MOE_ROUTE_IDS) in registers.
+constexpr int MOE_ROUTE_IDS = MOE_FUSED_MAX_SLOTS / MOE_SB_PREP_THREADS;
+struct MoeRouteLds {
+  int32_t cnt[MAX_EXPERTS];
+  int32_t off[MAX_EXPERTS + 1];    // first sorted row of each expert
+  int32_t items[MAX_EXPERTS + 1];  // first work item of each expert
+  int32_t wsum[2][MAX_EXPERTS / 64];
+  int32_t scan[MOE_SB_PREP_THREADS / 64];
+  int32_t rows[MOE_SB_ROWS];       // slots of the block's item, in row order
+  int32_t expert;
+};
+
 // Block (work item, row group g), MOE_SB_PREP_THREADS threads: the group's
 // 16 activation rows are staged whole in LDS (rb rows per pass, coalesced
 // 16-byte loads when x and ldx allow them; the row stride carries 16 bytes
@@ -78,21 +97,134 @@ __host__ __device__ __forceinline__ size_t moe_sb_xa_off(int wi, int units, int 
 // expert's permutation.  Wave w writes fragment group q = w & 3 of the units
 // u = w >> 2 (mod MOE_SB_PREP_THREADS / 256): lane L owns row 16g + (L & 15)
 // and the slots of code column 16ci + 4(L >> 4) + q.  Rows past the item and
-// slots past k are zeros.
+// slots past k are zeros.  With ROUTE the block first does the routing
+// (above); row group 0 of every item writes the item's work record and
+// sorted slots for the product launch, block 0 the item count.
+template <bool ROUTE>
 __global__ __launch_bounds__(MOE_SB_PREP_THREADS) void moe_sb_prep_kernel(
     MoeShape sh, ExpertTable tab, const uint16_t *__restrict__ x, int64_t ldx, int x_per_slot, int topk,
-    int vec, int rb, const int32_t *__restrict__ work, const int32_t *__restrict__ nwork,
-    const int32_t *__restrict__ sorted, uint8_t *__restrict__ xa) {
+    int vec, int rb, MoeRoute route, int32_t *__restrict__ work, int32_t *__restrict__ nwork,
+    int32_t *__restrict__ sorted, uint8_t *__restrict__ xa) {
   constexpr int NT = MOE_SB_PREP_THREADS, USTEP = NT / 256;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ MoeRouteLds R;
+  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63, s = L >> 4, rl = L & 15;
   const int wi = (int)blockIdx.x / MOE_SB_G, g = (int)blockIdx.x - wi * MOE_SB_G;
-  if (wi >= *nwork) return;  // block-uniform, before any barrier
-  const int e = work[3 * wi], r0 = work[3 * wi + 1], rows = work[3 * wi + 2] - r0;
-  if (16 * g >= rows) return;  // block-uniform
+  int e, r0, rows;
+  if constexpr (ROUTE) {
+    const int S = route.slots, E = sh.num_experts;
+    const int C = (S + NT - 1) / NT;  // <= MOE_ROUTE_IDS (host check)
+    int my[MOE_ROUTE_IDS];
+#pragma unroll
+    for (int j = 0; j < MOE_ROUTE_IDS; ++j) {
+      const int q = tid * C + j;
+      my[j] = (j < C && q < S) ? route.ids[q] : -1;
+    }
+    for (int i = tid; i < E; i += NT) R.cnt[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < MOE_ROUTE_IDS; ++j) {
+      const int q = tid * C + j;
+      if (my[j] >= 0 && my[j] < E) {
+        atomicAdd(&R.cnt[my[j]], 1);
+      } else if (j < C && q < S && q % (int)gridDim.x == (int)blockIdx.x) {
+        // a slot with an id outside [0, E): its output row is zeros
+        char *yr = (char *)route.y + (size_t)q * route.ldy * (route.ydt == 0 ? 2 : 4);
+        for (int c = 0; c < sh.n; ++c) store_out(yr, (size_t)c, 0.f, route.ydt);
+      }
+    }
+    __syncthreads();
+    // exclusive scans of the slot counts and of the items per expert (threads
+    // 0 .. MAX_EXPERTS-1, one expert each: within each wave, then the wave
+    // totals)
+    int cn = 0, it = 0, ci = 0, ii = 0;
+    if (tid < MAX_EXPERTS) {
+      cn = tid < E ? R.cnt[tid] : 0;
+      it = (cn + MOE_SB_ROWS - 1) / MOE_SB_ROWS;
+      ci = cn;
+      ii = it;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int uc = __shfl_up(ci, d), ui = __shfl_up(ii, d);
+        if (L >= d) {
+          ci += uc;
+          ii += ui;
+        }
+      }
+      if (L == 63) {
+        R.wsum[0][w] = ci;
+        R.wsum[1][w] = ii;
+      }
+    }
+    __syncthreads();
+    if (tid < MAX_EXPERTS) {
+      int bc = 0, bi = 0;
+      for (int v = 0; v < w; ++v) {
+        bc += R.wsum[0][v];
+        bi += R.wsum[1][v];
+      }
+      if (tid < E) {
+        R.off[tid] = bc + ci - cn;
+        R.items[tid] = bi + ii - it;
+      }
+      if (tid == E - 1) {
+        R.off[E] = bc + ci;
+        R.items[E] = bi + ii;
+      }
+    }
+    __syncthreads();
+    const int nitems = R.items[E];
+    if (blockIdx.x == 0 && tid == 0) *nwork = nitems;
+    if (wi >= nitems) return;  // block-uniform
+    if (tid < E && R.items[tid] <= wi && wi < R.items[tid + 1]) R.expert = tid;
+    __syncthreads();
+    e = R.expert;
+    const int n_items = R.items[e + 1] - R.items[e], cnt = R.cnt[e], c = wi - R.items[e];
+    const int lo = (int)((int64_t)c * cnt / n_items), hi = (int)((int64_t)(c + 1) * cnt / n_items);
+    r0 = R.off[e] + lo;
+    rows = hi - lo;
+    if (16 * g >= rows) return;  // block-uniform
+    // rank of each of the expert's slots among them (slot order): the
+    // thread's matches, then a block exclusive scan
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_ROUTE_IDS; ++j) mine += my[j] == e ? 1 : 0;
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(incl, d);
+      if (L >= d) incl += u;
+    }
+    if (L == 63) R.scan[w] = incl;
+    __syncthreads();
+    int rank = incl - mine;
+    for (int v = 0; v < w; ++v) rank += R.scan[v];
+#pragma unroll
+    for (int j = 0; j < MOE_ROUTE_IDS; ++j) {
+      if (my[j] == e) {
+        if (rank >= lo && rank < hi) R.rows[rank - lo] = tid * C + j;
+        ++rank;
+      }
+    }
+    __syncthreads();
+    if (g == 0) {
+      if (tid < rows) sorted[r0 + tid] = R.rows[tid];
+      if (tid == 0) {
+        work[3 * wi + 0] = e;
+        work[3 * wi + 1] = r0;
+        work[3 * wi + 2] = r0 + rows;
+      }
+    }
+  } else {
+    if (wi >= *nwork) return;  // block-uniform, before any barrier
+    e = work[3 * wi];
+    r0 = work[3 * wi + 1];
+    rows = work[3 * wi + 2] - r0;
+    if (16 * g >= rows) return;  // block-uniform
+  }
   const int U = sh.units, kp = U * UNIT_SLOTS, k = sh.k;
   const int stride = moe_sb_prep_stride(kp);  // bytes per staged row
   const uint16_t *perm = (const uint16_t *)(tab.base[e] + sh.off_perm);
-  const int tid = threadIdx.x, w = tid >> 6, L = tid & 63, s = L >> 4, rl = L & 15;
   const int q = w & 3, u0 = w >> 2;
   const int chunks = kp / 8;  // 16-byte pieces of a staged row
   constexpr int BATCH = 4;
@@ -108,7 +240,7 @@ __global__ __launch_bounds__(MOE_SB_PREP_THREADS) void moe_sb_prep_kernel(
         const int c = c0 + tid + NT * i;
         const int rr = c / chunks, cc = c - rr * chunks, row = 16 * g + rb0 + rr;
         if (c < nstage && row < rows && 8 * cc < k) {
-          const int slot = sorted[r0 + row];
+          const int slot = ROUTE ? R.rows[row] : sorted[r0 + row];
           const uint16_t *xr = x + (int64_t)(x_per_slot ? slot : slot / topk) * ldx + 8 * cc;
           if (vec) {
             v[i] = *(const u4 *)xr;  // k is a multiple of 8
@@ -396,17 +528,28 @@ static int moe_sb_prep_rb(int kp) {
 }
 
 hipError_t launch_moe_sb(const MoeShape &sh, const ExpertTable &tab, const uint16_t *x, int64_t ldx,
-                         int x_per_slot, int topk, const int32_t *work, const int32_t *nwork,
-                         const int32_t *sorted, int max_work, uint8_t *xa, void *y, int64_t ldy,
-                         int ydt, hipStream_t s) {
+                         int x_per_slot, int topk, const MoeRoute &route, int32_t *work,
+                         int32_t *nwork, int32_t *sorted, int max_work, uint8_t *xa, void *y,
+                         int64_t ldy, int ydt, hipStream_t s) {
   const int kp = sh.units * UNIT_SLOTS;
   const int rb = moe_sb_prep_rb(kp);
   const size_t prep_lds = (size_t)rb * moe_sb_prep_stride(kp);
   const int vec = ((uintptr_t)x % 16 == 0 && ldx % 8 == 0) ? 1 : 0;
-  hipError_t e = allow_smem(moe_sb_prep_kernel, (int)prep_lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_sb_prep_kernel, dim3(max_work * MOE_SB_G), dim3(MOE_SB_PREP_THREADS), prep_lds, s, sh, tab, x, ldx,
-                     x_per_slot, topk, vec, rb, work, nwork, sorted, xa);
+  const dim3 pgrid(max_work * MOE_SB_G), pblock(MOE_SB_PREP_THREADS);
+  hipError_t e;
+  if (route.ids) {
+    if (route.slots > MOE_FUSED_MAX_SLOTS || sh.num_experts < 1 || sh.num_experts > MAX_EXPERTS)
+      return hipErrorInvalidValue;
+    e = allow_smem(moe_sb_prep_kernel<true>, (int)prep_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(moe_sb_prep_kernel<true>, pgrid, pblock, prep_lds, s, sh, tab, x, ldx, x_per_slot,
+                       topk, vec, rb, route, work, nwork, sorted, xa);
+  } else {
+    e = allow_smem(moe_sb_prep_kernel<false>, (int)prep_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(moe_sb_prep_kernel<false>, pgrid, pblock, prep_lds, s, sh, tab, x, ldx, x_per_slot,
+                       topk, vec, rb, route, work, nwork, sorted, xa);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = allow_smem(moe_sb_kernel, MOE_SB_SMEM);

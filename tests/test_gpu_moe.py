@@ -161,3 +161,27 @@ def test_moe_grouped_strided_unaligned(svq, x_per_slot):
         assert torch.all(yb[:, n:] == 7.0)
         y64 = out_to_f64(y)
         _check_slots(y64, x, ids, topk, x_per_slot, Ws, range(n_exp), f"strided moe {dt}")
+
+
+@pytest.mark.parametrize("m,topk", [(2048, 4), (2100, 4)])
+def test_moe_routing_paths(svq, m, topk):
+    """8192 slots (the routing done inside the prep launch, its largest case)
+    and 8400 slots (the separate routing launch), some ids out of range:
+    every valid slot matches the oracle, every invalid slot gets a zero row."""
+    n_exp, n, k = 6, 40, 520
+    mats = [synth.random_matrix(n, k, 6 + e % 3, seed=(49, e, 0)) for e in range(n_exp)]
+    Ws = [so.decode_matrix(w.codes, n, k, w.bd, w.codebook, w.radius, w.perm) for w in mats]
+    pms = [svq.pack(w) for w in mats]
+    rng = np.random.default_rng(50 + m)
+    ids = rng.integers(0, n_exp, size=m * topk).astype(np.int32)
+    bad = np.arange(3, ids.size, 97)
+    ids[bad] = np.where(bad % 2 == 0, -2, n_exp)
+    x = synth.random_activations(m, k, seed=(51, m, 0))
+    for dt in (torch.float32, torch.bfloat16):
+        y = _run_moe(svq, pms, x, ids, topk, 0, dt)
+        assert np.all(y[bad] == 0)
+        good = np.setdiff1d(np.arange(ids.size), bad)
+        for e in range(n_exp):
+            slots = good[ids[good] == e]
+            assert_within_tolerance(y[slots], so.linear(x[slots // topk], Ws[e]), x[slots // topk], Ws[e],
+                                    label=f"{m * topk} slots, expert {e}, {dt}")
