@@ -30,6 +30,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+# default warm-up: steps of the same work until the GPU has been busy this
+# long (see warm_up), at most this many steps
+WARMUP_MIN_S = 0.2
+WARMUP_MAX_STEPS = 200000
 FP64_VALU_PEAK_TFLOPS = 78.6  # MI355X published fp64 vector peak
 COLD_BYTES = 600 << 20  # > 2 x 256 MB MALL
 
@@ -89,7 +93,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed region (default: as many as keep the GPU "
+                         "busy for at least %.1f s, so that its clocks have settled)" % WARMUP_MIN_S)
     ap.add_argument("--workload", default="layer4b_m1",
                     choices=["layer4b_m1", "layer4b_m4", "layer4b_m16", "single_512x1024_m1",
                              "prefill_m2048", "moe128_m1", "moe128_m512", "encode_gate_bd7",
@@ -272,13 +278,11 @@ def bench_moe(args, wl, svq, synth, dev, stream):
         for call in calls[i % copies]:
             call()
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    nw = warm_up(args, step, stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(nw + i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
@@ -301,7 +305,7 @@ def bench_moe(args, wl, svq, synth, dev, stream):
         "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup_done,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -378,9 +382,7 @@ def bench_encode(args, wl, svq, synth, stream):
                                    codes.data_ptr(), ws.data_ptr(), need, sh)
         assert st == svq.SVQ_OK
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(args, lambda i: step(), stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
@@ -411,7 +413,7 @@ def bench_encode(args, wl, svq, synth, stream):
         "unit": "Mcodes/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup_done,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -462,9 +464,8 @@ def bench_decode(args, wl, svq, synth, dev):
             call()
 
     side.wait_stream(torch.cuda.current_stream())
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        warm_up(args, lambda i: step(), side)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     ev[0].record(side)
     for _ in range(args.steps):
@@ -478,9 +479,7 @@ def bench_decode(args, wl, svq, synth, dev):
         step()
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
+        nw_graph = warm_up(args, lambda i: graph.replay(), side)
         ev[2].record(side)
         for _ in range(args.steps):
             graph.replay()
@@ -488,6 +487,7 @@ def bench_decode(args, wl, svq, synth, dev):
     torch.cuda.synchronize()
     ms_per_step = ev[2].elapsed_time(ev[3]) / args.steps
     ttft = bench_first_token(args, wl, svq, synth, dev, side, layers)
+    args.warmup_done = nw_graph  # the bench line's warm-up: that of the timed graph replays
     value = code_bytes / (ms_per_step * 1e-3) / 1e9
     # roofline.achieved: the step's code bytes over the mean step duration;
     # a step is 144 back-to-back launches, so the gaps between them count
@@ -505,7 +505,7 @@ def bench_decode(args, wl, svq, synth, dev):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup_done,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -553,9 +553,7 @@ def bench_first_token(args, wl, svq, synth, dev, side, layers):
     reps = max(1, min(args.steps, 10))
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for _ in range(max(1, args.warmup)):
-            step()
-    torch.cuda.synchronize()
+        warm_up(args, lambda i: step(), side)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     ev[0].record(side)
     for _ in range(reps):
@@ -580,13 +578,45 @@ def bench_first_token(args, wl, svq, synth, dev, side, layers):
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "reps": reps}
 
 
+def warm_up(args, step, stream):
+    """Untimed steps before a timed region; step(i) runs step i on `stream`.
+    With --warmup W exactly W of them.  By default 20 steps, 20 more timed
+    with HIP events, then as many as keep the GPU busy for WARMUP_MIN_S in
+    all: the GPU reaches its loaded clocks only after some tens of
+    milliseconds of work, and a few hundred microseconds of warm-up leave
+    the batch-1 layer ~10 % slower.  Returns the number of warm-up steps run
+    (also kept in args.warmup_done for the bench line)."""
+    import torch
+    if args.warmup is not None:
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        args.warmup_done = args.warmup
+        return args.warmup
+    n = 20
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n, 2 * n):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_s = max(e0.elapsed_time(e1) * 1e-3 / n, 1e-7)
+    more = min(int(WARMUP_MIN_S / per_s), WARMUP_MAX_STEPS)
+    for i in range(2 * n, 2 * n + more):
+        step(i)
+    torch.cuda.synchronize()
+    args.warmup_done = 2 * n + more
+    return args.warmup_done
+
+
 def _timed(args, stream, fn):
-    """Mean milliseconds of fn() over args.steps calls after args.warmup,
+    """Mean milliseconds of fn() over args.steps calls after the warm-up,
     between HIP events on the launch stream."""
     import torch
-    for _ in range(args.warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(args, lambda i: fn(), stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
@@ -671,7 +701,7 @@ def bench_calib(args, wl, svq, synth, stream):
     config["launches_per_step"] = launches
     out = {
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "steps": args.steps, "warmup": args.warmup_done, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic (seeded activations, weights, codebooks, radii)",
         "config": config, "roofline": roof, "cpu_baseline": cpu,
@@ -817,16 +847,14 @@ def main():
     def step(i):
         calls[i % copies]()
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    nw = warm_up(args, step, stream)
     # Timed region: back-to-back steps on the launch stream between two HIP
     # events (no per-step events: an event pair around every step adds a few
     # microseconds of dispatch latency to each step).
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(nw + i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
@@ -862,12 +890,10 @@ def main():
         for j, mat in enumerate(mats):
             cj = [svq.BatchedCall([rot[c][j]], [x_dev[j]], [y_dev[j]], workspace=ws, stream=stream)
                   for c in range(copies)]
-            for i in range(args.warmup):
-                cj[i % copies]()
-            torch.cuda.synchronize()
+            nwj = warm_up(args, lambda i: cj[i % copies](), stream)
             e0.record(stream)
             for i in range(args.steps):
-                cj[(args.warmup + i) % copies]()
+                cj[(nwj + i) % copies]()
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) / args.steps * 1e3
@@ -888,7 +914,7 @@ def main():
         "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup_done,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
