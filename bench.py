@@ -49,8 +49,8 @@ COLD_BYTES = 600 << 20  # > 2 x 256 MB MALL
 TRAFFIC = {
     # gemv_fused_kernel (profiles/gemv_fused_kernel_layer4b_m1_counters.md)
     "layer4b_m1": {"sources": ("svq_kernels.hip", "svq_device.h"),
-                   "kernel_src_sha256": "061290236f436d7a",
-                   "fetch_kib": 14671.0, "fetch_factor": 2.0,
+                   "kernel_src_sha256": "206a82fc33ec2297",
+                   "fetch_kib": 14675.8, "fetch_factor": 2.0,
                    "write_kib": 60.0, "write_factor": 1.0},
     # sb_gemm_kernel (profiles/sb_gemm_kernel_layer4b_m16_counters.md)
     "layer4b_m16": {"sources": ("svq_small.hip", "svq_device.h"),
@@ -239,7 +239,9 @@ def cpu_baseline_moe(mats, xs, ids, m, budget_s=12.0):
 
 def bench_moe(args, wl, svq, synth, dev, stream):
     """MoE FFN step: the gate, up and down projections of the routed experts
-    for m tokens (top-8 of 128 experts), one svq_moe_linear call each."""
+    for m tokens (top-8 of 128 experts): gate and up in one
+    svq_moe_linear_batched call (they share the routing), down in one
+    svq_moe_linear call."""
     import numpy as np
     import torch
     m = wl["m"]
@@ -260,7 +262,7 @@ def bench_moe(args, wl, svq, synth, dev, stream):
     y_dev = [torch.empty((ids.size, mats[p][0].n), dtype=torch.bfloat16, device=dev) for p in range(3)]
     calls, ws = [], None
     for c in range(copies):
-        group = []
+        sets = []
         for p in range(3):
             pms = []
             for pm in packed[p]:
@@ -268,11 +270,14 @@ def bench_moe(args, wl, svq, synth, dev, stream):
                 h = svq.Handle.from_buffer_copy(pm.handle)
                 h.dev = buf.data_ptr()
                 pms.append(svq.PackedMatrix(buf, h))
-            call = svq.MoeCall(pms, x_dev[p], d_ids, topk, p == 2, y_dev[p], workspace=ws,
-                               stream=stream)
-            ws = call.workspace if ws is None or call.workspace.numel() > ws.numel() else ws
-            group.append(call)
-        calls.append(group)
+            sets.append(pms)
+        # gate and up share the routing: one batched call; down on its own
+        gate_up = svq.MoeBatchedCall(sets[:2], x_dev[:2], d_ids, topk, False, y_dev[:2], workspace=ws,
+                                     stream=stream)
+        ws = gate_up.workspace
+        down = svq.MoeCall(sets[2], x_dev[2], d_ids, topk, True, y_dev[2], workspace=ws, stream=stream)
+        ws = down.workspace if down.workspace.numel() > ws.numel() else ws
+        calls.append([gate_up, down])
 
     def step(i):
         for call in calls[i % copies]:
@@ -314,7 +319,8 @@ def bench_moe(args, wl, svq, synth, dev, stream):
         "data": "synthetic (seeded codes, codebooks, radii, permutations, routing, activations)",
         "config": {"workload": args.workload, "experts": synth.MOE_EXPERTS, "topk": topk, "m": m,
                    "routed_experts": int(routed.size), "routed_code_bytes": int(step_bytes),
-                   "cold_copies": int(copies), "launch_calls_per_step": 3},
+                   "cold_copies": int(copies), "library_calls_per_step": 2,
+                   "gate_up": "one svq_moe_linear_batched call"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -13,9 +13,10 @@
 #include "svq_internal.h"
 
 namespace svq {
-hipError_t launch_moe(const svq_handle *experts, int32_t num_experts, const void *x, int64_t ldx,
-                      int32_t x_per_slot, const int32_t *expert_ids, int64_t m, int32_t topk,
-                      void *y, int64_t ldy, int ydt, void *ws, size_t ws_bytes, hipStream_t s,
+hipError_t launch_moe(const svq_handle *const *experts, int32_t count, int32_t num_experts,
+                      const void *const *x, const int64_t *ldx, int32_t x_per_slot,
+                      const int32_t *expert_ids, int64_t m, int32_t topk, void *const *y,
+                      const int64_t *ldy, int ydt, void *ws, size_t ws_bytes, hipStream_t s,
                       size_t *need);
 }
 
@@ -756,33 +757,76 @@ svq_status svq_linear_noalloc(const svq_handle *w, const void *x, int64_t m, int
   return svq_linear(w, x, m, ldx, y, ldy, ydt, ws, &cap, stream);
 }
 
-svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts, const void *x,
-                          int64_t ldx, int32_t x_per_slot, const int32_t *expert_ids, int64_t m,
-                          int32_t topk, void *y, int64_t ldy, svq_dtype ydt, void *workspace,
-                          size_t *workspace_bytes, void *stream) {
-  if (!workspace_bytes || !experts) return SVQ_ERR_INVALID_ARG;
+// Checks shared by the MoE calls: the routing arguments, then every
+// projection's experts (one n and k per projection).
+static svq_status moe_check(const svq_handle *const *experts, int32_t count, int32_t num_experts,
+                            int32_t x_per_slot, int64_t m, int32_t topk, svq_dtype ydt) {
   if (num_experts < 1 || num_experts > MAX_EXPERTS) return SVQ_ERR_UNSUPPORTED;
+  if (count < 1 || count > MOE_BATCH_MAX) return SVQ_ERR_INVALID_ARG;
+  if (count * num_experts > MAX_EXPERTS) return SVQ_ERR_UNSUPPORTED;
   if (topk < 1 || topk > num_experts || m < 1 || m > (1 << 20)) return SVQ_ERR_INVALID_ARG;
   if (x_per_slot != 0 && x_per_slot != 1) return SVQ_ERR_INVALID_ARG;
   if (ydt != SVQ_BF16 && ydt != SVQ_F32) return SVQ_ERR_INVALID_ARG;
-  for (int32_t e = 0; e < num_experts; ++e) {
-    const svq_status st = validate_handle(&experts[e]);
-    if (st != SVQ_OK) return st;
-    if (experts[e].n != experts[0].n || experts[e].k != experts[0].k) return SVQ_ERR_INVALID_ARG;
+  for (int32_t c = 0; c < count; ++c) {
+    if (!experts[c]) return SVQ_ERR_INVALID_ARG;
+    for (int32_t e = 0; e < num_experts; ++e) {
+      const svq_status st = validate_handle(&experts[c][e]);
+      if (st != SVQ_OK) return st;
+      if (experts[c][e].n != experts[c][0].n || experts[c][e].k != experts[c][0].k)
+        return SVQ_ERR_INVALID_ARG;
+    }
   }
-  if (ldx < experts[0].k || ldy < experts[0].n) return SVQ_ERR_INVALID_ARG;
+  return SVQ_OK;
+}
+
+static svq_status moe_impl(const svq_handle *const *experts, int32_t count, int32_t num_experts,
+                           const void *const *x, const int64_t *ldx, int32_t x_per_slot,
+                           const int32_t *expert_ids, int64_t m, int32_t topk, void *const *y,
+                           const int64_t *ldy, svq_dtype ydt, void *workspace,
+                           size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes || !experts) return SVQ_ERR_INVALID_ARG;
+  svq_status st = moe_check(experts, count, num_experts, x_per_slot, m, topk, ydt);
+  if (st != SVQ_OK) return st;
+  // strides are checked whenever they are given (the query may omit them)
+  for (int32_t c = 0; c < count; ++c) {
+    if (ldx && ldx[c] < experts[c][0].k) return SVQ_ERR_INVALID_ARG;
+    if (ldy && ldy[c] < experts[c][0].n) return SVQ_ERR_INVALID_ARG;
+  }
   size_t need = 0;
-  hipError_t e = launch_moe(experts, num_experts, x, ldx, x_per_slot, expert_ids, m, topk, y, ldy,
-                            (int)ydt, nullptr, 0, (hipStream_t)stream, &need);
+  hipError_t e = launch_moe(experts, count, num_experts, nullptr, nullptr, x_per_slot, expert_ids, m,
+                            topk, nullptr, nullptr, (int)ydt, nullptr, 0, (hipStream_t)stream, &need);
+  if (e != hipSuccess) return SVQ_ERR_INVALID_ARG;
   if (!workspace) {
     *workspace_bytes = need;
     return SVQ_OK;
   }
   if (*workspace_bytes < need) return SVQ_ERR_BUFFER_TOO_SMALL;
-  if (!x || !y || !expert_ids) return SVQ_ERR_INVALID_ARG;
-  e = launch_moe(experts, num_experts, x, ldx, x_per_slot, expert_ids, m, topk, y, ldy, (int)ydt,
+  if (!x || !ldx || !y || !ldy || !expert_ids) return SVQ_ERR_INVALID_ARG;
+  for (int32_t c = 0; c < count; ++c)
+    if (!x[c] || !y[c]) return SVQ_ERR_INVALID_ARG;
+  e = launch_moe(experts, count, num_experts, x, ldx, x_per_slot, expert_ids, m, topk, y, ldy, (int)ydt,
                  workspace, *workspace_bytes, (hipStream_t)stream, &need);
   return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+}
+
+svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts, const void *x,
+                          int64_t ldx, int32_t x_per_slot, const int32_t *expert_ids, int64_t m,
+                          int32_t topk, void *y, int64_t ldy, svq_dtype ydt, void *workspace,
+                          size_t *workspace_bytes, void *stream) {
+  const svq_handle *const sets[1] = {experts};
+  const void *const xs[1] = {x};
+  void *const ys[1] = {y};
+  return moe_impl(sets, 1, num_experts, xs, &ldx, x_per_slot, expert_ids, m, topk, ys, &ldy, ydt,
+                  workspace, workspace_bytes, stream);
+}
+
+svq_status svq_moe_linear_batched(const svq_handle *const *experts, int32_t count,
+                                  int32_t num_experts, const void *const *x, const int64_t *ldx,
+                                  int32_t x_per_slot, const int32_t *expert_ids, int64_t m,
+                                  int32_t topk, void *const *y, const int64_t *ldy, svq_dtype ydt,
+                                  void *workspace, size_t *workspace_bytes, void *stream) {
+  return moe_impl(experts, count, num_experts, x, ldx, x_per_slot, expert_ids, m, topk, y, ldy, ydt,
+                  workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

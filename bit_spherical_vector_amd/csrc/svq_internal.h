@@ -332,6 +332,19 @@ struct MoeShape {
   int32_t num_experts;
 };
 
+// Projections of one svq_moe_linear_batched call that share the routing
+// (the per-slot launch serves all of them; their experts fill one
+// ExpertTable, projection c at entries c*E .. c*E + E - 1).
+constexpr int MOE_BATCH_MAX = 4;
+struct MoeGemvBatch {
+  MoeShape sh[MOE_BATCH_MAX];
+  const uint16_t *x[MOE_BATCH_MAX];
+  int64_t ldx[MOE_BATCH_MAX];
+  void *y[MOE_BATCH_MAX];
+  int64_t ldy[MOE_BATCH_MAX];
+  int32_t R[MOE_BATCH_MAX];  // row tiles per block
+};
+
 // Grouped MoE product (svq_moe.hip) for routed slots: activation rows per
 // work item, workspace bytes of the fragment-ordered activations, and the
 // prep + product launches over the routing's work list (expert, sorted rows

@@ -24,6 +24,7 @@
 //   per direction/radius index): straight into a v_mfma_f32_16x16x32_bf16
 //   operand up to m = 16, through an LDS weight tile for
 //   v_mfma_f32_32x32x16_bf16 above.
+#include <cstring>
 #include <type_traits>
 
 #include "svq_device.h"
@@ -1049,34 +1050,36 @@ hipError_t launch_gemv_fused(GemvBatch &b, int blocks, size_t smem, hipStream_t 
 // the usual top-k slot convention: slot q = t*topk + j)
 // ---------------------------------------------------------------------------
 
-// Per-slot fused GEMV (one activation row per slot): block (row tile, slot),
-// matrix = the slot's expert.
+// Per-slot fused GEMV (one activation row per slot): block (row-tile group,
+// slot, projection), matrix = the slot's expert of that projection.
 template <bool XVEC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_gemv_kernel(MoeShape sh, ExpertTable tab,
-                                                       const int32_t *__restrict__ ids,
-                                                       const uint16_t *__restrict__ x, int64_t ldx,
-                                                       int x_per_slot, int topk,
-                                                       void *__restrict__ y, int64_t ldy, int ydt,
-                                                       int R) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_gemv_kernel(
+    MoeGemvBatch mb, ExpertTable tab, const int32_t *__restrict__ ids, int x_per_slot, int topk, int ydt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int c = blockIdx.z;  // projection
+  const MoeShape &sh = mb.sh[c];
+  const int R = mb.R[c];
+  const int rt0 = blockIdx.x * R;
+  if (rt0 >= sh.n_tiles) return;  // block-uniform: the grid covers the widest projection
   const int q = blockIdx.y;
   const int e = ids[q];
-  const int rt0 = blockIdx.x * R;
-  char *yq = (char *)y + (size_t)q * ldy * (ydt == 0 ? 2 : 4);
+  char *yq = (char *)mb.y[c] + (size_t)q * mb.ldy[c] * (ydt == 0 ? 2 : 4);
   if (e < 0 || e >= sh.num_experts) {  // block-uniform: the slot is skipped, its rows are zero
     for (int r = rt0 * 16 + (int)threadIdx.x; r < min(sh.n, (rt0 + R) * 16); r += 256)
       store_out(yq, (size_t)r, 0.f, ydt);
     return;
   }
-  const MatView w = expert_view(sh, tab, e);
+  // projection c's experts are entries c * E .. c * E + E - 1 of the table
+  const MatView w = expert_view(sh, tab, c * sh.num_experts + e);
   const int src = x_per_slot ? q : q / topk;
+  const uint16_t *xr = mb.x[c] + (int64_t)src * mb.ldx[c];
   const int reff = min(R, w.n_tiles - rt0);
   if (w.bd >= 8)
-    gemv_fused_block<1, XVEC, 8>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, reff, smem);
+    gemv_fused_block<1, XVEC, 8>(w, xr, mb.ldx[c], yq, mb.ldy[c], ydt, rt0, R, reff, smem);
   else if (w.bd == 7)
-    gemv_fused_block<1, XVEC, 7>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, reff, smem);
+    gemv_fused_block<1, XVEC, 7>(w, xr, mb.ldx[c], yq, mb.ldy[c], ydt, rt0, R, reff, smem);
   else
-    gemv_fused_block<1, XVEC, 6>(w, x + (int64_t)src * ldx, ldx, yq, ldy, ydt, rt0, R, reff, smem);
+    gemv_fused_block<1, XVEC, 6>(w, xr, mb.ldx[c], yq, mb.ldy[c], ydt, rt0, R, reff, smem);
 }
 
 // Routing for the grouped GEMM: counting sort of slots by expert and a list
@@ -1178,18 +1181,20 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
 
 // ---------------------------------------------------------------------------
 // MoE launcher.  Workspace layout depends on the path:
-//   exact (m*topk <= MOE_EXACT_MAX_SLOTS): none (the fused per-slot launch)
+//   exact (m*topk <= MOE_EXACT_MAX_SLOTS): none (one fused per-slot launch
+//            for all projections of the call)
 //   grouped: counts[E], offsets[E+1], sorted[S], work[3*max_work], nwork,
 //            fragment-ordered activations (moe_sb_xa_bytes); the routing
 //            is done by the prep launch up to MOE_FUSED_MAX_SLOTS slots
-//            (counts and offsets unused), by moe_route_kernel beyond
+//            (counts and offsets unused), by moe_route_kernel beyond.  The
+//            projections of a call run one after another on the same
+//            workspace (its size is the largest any of them needs).
 // ---------------------------------------------------------------------------
 constexpr int MOE_EXACT_MAX_SLOTS = 64;
 
-hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64_t ldx,
-                      int32_t x_per_slot, const int32_t *ids, int64_t m, int32_t topk, void *y,
-                      int64_t ldy, int ydt, void *ws, size_t ws_bytes, hipStream_t s, size_t *need) {
-  const int S = (int)(m * topk);
+// Layout of one projection's experts (all share n, k and the region
+// offsets; bd may differ, and lives in the expert table).
+static MoeShape moe_shape(const svq_handle *experts, int32_t E) {
   const svq_handle &h0 = experts[0];
   MoeShape sh;
   sh.off_dtab = (uint32_t)h0.off_dtab;
@@ -1203,42 +1208,15 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   sh.n_tiles = h0.n_tiles;
   sh.units = h0.units;
   sh.num_experts = E;
-  const size_t Kp = (size_t)sh.units * UNIT_SLOTS;
-  ExpertTable tab;
-  for (int e = 0; e < MAX_EXPERTS; ++e) {
-    tab.base[e] = e < E ? (const uint8_t *)experts[e].dev : nullptr;
-    tab.bd[e] = e < E ? (uint8_t)experts[e].bd : 0;
-  }
-  const uint16_t *xp = (const uint16_t *)x;
-  if (S <= MOE_EXACT_MAX_SLOTS) {
-    *need = 256;
-    if (!ws) return hipSuccess;
-    // row tiles per block: about 5 units per wave to amortise the gather,
-    // while the launch keeps >= 256 blocks
-    constexpr int ITEMS_PER_WAVE = 5;
-    int R = sh.units <= ITEMS_PER_WAVE ? 4 : (sh.units <= 2 * ITEMS_PER_WAVE ? 2 : 1);
-    while (R > 1 && ((sh.n_tiles + R - 1) / R) * S < 256) R /= 2;
-    size_t smem = 0;
-    for (int e = 0; e < E; ++e) {
-      const size_t b = gemv_fused_smem_bytes(sh.k, sh.units, experts[e].bd, R);
-      smem = b > smem ? b : smem;
-    }
-    if (smem > GV_LDS_LIMIT) return hipErrorInvalidValue;
-    const bool xvec = ((((uintptr_t)x) | ((uintptr_t)ldx * 2)) & 15) == 0;
-    static const hipError_t lds_ok_t = check_no_static_lds(moe_gemv_kernel<true>);
-    static const hipError_t lds_ok_f = check_no_static_lds(moe_gemv_kernel<false>);
-    if ((xvec ? lds_ok_t : lds_ok_f) != hipSuccess) return xvec ? lds_ok_t : lds_ok_f;
-    hipError_t e = xvec ? allow_smem(moe_gemv_kernel<true>, smem) : allow_smem(moe_gemv_kernel<false>, smem);
-    if (e != hipSuccess) return e;
-    const dim3 grid((sh.n_tiles + R - 1) / R, S);
-    if (xvec)
-      hipLaunchKernelGGL(moe_gemv_kernel<true>, grid, dim3(256), smem, s, sh, tab, ids, xp, ldx,
-                         x_per_slot, topk, y, ldy, ydt, R);
-    else
-      hipLaunchKernelGGL(moe_gemv_kernel<false>, grid, dim3(256), smem, s, sh, tab, ids, xp, ldx,
-                         x_per_slot, topk, y, ldy, ydt, R);
-    return hipGetLastError();
-  }
+  return sh;
+}
+
+// The grouped path for one projection.
+static hipError_t launch_moe_grouped(const svq_handle *experts, int32_t E, const void *x, int64_t ldx,
+                                     int32_t x_per_slot, const int32_t *ids, int S, int32_t topk,
+                                     void *y, int64_t ldy, int ydt, void *ws, size_t ws_bytes,
+                                     hipStream_t s, size_t *need) {
+  const MoeShape sh = moe_shape(experts, E);
   const int rows_per_item = MOE_SB_ROWS;
   const int max_work = (S + rows_per_item - 1) / rows_per_item + E;
   size_t off = 0;
@@ -1257,6 +1235,11 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
   *need = off;
   if (!ws) return hipSuccess;
   if (ws_bytes < *need) return hipErrorInvalidValue;
+  ExpertTable tab;
+  for (int e = 0; e < MAX_EXPERTS; ++e) {
+    tab.base[e] = e < E ? (const uint8_t *)experts[e].dev : nullptr;
+    tab.bd[e] = e < E ? (uint8_t)experts[e].bd : 0;
+  }
   uint8_t *b = (uint8_t *)ws;
   int32_t *counts = (int32_t *)(b + o_counts), *offsets = (int32_t *)(b + o_offsets);
   int32_t *sorted = (int32_t *)(b + o_sorted), *work = (int32_t *)(b + o_work);
@@ -1276,8 +1259,73 @@ hipError_t launch_moe(const svq_handle *experts, int32_t E, const void *x, int64
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_moe_sb(sh, tab, xp, ldx, x_per_slot, topk, route, work, nwork, sorted, max_work, xb,
-                       y, ldy, ydt, s);
+  return launch_moe_sb(sh, tab, (const uint16_t *)x, ldx, x_per_slot, topk, route, work, nwork, sorted,
+                       max_work, xb, y, ldy, ydt, s);
+}
+
+hipError_t launch_moe(const svq_handle *const *experts, int32_t count, int32_t E, const void *const *x,
+                      const int64_t *ldx, int32_t x_per_slot, const int32_t *ids, int64_t m,
+                      int32_t topk, void *const *y, const int64_t *ldy, int ydt, void *ws,
+                      size_t ws_bytes, hipStream_t s, size_t *need) {
+  const int S = (int)(m * topk);
+  if (count < 1 || count > MOE_BATCH_MAX || count * E > MAX_EXPERTS) return hipErrorInvalidValue;
+  if (S > MOE_EXACT_MAX_SLOTS) {
+    size_t most = 0;
+    for (int c = 0; c < count; ++c) {
+      size_t nc = 0;
+      const hipError_t e = launch_moe_grouped(experts[c], E, ws ? x[c] : nullptr, ws ? ldx[c] : 0,
+                                              x_per_slot, ids, S, topk, ws ? y[c] : nullptr,
+                                              ws ? ldy[c] : 0, ydt, ws, ws_bytes, s, &nc);
+      if (e != hipSuccess) return e;
+      most = nc > most ? nc : most;
+    }
+    *need = most;
+    return hipSuccess;
+  }
+  *need = 256;
+  if (!ws) return hipSuccess;
+  MoeGemvBatch mb;
+  std::memset(&mb, 0, sizeof(mb));
+  ExpertTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  bool xvec = true;
+  size_t smem = 0;
+  int gx = 1;
+  for (int c = 0; c < count; ++c) {
+    const MoeShape sh = moe_shape(experts[c], E);
+    // row tiles per block: about 5 units per wave to amortise the gather,
+    // while the launch keeps >= 256 blocks
+    constexpr int ITEMS_PER_WAVE = 5;
+    int R = sh.units <= ITEMS_PER_WAVE ? 4 : (sh.units <= 2 * ITEMS_PER_WAVE ? 2 : 1);
+    while (R > 1 && ((sh.n_tiles + R - 1) / R) * S < 256) R /= 2;
+    for (int e = 0; e < E; ++e) {
+      tab.base[c * E + e] = (const uint8_t *)experts[c][e].dev;
+      tab.bd[c * E + e] = (uint8_t)experts[c][e].bd;
+      const size_t b = gemv_fused_smem_bytes(sh.k, sh.units, experts[c][e].bd, R);
+      smem = b > smem ? b : smem;
+    }
+    mb.sh[c] = sh;
+    mb.x[c] = (const uint16_t *)x[c];
+    mb.ldx[c] = ldx[c];
+    mb.y[c] = y[c];
+    mb.ldy[c] = ldy[c];
+    mb.R[c] = R;
+    if (((((uintptr_t)x[c]) | ((uintptr_t)ldx[c] * 2)) & 15) != 0) xvec = false;
+    const int g = (sh.n_tiles + R - 1) / R;
+    gx = g > gx ? g : gx;
+  }
+  if (smem > GV_LDS_LIMIT) return hipErrorInvalidValue;
+  static const hipError_t lds_ok_t = check_no_static_lds(moe_gemv_kernel<true>);
+  static const hipError_t lds_ok_f = check_no_static_lds(moe_gemv_kernel<false>);
+  if ((xvec ? lds_ok_t : lds_ok_f) != hipSuccess) return xvec ? lds_ok_t : lds_ok_f;
+  hipError_t e = xvec ? allow_smem(moe_gemv_kernel<true>, smem) : allow_smem(moe_gemv_kernel<false>, smem);
+  if (e != hipSuccess) return e;
+  const dim3 grid(gx, S, count);
+  if (xvec)
+    hipLaunchKernelGGL(moe_gemv_kernel<true>, grid, dim3(256), smem, s, mb, tab, ids, x_per_slot, topk, ydt);
+  else
+    hipLaunchKernelGGL(moe_gemv_kernel<false>, grid, dim3(256), smem, s, mb, tab, ids, x_per_slot, topk, ydt);
+  return hipGetLastError();
 }
 
 }  // namespace svq

@@ -34,7 +34,7 @@ SVQ_BF16 = 0
 SVQ_F32 = 1
 
 EXPORTED = ("svq_pack", "svq_linear", "svq_linear_batched", "svq_linear_noalloc",
-            "svq_moe_linear", "svq_encode", "svq_encode_weighted", "svq_esg_perm", "svq_abs_select",
+            "svq_moe_linear", "svq_moe_linear_batched", "svq_encode", "svq_encode_weighted", "svq_esg_perm", "svq_abs_select",
             "svq_status_string")
 SVQ_SCRATCH_BYTES = 64 << 20
 SVQ_NO_EXACT_SPLIT = -(1 << 31)
@@ -103,6 +103,15 @@ def _load() -> ctypes.CDLL:
                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                    ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
+    lib.svq_moe_linear_batched.restype = ctypes.c_int
+    lib.svq_moe_linear_batched.argtypes = [ctypes.POINTER(ctypes.POINTER(Handle)), ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                           ctypes.POINTER(ctypes.c_int64), ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.POINTER(ctypes.c_void_p),
+                                           ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.c_void_p]
     lib.svq_encode.restype = ctypes.c_int
     lib.svq_encode.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -179,6 +188,26 @@ def svq_moe_linear(handles, num_experts: int, x_ptr: int, ldx: int, x_per_slot: 
     nbytes = ctypes.c_size_t(ws_bytes)
     st = LIB.svq_moe_linear(handles, num_experts, x_ptr, ldx, x_per_slot, ids_ptr, m, topk,
                             y_ptr, ldy, ydt, ws_ptr, ctypes.byref(nbytes), stream)
+    return st, nbytes.value
+
+
+def svq_moe_linear_batched(handle_sets, count: int, num_experts: int, x_ptrs, ldx, x_per_slot: int,
+                           ids_ptr: int, m: int, topk: int, y_ptrs, ldy, ydt: int,
+                           ws_ptr: Optional[int], ws_bytes: int, stream: int) -> tuple:
+    """handle_sets: sequence of `count` Handle arrays (one per projection);
+    x_ptrs / ldx / y_ptrs / ldy: sequences of length count, or None (the
+    workspace query)."""
+    # arrays are sized by what is given (count itself is passed as is, so
+    # that the library's own checks of it can be exercised)
+    sets = (ctypes.POINTER(Handle) * len(handle_sets))(
+        *[ctypes.cast(h, ctypes.POINTER(Handle)) for h in handle_sets])
+    xp = (ctypes.c_void_p * len(x_ptrs))(*x_ptrs) if x_ptrs is not None else None
+    lx = (ctypes.c_int64 * len(ldx))(*ldx) if ldx is not None else None
+    yp = (ctypes.c_void_p * len(y_ptrs))(*y_ptrs) if y_ptrs is not None else None
+    ly = (ctypes.c_int64 * len(ldy))(*ldy) if ldy is not None else None
+    nbytes = ctypes.c_size_t(ws_bytes)
+    st = LIB.svq_moe_linear_batched(sets, count, num_experts, xp, lx, x_per_slot, ids_ptr, m, topk, yp,
+                                    ly, ydt, ws_ptr, ctypes.byref(nbytes), stream)
     return st, nbytes.value
 
 
@@ -404,6 +433,57 @@ class MoeCall:
                                self.args_y[1], self.ydt, self.workspace.data_ptr(),
                                self.workspace.numel(), self.stream)
         _check(st, "svq_moe_linear")
+
+
+class MoeBatchedCall:
+    """Pre-marshalled arguments of one svq_moe_linear_batched call: several
+    projections (e.g. an FFN's gate and up) that share expert_ids, topk and
+    x_per_slot.  pm_sets[c] are projection c's packed experts, xs[c] / ys[c]
+    its device input and output (owned by the caller; they must outlive the
+    object)."""
+
+    def __init__(self, pm_sets, xs, expert_ids, topk: int, x_per_slot: bool, ys, workspace=None,
+                 stream=None):
+        import torch
+        self.keep = ([list(p) for p in pm_sets], list(xs), expert_ids, list(ys))
+        self.sets = [handle_array(p) for p in pm_sets]
+        self.count = len(self.sets)
+        self.n_exp = len(pm_sets[0])
+        self.topk = topk
+        self.m = expert_ids.numel() // topk
+        self.x_per_slot = int(x_per_slot)
+        self.x_ptrs = [x.data_ptr() for x in xs]
+        self.ldx = [x.stride(0) for x in xs]
+        self.ids = expert_ids.data_ptr()
+        self.y_ptrs = [y.data_ptr() for y in ys]
+        self.ldy = [y.stride(0) for y in ys]
+        self.ydt = SVQ_F32 if ys[0].dtype == torch.float32 else SVQ_BF16
+        st, need = svq_moe_linear_batched(self.sets, self.count, self.n_exp, None, None, self.x_per_slot,
+                                          None, self.m, topk, None, None, self.ydt, None, 0, 0)
+        _check(st, "svq_moe_linear_batched (workspace query)")
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xs[0].device)
+        self.workspace = workspace
+        self.stream = _stream_handle(stream)
+
+    def __call__(self) -> None:
+        st, _ = svq_moe_linear_batched(self.sets, self.count, self.n_exp, self.x_ptrs, self.ldx,
+                                       self.x_per_slot, self.ids, self.m, self.topk, self.y_ptrs,
+                                       self.ldy, self.ydt, self.workspace.data_ptr(),
+                                       self.workspace.numel(), self.stream)
+        _check(st, "svq_moe_linear_batched")
+
+
+def moe_linear_batched(pm_sets, xs, expert_ids, topk: int, x_per_slot: bool, outs=None,
+                       out_dtype=None, stream=None):
+    """Several MoE projections sharing the routing in one call; returns the
+    outputs (one [m*topk, n_c] tensor per projection)."""
+    import torch
+    if outs is None:
+        outs = [torch.empty((expert_ids.numel(), p[0].n), dtype=out_dtype or torch.bfloat16,
+                            device=x.device) for p, x in zip(pm_sets, xs)]
+    MoeBatchedCall(pm_sets, xs, expert_ids, topk, x_per_slot, outs, stream=stream)()
+    return outs
 
 
 def linear_batched(pms: Sequence[PackedMatrix], xs, outs=None, out_dtype=None, stream=None):

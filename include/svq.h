@@ -213,6 +213,35 @@ svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts,
                           void *y, int64_t ldy, svq_dtype ydt,
                           void *workspace, size_t *workspace_bytes, void *stream);
 
+/* svq_moe_linear_batched: svq_moe_linear for `count` (1..4) projections that
+ * share the routing (expert_ids, m, topk, x_per_slot), e.g. the gate and up
+ * projections of one FFN, which read the same token rows.  Up to 64 slots
+ * every projection is served by one kernel launch; beyond that the
+ * projections run one after another.
+ *   experts:      host array of count pointers; experts[c] is a host array
+ *                 of num_experts packed matrices of projection c (one n and k
+ *                 per projection; projections may differ).
+ *   num_experts:  1..256, and count * num_experts <= 256
+ *                 (SVQ_ERR_UNSUPPORTED otherwise).
+ *   x, ldx:       host arrays of count device bf16 inputs and their strides
+ *                 (rows as in svq_moe_linear; the same pointer may repeat).
+ *   y, ldy:       host arrays of count device outputs of type ydt,
+ *                 [m*topk][ldy[c]] each, slot-major.
+ *   workspace:    as for svq_moe_linear; its size (the query: workspace ==
+ *                 NULL, which needs only experts, count, num_experts, m,
+ *                 topk, x_per_slot and ydt; x, ldx, y, ldy may then be NULL)
+ *                 is the largest any single projection needs, and the
+ *                 projections use it in turn.
+ * Results, numerics, the treatment of ids outside [0, num_experts) and the
+ * error rules are those of count separate svq_moe_linear calls with the same
+ * arguments, in order, on the same stream. */
+svq_status svq_moe_linear_batched(const svq_handle *const *experts, int32_t count,
+                                  int32_t num_experts, const void *const *x,
+                                  const int64_t *ldx, int32_t x_per_slot,
+                                  const int32_t *expert_ids, int64_t m, int32_t topk,
+                                  void *const *y, const int64_t *ldy, svq_dtype ydt,
+                                  void *workspace, size_t *workspace_bytes, void *stream);
+
 /* svq_encode: the codes of a float weight matrix for given tables -- the
  * step before svq_pack (SAGE Fig. 2 caption: each 8-weight subvector, taken
  * along the channel permutation, is coded by its signs, a direction index

@@ -232,9 +232,9 @@ hipError_t launch_prefill_reduce(PrefillBatch &b, int blocks, hipStream_t) {
 }
 
 // ---- calls the harness does not drive ---------------------------------------
-hipError_t launch_moe(const svq_handle *, int32_t, const void *, int64_t, int32_t, const int32_t *,
-                      int64_t, int32_t, void *, int64_t, int, void *, size_t, hipStream_t,
-                      size_t *need) {
+hipError_t launch_moe(const svq_handle *const *, int32_t, int32_t, const void *const *,
+                      const int64_t *, int32_t, const int32_t *, int64_t, int32_t, void *const *,
+                      const int64_t *, int, void *, size_t, hipStream_t, size_t *need) {
   *need = 256;
   return hipSuccess;
 }

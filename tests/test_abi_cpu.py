@@ -23,7 +23,7 @@ def _declared_functions():
 def test_exports_every_declared_symbol():
     declared = _declared_functions()
     assert set(declared) == {"svq_pack", "svq_linear", "svq_linear_batched", "svq_linear_noalloc",
-                             "svq_moe_linear", "svq_encode", "svq_encode_weighted", "svq_esg_perm",
+                             "svq_moe_linear", "svq_moe_linear_batched", "svq_encode", "svq_encode_weighted", "svq_esg_perm",
                              "svq_abs_select", "svq_status_string"}
     for name in declared:
         assert hasattr(svq.LIB, name), name
@@ -270,6 +270,33 @@ def test_moe_workspace_query_and_validation():
         svq.SVQ_ERR_INVALID_ARG
     assert svq.svq_moe_linear(hs, 0, None, 2048, 0, None, 1, 1, None, 768, 0, None, 0, 0)[0] == \
         svq.SVQ_ERR_UNSUPPORTED
+
+
+def test_moe_batched_query_and_validation():
+    gate = (svq.Handle * 4)(*[_fake_handle(768, 2048, 6 + e % 3) for e in range(4)])
+    down = (svq.Handle * 4)(*[_fake_handle(2048, 768, 6 + e % 3) for e in range(4)])
+    for m in (1, 512):
+        singles = [svq.svq_moe_linear(h, 4, None, h[0].k, 0, None, m, 2, None, h[0].n, 0, None, 0, 0)
+                   for h in (gate, down)]
+        assert all(st == svq.SVQ_OK for st, _ in singles)
+        st, need = svq.svq_moe_linear_batched([gate, down], 2, 4, None, None, 0, None, m, 2, None, None,
+                                              0, None, 0, 0)
+        assert st == svq.SVQ_OK and need == max(n for _, n in singles)
+    # projection count outside 1..4; count * num_experts beyond 256
+    for count in (0, 5):
+        assert svq.svq_moe_linear_batched([gate] * max(count, 1), count, 4, None, None, 0, None, 1, 2,
+                                          None, None, 0, None, 0, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    wide = (svq.Handle * 128)(*[_fake_handle(64, 512, 6) for _ in range(128)])
+    assert svq.svq_moe_linear_batched([wide] * 2, 2, 128, None, None, 0, None, 1, 2, None, None, 0,
+                                      None, 0, 0)[0] == svq.SVQ_OK
+    assert svq.svq_moe_linear_batched([wide] * 3, 3, 128, None, None, 0, None, 1, 2, None, None, 0,
+                                      None, 0, 0)[0] == svq.SVQ_ERR_UNSUPPORTED
+    # a stride below a projection's k or n; one projection with mixed shapes
+    assert svq.svq_moe_linear_batched([gate, down], 2, 4, None, [2048, 700], 0, None, 1, 2, None,
+                                      [768, 2048], 0, None, 0, 0)[0] == svq.SVQ_ERR_INVALID_ARG
+    mixed = (svq.Handle * 4)(*[_fake_handle(768, 2048, 7) for _ in range(3)] + [_fake_handle(768, 1024, 7)])
+    assert svq.svq_moe_linear_batched([gate, mixed], 2, 4, None, None, 0, None, 1, 2, None, None, 0,
+                                      None, 0, 0)[0] == svq.SVQ_ERR_INVALID_ARG
 
 
 def test_linear_batched_query_and_validation():

@@ -185,3 +185,60 @@ def test_moe_routing_paths(svq, m, topk):
             slots = good[ids[good] == e]
             assert_within_tolerance(y[slots], so.linear(x[slots // topk], Ws[e]), x[slots // topk], Ws[e],
                                     label=f"{m * topk} slots, expert {e}, {dt}")
+
+
+def _separate(svq, sets, xs, ids, topk, x_per_slot, dt):
+    d_ids = torch.from_numpy(ids).cuda()
+    return [out_to_f64(svq.moe_linear(p, to_device_bf16(x), d_ids, topk, x_per_slot, out_dtype=dt))
+            for p, x in zip(sets, xs)]
+
+
+@pytest.mark.parametrize("m,topk,x_per_slot", [(1, 3, 0), (4, 4, 1), (16, 4, 0), (40, 4, 0)])
+def test_moe_batched_equals_separate_calls(svq, m, topk, x_per_slot):
+    """Three projections of different shapes (the first two reading one
+    input) in one svq_moe_linear_batched call give the outputs of three
+    svq_moe_linear calls bit for bit: one launch up to 64 slots (m = 1, 4,
+    16), the projections in turn beyond (m = 40); some ids out of range."""
+    n_exp = 6
+    shapes = [(48, 520), (40, 520), (56, 264)]
+    sets_in, sets, Ws = [], [], []
+    for c, (n, k) in enumerate(shapes):
+        mats = [synth.random_matrix(n, k, 6 + (e + c) % 3, seed=(52, c, e)) for e in range(n_exp)]
+        sets_in.append(mats)
+        sets.append([svq.pack(w) for w in mats])
+        Ws.append([so.decode_matrix(w.codes, n, k, w.bd, w.codebook, w.radius, w.perm) for w in mats])
+    ids = _ids(m, topk, n_exp, 53 + m)
+    bad = np.arange(2, ids.size, 7)
+    ids[bad] = np.where(bad % 2 == 0, -1, n_exp)
+    rows = m * topk if x_per_slot else m
+    xa = synth.random_activations(rows, 520, seed=(54, m, 0))
+    xb = synth.random_activations(rows, 264, seed=(54, m, 1))
+    xs = [xa, xa, xb]
+    d_ids = torch.from_numpy(ids).cuda()
+    xd = [to_device_bf16(x) for x in (xa, xb)]
+    for dt in (torch.float32, torch.bfloat16):
+        outs = svq.moe_linear_batched(sets, [xd[0], xd[0], xd[1]], d_ids, topk, bool(x_per_slot), out_dtype=dt)
+        torch.cuda.synchronize()
+        got = [out_to_f64(o) for o in outs]
+        want = _separate(svq, sets, xs, ids, topk, bool(x_per_slot), dt)
+        for c in range(3):
+            assert np.array_equal(got[c], want[c]), f"projection {c}, {dt}"
+            assert np.all(got[c][bad] == 0)
+            # slots with an id outside [0, E) match no expert and are skipped here
+            _check_slots(got[c], xs[c], ids, topk, x_per_slot, Ws[c], range(n_exp),
+                         f"batched projection {c} m={m}")
+
+
+def test_moe128_m1_gate_up_batched(svq):
+    """The 128-expert gate and up projections of one token in one launch,
+    bit for bit against two separate calls."""
+    bd = synth.moe_expert_bd()
+    sets = [[svq.pack(synth.moe_expert(e, p, int(bd[e]))) for e in range(synth.MOE_EXPERTS)]
+            for p in (0, 1)]
+    ids = synth.moe_routing(1)
+    x = synth.moe_activations(1, 0)
+    got = svq.moe_linear_batched(sets, [to_device_bf16(x)] * 2, torch.from_numpy(ids).cuda(),
+                                 synth.MOE_TOPK, False, out_dtype=torch.float32)
+    want = _separate(svq, sets, [x, x], ids, synth.MOE_TOPK, False, torch.float32)
+    for c in range(2):
+        assert np.array_equal(out_to_f64(got[c]), want[c])
