@@ -62,12 +62,12 @@ TRAFFIC = {
                       "kernel_src_sha256": "875da4cd24cf768d",
                       "fetch_kib": 127723.4, "fetch_factor": 2.0,
                       "write_kib": 88064.0, "write_factor": 1.0},
-    # moe_sb_kernel, mean over the step's three launches (gate, up, down;
-    # profiles/moe_sb_kernel_moe128_m512_counters.md)
+    # moe_sb_kernel, mean over the step's two launches (gate + up batched,
+    # down; profiles/moe_sb_kernel_moe128_m512_counters.md)
     "moe128_m512": {"sources": ("svq_moe.hip", "svq_device.h"),
-                    "kernel_src_sha256": "9cad67bccdd9f870",
-                    "fetch_kib": 63408.5, "fetch_factor": 2.0,
-                    "write_kib": 11327.6, "write_factor": 1.0},
+                    "kernel_src_sha256": "bc7deb86318fef23",
+                    "fetch_kib": 97066.5, "fetch_factor": 2.0,
+                    "write_kib": 16982.2, "write_factor": 1.0},
 }
 
 

@@ -349,23 +349,39 @@ struct MoeGemvBatch {
 // work item, workspace bytes of the fragment-ordered activations, and the
 // prep + product launches over the routing's work list (expert, sorted rows
 // r0..r1).  Up to MOE_FUSED_MAX_SLOTS slots the prep launch also does the
-// routing (route.ids set): every prep block sorts the slots itself and
-// writes the work list, the sorted slots and the zero rows of slots with
-// invalid ids; beyond that moe_route_kernel has written them (route.ids
-// null).
+// routing (route.ids set): every prep block sorts the slots itself;
+// projection 0's blocks write the work list and the sorted slots, and every
+// projection's blocks zero their output rows of slots with invalid ids.
+// Beyond that moe_route_kernel has written them (route.ids null, one
+// projection per call).  The launches serve every projection of the batch
+// (grid y), each with its own staged activations.
 constexpr int MOE_SB_ROWS = 48;
 constexpr int MOE_FUSED_MAX_SLOTS = 8192;
 struct MoeRoute {
   const int32_t *ids;  // expert id per slot, or null when the work list is given
   int32_t slots;       // S = m * topk
-  void *y;             // output rows of invalid slots are zeroed here
-  int64_t ldy;
   int32_t ydt;
 };
+struct MoeSbProj {  // one projection: its experts' layout, input, staging and output
+  MoeShape sh;
+  const uint16_t *x;
+  int64_t ldx;
+  uint8_t *xa;  // fragment-ordered activations (moe_sb_xa_bytes)
+  void *y;
+  int64_t ldy;
+  int32_t rb;   // rows staged per pass of the prep launch
+};
+struct MoeSbBatch {
+  MoeSbProj p[MOE_BATCH_MAX];
+  int32_t count;
+  int32_t vec;   // every x and ldx allow 16-byte loads
+  int32_t yvec;  // every y and ldy allow 16-byte stores
+};
 size_t moe_sb_xa_bytes(int max_work, int units);
-hipError_t launch_moe_sb(const MoeShape &sh, const ExpertTable &tab, const uint16_t *x, int64_t ldx,
-                         int x_per_slot, int topk, const MoeRoute &route, int32_t *work,
-                         int32_t *nwork, int32_t *sorted, int max_work, uint8_t *xa, void *y,
-                         int64_t ldy, int ydt, hipStream_t s);
+int moe_sb_prep_rb(int kp);
+size_t moe_sb_prep_lds(int kp);
+hipError_t launch_moe_sb(MoeSbBatch &b, const ExpertTable &tab, int x_per_slot, int topk,
+                         const MoeRoute &route, int32_t *work, int32_t *nwork, int32_t *sorted,
+                         int max_work, int ydt, hipStream_t s);
 
 }  // namespace svq

@@ -1186,9 +1186,12 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
 //   grouped: counts[E], offsets[E+1], sorted[S], work[3*max_work], nwork,
 //            fragment-ordered activations (moe_sb_xa_bytes); the routing
 //            is done by the prep launch up to MOE_FUSED_MAX_SLOTS slots
-//            (counts and offsets unused), by moe_route_kernel beyond.  The
-//            projections of a call run one after another on the same
-//            workspace (its size is the largest any of them needs).
+//            (counts and offsets unused), by moe_route_kernel beyond.  Up to
+//            MOE_FUSED_MAX_SLOTS one prep and one product launch serve every
+//            projection of the call (one fragment area each, after the
+//            shared routing tables); beyond, the projections run one after
+//            another on the same workspace (its size is the largest any of
+//            them needs).
 // ---------------------------------------------------------------------------
 constexpr int MOE_EXACT_MAX_SLOTS = 64;
 
@@ -1211,12 +1214,14 @@ static MoeShape moe_shape(const svq_handle *experts, int32_t E) {
   return sh;
 }
 
-// The grouped path for one projection.
-static hipError_t launch_moe_grouped(const svq_handle *experts, int32_t E, const void *x, int64_t ldx,
-                                     int32_t x_per_slot, const int32_t *ids, int S, int32_t topk,
-                                     void *y, int64_t ldy, int ydt, void *ws, size_t ws_bytes,
+// The grouped path for `count` projections in one prep and one product
+// launch (count > 1 only with the routing inside the prep launch).
+// Workspace: the routing tables, then each projection's staged activations.
+static hipError_t launch_moe_grouped(const svq_handle *const *experts, int count, int32_t E,
+                                     const void *const *x, const int64_t *ldx, int32_t x_per_slot,
+                                     const int32_t *ids, int S, int32_t topk, void *const *y,
+                                     const int64_t *ldy, int ydt, void *ws, size_t ws_bytes,
                                      hipStream_t s, size_t *need) {
-  const MoeShape sh = moe_shape(experts, E);
   const int rows_per_item = MOE_SB_ROWS;
   const int max_work = (S + rows_per_item - 1) / rows_per_item + E;
   size_t off = 0;
@@ -1230,37 +1235,54 @@ static hipError_t launch_moe_grouped(const svq_handle *experts, int32_t E, const
   off += align256((size_t)max_work * 12);
   const size_t o_nwork = off;
   off += 256;
-  const size_t o_xb = off;
-  off += align256(moe_sb_xa_bytes(max_work, sh.units));
+  size_t o_xb[MOE_BATCH_MAX];
+  for (int c = 0; c < count; ++c) {
+    o_xb[c] = off;
+    off += align256(moe_sb_xa_bytes(max_work, experts[c][0].units));
+  }
   *need = off;
   if (!ws) return hipSuccess;
   if (ws_bytes < *need) return hipErrorInvalidValue;
+  uint8_t *base = (uint8_t *)ws;
+  int32_t *counts = (int32_t *)(base + o_counts), *offsets = (int32_t *)(base + o_offsets);
+  int32_t *sorted = (int32_t *)(base + o_sorted), *work = (int32_t *)(base + o_work);
+  int32_t *nwork = (int32_t *)(base + o_nwork);
+  MoeSbBatch b;
+  std::memset(&b, 0, sizeof(b));
   ExpertTable tab;
-  for (int e = 0; e < MAX_EXPERTS; ++e) {
-    tab.base[e] = e < E ? (const uint8_t *)experts[e].dev : nullptr;
-    tab.bd[e] = e < E ? (uint8_t)experts[e].bd : 0;
+  std::memset(&tab, 0, sizeof(tab));
+  b.count = count;
+  b.vec = 1;
+  b.yvec = 1;
+  const int esz = ydt == 0 ? 2 : 4;
+  for (int c = 0; c < count; ++c) {
+    b.p[c].sh = moe_shape(experts[c], E);
+    b.p[c].x = (const uint16_t *)x[c];
+    b.p[c].ldx = ldx[c];
+    b.p[c].xa = base + o_xb[c];
+    b.p[c].y = y[c];
+    b.p[c].ldy = ldy[c];
+    if (!((uintptr_t)x[c] % 16 == 0 && ldx[c] % 8 == 0)) b.vec = 0;
+    if (!((uintptr_t)y[c] % 16 == 0 && (ldy[c] * esz) % 16 == 0)) b.yvec = 0;
+    for (int e = 0; e < E; ++e) {
+      tab.base[c * E + e] = (const uint8_t *)experts[c][e].dev;
+      tab.bd[c * E + e] = (uint8_t)experts[c][e].bd;
+    }
   }
-  uint8_t *b = (uint8_t *)ws;
-  int32_t *counts = (int32_t *)(b + o_counts), *offsets = (int32_t *)(b + o_offsets);
-  int32_t *sorted = (int32_t *)(b + o_sorted), *work = (int32_t *)(b + o_work);
-  int32_t *nwork = (int32_t *)(b + o_nwork);
-  uint8_t *xb = b + o_xb;
   MoeRoute route;
   route.ids = nullptr;
   route.slots = S;
-  route.y = y;
-  route.ldy = ldy;
   route.ydt = ydt;
   if (S <= MOE_FUSED_MAX_SLOTS) {
     route.ids = ids;  // the prep launch does the routing
   } else {
+    if (count != 1) return hipErrorInvalidValue;
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), 0, s, ids, S, E, rows_per_item, counts,
-                       offsets, sorted, work, nwork, y, ldy, sh.n, ydt);
+                       offsets, sorted, work, nwork, y[0], ldy[0], b.p[0].sh.n, ydt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_moe_sb(sh, tab, (const uint16_t *)x, ldx, x_per_slot, topk, route, work, nwork, sorted,
-                       max_work, xb, y, ldy, ydt, s);
+  return launch_moe_sb(b, tab, x_per_slot, topk, route, work, nwork, sorted, max_work, ydt, s);
 }
 
 hipError_t launch_moe(const svq_handle *const *experts, int32_t count, int32_t E, const void *const *x,
@@ -1270,12 +1292,18 @@ hipError_t launch_moe(const svq_handle *const *experts, int32_t count, int32_t E
   const int S = (int)(m * topk);
   if (count < 1 || count > MOE_BATCH_MAX || count * E > MAX_EXPERTS) return hipErrorInvalidValue;
   if (S > MOE_EXACT_MAX_SLOTS) {
+    // one prep and one product launch for all projections while the prep
+    // does the routing; beyond, each projection with its own routing launch
+    if (S <= MOE_FUSED_MAX_SLOTS)
+      return launch_moe_grouped(experts, count, E, x, ldx, x_per_slot, ids, S, topk, y, ldy, ydt, ws,
+                                ws_bytes, s, need);
     size_t most = 0;
     for (int c = 0; c < count; ++c) {
       size_t nc = 0;
-      const hipError_t e = launch_moe_grouped(experts[c], E, ws ? x[c] : nullptr, ws ? ldx[c] : 0,
-                                              x_per_slot, ids, S, topk, ws ? y[c] : nullptr,
-                                              ws ? ldy[c] : 0, ydt, ws, ws_bytes, s, &nc);
+      const hipError_t e =
+          launch_moe_grouped(&experts[c], 1, E, ws ? &x[c] : nullptr, ws ? &ldx[c] : nullptr, x_per_slot,
+                             ids, S, topk, ws ? &y[c] : nullptr, ws ? &ldy[c] : nullptr, ydt, ws, ws_bytes,
+                             s, &nc);
       if (e != hipSuccess) return e;
       most = nc > most ? nc : most;
     }

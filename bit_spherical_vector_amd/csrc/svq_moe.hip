@@ -102,12 +102,18 @@ struct MoeRouteLds {
 // sorted slots for the product launch, block 0 the item count.
 template <bool ROUTE>
 __global__ __launch_bounds__(MOE_SB_PREP_THREADS) void moe_sb_prep_kernel(
-    MoeShape sh, ExpertTable tab, const uint16_t *__restrict__ x, int64_t ldx, int x_per_slot, int topk,
-    int vec, int rb, MoeRoute route, int32_t *__restrict__ work, int32_t *__restrict__ nwork,
-    int32_t *__restrict__ sorted, uint8_t *__restrict__ xa) {
+    MoeSbBatch b, ExpertTable tab, int x_per_slot, int topk, MoeRoute route, int32_t *__restrict__ work,
+    int32_t *__restrict__ nwork, int32_t *__restrict__ sorted) {
   constexpr int NT = MOE_SB_PREP_THREADS, USTEP = NT / 256;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ MoeRouteLds R;
+  const int pc = blockIdx.y;  // projection
+  const MoeSbProj &P = b.p[pc];
+  const MoeShape &sh = P.sh;
+  const uint16_t *__restrict__ x = P.x;
+  const int64_t ldx = P.ldx;
+  uint8_t *__restrict__ xa = P.xa;
+  const int rb = P.rb, vec = b.vec;
   const int tid = threadIdx.x, w = tid >> 6, L = tid & 63, s = L >> 4, rl = L & 15;
   const int wi = (int)blockIdx.x / MOE_SB_G, g = (int)blockIdx.x - wi * MOE_SB_G;
   int e, r0, rows;
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(MOE_SB_PREP_THREADS) void moe_sb_prep_kernel(
         atomicAdd(&R.cnt[my[j]], 1);
       } else if (j < C && q < S && q % (int)gridDim.x == (int)blockIdx.x) {
         // a slot with an id outside [0, E): its output row is zeros
-        char *yr = (char *)route.y + (size_t)q * route.ldy * (route.ydt == 0 ? 2 : 4);
+        char *yr = (char *)P.y + (size_t)q * P.ldy * (route.ydt == 0 ? 2 : 4);
         for (int c = 0; c < sh.n; ++c) store_out(yr, (size_t)c, 0.f, route.ydt);
       }
     }
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(MOE_SB_PREP_THREADS) void moe_sb_prep_kernel(
     }
     __syncthreads();
     const int nitems = R.items[E];
-    if (blockIdx.x == 0 && tid == 0) *nwork = nitems;
+    if (pc == 0 && blockIdx.x == 0 && tid == 0) *nwork = nitems;
     if (wi >= nitems) return;  // block-uniform
     if (tid < E && R.items[tid] <= wi && wi < R.items[tid + 1]) R.expert = tid;
     __syncthreads();
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(MOE_SB_PREP_THREADS) void moe_sb_prep_kernel(
       }
     }
     __syncthreads();
-    if (g == 0) {
+    if (pc == 0 && g == 0) {  // the routing is the same for every projection
       if (tid < rows) sorted[r0 + tid] = R.rows[tid];
       if (tid == 0) {
         work[3 * wi + 0] = e;
@@ -224,7 +230,7 @@ __global__ __launch_bounds__(MOE_SB_PREP_THREADS) void moe_sb_prep_kernel(
   }
   const int U = sh.units, kp = U * UNIT_SLOTS, k = sh.k;
   const int stride = moe_sb_prep_stride(kp);  // bytes per staged row
-  const uint16_t *perm = (const uint16_t *)(tab.base[e] + sh.off_perm);
+  const uint16_t *perm = (const uint16_t *)(tab.base[pc * sh.num_experts + e] + sh.off_perm);
   const int q = w & 3, u0 = w >> 2;
   const int chunks = kp / 8;  // 16-byte pieces of a staged row
   constexpr int BATCH = 4;
@@ -495,10 +501,16 @@ __device__ __forceinline__ void moe_sb_block(const MatView &w, int tg, int wi, i
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_sb_kernel(
-    MoeShape sh, ExpertTable tab, const int32_t *__restrict__ work, const int32_t *__restrict__ nwork,
-    const int32_t *__restrict__ sorted, const uint8_t *__restrict__ xa, void *__restrict__ y,
-    int64_t ldy, int ydt, int yvec) {
+    MoeSbBatch b, ExpertTable tab, const int32_t *__restrict__ work, const int32_t *__restrict__ nwork,
+    const int32_t *__restrict__ sorted, int ydt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int pc = blockIdx.y;  // projection
+  const MoeSbProj &P = b.p[pc];
+  const MoeShape &sh = P.sh;
+  const uint8_t *__restrict__ xa = P.xa;
+  void *__restrict__ y = P.y;
+  const int64_t ldy = P.ldy;
+  const int yvec = b.yvec;
   const int tgroups = (sh.n_tiles + MOE_SB_TILES - 1) / MOE_SB_TILES;
   // Blocks are dealt to the XCDs round-robin by index (block b runs on XCD
   // b % MOE_XCDS).  The active (item, column group) pairs are split into
@@ -511,7 +523,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   if (j >= share || l >= active) return;  // block-uniform, before any barrier
   const int wi = l / tgroups, tg = l - wi * tgroups;
   const int e = work[3 * wi], r0 = work[3 * wi + 1], rows = work[3 * wi + 2] - r0;
-  const MatView w = expert_view(sh, tab, e);
+  const MatView w = expert_view(sh, tab, pc * sh.num_experts + e);
   switch ((rows + 15) >> 4) {  // block-uniform
     case 1: moe_sb_block<1>(w, tg, wi, r0, rows, sorted, xa, y, ldy, ydt, yvec, smem); break;
     case 2: moe_sb_block<2>(w, tg, wi, r0, rows, sorted, xa, y, ldy, ydt, yvec, smem); break;
@@ -523,43 +535,46 @@ size_t moe_sb_xa_bytes(int max_work, int units) { return moe_sb_xa_off(max_work,
 
 // Rows of a group staged per pass of the prep launch: all 16 when they fit
 // the LDS budget, fewer for wide inputs (kp <= 65536 keeps it >= 1).
-static int moe_sb_prep_rb(int kp) {
+int moe_sb_prep_rb(int kp) {
   return std::max(1, std::min(16, MOE_SB_PREP_LDS / moe_sb_prep_stride(kp)));
 }
+size_t moe_sb_prep_lds(int kp) { return (size_t)moe_sb_prep_rb(kp) * moe_sb_prep_stride(kp); }
 
-hipError_t launch_moe_sb(const MoeShape &sh, const ExpertTable &tab, const uint16_t *x, int64_t ldx,
-                         int x_per_slot, int topk, const MoeRoute &route, int32_t *work,
-                         int32_t *nwork, int32_t *sorted, int max_work, uint8_t *xa, void *y,
-                         int64_t ldy, int ydt, hipStream_t s) {
-  const int kp = sh.units * UNIT_SLOTS;
-  const int rb = moe_sb_prep_rb(kp);
-  const size_t prep_lds = (size_t)rb * moe_sb_prep_stride(kp);
-  const int vec = ((uintptr_t)x % 16 == 0 && ldx % 8 == 0) ? 1 : 0;
-  const dim3 pgrid(max_work * MOE_SB_G), pblock(MOE_SB_PREP_THREADS);
+hipError_t launch_moe_sb(MoeSbBatch &b, const ExpertTable &tab, int x_per_slot, int topk,
+                         const MoeRoute &route, int32_t *work, int32_t *nwork, int32_t *sorted,
+                         int max_work, int ydt, hipStream_t s) {
+  if (b.count < 1 || b.count > MOE_BATCH_MAX || (!route.ids && b.count != 1)) return hipErrorInvalidValue;
+  size_t prep_lds = 0;
+  int tgroups = 1;
+  for (int c = 0; c < b.count; ++c) {
+    const int kp = b.p[c].sh.units * UNIT_SLOTS;
+    b.p[c].rb = moe_sb_prep_rb(kp);
+    prep_lds = std::max(prep_lds, moe_sb_prep_lds(kp));
+    tgroups = std::max(tgroups, (b.p[c].sh.n_tiles + MOE_SB_TILES - 1) / MOE_SB_TILES);
+  }
+  const dim3 pgrid(max_work * MOE_SB_G, b.count), pblock(MOE_SB_PREP_THREADS);
   hipError_t e;
   if (route.ids) {
-    if (route.slots > MOE_FUSED_MAX_SLOTS || sh.num_experts < 1 || sh.num_experts > MAX_EXPERTS)
+    if (route.slots > MOE_FUSED_MAX_SLOTS || b.p[0].sh.num_experts < 1 || b.p[0].sh.num_experts > MAX_EXPERTS)
       return hipErrorInvalidValue;
     e = allow_smem(moe_sb_prep_kernel<true>, (int)prep_lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_sb_prep_kernel<true>, pgrid, pblock, prep_lds, s, sh, tab, x, ldx, x_per_slot,
-                       topk, vec, rb, route, work, nwork, sorted, xa);
+    hipLaunchKernelGGL(moe_sb_prep_kernel<true>, pgrid, pblock, prep_lds, s, b, tab, x_per_slot, topk, route,
+                       work, nwork, sorted);
   } else {
     e = allow_smem(moe_sb_prep_kernel<false>, (int)prep_lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_sb_prep_kernel<false>, pgrid, pblock, prep_lds, s, sh, tab, x, ldx, x_per_slot,
-                       topk, vec, rb, route, work, nwork, sorted, xa);
+    hipLaunchKernelGGL(moe_sb_prep_kernel<false>, pgrid, pblock, prep_lds, s, b, tab, x_per_slot, topk,
+                       route, work, nwork, sorted);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = allow_smem(moe_sb_kernel, MOE_SB_SMEM);
   if (e != hipSuccess) return e;
-  const int tgroups = (sh.n_tiles + MOE_SB_TILES - 1) / MOE_SB_TILES;
-  const int esz = ydt == 0 ? 2 : 4;
-  const int yvec = ((uintptr_t)y % 16 == 0 && (ldy * esz) % 16 == 0) ? 1 : 0;
+  // every projection's active pairs fit: the grid covers the widest one
   const int blocks = (max_work * tgroups + MOE_XCDS - 1) / MOE_XCDS * MOE_XCDS;
-  hipLaunchKernelGGL(moe_sb_kernel, dim3(blocks), dim3(256), MOE_SB_SMEM, s, sh, tab, work,
-                     nwork, sorted, xa, y, ldy, ydt, yvec);
+  hipLaunchKernelGGL(moe_sb_kernel, dim3(blocks, b.count), dim3(256), MOE_SB_SMEM, s, b, tab, work, nwork,
+                     sorted, ydt);
   return hipGetLastError();
 }
 

@@ -216,8 +216,10 @@ svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts,
 /* svq_moe_linear_batched: svq_moe_linear for `count` (1..4) projections that
  * share the routing (expert_ids, m, topk, x_per_slot), e.g. the gate and up
  * projections of one FFN, which read the same token rows.  Up to 64 slots
- * every projection is served by one kernel launch; beyond that the
- * projections run one after another.
+ * one kernel launch serves every projection; up to 8192 slots one
+ * activation-staging launch and one product launch serve every projection
+ * (the routing is worked out once); beyond that the projections run one
+ * after another.
  *   experts:      host array of count pointers; experts[c] is a host array
  *                 of num_experts packed matrices of projection c (one n and k
  *                 per projection; projections may differ).
@@ -227,11 +229,12 @@ svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts,
  *                 (rows as in svq_moe_linear; the same pointer may repeat).
  *   y, ldy:       host arrays of count device outputs of type ydt,
  *                 [m*topk][ldy[c]] each, slot-major.
- *   workspace:    as for svq_moe_linear; its size (the query: workspace ==
- *                 NULL, which needs only experts, count, num_experts, m,
- *                 topk, x_per_slot and ydt; x, ldx, y, ldy may then be NULL)
- *                 is the largest any single projection needs, and the
- *                 projections use it in turn.
+ *   workspace:    as for svq_moe_linear; the query (workspace == NULL)
+ *                 needs only experts, count, num_experts, m, topk,
+ *                 x_per_slot and ydt (x, ldx, y, ldy may then be NULL).  Up
+ *                 to 8192 slots it holds the routing once and the staged
+ *                 activations of every projection; beyond, it is the
+ *                 largest any single projection needs, used in turn.
  * Results, numerics, the treatment of ids outside [0, num_experts) and the
  * error rules are those of count separate svq_moe_linear calls with the same
  * arguments, in order, on the same stream. */

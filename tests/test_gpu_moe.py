@@ -193,12 +193,15 @@ def _separate(svq, sets, xs, ids, topk, x_per_slot, dt):
             for p, x in zip(sets, xs)]
 
 
-@pytest.mark.parametrize("m,topk,x_per_slot", [(1, 3, 0), (4, 4, 1), (16, 4, 0), (40, 4, 0)])
+@pytest.mark.parametrize("m,topk,x_per_slot", [(1, 3, 0), (4, 4, 1), (16, 4, 0), (40, 4, 0), (37, 5, 1),
+                                                (2100, 4, 0)])
 def test_moe_batched_equals_separate_calls(svq, m, topk, x_per_slot):
     """Three projections of different shapes (the first two reading one
     input) in one svq_moe_linear_batched call give the outputs of three
     svq_moe_linear calls bit for bit: one launch up to 64 slots (m = 1, 4,
-    16), the projections in turn beyond (m = 40); some ids out of range."""
+    16), one staging and one product launch for all three up to 8192 slots
+    (160 and 185 slots), the projections in turn beyond (8400 slots); some
+    ids out of range."""
     n_exp = 6
     shapes = [(48, 520), (40, 520), (56, 264)]
     sets_in, sets, Ws = [], [], []
