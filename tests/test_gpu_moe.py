@@ -245,3 +245,31 @@ def test_moe128_m1_gate_up_batched(svq):
     want = _separate(svq, sets, [x, x], ids, synth.MOE_TOPK, False, torch.float32)
     for c in range(2):
         assert np.array_equal(out_to_f64(got[c]), want[c])
+
+
+@pytest.mark.parametrize("m,topk", [(3, 4), (40, 4)])
+def test_moe_batched_mixed_alignment(svq, m, topk):
+    """A batched call whose first projection has 16-byte aligned rows and
+    whose second has odd row strides (x and y), on the per-slot path (12
+    slots) and the grouped path (160 slots): every projection equals its
+    separate call bit for bit, and the padding columns of y are untouched."""
+    n_exp, n, k = 6, 44, 520
+    sets = [[svq.pack(synth.random_matrix(n, k, 6 + (e + c) % 3, seed=(55, c, e))) for e in range(n_exp)]
+            for c in range(2)]
+    ids = _ids(m, topk, n_exp, 56 + m)
+    x = synth.random_activations(m, k, seed=(57, m, 0))
+    d_ids = torch.from_numpy(ids).cuda()
+    xa = to_device_bf16(x)
+    xb_pad = torch.zeros((m, k + 3), dtype=torch.int16)
+    xb_pad[:, :k] = torch.from_numpy(x.view(np.int16))
+    xb = xb_pad.cuda().view(torch.bfloat16)[:, :k]
+    for dt in (torch.float32, torch.bfloat16):
+        ya = torch.empty((m * topk, n), dtype=dt, device="cuda")
+        yb_pad = torch.full((m * topk, n + 5), 7.0, dtype=dt, device="cuda")
+        yb = yb_pad[:, :n]
+        svq.MoeBatchedCall(sets, [xa, xb], d_ids, topk, False, [ya, yb])()
+        torch.cuda.synchronize()
+        assert torch.all(yb_pad[:, n:] == 7.0)
+        want = [svq.moe_linear(sets[c], xa, d_ids, topk, False, out_dtype=dt) for c in range(2)]
+        torch.cuda.synchronize()
+        assert torch.equal(ya, want[0]) and torch.equal(yb, want[1]), f"{dt}"
