@@ -273,3 +273,21 @@ def test_moe_batched_mixed_alignment(svq, m, topk):
         want = [svq.moe_linear(sets[c], xa, d_ids, topk, False, out_dtype=dt) for c in range(2)]
         torch.cuda.synchronize()
         assert torch.equal(ya, want[0]) and torch.equal(yb, want[1]), f"{dt}"
+
+
+@pytest.mark.parametrize("m", [8, 100])
+def test_moe_batched_full_expert_table(svq, m):
+    """Four projections of 64 experts each fill the 256-entry expert table of
+    the batched launches (per-slot path at 32 slots, grouped path at 400):
+    every projection equals its separate call bit for bit."""
+    n_exp, topk, shapes = 64, 4, [(40, 264), (24, 264), (40, 520), (16, 8)]
+    sets = [[svq.pack(synth.random_matrix(n, k, 6 + (e + c) % 3, seed=(58, c, e))) for e in range(n_exp)]
+            for c, (n, k) in enumerate(shapes)]
+    ids = _ids(m, topk, n_exp, 59 + m)
+    d_ids = torch.from_numpy(ids).cuda()
+    xs = [to_device_bf16(synth.random_activations(m, k, seed=(60, m, c))) for c, (_, k) in enumerate(shapes)]
+    got = svq.moe_linear_batched(sets, xs, d_ids, topk, False, out_dtype=torch.float32)
+    want = [svq.moe_linear(sets[c], xs[c], d_ids, topk, False, out_dtype=torch.float32) for c in range(4)]
+    torch.cuda.synchronize()
+    for c in range(4):
+        assert torch.equal(got[c], want[c]), f"projection {c}"
