@@ -235,9 +235,11 @@ svq_status svq_moe_linear(const svq_handle *experts, int32_t num_experts,
  *                 to 8192 slots it holds the routing once and the staged
  *                 activations of every projection; beyond, it is the
  *                 largest any single projection needs, used in turn.
- * Results, numerics, the treatment of ids outside [0, num_experts) and the
- * error rules are those of count separate svq_moe_linear calls with the same
- * arguments, in order, on the same stream. */
+ * The outputs must not overlap one another, the inputs or the workspace
+ * (inputs may be shared).  Results, numerics, the treatment of ids outside
+ * [0, num_experts) and the error rules are those of count separate
+ * svq_moe_linear calls with the same arguments, in order, on the same
+ * stream. */
 svq_status svq_moe_linear_batched(const svq_handle *const *experts, int32_t count,
                                   int32_t num_experts, const void *const *x,
                                   const int64_t *ldx, int32_t x_per_slot,
