@@ -303,26 +303,62 @@ svq_status svq_pack(const svq_matrix_desc *src, void *dst_dev, size_t *dst_bytes
 }
 
 // Exact path (m <= 4): plan the blocks of the gather and main launches over
-// `count` matrices.  R (row tiles per main block) is the largest that keeps
-// the block's units (R*U, split evenly between its 4 waves) near
-// GV_UNITS_PER_WAVE per wave, at most GV_MAX_R.  Jobs with the largest k
-// come first (their blocks run longest).  Returns the main launch's blocks.
+// `count` matrices.  R (row tiles per main block) starts as the largest that
+// keeps the block's units (R*U, split evenly between its 4 waves) near
+// GV_UNITS_PER_WAVE per wave, at most GV_MAX_R.  Three main blocks share a
+// compute unit (registers and LDS allow it at every m), so while the launch
+// has more blocks than that, the smallest blocks grow: a block left for a
+// second round would start only when a first-round block ends.  Jobs are
+// ordered by units per block, largest first: the dispatcher gives blocks i,
+// i + CUs and i + 2 CUs to one unit, so a large block runs beside smaller
+// ones.  Returns the main launch's blocks.
+static int device_cus();
 static int plan_gemv(GemvBatch &b, int *gather_blocks) {
-  for (int i = 1; i < b.count; ++i)
-    for (int j = i; j > 0 && b.job[j].w.k > b.job[j - 1].w.k; --j) {
-      const GemvJob t = b.job[j];
-      b.job[j] = b.job[j - 1];
-      b.job[j - 1] = t;
-    }
-  int begin = 0, gbegin = 0;
+  int R[GV_MAX_JOBS];
   for (int j = 0; j < b.count; ++j) {
     const int U = b.job[j].w.units;
-    int R = 4 * GV_UNITS_PER_WAVE / U;
-    R = R < 1 ? 1 : (R > GV_MAX_R ? GV_MAX_R : R);
-    b.job[j].R = R;
+    const int r = 4 * GV_UNITS_PER_WAVE / U;
+    R[j] = r < 1 ? 1 : (r > GV_MAX_R ? GV_MAX_R : r);
+  }
+  auto blocks_of = [&](int j) { return (b.job[j].w.n_tiles + R[j] - 1) / R[j]; };
+  auto total_blocks = [&]() {
+    int t = 0;
+    for (int j = 0; j < b.count; ++j) t += blocks_of(j);
+    return t;
+  };
+  const int slots = 3 * device_cus();
+  while (total_blocks() > slots) {
+    int best = -1;
+    for (int j = 0; j < b.count; ++j)
+      if (R[j] < GV_MAX_R && blocks_of(j) > 1 &&
+          (best < 0 || R[j] * b.job[j].w.units < R[best] * b.job[best].w.units))
+        best = j;
+    if (best < 0) break;
+    ++R[best];
+  }
+  // order by units per block, largest first (stable)
+  int order[GV_MAX_JOBS];
+  for (int j = 0; j < b.count; ++j) order[j] = j;
+  for (int i = 1; i < b.count; ++i)
+    for (int j = i; j > 0 && R[order[j]] * b.job[order[j]].w.units > R[order[j - 1]] * b.job[order[j - 1]].w.units; --j) {
+      const int t = order[j];
+      order[j] = order[j - 1];
+      order[j - 1] = t;
+    }
+  GemvJob sorted[GV_MAX_JOBS];
+  int Rs[GV_MAX_JOBS];
+  for (int j = 0; j < b.count; ++j) {
+    sorted[j] = b.job[order[j]];
+    Rs[j] = R[order[j]];
+  }
+  int begin = 0, gbegin = 0;
+  for (int j = 0; j < b.count; ++j) {
+    b.job[j] = sorted[j];
+    const int U = b.job[j].w.units;
+    b.job[j].R = Rs[j];
     b.job[j].block_begin = begin;
     b.starts.first[j] = begin;
-    begin += (b.job[j].w.n_tiles + R - 1) / R;
+    begin += (b.job[j].w.n_tiles + Rs[j] - 1) / Rs[j];
     b.gather_starts.first[j] = gbegin;
     gbegin += b.m * ((U + 3) / 4);
   }
@@ -343,7 +379,6 @@ static int plan_gemv(GemvBatch &b, int *gather_blocks) {
 // them fit at once.  So: about total / (3 CUs) items per block (R tiles of
 // U units), at most 3 CUs blocks, and jobs ordered by items per block,
 // largest first, which puts a large block beside two small ones.
-static int device_cus();
 static int plan_fused(GemvBatch &b) {
   int64_t total = 0;
   for (int j = 0; j < b.count; ++j) total += (int64_t)b.job[j].w.n_tiles * b.job[j].w.units;
