@@ -65,9 +65,9 @@ TRAFFIC = {
     # moe_sb_kernel, mean over the step's two launches (gate + up batched,
     # down; profiles/moe_sb_kernel_moe128_m512_counters.md)
     "moe128_m512": {"sources": ("svq_moe.hip", "svq_device.h"),
-                    "kernel_src_sha256": "bc7deb86318fef23",
-                    "fetch_kib": 97066.5, "fetch_factor": 2.0,
-                    "write_kib": 16982.2, "write_factor": 1.0},
+                    "kernel_src_sha256": "d6e406a7bf3c2fab",
+                    "fetch_kib": 89731.2, "fetch_factor": 2.0,
+                    "write_kib": 18303.4, "write_factor": 1.0},
 }
 
 

@@ -27,8 +27,8 @@
 //   expert's 1024-row table of RNE_bf16(R*D) rows, signs by XOR), and
 //   multiplied with all G row groups.  The activation fragments stream
 //   through a three-slot LDS ring, a quarter unit (fragments 4ci + q) per
-//   slot, filled by direct global-to-LDS loads two slices ahead; the last
-//   unit's padded half (k = 768) is skipped.  A wave owns
+//   slot, loaded into registers two slices ahead and written to the ring one
+//   slice ahead; the last unit's padded half (k = 768) is skipped.  A wave owns
 //   two row tiles and reads each activation fragment once for both.  The
 //   block's outputs are staged in LDS and leave as 16-byte row pieces.
 //   Blocks are mapped so that the column groups of one item share an XCD
@@ -312,24 +312,26 @@ __device__ __forceinline__ u4 moe_signed(const u4 &D, uint64_t S01, uint64_t S23
               D[2] ^ ((uint32_t)c23 & SM), D[3] ^ ((uint32_t)(c23 >> 32) & SM)};
 }
 
-typedef __attribute__((address_space(3))) void moe_lds_t;
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// the wave are outstanding (other counters left free); n < 64.
-constexpr int moe_vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
 // Workgroup barrier for the slice loop: this wave's LDS operations are
-// complete, then s_barrier (the slice's direct-to-LDS loads are waited for
-// explicitly before it).  The memory clobber keeps every memory access on
-// its side of the barrier.
+// complete, then s_barrier.  Outstanding global loads are not waited for:
+// each is waited for (by the compiler, per register) where its data is
+// used.  The memory clobber keeps every memory access on its side of the
+// barrier.
 __device__ __forceinline__ void moe_slice_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // One block's product over G row groups (see moe_sb_kernel).  The unit
 // loop runs in slices i = 4u + q (the fragments 4ci + q of unit u, all
-// groups): slice i is multiplied from LDS ring slot i % 3, which direct
-// global-to-LDS loads filled two slices earlier; one barrier per slice.
-// Codes are requested a whole unit ahead, slice by slice, into the registers
-// each slice frees.
+// groups): slice i is multiplied from LDS ring slot i % 3.  Its fragments
+// are loaded into registers during slice i - 2 and written to the slot
+// during slice i - 1; one barrier per slice.  Codes are requested a whole
+// unit ahead, slice by slice, into the registers each slice frees.
+//
+// Every global load here goes to registers, and the loads of one wave
+// complete in the order they were issued, so the wait for a slice's
+// fragments leaves the code loads issued after them in flight.  (With
+// direct global-to-LDS loads the slice barrier had to wait for every
+// outstanding load, codes included: those loads do not complete in order
+// with the others, and nothing tracks their data per register.)
 template <int G>
 __device__ __forceinline__ void moe_sb_block(const MatView &w, int tg, int wi, int r0, int rows,
                                              const int32_t *__restrict__ sorted,
@@ -364,32 +366,42 @@ __device__ __forceinline__ void moe_sb_block(const MatView &w, int tg, int wi, i
     c.L[q] = __builtin_nontemporal_load((const uint32_t *)(ub + PLANE_LOW + 64 * q + offs.L));
     c.H[q] = __builtin_nontemporal_load((const uint32_t *)(ub + PLANE_HIGH + 16 * q + offs.H));
   };
-  // slice i into ring slot i % 3: wave wv moves fragment 4 wv + q of each
-  // group (G loads of 1 KB per wave)
-  auto dma_slice = [&](int i) __attribute__((always_inline)) {
+  // slice i: wave wv moves fragment 4 wv + q of each group (G loads of
+  // 1 KB per wave) into rA, then from rA into ring slot i % 3
+  u4 rA[G];
+  auto load_slice = [&](int i) __attribute__((always_inline)) {
     const int u = i >> 2, q = i & 3;
-    uint8_t *b = smem + MOE_SB_OFF_A + (i % MOE_SB_RING) * MOE_SB_SLICE_BYTES + wv * 1024;
 #pragma unroll
     for (int g = 0; g < G; ++g)
-      __builtin_amdgcn_global_load_lds(
-          xa + moe_sb_xa_off(wi, U, u, g) + ((size_t)(4 * wv + q) * 64 + lane) * 16,
-          (moe_lds_t *)((uint8_t __attribute__((address_space(3))) *)b + g * 4096), 16, 0, 0);
+      rA[g] = *(const u4 *)(xa + moe_sb_xa_off(wi, U, u, g) + ((size_t)(4 * wv + q) * 64 + lane) * 16);
+  };
+  auto store_slice = [&](int i) __attribute__((always_inline)) {
+    uint8_t *b = smem + MOE_SB_OFF_A + (i % MOE_SB_RING) * MOE_SB_SLICE_BYTES + wv * 1024 + lane * 16;
+#pragma unroll
+    for (int g = 0; g < G; ++g) *(u4 *)(b + g * 4096) = rA[g];
   };
 
-  // table, the first two slices and the first unit's codes requested first
+  // table, slice 0 and the first unit's codes requested first
   u4 bt[4];
   const u4 *gbt = (const u4 *)(w.base + w.off_btab);
 #pragma unroll
   for (int i = 0; i < 4; ++i) bt[i] = gbt[tid + 256 * i];
-  dma_slice(0);
-  dma_slice(1);  // NS >= 4
+  load_slice(0);
   SbCodes cd[MOE_SB_TW];
 #pragma unroll
   for (int t = 0; t < MOE_SB_TW; ++t)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) unit_codes_q(cd[t], t, 0, q);
+    for (int q = 0; q < 3; ++q) unit_codes_q(cd[t], t, 0, q);
 #pragma unroll
   for (int i = 0; i < 4; ++i) *(u4 *)(smem + MOE_SB_OFF_BTAB + 16 * (tid + 256 * i)) = bt[i];
+  store_slice(0);
+  load_slice(1);  // NS >= 4
+  // the last record's codes after slice 1's loads, the order every slice
+  // keeps: the compiler's wait for slice 1 at the loop head then leaves
+  // them in flight (a different order on the way in would make it wait for
+  // everything there)
+#pragma unroll
+  for (int t = 0; t < MOE_SB_TW; ++t) unit_codes_q(cd[t], t, 0, 3);
 
   f4 C[MOE_SB_TW][G];
 #pragma unroll
@@ -405,15 +417,12 @@ __device__ __forceinline__ void moe_sb_block(const MatView &w, int tg, int wi, i
     constexpr int q = decltype(Q)::value, nci = decltype(NCI)::value;
     const int i = 4 * u + q;
     const int un = min(u + 1, U - 1);
-    // this wave's part of slice i has landed.  A count above zero would
-    // rely on the direct-to-LDS loads completing in order with the later
-    // (non-temporal) code loads, which does not hold: every outstanding load
-    // is waited for.
-    __builtin_amdgcn_s_waitcnt(moe_vmcnt_imm(0));
-    // every wave's part has landed, and every wave is done with slice
-    // i - 1, whose slot (i + 2) % 3 is refilled next
+    // every wave's part of slice i is in LDS (written during slice i - 1),
+    // and every wave is done with slice i - 2, whose slot (i + 1) % 3 is
+    // written now
     moe_slice_barrier();
-    if (i + 2 < NS) dma_slice(i + 2);
+    if (i + 1 < NS) store_slice(i + 1);
+    if (i + 2 < NS) load_slice(i + 2);
     const uint8_t *ab = smem + MOE_SB_OFF_A + (i % MOE_SB_RING) * MOE_SB_SLICE_BYTES;
     u4 D[MOE_SB_TW][4];
 #pragma unroll
