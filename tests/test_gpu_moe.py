@@ -136,6 +136,30 @@ def test_moe_out_of_range_ids_are_skipped(svq, m, topk):
                                         Ws[e], label=f"valid slots of expert {e}")
 
 
+@pytest.mark.parametrize("k", [8, 200, 256])
+def test_moe_grouped_single_half_unit(svq, k):
+    """Grouped path (120 slots) for matrices of one 512-slot unit whose real
+    slots end within its first half: every slice of the product is a half
+    slice and the full-unit loop runs zero times.  Against the oracle, both
+    output types, and one-hot columns against RNE_bf16 of the decoded
+    weights."""
+    n_exp, n, m, topk = 5, 40, 40, 3
+    mats = [synth.random_matrix(n, k, 6 + e % 3, seed=(49, e, k)) for e in range(n_exp)]
+    Ws = [so.decode_matrix(w.codes, n, k, w.bd, w.codebook, w.radius, w.perm) for w in mats]
+    pms = [svq.pack(w) for w in mats]
+    ids = _ids(m, topk, n_exp, 50 + k)
+    x = synth.random_activations(m, k, seed=(51, k, 0))
+    for dt in (torch.float32, torch.bfloat16):
+        y = _run_moe(svq, pms, x, ids, topk, 0, dt)
+        _check_slots(y, x, ids, topk, 0, Ws, range(n_exp), f"half-unit moe k={k} {dt}")
+    cols = np.arange(m) * 5 % k
+    xo = np.zeros_like(x)
+    xo[np.arange(m), cols] = 0x3F80
+    y = _run_moe(svq, pms, xo, ids, topk, 0, torch.float32)
+    for q, e in enumerate(ids):
+        assert equal_pm0(y[q], so.round_to_bf16(Ws[e][:, cols[q // topk]])).all(), f"slot {q}"
+
+
 @pytest.mark.parametrize("x_per_slot", [0, 1])
 def test_moe_grouped_strided_unaligned(svq, x_per_slot):
     """Grouped path (160 slots) with odd row strides for x and y (rows only
