@@ -80,6 +80,8 @@ def test_dense_layer_m1(svq, j):
     rng = np.random.default_rng(100 + j)
     cols = sorted(rng.choice(mat.k, 256, replace=False).tolist())
     _one_hot_check(svq, pm, W, cols, 4)
+    # and 24 of them through m = 1 itself (its own kernel body)
+    _one_hot_check(svq, pm, W, cols[::11], 1)
 
 
 @pytest.mark.parametrize("m", [4, 16])
@@ -271,6 +273,7 @@ def test_subnormal_codebook_entries_decode_exactly(svq):
     W = so.decode_matrix(mat.codes, mat.n, mat.k, mat.bd, mat.codebook, mat.radius, mat.perm)
     _one_hot_check(svq, pm, W, list(range(0, 512, 3)), 4)
     _one_hot_check(svq, pm, W, list(range(0, 512, 37)), 16)
+    _one_hot_check(svq, pm, W, list(range(0, 512, 7)), 1)
 
 
 @pytest.mark.parametrize("m", [1, 2, 4, 8])
