@@ -145,11 +145,14 @@ constexpr int GF_MAX_R = 8;
 // 2^(10-bd) fp32 radii) [0, gf_off_d(bd)); then the direction copies (bd <= 7: 16 copies
 // of 2^bd rows at a 256-byte stride; bd = 8: 8 copies of 256 rows at a
 // 128-byte stride, sharing their region with the activation staging row,
-// which is dead once the gather is done); then unit scales, cross-wave
-// partial sums, the permuted activations and (bd <= 7) the staging row.
+// which is dead once the gather is done; bd <= 7: the staging row follows the
+// copies), so the staging row starts at a fixed offset for each bd and the
+// gather's reads carry it as an instruction offset; then unit scales,
+// cross-wave partial sums and the permuted activations.
 constexpr int GF_OFF_R = 0;
 __host__ __device__ constexpr int gf_off_d(int bd) { return 256 << (10 - bd); }  // after 2^(10-bd) radii x 64 lanes
 __host__ __device__ constexpr int gf_dir_bytes(int bd) { return bd >= 8 ? 256 * 8 * 16 : (16 << bd) * 16; }
+__host__ __device__ constexpr int gf_off_stage(int bd) { return bd >= 8 ? gf_off_d(bd) : gf_off_d(bd) + gf_dir_bytes(bd); }
 struct GfLds {
   int scale, red, xp, stage, total;
 };
@@ -157,19 +160,14 @@ struct GfLds {
 __host__ __device__ inline GfLds gf_lds(int bd, int k, int units, int m, int r) {
   GfLds L;
   const int stage = (k * 2 + 15) & ~15, dir = gf_dir_bytes(bd);
-  int off = gf_off_d(bd) + (bd >= 8 ? (dir > stage ? dir : stage) : dir);
+  L.stage = gf_off_stage(bd);
+  int off = bd >= 8 ? gf_off_d(bd) + (dir > stage ? dir : stage) : L.stage + stage;
   L.scale = off;
   off += (units * m * 4 + 15) & ~15;
   L.red = off;
   off += r * GV_WAVES * 4 * 4 * 4 * m;
   L.xp = off;
   off += units * UNIT_SLOTS * 2 * m;
-  if (bd >= 8) {
-    L.stage = gf_off_d(bd);
-  } else {
-    L.stage = off;
-    off += stage;
-  }
   L.total = off;
   return L;
 }

@@ -669,6 +669,39 @@ __device__ __forceinline__ void byte_shr_to_b1(uint32_t &dst, uint32_t v) {
 typedef __attribute__((address_space(3))) const float lds_f32_t;
 __device__ __forceinline__ float lds_f32(uint32_t addr) { return *(lds_f32_t *)(size_t)addr; }
 
+// (16-bit word W of v) << SH in one VALU op (SDWA source select).
+template <int W, int SH>
+__device__ __forceinline__ uint32_t word_shl(uint32_t v) {
+  uint32_t r;
+  if (W == 0)
+    asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_0"
+        : "=v"(r) : "v"(v), "i"(SH));
+  else
+    asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+        : "=v"(r) : "v"(v), "i"(SH));
+  return r;
+}
+
+typedef __attribute__((address_space(3))) const uint16_t lds_u16_t;
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+// The two staged bf16 values one dword of permutation entries names:
+// x[c0] in bits 0..15, x[c1] in bits 16..31 (c0, c1: the dword's low and
+// high entries; the staging row starts at the constant STAGE).
+template <int STAGE>
+__device__ __forceinline__ uint32_t stage_pair(uint32_t pv) {
+  const uint32_t lo = *(lds_u16_t *)(size_t)(STAGE + word_shl<0, 1>(pv));
+  const uint32_t hi = *(lds_u16_t *)(size_t)(STAGE + word_shl<1, 1>(pv));
+  return lo | (hi << 16);
+}
+
+// Elementwise max of the magnitudes of two packed bf16 pairs, as 16-bit
+// integers (finite bf16 magnitudes order as their bit patterns).
+__device__ __forceinline__ uint32_t pk_absmax(uint32_t m, uint32_t p) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, m),
+                                                                __builtin_bit_cast(us2, p & 0x7FFF7FFFu)));
+}
+
 // dad: direction addresses (bd <= 7: byte 0 = the lane's copy * 16, byte 1
 // rewritten per code); rad: radius addresses (bd <= 7: byte 0 = 4 * lane,
 // byte 1 rewritten per code); loff: the lane's copy offset (bd = 8) and 4 * lane.
@@ -802,17 +835,38 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
 
   // fp16 copy of gathered unit uu of activation row a with its exact
   // power-of-two scale: 2^e with max|x_unit| * 2^e in [2^14, 2^15), i.e.
-  // e = 14 - ilogb(max) = 15 - (frexp exponent of max).
-  auto gather_store = [&](int a, int uu, const float (&v)[8], float mxw) __attribute__((always_inline)) {
+  // e = 14 - ilogb(max) = 15 - (frexp exponent of max).  pr: the lane's
+  // eight slots as packed bf16 pairs; mxb: bf16 bits of the unit's largest
+  // magnitude.
+  auto gather_store = [&](int a, int uu, const uint32_t (&pr)[4], uint32_t mxb) __attribute__((always_inline)) {
+    const float mxw = bf16_bits_to_f32(mxb);
     const int e = mxw > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mxw) : 0;
     u4 h;
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
-      const _Float16 lo = (_Float16)ldexpf(v[2 * l], e), hi = (_Float16)ldexpf(v[2 * l + 1], e);
+      const _Float16 lo = (_Float16)ldexpf(bf16_bits_to_f32(pr[l] & 0xFFFFu), e);
+      const _Float16 hi = (_Float16)ldexpf(__builtin_bit_cast(float, pr[l] & 0xFFFF0000u), e);
       h[l] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
     ((u4 *)(s_xp + (size_t)a * Kp))[64 * uu + lane] = h;
     if (lane == 0) s_scale[uu * M + a] = ldexpf(1.f, -e);
+  };
+  // The lane's eight slots of unit uu (permutation entries pv) as packed
+  // bf16 pairs, and their largest magnitude per pair half.  k is a multiple
+  // of 8, so a lane's eight slots are all inside k or all padding (zeros).
+  auto gather_pairs = [&](const u4 &pv, int uu, uint32_t (&pr)[4]) __attribute__((always_inline)) {
+    const bool valid = uu * UNIT_SLOTS + 8 * lane < K;
+    uint32_t m2 = 0;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const uint32_t p = stage_pair<gf_off_stage(BD)>(pv[l]);
+      pr[l] = valid ? p : 0u;
+      m2 = pk_absmax(m2, pr[l]);
+    }
+    return max(m2 & 0xFFFFu, m2 >> 16);
+  };
+  auto wave_max_bits = [](uint32_t b) __attribute__((always_inline)) {
+    return __builtin_bit_cast(uint32_t, wave_max(__builtin_bit_cast(float, b)));
   };
 
   // One activation row at a time: stage it in LDS, then every wave gathers
@@ -852,45 +906,24 @@ __device__ void gemv_fused_block(const MatView &w, const uint16_t *__restrict__ 
     const int npre = min(g_hi - g_lo + 1, GF_PRE_UNITS);  // may be <= 0
     auto gather_group = [&](auto J0, auto NJ) __attribute__((always_inline)) {
       constexpr int j0 = decltype(J0)::value, nj = decltype(NJ)::value;
-      float v[nj][8], mx[nj];
+      uint32_t pr[nj][4], mx[nj];
 #pragma unroll
-      for (int jj = 0; jj < nj; ++jj) {
-        const int p0 = (g_lo + j0 + jj) * UNIT_SLOTS + 8 * lane;
-        mx[jj] = 0.f;
+      for (int jj = 0; jj < nj; ++jj) mx[jj] = gather_pairs(pvec[j0 + jj], g_lo + j0 + jj, pr[jj]);
 #pragma unroll
-        for (int l = 0; l < 4; ++l) {
-          const uint32_t c0 = pvec[j0 + jj][l] & 0xFFFFu, c1 = pvec[j0 + jj][l] >> 16;
-          // perm is zero padded to the unit width, so c0, c1 < K always
-          const float g0 = bf16_bits_to_f32(s_stage[c0]), g1 = bf16_bits_to_f32(s_stage[c1]);
-          v[jj][2 * l] = (p0 + 2 * l < K) ? g0 : 0.f;
-          v[jj][2 * l + 1] = (p0 + 2 * l + 1 < K) ? g1 : 0.f;
-          mx[jj] = fmaxf(mx[jj], fmaxf(fabsf(v[jj][2 * l]), fabsf(v[jj][2 * l + 1])));
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < nj; ++jj) mx[jj] = wave_max(mx[jj]);
+      for (int jj = 0; jj < nj; ++jj) mx[jj] = wave_max_bits(mx[jj]);
 #pragma unroll
       for (int jj = 0; jj < nj; ++jj)
-        if (j0 + jj < npre) gather_store(a, g_lo + j0 + jj, v[jj], mx[jj]);
+        if (j0 + jj < npre) gather_store(a, g_lo + j0 + jj, pr[jj], mx[jj]);
     };
     static_assert(GF_PRE_UNITS == 5, "gather groups cover 2 + 3 units");
     if (npre > 0) gather_group(std::integral_constant<int, 0>(), std::integral_constant<int, 2>());
     if (npre > 2) gather_group(std::integral_constant<int, 2>(), std::integral_constant<int, 3>());
     // units beyond the prefetched ones (k > 4 * GF_PRE_UNITS * 512 only)
     for (int uu = g_lo + GF_PRE_UNITS; uu <= g_hi; ++uu) {
-      const int p0 = uu * UNIT_SLOTS + 8 * lane;
-      const u4 pv = *(const u4 *)(perm + p0);
-      float w8[8];
-      float m1 = 0.f;
-#pragma unroll
-      for (int l = 0; l < 4; ++l) {
-        const uint32_t c0 = pv[l] & 0xFFFFu, c1 = pv[l] >> 16;
-        const float g0 = bf16_bits_to_f32(s_stage[c0]), g1 = bf16_bits_to_f32(s_stage[c1]);
-        w8[2 * l] = (p0 + 2 * l < K) ? g0 : 0.f;
-        w8[2 * l + 1] = (p0 + 2 * l + 1 < K) ? g1 : 0.f;
-        m1 = fmaxf(m1, fmaxf(fabsf(w8[2 * l]), fabsf(w8[2 * l + 1])));
-      }
-      gather_store(a, uu, w8, wave_max(m1));
+      const u4 pv = *(const u4 *)(perm + uu * UNIT_SLOTS + 8 * lane);
+      uint32_t pr[4];
+      const uint32_t mxb = gather_pairs(pv, uu, pr);
+      gather_store(a, uu, pr, wave_max_bits(mxb));
     }
   }
   if constexpr (BD == 8) {
