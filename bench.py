@@ -49,8 +49,8 @@ COLD_BYTES = 600 << 20  # > 2 x 256 MB MALL
 TRAFFIC = {
     # gemv_fused_kernel (profiles/gemv_fused_kernel_layer4b_m1_counters.md)
     "layer4b_m1": {"sources": ("svq_kernels.hip", "svq_device.h"),
-                   "kernel_src_sha256": "00ba23309e3a188c",
-                   "fetch_kib": 14675.8, "fetch_factor": 2.0,
+                   "kernel_src_sha256": "4a04759af7c578a4",
+                   "fetch_kib": 14658.1, "fetch_factor": 2.0,
                    "write_kib": 60.0, "write_factor": 1.0},
     # sb_gemm_kernel (profiles/sb_gemm_kernel_layer4b_m16_counters.md)
     "layer4b_m16": {"sources": ("svq_small.hip", "svq_device.h"),
