@@ -562,10 +562,37 @@ __device__ void dq_tile_w8(const DqTile &T, uint8_t *smem) {
     rB = nB;
   }
 
-  // Epilogue through LDS (the operand stages are free now): each wave turns
+  // Epilogue.  A tile whose rows and columns all lie inside the output is
+  // stored straight from the accumulators: for each accumulator element the
+  // lanes 0..31 (and 32..63) write 32 consecutive columns of one output row,
+  // 64 or 128 contiguous bytes per store, with no LDS round trip and no
+  // barrier (measured: the staging through LDS cost ~16 us of a 308 us
+  // prefill step).
+  if (T.m_valid >= 256 && rt0 * UNIT_ROWS + P_BN <= T.nlim && T.ymap == nullptr) {
+    const int esz = T.bf ? 2 : 4;
+    const size_t rs = (size_t)T.ldy * esz;  // bytes per output row
+    // row (e & 3) + 8(e >> 2) + 4(lane >> 5) of 32-row block i, column
+    // 32jj + (lane & 31) of the wave's 64 columns
+    char *yb = (char *)T.y + (size_t)(m0 + TM * wm + 4 * (lane >> 5)) * rs +
+               (size_t)(rt0 * UNIT_ROWS + TN * wn + (lane & 31)) * esz;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        char *p = yb + (size_t)(32 * i + (e & 3) + 8 * (e >> 2)) * rs;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          if (T.bf) ((uint16_t *)p)[32 * jj] = f32_to_bf16_bits(C[i][jj][e]);
+          else ((float *)p)[32 * jj] = C[i][jj][e];
+        }
+      }
+    return;
+  }
+  // Otherwise through LDS (the operand stages are free now): each wave turns
   // its TM x TN accumulator tile into output-type rows in a private 16 KB
   // region, as many 32-row blocks per pass as fit, and writes them back as
-  // whole 16-byte pieces of consecutive output columns.
+  // whole 16-byte pieces of consecutive output columns (element-wise at the
+  // output's edges).
   {
     uint8_t *s_c = smem + wv * 16384;
     void *const ybase = T.y;
