@@ -59,8 +59,8 @@ TRAFFIC = {
                     "write_kib": 1604.0, "write_factor": 1.0},
     # prefill_w8_kernel (profiles/prefill_w8_kernel_prefill_m2048_counters.md)
     "prefill_m2048": {"sources": ("svq_prefill.hip", "svq_device.h"),
-                      "kernel_src_sha256": "875da4cd24cf768d",
-                      "fetch_kib": 127723.4, "fetch_factor": 2.0,
+                      "kernel_src_sha256": "789442236a37f692",
+                      "fetch_kib": 127799.6, "fetch_factor": 2.0,
                       "write_kib": 88064.0, "write_factor": 1.0},
     # moe_sb_kernel, mean over the step's two launches (gate + up batched,
     # down; profiles/moe_sb_kernel_moe128_m512_counters.md)
