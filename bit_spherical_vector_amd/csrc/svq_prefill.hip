@@ -313,53 +313,59 @@ __device__ __forceinline__ void dq_tile(const DqTile &T, uint8_t *smem) {
   // whole 16-byte pieces of consecutive output columns.
   __syncthreads();
   {
-    uint8_t *s_c = smem + wv * 16384;
-    void *const ybase = T.y;
-    const int64_t yld = T.ldy;
-    const int nlim = T.nlim;
-    const bool yv = T.yvec;
-    const bool bf = T.bf;
-    const int esz = bf ? 2 : 4;
-    const int ipp = min(NI, 16384 / (32 * TN * esz));  // 32-row blocks per pass
-    const int cpr = TN * esz / 16;                      // 16-byte pieces per row
-    const int per = 16 / esz;                           // columns per piece
+    // the output type is a template parameter of the body: a test per
+    // element in the unrolled loops left a branch at every store
+    auto epi = [&](auto BF) __attribute__((always_inline)) {
+      uint8_t *s_c = smem + wv * 16384;
+      void *const ybase = T.y;
+      const int64_t yld = T.ldy;
+      const int nlim = T.nlim;
+      const bool yv = T.yvec;
+      constexpr bool bf = decltype(BF)::value;
+      constexpr int esz = bf ? 2 : 4;
+      constexpr int ipp = NI < 16384 / (32 * TN * esz) ? NI : 16384 / (32 * TN * esz);  // 32-row blocks per pass
+      constexpr int cpr = TN * esz / 16;                     // 16-byte pieces per row
+      constexpr int per = 16 / esz;                         // columns per piece
 #pragma unroll
-    for (int i0 = 0; i0 < NI; ++i0) {
-      if (i0 % ipp != 0) continue;
+      for (int i0 = 0; i0 < NI; ++i0) {
+        if (i0 % ipp != 0) continue;
 #pragma unroll
-      for (int ii = 0; ii < NI; ++ii) {
-        if (ii >= ipp || i0 + ii >= NI) continue;
+        for (int ii = 0; ii < NI; ++ii) {
+          if (ii >= ipp || i0 + ii >= NI) continue;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+          for (int j = 0; j < NJ; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = 32 * ii + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5), c = 32 * j + (lane & 31);
-            const float val = C[i0 + ii][j][e];
-            if (bf) ((uint16_t *)s_c)[r * TN + c] = f32_to_bf16_bits(val);
-            else ((float *)s_c)[r * TN + c] = val;
-          }
-      }
-      __syncthreads();
-      for (int q = lane; q < 32 * ipp * cpr; q += 64) {
-        const int r = q / cpr, ch = q % cpr;
-        const int rr = TM * wm + 32 * i0 + r;  // row of the tile
-        const int n0 = rt0 * UNIT_ROWS + TN * wn + ch * per;
-        if (rr >= T.m_valid) continue;
-        const int orow = T.ymap ? T.ymap[rr] : m0 + rr;
-        const u4 v = *(const u4 *)(s_c + r * TN * esz + ch * 16);
-        char *dst = (char *)ybase + ((size_t)orow * yld + n0) * esz;
-        if (yv && n0 + per <= nlim) {
-          *(u4 *)dst = v;
-        } else {
-          for (int l = 0; l < per; ++l) {
-            if (n0 + l >= nlim) break;
-            if (bf) ((uint16_t *)dst)[l] = (uint16_t)(v[l >> 1] >> (16 * (l & 1)));
-            else ((uint32_t *)dst)[l] = v[l];
+            for (int e = 0; e < 16; ++e) {
+              const int r = 32 * ii + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5), c = 32 * j + (lane & 31);
+              const float val = C[i0 + ii][j][e];
+              if constexpr (bf) ((uint16_t *)s_c)[r * TN + c] = f32_to_bf16_bits(val);
+              else ((float *)s_c)[r * TN + c] = val;
+            }
+        }
+        __syncthreads();
+        for (int q = lane; q < 32 * ipp * cpr; q += 64) {
+          const int r = q / cpr, ch = q % cpr;
+          const int rr = TM * wm + 32 * i0 + r;  // row of the tile
+          const int n0 = rt0 * UNIT_ROWS + TN * wn + ch * per;
+          if (rr >= T.m_valid) continue;
+          const int orow = T.ymap ? T.ymap[rr] : m0 + rr;
+          const u4 v = *(const u4 *)(s_c + r * TN * esz + ch * 16);
+          char *dst = (char *)ybase + ((size_t)orow * yld + n0) * esz;
+          if (yv && n0 + per <= nlim) {
+            *(u4 *)dst = v;
+          } else {
+            for (int l = 0; l < per; ++l) {
+              if (n0 + l >= nlim) break;
+              if constexpr (bf) ((uint16_t *)dst)[l] = (uint16_t)(v[l >> 1] >> (16 * (l & 1)));
+              else ((uint32_t *)dst)[l] = v[l];
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
-    }
+    };
+    if (T.bf) epi(std::true_type());
+    else epi(std::false_type());
   }
 }
 
@@ -569,23 +575,30 @@ __device__ void dq_tile_w8(const DqTile &T, uint8_t *smem) {
   // barrier (measured: the staging through LDS cost ~16 us of a 308 us
   // prefill step).
   if (T.m_valid >= 256 && rt0 * UNIT_ROWS + P_BN <= T.nlim && T.ymap == nullptr) {
-    const int esz = T.bf ? 2 : 4;
-    const size_t rs = (size_t)T.ldy * esz;  // bytes per output row
-    // row (e & 3) + 8(e >> 2) + 4(lane >> 5) of 32-row block i, column
-    // 32jj + (lane & 31) of the wave's 64 columns
-    char *yb = (char *)T.y + (size_t)(m0 + TM * wm + 4 * (lane >> 5)) * rs +
-               (size_t)(rt0 * UNIT_ROWS + TN * wn + (lane & 31)) * esz;
+    // the output type is decided once, outside the unrolled stores (a test
+    // per element left a branch and an exec-mask update at every store)
+    auto store_tile = [&](auto BF) __attribute__((always_inline)) {
+      constexpr bool bf = decltype(BF)::value;
+      constexpr int esz = bf ? 2 : 4;
+      const size_t rs = (size_t)T.ldy * esz;  // bytes per output row
+      // row (e & 3) + 8(e >> 2) + 4(lane >> 5) of 32-row block i, column
+      // 32jj + (lane & 31) of the wave's 64 columns
+      char *yb = (char *)T.y + (size_t)(m0 + TM * wm + 4 * (lane >> 5)) * rs +
+                 (size_t)(rt0 * UNIT_ROWS + TN * wn + (lane & 31)) * esz;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        char *p = yb + (size_t)(32 * i + (e & 3) + 8 * (e >> 2)) * rs;
+        for (int e = 0; e < 16; ++e) {
+          char *p = yb + (size_t)(32 * i + (e & 3) + 8 * (e >> 2)) * rs;
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          if (T.bf) ((uint16_t *)p)[32 * jj] = f32_to_bf16_bits(C[i][jj][e]);
-          else ((float *)p)[32 * jj] = C[i][jj][e];
+          for (int jj = 0; jj < NJ; ++jj) {
+            if constexpr (bf) ((uint16_t *)p)[32 * jj] = f32_to_bf16_bits(C[i][jj][e]);
+            else ((float *)p)[32 * jj] = C[i][jj][e];
+          }
         }
-      }
+    };
+    if (T.bf) store_tile(std::true_type());
+    else store_tile(std::false_type());
     return;
   }
   // Otherwise through LDS (the operand stages are free now): each wave turns
@@ -594,53 +607,59 @@ __device__ void dq_tile_w8(const DqTile &T, uint8_t *smem) {
   // whole 16-byte pieces of consecutive output columns (element-wise at the
   // output's edges).
   {
-    uint8_t *s_c = smem + wv * 16384;
-    void *const ybase = T.y;
-    const int64_t yld = T.ldy;
-    const int nlim = T.nlim;
-    const bool yv = T.yvec;
-    const bool bf16o = T.bf;
-    const int esz = bf16o ? 2 : 4;
-    const int ipp = min(NI, 16384 / (32 * TN * esz));  // 32-row blocks per pass
-    const int cpr = TN * esz / 16;                      // 16-byte pieces per row
-    const int per = 16 / esz;                           // columns per piece
+    // the output type is a template parameter of the body: a test per
+    // element in the unrolled loops left a branch at every store
+    auto epi = [&](auto BF) __attribute__((always_inline)) {
+      uint8_t *s_c = smem + wv * 16384;
+      void *const ybase = T.y;
+      const int64_t yld = T.ldy;
+      const int nlim = T.nlim;
+      const bool yv = T.yvec;
+      constexpr bool bf16o = decltype(BF)::value;
+      constexpr int esz = bf16o ? 2 : 4;
+      constexpr int ipp = NI < 16384 / (32 * TN * esz) ? NI : 16384 / (32 * TN * esz);  // 32-row blocks per pass
+      constexpr int cpr = TN * esz / 16;                     // 16-byte pieces per row
+      constexpr int per = 16 / esz;                         // columns per piece
 #pragma unroll
-    for (int i0 = 0; i0 < NI; ++i0) {
-      if (i0 % ipp != 0) continue;
+      for (int i0 = 0; i0 < NI; ++i0) {
+        if (i0 % ipp != 0) continue;
 #pragma unroll
-      for (int ii = 0; ii < NI; ++ii) {
-        if (ii >= ipp || i0 + ii >= NI) continue;
+        for (int ii = 0; ii < NI; ++ii) {
+          if (ii >= ipp || i0 + ii >= NI) continue;
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
+          for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = 32 * ii + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5), cc = 32 * jj + (lane & 31);
-            const float val = C[i0 + ii][jj][e];
-            if (bf16o) ((uint16_t *)s_c)[r * TN + cc] = f32_to_bf16_bits(val);
-            else ((float *)s_c)[r * TN + cc] = val;
-          }
-      }
-      __syncthreads();
-      for (int q = lane; q < 32 * ipp * cpr; q += 64) {
-        const int r = q / cpr, ch = q % cpr;
-        const int rr = TM * wm + 32 * i0 + r;  // row of the tile
-        const int n0 = rt0 * UNIT_ROWS + TN * wn + ch * per;
-        if (rr >= T.m_valid) continue;
-        const int orow = T.ymap ? T.ymap[rr] : m0 + rr;
-        const u4 vv = *(const u4 *)(s_c + r * TN * esz + ch * 16);
-        char *dst = (char *)ybase + ((size_t)orow * yld + n0) * esz;
-        if (yv && n0 + per <= nlim) {
-          *(u4 *)dst = vv;
-        } else {
-          for (int l = 0; l < per; ++l) {
-            if (n0 + l >= nlim) break;
-            if (bf16o) ((uint16_t *)dst)[l] = (uint16_t)(vv[l >> 1] >> (16 * (l & 1)));
-            else ((uint32_t *)dst)[l] = vv[l];
+            for (int e = 0; e < 16; ++e) {
+              const int r = 32 * ii + (e & 3) + 8 * (e >> 2) + 4 * (lane >> 5), cc = 32 * jj + (lane & 31);
+              const float val = C[i0 + ii][jj][e];
+              if constexpr (bf16o) ((uint16_t *)s_c)[r * TN + cc] = f32_to_bf16_bits(val);
+              else ((float *)s_c)[r * TN + cc] = val;
+            }
+        }
+        __syncthreads();
+        for (int q = lane; q < 32 * ipp * cpr; q += 64) {
+          const int r = q / cpr, ch = q % cpr;
+          const int rr = TM * wm + 32 * i0 + r;  // row of the tile
+          const int n0 = rt0 * UNIT_ROWS + TN * wn + ch * per;
+          if (rr >= T.m_valid) continue;
+          const int orow = T.ymap ? T.ymap[rr] : m0 + rr;
+          const u4 vv = *(const u4 *)(s_c + r * TN * esz + ch * 16);
+          char *dst = (char *)ybase + ((size_t)orow * yld + n0) * esz;
+          if (yv && n0 + per <= nlim) {
+            *(u4 *)dst = vv;
+          } else {
+            for (int l = 0; l < per; ++l) {
+              if (n0 + l >= nlim) break;
+              if constexpr (bf16o) ((uint16_t *)dst)[l] = (uint16_t)(vv[l >> 1] >> (16 * (l & 1)));
+              else ((uint32_t *)dst)[l] = vv[l];
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
-    }
+    };
+    if (T.bf) epi(std::true_type());
+    else epi(std::false_type());
   }
 }
 
