@@ -472,41 +472,49 @@ __device__ __forceinline__ void moe_sb_block(const MatView &w, int tg, int wi, i
   // n0 + nb (n0 = 128 tg), row stride padded by 16 bytes, then 16-byte pieces
   // of whole rows go to y.  Accumulator element i of lane L is activation
   // row 16g + 4(L >> 4) + i, column 16 (tile within the block) + (L & 15).
-  const int esz = ydt == 0 ? 2 : 4;
-  const int ostride = 128 * esz + 16;
-  uint8_t *ob = smem + MOE_SB_OFF_A;
-  __syncthreads();  // every wave is done with the staged activations
+  // The output type is a template parameter of the store loops (a test per
+  // element left a branch at every store).
+  auto epi = [&](auto BF) __attribute__((always_inline)) {
+    constexpr bool bf = decltype(BF)::value;
+    constexpr int esz = bf ? 2 : 4;
+    const int ostride = 128 * esz + 16;
+    uint8_t *ob = smem + MOE_SB_OFF_A;
+    __syncthreads();  // every wave is done with the staged activations
 #pragma unroll
-  for (int t = 0; t < MOE_SB_TW; ++t) {
-    const int nb = 16 * (MOE_SB_TW * wv + t) + (lane & 15);
+    for (int t = 0; t < MOE_SB_TW; ++t) {
+      const int nb = 16 * (MOE_SB_TW * wv + t) + (lane & 15);
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint8_t *o = ob + (16 * g + 4 * (int)s + i) * ostride;
-        if (ydt == 0) *(uint16_t *)(o + 2 * nb) = f32_to_bf16_bits(C[t][g][i]);
-        else *(float *)(o + 4 * nb) = C[t][g][i];
-      }
-  }
-  __syncthreads();
-  const int n0 = tg * (MOE_SB_TILES * UNIT_ROWS), per = 16 / esz;  // elements per piece
-  const int pieces = 128 / per, total = rows * pieces;
-  constexpr int PER_THREAD = 16 * G * 32 / 256;  // pieces of 16 G rows of f32, per thread
-#pragma unroll
-  for (int i = 0; i < PER_THREAD; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c / pieces, pc = c - r * pieces, n = n0 + pc * per;
-    if (c >= total || n >= w.n) continue;
-    const int slot = sorted[r0 + r];
-    const uint8_t *src = ob + r * ostride + pc * 16;
-    uint8_t *dst = (uint8_t *)y + ((size_t)slot * ldy + n) * esz;
-    if (yvec && n + per <= w.n) {
-      *(u4 *)dst = *(const u4 *)src;
-    } else {
-      for (int e = 0; e < per && n + e < w.n; ++e)
-        for (int b = 0; b < esz; ++b) dst[e * esz + b] = src[e * esz + b];
+        for (int i = 0; i < 4; ++i) {
+          uint8_t *o = ob + (16 * g + 4 * (int)s + i) * ostride;
+          if constexpr (bf) *(uint16_t *)(o + 2 * nb) = f32_to_bf16_bits(C[t][g][i]);
+          else *(float *)(o + 4 * nb) = C[t][g][i];
+        }
     }
-  }
+    __syncthreads();
+    const int n0 = tg * (MOE_SB_TILES * UNIT_ROWS);
+    constexpr int per = 16 / esz;  // elements per piece
+    const int pieces = 128 / per, total = rows * pieces;
+    constexpr int PER_THREAD = 16 * G * 32 / 256;  // pieces of 16 G rows of f32, per thread
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / pieces, pc = c - r * pieces, n = n0 + pc * per;
+      if (c >= total || n >= w.n) continue;
+      const int slot = sorted[r0 + r];
+      const uint8_t *src = ob + r * ostride + pc * 16;
+      uint8_t *dst = (uint8_t *)y + ((size_t)slot * ldy + n) * esz;
+      if (yvec && n + per <= w.n) {
+        *(u4 *)dst = *(const u4 *)src;
+      } else {
+        for (int e = 0; e < per && n + e < w.n; ++e)
+          for (int b = 0; b < esz; ++b) dst[e * esz + b] = src[e * esz + b];
+      }
+    }
+  };
+  if (ydt == 0) epi(std::true_type());
+  else epi(std::false_type());
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_sb_kernel(
