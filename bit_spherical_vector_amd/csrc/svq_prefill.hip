@@ -828,16 +828,14 @@ __device__ __forceinline__ void dq_gather_rows(const uint16_t *const *src, int r
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {
       const int c = cb + bb * cstep;
-      if (c >= c_hi) break;
-      // perm is zero padded to the unit width, so every index is < k
+      // perm is zero padded to the unit width, so every index is < k and
+      // the reads need no guard; k is a multiple of 8, so a chunk is inside
+      // k or all padding (zeros)
       u4 v;
 #pragma unroll
-      for (int l = 0; l < 4; ++l) {
-        const uint32_t lo = live && 8 * c + 2 * l < K ? row[pv[bb][l] & 0xFFFFu] : 0u;
-        const uint32_t hi = live && 8 * c + 2 * l + 1 < K ? row[pv[bb][l] >> 16] : 0u;
-        v[l] = lo | (hi << 16);
-      }
-      *(u4 *)(xb + xb_frag_offset(xrow0 + rr, 8 * c, S)) = v;
+      for (int l = 0; l < 4; ++l) v[l] = (uint32_t)row[pv[bb][l] & 0xFFFFu] | ((uint32_t)row[pv[bb][l] >> 16] << 16);
+      if (!live || 8 * c >= K) v = (u4){0u, 0u, 0u, 0u};
+      if (c < c_hi) *(u4 *)(xb + xb_frag_offset(xrow0 + rr, 8 * c, S)) = v;
     }
   }
 }
