@@ -59,15 +59,15 @@ TRAFFIC = {
                     "write_kib": 1604.0, "write_factor": 1.0},
     # prefill_w8_kernel (profiles/prefill_w8_kernel_prefill_m2048_counters.md)
     "prefill_m2048": {"sources": ("svq_prefill.hip", "svq_device.h"),
-                      "kernel_src_sha256": "789442236a37f692",
-                      "fetch_kib": 127799.6, "fetch_factor": 2.0,
+                      "kernel_src_sha256": "4c0343ef209bd03b",
+                      "fetch_kib": 127727.7, "fetch_factor": 2.0,
                       "write_kib": 88064.0, "write_factor": 1.0},
     # moe_sb_kernel, mean over the step's two launches (gate + up batched,
     # down; profiles/moe_sb_kernel_moe128_m512_counters.md)
     "moe128_m512": {"sources": ("svq_moe.hip", "svq_device.h"),
-                    "kernel_src_sha256": "d6e406a7bf3c2fab",
-                    "fetch_kib": 89731.2, "fetch_factor": 2.0,
-                    "write_kib": 18303.4, "write_factor": 1.0},
+                    "kernel_src_sha256": "09001c6073b1e389",
+                    "fetch_kib": 89439.5, "fetch_factor": 2.0,
+                    "write_kib": 16928.9, "write_factor": 1.0},
 }
 
 
