@@ -216,6 +216,19 @@ def test_strided_input_output(svq, m):
     assert_within_tolerance(y, y64, x, W, label="strided")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_prefill_full_tiles_strided(svq, dt):
+    """The 256-row tile's full output tiles store straight from the
+    accumulators: 512 tokens x 512 rows is four full tiles, written through
+    a row stride wider than n (padding columns must stay untouched)."""
+    mat = synth.random_matrix(512, 1024, 7, seed=(36, 0, 0))
+    x = synth.random_activations(512, 1024, seed=(36, 0, 1))
+    pm = svq.pack(mat)
+    y64, W = so.linear_from_inputs(mat, x)
+    y = _run(svq, pm, x, dt, ldx_pad=8, ldy_pad=24)
+    assert_within_tolerance(y, y64, x, W, label=f"prefill full tiles, strided {dt}")
+
+
 @pytest.mark.parametrize("m", [1, 2, 4, 8])
 def test_unaligned_activations(svq, m):
     """Rows that do not start 16-byte aligned (odd row stride, base pointer
